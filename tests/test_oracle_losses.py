@@ -1,0 +1,279 @@
+"""Pins of the oracle's BCE / CE / SGD definitions.
+
+Each pin is independent of the oracle's own formula: closed forms at A = 0 and
+E = 0 (worked out by hand, evaluated with explicit loops), torch's library
+BCE-with-logits / cross-entropy with autograd, central finite differences,
+the dense+sparse identity named by Cut BCE §I-B, invariants, and the printed
+logit-memory figure of Cut BCE §I-A.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import head_loss as H
+from oracle.formats import decode_fp8_e4m3fn, encode_fp8_e4m3fn
+from oracle.targets import canonical_csr, dense_labels
+
+
+def _problem(T, D, V, seed, std=None, L=4, pad=0, mask_frac=0.25):
+    rng = np.random.default_rng(seed)
+    s = 1.0 / math.sqrt(D) if std is None else std
+    A = rng.normal(0, s, (T, D))
+    E = rng.normal(0, s, (V, D))
+    rows = [rng.integers(0, V, size=L).tolist() for _ in range(T)]   # pads, repeats allowed
+    row_ptr = np.zeros(T + 1, np.int64)
+    row_ptr[1:] = np.cumsum([len(r) for r in rows])
+    ids = np.array([v for r in rows for v in r], np.int64)
+    mask = (rng.random(T) >= mask_frac).astype(np.uint8)
+    crow, cids, _ = canonical_csr(row_ptr, ids, mask, V, pad)
+    w = rng.uniform(0.5, 1.5, T)
+    return A, E, crow, cids, mask, w
+
+
+# ---------------------------------------------------------------------------- BCE
+
+def test_bce_closed_form_at_A_zero():
+    T, D, V = 6, 5, 23
+    _, E, crow, cids, mask, w = _problem(T, D, V, 0)
+    A = np.zeros((T, D))
+    loss = H.bce_loss(A, E, crow, cids, mask)
+    dA, dE = H.bce_grads(A, E, crow, cids, mask, w)
+    for t in range(T):
+        want_loss = V * math.log(2.0) if mask[t] else 0.0
+        assert loss[t] == pytest.approx(want_loss, rel=1e-14, abs=0)
+        want = np.zeros(D)
+        if mask[t]:
+            for v in range(V):
+                want += 0.5 * E[v]
+            for p in cids[crow[t]:crow[t + 1]]:
+                want -= E[p]
+            want *= w[t]
+        np.testing.assert_allclose(dA[t], want, rtol=1e-12, atol=1e-13)
+    assert np.all(dE == 0)
+
+
+def test_bce_closed_form_at_E_zero():
+    T, D, V = 7, 4, 19
+    A, _, crow, cids, mask, w = _problem(T, D, V, 1)
+    E = np.zeros((V, D))
+    loss = H.bce_loss(A, E, crow, cids, mask)
+    dA, dE = H.bce_grads(A, E, crow, cids, mask, w)
+    np.testing.assert_allclose(loss, np.where(mask != 0, V * math.log(2.0), 0.0), rtol=1e-14)
+    assert np.all(dA == 0)
+    for v in range(V):
+        want = np.zeros(D)
+        for t in range(T):
+            if not mask[t]:
+                continue
+            y = 1.0 if v in set(cids[crow[t]:crow[t + 1]].tolist()) else 0.0
+            want += w[t] * (0.5 - y) * A[t]
+        np.testing.assert_allclose(dE[v], want, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("std", [None, 1.0, 4.0])
+def test_bce_dense_sparse_identity(std):
+    # Cut BCE §I-B: exact split into dense background and sparse correction;
+    # std=1.0, D=128 is the mini-benchmark's A, E ~ N(0, I) (§IV-A)
+    T, D, V = 9, 128, 301
+    A, E, crow, cids, mask, _ = _problem(T, D, V, 2, std=std, L=8)
+    a = H.bce_loss(A, E, crow, cids, mask)
+    b = H.bce_loss_dense_sparse(A, E, crow, cids, mask)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=0)
+
+
+def _torch_bce(A, E, crow, cids, mask, w):
+    T, V = A.shape[0], E.shape[0]
+    At = torch.tensor(A, requires_grad=True)
+    Et = torch.tensor(E, requires_grad=True)
+    X = At @ Et.T
+    Y = torch.tensor(dense_labels(crow, cids, T, V))
+    per = torch.nn.functional.binary_cross_entropy_with_logits(X, Y, reduction="none").sum(1)
+    per = per * torch.tensor(mask, dtype=torch.float64)
+    (per * torch.tensor(w)).sum().backward()
+    return per.detach().numpy(), At.grad.numpy(), Et.grad.numpy()
+
+
+@pytest.mark.parametrize("seed,std", [(3, None), (4, 1.0), (5, 3.0)])
+def test_bce_matches_torch_library_and_autograd(seed, std):
+    T, D, V = 8, 16, 77
+    A, E, crow, cids, mask, w = _problem(T, D, V, seed, std=std)
+    loss_t, dA_t, dE_t = _torch_bce(A, E, crow, cids, mask, w)
+    loss = H.bce_loss(A, E, crow, cids, mask)
+    dA, dE = H.bce_grads(A, E, crow, cids, mask, w)
+    np.testing.assert_allclose(loss, loss_t, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dA, dA_t, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dE, dE_t, rtol=1e-10, atol=1e-12)
+
+
+def test_bce_finite_differences():
+    T, D, V = 3, 6, 37
+    A, E, crow, cids, mask, w = _problem(T, D, V, 6, std=0.7, mask_frac=0.0)
+    dA, dE = H.bce_grads(A, E, crow, cids, mask, w)
+    L = lambda A_, E_: float((w * H.bce_loss(A_, E_, crow, cids, mask)).sum())
+    h = 1e-6
+    for (t, d) in [(0, 0), (1, 3), (2, 5)]:
+        Ap, Am = A.copy(), A.copy()
+        Ap[t, d] += h
+        Am[t, d] -= h
+        assert (L(Ap, E) - L(Am, E)) / (2 * h) == pytest.approx(dA[t, d], rel=1e-6, abs=1e-8)
+    for (v, d) in [(0, 1), (int(cids[0]), 2), (36, 5)]:
+        Ep, Em = E.copy(), E.copy()
+        Ep[v, d] += h
+        Em[v, d] -= h
+        assert (L(A, Ep) - L(A, Em)) / (2 * h) == pytest.approx(dE[v, d], rel=1e-6, abs=1e-8)
+
+
+def test_bce_invariants():
+    T, D, V = 10, 8, 40
+    rng = np.random.default_rng(7)
+    A, E, crow, cids, mask, w = _problem(T, D, V, 7, std=0.5, L=5)
+    loss = H.bce_loss(A, E, crow, cids, mask)
+    dA, dE = H.bce_grads(A, E, crow, cids, mask, w)
+    # masked rows: exact zeros
+    assert np.all(loss[mask == 0] == 0) and np.all(dA[mask == 0] == 0)
+    # permuting E rows together with relabelled ids
+    perm = rng.permutation(V)
+    inv = np.argsort(perm)                  # new id of old item v is inv[v]
+    E2 = E[perm]
+    cids2 = inv[cids]
+    crow2 = crow
+    # re-sort each row to keep the canonical order
+    cids2 = np.concatenate([np.sort(cids2[crow[t]:crow[t + 1]]) for t in range(T)])
+    np.testing.assert_allclose(H.bce_loss(A, E2, crow2, cids2, mask), loss, rtol=1e-12)
+    dA2, dE2 = H.bce_grads(A, E2, crow2, cids2, mask, w)
+    np.testing.assert_allclose(dA2, dA, rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(dE2, dE[perm], rtol=1e-10, atol=1e-13)
+    # permuting rows permutes outputs
+    rp = rng.permutation(T)
+    sets = [cids[crow[t]:crow[t + 1]] for t in range(T)]
+    crow3 = np.zeros(T + 1, np.int64)
+    crow3[1:] = np.cumsum([len(sets[t]) for t in rp])
+    cids3 = np.concatenate([sets[t] for t in rp])
+    np.testing.assert_allclose(H.bce_loss(A[rp], E, crow3, cids3, mask[rp]), loss[rp], rtol=1e-12)
+    # a positive changes the loss by exactly -x (dense part unchanged)
+    X = A @ E.T
+    t = int(np.nonzero(mask)[0][0])
+    extra = [v for v in range(V) if v not in set(sets[t].tolist())][0]
+    sets4 = list(sets)
+    sets4[t] = np.sort(np.append(sets[t], extra))
+    crow4 = np.zeros(T + 1, np.int64)
+    crow4[1:] = np.cumsum([len(s) for s in sets4])
+    loss4 = H.bce_loss(A, E, crow4, np.concatenate(sets4), mask)
+    assert loss4[t] - loss[t] == pytest.approx(-X[t, extra], rel=1e-9, abs=1e-12)
+
+
+def test_bce_sampled_equals_full():
+    T, D, V = 12, 8, 50
+    A, E, crow, cids, mask, w = _problem(T, D, V, 8)
+    loss = H.bce_loss(A, E, crow, cids, mask)
+    dA, dE = H.bce_grads(A, E, crow, cids, mask, w)
+    rows = np.array([0, 5, 11, 3])
+    items = np.array([0, 1, 49, 17, int(cids[0])])
+    lr, dAr = H.bce_rows(A, E, crow, cids, rows, mask, w)
+    dEc = H.bce_items(A, E, crow, cids, items, mask, w)
+    np.testing.assert_allclose(lr, loss[rows], rtol=1e-13)
+    np.testing.assert_allclose(dAr, dA[rows], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(dEc, dE[items], rtol=1e-12, atol=1e-15)
+
+
+def test_logit_memory_formula_matches_printed_figure():
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "logit_memory.json")))
+    gib = H.logits_bytes_fp32(g["B_local"] * g["N"], g["V"]) / 2 ** 30
+    assert round(gib, 2) == g["gib_printed"]
+
+
+# ---------------------------------------------------------------------------- CE
+
+def _ce_problem(T, D, V, seed, std=None, ign=2):
+    rng = np.random.default_rng(seed)
+    s = 1.0 / math.sqrt(D) if std is None else std
+    A = rng.normal(0, s, (T, D))
+    E = rng.normal(0, s, (V, D))
+    tgt = rng.integers(0, V, T)
+    tgt[rng.permutation(T)[:ign]] = -100
+    return A, E, tgt, rng.uniform(0.5, 1.5, T)
+
+
+def test_ce_closed_form_at_A_zero():
+    T, D, V = 5, 4, 31
+    _, E, tgt, w = _ce_problem(T, D, V, 10)
+    A = np.zeros((T, D))
+    loss, lse = H.ce_forward(A, E, tgt)
+    np.testing.assert_allclose(lse, math.log(V), rtol=1e-14)
+    dA, dE = H.ce_grads(A, E, tgt, dloss=w)
+    for t in range(T):
+        if tgt[t] == -100:
+            assert loss[t] == 0 and np.all(dA[t] == 0)
+            continue
+        assert loss[t] == pytest.approx(math.log(V), rel=1e-14)
+        want = w[t] * (sum(E[v] for v in range(V)) / V - E[tgt[t]])
+        np.testing.assert_allclose(dA[t], want, rtol=1e-12, atol=1e-14)
+    assert np.all(dE == 0)
+
+
+@pytest.mark.parametrize("seed,std", [(11, None), (12, 1.0)])
+def test_ce_matches_torch_library_and_autograd(seed, std):
+    T, D, V = 9, 16, 67
+    A, E, tgt, w = _ce_problem(T, D, V, seed, std=std)
+    At = torch.tensor(A, requires_grad=True)
+    Et = torch.tensor(E, requires_grad=True)
+    per = torch.nn.functional.cross_entropy(At @ Et.T, torch.tensor(tgt), ignore_index=-100, reduction="none")
+    (per * torch.tensor(w)).sum().backward()
+    loss, lse = H.ce_forward(A, E, tgt)
+    dA, dE = H.ce_grads(A, E, tgt, dloss=w)
+    np.testing.assert_allclose(loss, per.detach().numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, torch.logsumexp(torch.tensor(A @ E.T), 1).numpy(), rtol=1e-13)
+    np.testing.assert_allclose(dA, At.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(dE, Et.grad.numpy(), rtol=1e-10, atol=1e-13)
+
+
+def test_ce_finite_differences():
+    T, D, V = 3, 5, 29
+    A, E, tgt, w = _ce_problem(T, D, V, 13, std=0.8, ign=1)
+    dA, dE = H.ce_grads(A, E, tgt, dloss=w)
+    L = lambda A_, E_: float((w * H.ce_forward(A_, E_, tgt)[0]).sum())
+    h = 1e-6
+    for (t, d) in [(0, 0), (1, 2), (2, 4)]:
+        Ap, Am = A.copy(), A.copy()
+        Ap[t, d] += h
+        Am[t, d] -= h
+        assert (L(Ap, E) - L(Am, E)) / (2 * h) == pytest.approx(dA[t, d], rel=1e-6, abs=1e-9)
+    for (v, d) in [(0, 0), (int(tgt[tgt >= 0][0]), 3), (28, 1)]:
+        Ep, Em = E.copy(), E.copy()
+        Ep[v, d] += h
+        Em[v, d] -= h
+        assert (L(A, Ep) - L(A, Em)) / (2 * h) == pytest.approx(dE[v, d], rel=1e-6, abs=1e-9)
+
+
+def test_ce_sampled_equals_full():
+    T, D, V = 10, 8, 45
+    A, E, tgt, w = _ce_problem(T, D, V, 14)
+    loss, lse = H.ce_forward(A, E, tgt)
+    dA, dE = H.ce_grads(A, E, tgt, dloss=w)
+    rows = np.array([0, 9, 4])
+    items = np.array([0, 44, int(tgt[tgt >= 0][0])])
+    lr, lser, dAr = H.ce_rows(A, E, tgt, rows, dloss=w)
+    np.testing.assert_allclose(lr, loss[rows], rtol=1e-13)
+    np.testing.assert_allclose(lser, lse[rows], rtol=1e-13)
+    np.testing.assert_allclose(dAr, dA[rows], rtol=1e-12, atol=1e-15)
+    lse_all = H.ce_lse(A, E, np.arange(T))
+    np.testing.assert_allclose(H.ce_items(A, E, tgt, items, lse_all, dloss=w), dE[items], rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------- SGD
+
+def test_sgd_fp8_matches_torch_rounding():
+    rng = np.random.default_rng(15)
+    # lr a power of two and dE on a 2^-10 grid: E - lr dE is exact in float32, so torch's
+    # float64 -> float32 -> fp8 cast rounds once, like the oracle
+    E_codes = encode_fp8_e4m3fn(rng.normal(0, 0.05, (64, 32)))
+    dE = np.round(rng.normal(0, 3.0, (64, 32)) * 1024) / 1024
+    lr = 2.0 ** -7
+    ours = H.sgd_fp8(E_codes, dE, lr)
+    pre = decode_fp8_e4m3fn(E_codes) - lr * dE
+    ref = torch.from_numpy(pre).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
