@@ -1,0 +1,192 @@
+/*
+ * cutloss — fused large-vocabulary classifier-head losses for AMD Instinct MI355X (gfx950).
+ *
+ * Computes the loss and gradients of a classifier head over the logits X = A E^T
+ * (A[T,D] activations, E[V,D] item/class embeddings) without ever storing the
+ * T x V logits in device memory: logit tiles are formed on chip, reduced, and
+ * recomputed in the backward pass.
+ *
+ * Operations and the passages that define them:
+ *  - Multi-label BCE over the whole vocabulary, split into a dense background
+ *    sum_v softplus(x_tv) and a sparse correction -sum_{p in P_t} x_tp
+ *    (Cut Binary Cross Entropy, paperpeel: §I-B "Fused Direct BCE Formulation",
+ *    §III-A vocabulary chunking, §III-B custom-VJP rematerialization).
+ *  - Softmax cross-entropy as logsumexp(x_t) - x_{t,y_t}, the target logit by an
+ *    indexed dot product and the logsumexp by an online max/sum over vocabulary
+ *    tiles (Cut Your Losses, abeam.tech article: the sections on splitting the
+ *    loss into two needed quantities and on recomputing tiles in backward).
+ *  - BCE backward fused with a momentum-free SGD step on the embeddings, so dE
+ *    is never stored; E may be FP8 E4M3 (ELMO, ai.info summary: Key
+ *    Contributions 1-2 and Methodology).
+ *
+ * Conventions
+ *  - Every data pointer is a DEVICE pointer and must be 16-byte aligned. The
+ *    caller owns every buffer; the library never allocates device memory. Scratch
+ *    space comes from the caller's workspace, sized by the *_workspace_size query.
+ *  - Matrices are row-major and dense: A is [T, D] bf16; E is [V, D] bf16 or OCP FP8
+ *    E4M3FN (1 byte); dA is [T, D] bf16; dE is [V, D] bf16. D must be a positive
+ *    multiple of 64. loss/lse/dloss are [T] float32.
+ *  - All work is enqueued on `stream` (a hipStream_t, NULL = default stream);
+ *    no call synchronizes except cutloss_read_data_errors.
+ *  - Host-detectable errors (bad sizes, NULL or misaligned pointers, too small a
+ *    workspace, unsupported dtype) return a status before anything is launched.
+ *    Data errors found on the device (IDs outside [0, V), malformed CSR rows) are
+ *    counted in the workspace and the offending entries are ignored.
+ *  - The per-row loss is the sum over the vocabulary; the library applies no
+ *    batch reduction. A caller's mean or weighting is expressed through dloss
+ *    (dloss_t = dL/dloss_t; NULL means 1 for every row).
+ *  - Masked (BCE) and ignored (CE) rows give loss 0, a zero dA row and no dE
+ *    contribution.
+ *  - Results are deterministic: every reduction runs in a fixed order.
+ */
+#ifndef CUTLOSS_H
+#define CUTLOSS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CUTLOSS_OK = 0,
+  CUTLOSS_ERR_INVALID_ARG = 1,  /* a NULL/misaligned pointer or a bad size */
+  CUTLOSS_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement (e.g. D % 64 != 0) */
+  CUTLOSS_ERR_WORKSPACE = 3,    /* workspace smaller than the size query returned */
+  CUTLOSS_ERR_HIP = 4           /* a HIP launch/runtime error; text in cutloss_last_error() */
+} cutloss_status;
+
+typedef enum {
+  CUTLOSS_BF16 = 0,
+  CUTLOSS_FP8_E4M3 = 1          /* OCP E4M3FN: bias 7, no infinities, max 448 */
+} cutloss_dtype;
+
+/* Operation codes for the workspace queries. */
+typedef enum {
+  CUTLOSS_OP_FWD = 0,
+  CUTLOSS_OP_BWD = 1,
+  CUTLOSS_OP_BWD_SGD = 2
+} cutloss_op;
+
+/*
+ * Multi-label BCE problem. The positives of row t are pos_ids[pos_row_ptr[t] ..
+ * pos_row_ptr[t+1]) in any order; pad_id entries are not positives, repeats count
+ * once (Cut BCE §III-B/§III-E/§IV-A). Rows with row_mask[t] == 0 are padding rows.
+ */
+typedef struct {
+  int64_t T, D, V;
+  const void* A;                 /* [T, D] bf16 */
+  const void* E;                 /* [V, D] bf16 or fp8 (per e_dtype); updated in place by bwd_sgd */
+  cutloss_dtype e_dtype;
+  const int32_t* pos_row_ptr;    /* [T+1], pos_row_ptr[0] = 0, non-decreasing */
+  const int32_t* pos_ids;        /* [nnz] item IDs */
+  int64_t nnz;                   /* = pos_row_ptr[T]; passed by the caller (the host never reads device memory) */
+  const uint8_t* row_mask;       /* [T], 1 = valid row; NULL = all rows valid */
+  int32_t pad_id;                /* padding item ID (not a positive); < 0 = none */
+} cutloss_bce_problem;
+
+/* Softmax cross-entropy problem: one class target per row. */
+typedef struct {
+  int64_t T, D, V;
+  const void* A;                 /* [T, D] bf16 */
+  const void* E;                 /* [V, D] bf16 or fp8 */
+  cutloss_dtype e_dtype;
+  const int64_t* target;         /* [T] class IDs in [0, V), or ignore_index */
+  int64_t ignore_index;          /* e.g. -100 */
+} cutloss_ce_problem;
+
+/*
+ * Workspace size in bytes for `op` on problem `p` (0 if the problem is invalid).
+ * It grows with T, D, nnz and the vocabulary tile count, never with T*V.
+ */
+size_t cutloss_bce_workspace_size(const cutloss_bce_problem* p, int32_t op);
+size_t cutloss_ce_workspace_size(const cutloss_ce_problem* p, int32_t op);
+
+/*
+ * BCE forward: loss[t] = sum_v softplus(x_tv) - sum_{p in P_t} x_tp (0 on masked rows).
+ * Cut BCE §I-B (dense background + sparse correction), §III-A (vocabulary tiles).
+ */
+cutloss_status cutloss_bce_fwd(const cutloss_bce_problem* p, float* loss,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * BCE backward: with G = w (sigmoid(X) - Y), w_t = dloss_t * mask_t,
+ * dA = G E (bf16 [T,D]) and dE = G^T A (bf16 [V,D]). Logit tiles are recomputed
+ * (Cut BCE §III-B/§III-C). If loss_out is not NULL the forward loss is emitted by
+ * the same pass (fused forward+backward). dA or dE may be NULL to skip it.
+ */
+cutloss_status cutloss_bce_bwd(const cutloss_bce_problem* p, const float* dloss,
+                               void* dA, void* dE, float* loss_out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * BCE backward fused with SGD on E: E <- round(E - lr * dE), dE never stored
+ * (ELMO summary, Key Contributions 2: gradient fusion; Methodology: momentum-free
+ * SGD, FP8 E4M3 weights). Rounding to E's dtype is nearest-even; FP8 saturates at
+ * +-448. E (p->E) is modified in place, so the call is not idempotent. dA (bf16)
+ * and loss_out are optional outputs as in cutloss_bce_bwd.
+ */
+cutloss_status cutloss_bce_bwd_sgd(const cutloss_bce_problem* p, const float* dloss, float lr,
+                                   void* dA, float* loss_out,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Softmax CE forward: lse[t] = logsumexp_v x_tv (every row), loss[t] = lse[t] - x_{t,y_t}
+ * (0 on ignored rows). Cut Your Losses article: target logit by an indexed dot
+ * product, logsumexp by an online max/sum over vocabulary tiles.
+ */
+cutloss_status cutloss_ce_fwd(const cutloss_ce_problem* p, float* loss, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Softmax CE backward from the forward's lse: G = w (softmax(X) - onehot(y)),
+ * dA = G E, dE = G^T A (bf16). dA or dE may be NULL to skip it.
+ */
+cutloss_status cutloss_ce_bwd(const cutloss_ce_problem* p, const float* lse, const float* dloss,
+                              void* dA, void* dE,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Number of data errors counted by the last call that used this workspace
+ * (positive IDs / targets outside [0, V), malformed CSR rows). Synchronizes `stream`.
+ */
+cutloss_status cutloss_read_data_errors(const void* workspace, void* stream, int64_t* n_errors);
+
+/*
+ * Test hook: canonical positive sets of a BCE problem as computed on the device.
+ * Writes the canonical CSR (crow[T+1], cids[nnz'] sorted ascending within rows, no
+ * pads, repeats or masked rows) and the item-major pairs (items[nnz'], rows[nnz'],
+ * ordered by item then row) into the given device buffers (each sized for nnz
+ * entries), and *n_unique_pairs = nnz' (synchronizes `stream`).
+ */
+cutloss_status cutloss_bce_canonical_targets(const cutloss_bce_problem* p,
+                                             int32_t* crow, int32_t* cids,
+                                             int32_t* items, int32_t* rows, int64_t* n_unique_pairs,
+                                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Profiling hook. While enabled (process-wide), every entry point records a HIP event
+ * pair on the caller's stream around each of its kernel phases:
+ *   0 target canonicalization, 1 rows sweep (loss/LSE partials, dA partials),
+ *   2 row finalization (loss, lse, dA), 3 row weights + sparse item sums,
+ *   4 cols sweep (dE or the fused SGD step).
+ * cutloss_profile_read synchronizes on the recorded events, writes the summed
+ * milliseconds and the number of recorded launches per phase (arrays of n entries),
+ * and clears the records. Enabling costs one event record per phase boundary.
+ */
+enum { CUTLOSS_PHASE_TARGETS = 0, CUTLOSS_PHASE_ROWS = 1, CUTLOSS_PHASE_FINALIZE = 2,
+       CUTLOSS_PHASE_ITEM_SUMS = 3, CUTLOSS_PHASE_COLS = 4, CUTLOSS_N_PHASES = 5 };
+cutloss_status cutloss_profile_enable(int32_t enable);
+cutloss_status cutloss_profile_read(float* ms, int32_t* launches, int32_t n);
+
+const char* cutloss_status_string(cutloss_status s);
+/* Text of the last error on the calling thread ("" if none). */
+const char* cutloss_last_error(void);
+/* Library version string. */
+const char* cutloss_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CUTLOSS_H */

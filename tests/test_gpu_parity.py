@@ -1,0 +1,243 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Small cases run the full oracle (materialized logits) at sizes that still span
+several 128-row / 32-column tiles and ragged tails; the headline workload runs at
+full size and is compared on sampled rows and items, which the oracle computes
+one by one. Tolerances are those of tests/gpu_util.py.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import head_loss as H
+from oracle.targets import canonical_csr, item_major
+from workloads import make, workload
+from workloads.gen import Workload
+
+from gpu_util import (bf16_to_f64, canonical, check_grad, check_loss, decode_inputs, run_bce, run_ce,
+                       upload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    from vocabulary_loss_head_amd import binding
+    return binding
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _bce_full_check(B, inp, pad_id, dloss=None, loss_only=False):
+    w = inp["workload"]
+    A64, E64 = decode_inputs(inp)
+    crow, cids, n_bad = canonical(inp, w.V, pad_id)
+    g = upload(inp)
+    dl = None if dloss is None else torch.from_numpy(dloss).to(g["A"].device)
+    out = run_bce(B, g, pad_id, dloss=dl, want_dA=not loss_only, want_dE=not loss_only, fused_loss=not loss_only)
+    ref_loss = H.bce_loss(A64, E64, crow, cids, inp["mask"])
+    check_loss(out["loss"].cpu().numpy(), ref_loss, what="fwd loss")
+    assert out["n_err"] == n_bad
+    if loss_only:
+        return
+    check_loss(out["floss"].cpu().numpy(), ref_loss, what="fused loss")
+    dA, dE = H.bce_grads(A64, E64, crow, cids, inp["mask"], dloss)
+    check_grad(bf16_to_f64(out["dA"]), dA, "dA")
+    check_grad(bf16_to_f64(out["dE"]), dE, "dE")
+    # masked rows: exact zeros
+    m = inp["mask"] == 0
+    if m.any():
+        assert np.all(out["loss"].cpu().numpy()[m] == 0)
+        assert np.all(bf16_to_f64(out["dA"])[m] == 0)
+
+
+def test_tiny_bce_full(B):
+    _say("tiny_bce T=32 D=64 V=1000")
+    inp = make(workload("tiny_bce"), with_dloss=True)
+    _bce_full_check(B, inp, pad_id=0)
+    _bce_full_check(B, inp, pad_id=0, dloss=inp["dloss"])
+
+
+@pytest.mark.parametrize("T,D,V", [(1, 64, 33), (33, 128, 1001), (130, 256, 4097), (257, 64, 2000), (129, 512, 777)])
+def test_bce_ragged_with_pads_and_repeats(B, T, D, V):
+    _say(f"ragged T={T} D={D} V={V}")
+    w = Workload("ragged", "bce", T, D, V, "bf16", None, None, "uniform_any", L=12, pad_id=0, mask_frac=0.2,
+                 seed=100 + T)
+    inp = make(w, with_dloss=True)
+    _bce_full_check(B, inp, pad_id=0, dloss=inp["dloss"])
+
+
+def test_bce_high_scale_stress(B):
+    # Cut BCE §IV-A mini-benchmark distribution: A, E ~ N(0, I), D = 128, L = 8 uniform
+    # targets in [0, V) (pads and repeats included): saturated sigmoids, large softplus.
+    _say("stress N(0,1) T=96 D=128 V=5000")
+    w = Workload("stress", "bce", 96, 128, 5000, "bf16", 1.0, 1.0, "uniform_any", L=8, pad_id=0, seed=7)
+    inp = make(w)
+    _bce_full_check(B, inp, pad_id=0)
+
+
+def test_bce_closed_forms(B):
+    # A = 0: loss = V ln 2, dA_t = 0.5 sum_v E_v - sum_p E_p, dE = 0
+    # E = 0: loss = V ln 2, dA = 0, dE_v = sum_t w_t (0.5 - y_tv) A_t
+    w = Workload("cf", "bce", 70, 128, 3000, "bf16", None, None, "uniform_any", L=6, pad_id=0, mask_frac=0.1, seed=8)
+    inp = make(w)
+    for zero in ("A", "E"):
+        _say(f"closed form {zero}=0")
+        z = dict(inp)
+        z[zero] = np.zeros_like(inp[zero])
+        _bce_full_check(B, z, pad_id=0)
+        out = run_bce(B, upload(z), 0)
+        valid = z["mask"] != 0
+        np.testing.assert_allclose(out["loss"].cpu().numpy()[valid], w.V * math.log(2.0), rtol=1e-5)
+
+
+def test_canonical_targets_bit_exact(B):
+    _say("canonical targets")
+    w = Workload("canon", "bce", 300, 64, 5000, "bf16", None, None, "uniform_any", L=20, pad_id=0, mask_frac=0.3, seed=9)
+    inp = make(w)
+    # plant out-of-range IDs and an empty row
+    ids = inp["ids"].copy()
+    ids[::37] = 5000 + np.arange(len(ids[::37]))
+    ids[5::41] = -3
+    inp["ids"] = ids
+    g = upload(inp)
+    prob = B.bce_problem(g["A"], g["E"], g["row_ptr"], g["ids"], g["mask"], 0)
+    ws = B.workspace(B.cutloss_bce_workspace_size(prob, B.OP_BWD), g["A"].device)
+    n = len(ids)
+    dev = g["A"].device
+    crow = torch.empty(w.T + 1, dtype=torch.int32, device=dev)
+    cids, items, rows = (torch.empty(n, dtype=torch.int32, device=dev) for _ in range(3))
+    nu = B.cutloss_bce_canonical_targets(prob, crow, cids, items, rows, ws)
+    ref_crow, ref_cids, n_bad = canonical_csr(inp["row_ptr"], ids, inp["mask"], w.V, 0)
+    ref_items, ref_rows = item_major(ref_crow, ref_cids)
+    assert nu == len(ref_cids)
+    assert np.array_equal(crow.cpu().numpy(), ref_crow)
+    assert np.array_equal(cids.cpu().numpy()[:nu], ref_cids)
+    assert np.array_equal(items.cpu().numpy()[:nu], ref_items)
+    assert np.array_equal(rows.cpu().numpy()[:nu], ref_rows)
+    assert B.cutloss_read_data_errors(ws) == n_bad and n_bad > 0
+
+
+def test_determinism(B):
+    _say("determinism")
+    w = Workload("det", "bce", 200, 256, 9000, "bf16", None, None, "zipf", L=8, pad_id=0, mask_frac=0.1, seed=11)
+    g = upload(make(w))
+    a = run_bce(B, g, 0)
+    b = run_bce(B, g, 0)
+    for k in ("loss", "dA", "dE", "floss"):
+        assert torch.equal(a[k].view(torch.int16) if a[k].dtype == torch.bfloat16 else a[k],
+                           b[k].view(torch.int16) if b[k].dtype == torch.bfloat16 else b[k]), k
+
+
+@pytest.mark.parametrize("T,D,V", [(70, 128, 3001), (200, 256, 5000), (33, 64, 100)])
+def test_ce_small(B, T, D, V):
+    _say(f"ce T={T} D={D} V={V}")
+    w = Workload("ce", "ce", T, D, V, "bf16", None, None, "ce_uniform", L=1, pad_id=-1, ignore_frac=0.1, seed=12 + T)
+    inp = make(w, with_dloss=True)
+    tgt = inp["target"].copy()
+    tgt[3] = V + 5          # out of range: counted, row ignored
+    inp["target"] = tgt
+    g = upload(inp)
+    A64, E64 = decode_inputs(inp)
+    out = run_ce(B, g, dloss=g["dloss"])
+    loss, lse = H.ce_forward(A64, E64, tgt)
+    check_loss(out["lse"].cpu().numpy(), lse, what="lse")
+    check_loss(out["loss"].cpu().numpy(), loss, what="loss")
+    dA, dE = H.ce_grads(A64, E64, tgt, dloss=inp["dloss"])
+    check_grad(bf16_to_f64(out["dA"]), dA, "dA")
+    check_grad(bf16_to_f64(out["dE"]), dE, "dE")
+    assert out["n_err"] == 1
+
+
+def test_sgd_fp8_small(B):
+    _say("sgd fp8 T=40 D=128 V=2000")
+    w = Workload("sgd", "bce", 40, 128, 2000, "fp8", None, 0.05, "poisson_distinct", L=5, pad_id=-1, lr=0.01, seed=13)
+    inp = make(w)
+    A64, E64 = decode_inputs(inp)
+    crow, cids, _ = canonical(inp, w.V, -1)
+    g = upload(inp)
+    prob = B.bce_problem(g["A"], g["E"], g["row_ptr"], g["ids"], g["mask"], -1)
+    ws = B.workspace(B.cutloss_bce_workspace_size(prob, B.OP_BWD_SGD), g["A"].device)
+    # unfused dE on the same fp8 E first
+    dE = torch.empty(w.V, w.D, dtype=torch.bfloat16, device=g["A"].device)
+    B.cutloss_bce_bwd(prob, None, None, dE, None, ws)
+    loss = torch.empty(w.T, dtype=torch.float32, device=g["A"].device)
+    B.cutloss_bce_bwd_sgd(prob, None, w.lr, None, loss, ws)
+    torch.cuda.synchronize()
+    _, dE_ref = H.bce_grads(A64, E64, crow, cids, inp["mask"])
+    check_grad(bf16_to_f64(dE), dE_ref, "dE (fp8 E)")
+    check_loss(loss.cpu().numpy(), H.bce_loss(A64, E64, crow, cids, inp["mask"]), what="sgd fused loss")
+    _check_sgd(g["E"].cpu().numpy(), inp["E"], dE_ref, w.lr)
+
+
+def _check_sgd(E_new, E_old, dE_ref, lr):
+    """E' must be fp8(E - lr (dE_ref + delta)) for some |delta| <= 2e-2 max|dE_ref| per element."""
+    from oracle.formats import decode_fp8_e4m3fn
+    tol = 2e-2 * np.abs(dE_ref).max()
+    lo = H.sgd_fp8(E_old, dE_ref + tol, lr)
+    hi = H.sgd_fp8(E_old, dE_ref - tol, lr)
+    got = decode_fp8_e4m3fn(E_new)
+    vlo, vhi = decode_fp8_e4m3fn(lo), decode_fp8_e4m3fn(hi)
+    assert np.all((got >= vlo) & (got <= vhi)), "SGD result outside the rounding interval"
+    exact = decode_fp8_e4m3fn(H.sgd_fp8(E_old, dE_ref, lr))
+    frac = float(np.mean(got != exact))
+    print(f"[sgd] fraction differing from fp8(E - lr dE_ref): {frac:.2e}")
+    assert frac < 1e-2
+
+
+# ----------------------------------------------------------------------------- full size
+
+def _sample_rows(inp, T, n_rand=64, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = {0, T - 1}
+    masked = np.nonzero(inp["mask"] == 0)[0]
+    rows.update(masked[:4].tolist())
+    rp, ids = inp["row_ptr"], inp["ids"]
+    with1 = [t for t in range(min(T, 2000)) if 1 in set(ids[rp[t]:rp[t + 1]].tolist())]
+    rows.update(with1[:4])
+    rows.update(rng.choice(T, size=min(n_rand, T), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+def _sample_items(cids, V, n_rand=64, seed=1):
+    rng = np.random.default_rng(seed)
+    items = {0, V - 1, *range(1, 9)}
+    pos = np.unique(cids)
+    items.update(rng.choice(pos, size=min(16, len(pos)), replace=False).tolist())
+    items.update(rng.choice(V, size=n_rand, replace=False).tolist())
+    return np.array(sorted(items))
+
+
+@pytest.fixture(scope="module")
+def seqrec():
+    return make(workload("seqrec_bce"))
+
+
+def test_seqrec_full_size_fused_fwd_bwd(B, seqrec):
+    """T=4096, D=256, V=876,939, Zipf positives, 10% masked rows: the headline workload,
+    run in the same launch configuration the benchmark times (fused backward with loss)."""
+    inp = seqrec
+    w = inp["workload"]
+    _say(f"seqrec full size T={w.T} D={w.D} V={w.V}")
+    g = upload(inp)
+    out = run_bce(B, g, 0)
+    A64, E64 = decode_inputs(inp)
+    crow, cids, n_bad = canonical(inp, w.V, 0)
+    assert out["n_err"] == n_bad == 0
+    rows = _sample_rows(inp, w.T)
+    items = _sample_items(cids, w.V)
+    loss_r, dA_r = H.bce_rows(A64, E64, crow, cids, rows, inp["mask"])
+    check_loss(out["loss"].cpu().numpy()[rows], loss_r, what="fwd loss (sampled rows)")
+    check_loss(out["floss"].cpu().numpy()[rows], loss_r, what="fused loss (sampled rows)")
+    check_grad(bf16_to_f64(out["dA"][torch.from_numpy(rows).cuda()]), dA_r, "dA (sampled rows)")
+    dE_c = H.bce_items(A64, E64, crow, cids, items, inp["mask"])
+    check_grad(bf16_to_f64(out["dE"][torch.from_numpy(items).cuda()]), dE_c, "dE (sampled items)")
+    # the positive terms on their own scale: item sums of the sparse dE term show in items 1..8
+    m = inp["mask"] == 0
+    assert np.all(out["loss"].cpu().numpy()[m] == 0) and np.all(out["floss"].cpu().numpy()[m] == 0)

@@ -1,0 +1,466 @@
+// C ABI of the cutloss library: argument validation, workspace layout and kernel order.
+// Every entry point validates on the host and returns before launching anything if a
+// check fails; all work is then enqueued on the caller's stream without synchronizing.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+namespace {
+
+// ---- phase profiling (cutloss_profile_enable / cutloss_profile_read)
+struct PhaseRec {
+  int phase;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<PhaseRec> g_prof;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t prof_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// RAII scope that brackets one phase with events when profiling is on.
+struct Phase {
+  int phase;
+  hipStream_t st;
+  hipEvent_t a = nullptr;
+  Phase(int ph, hipStream_t s) : phase(ph), st(s) {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    if (!g_prof_on) return;
+    a = prof_event();
+    if (a) hipEventRecord(a, st);
+  }
+  ~Phase() {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    if (!a) return;
+    hipEvent_t b = prof_event();
+    if (!b) return;
+    hipEventRecord(b, st);
+    g_prof.push_back({phase, a, b});
+  }
+};
+
+thread_local std::string g_last_error;
+
+cutloss_status fail(cutloss_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+cutloss_status hip_check(hipError_t e, const char* where) {
+  if (e == hipSuccess) return CUTLOSS_OK;
+  return fail(CUTLOSS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+// Workspace carving: a bump allocator over the caller's buffer (or a null base to size it).
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <class T>
+  T* take(size_t n) {
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += up(sizeof(T) * (n > 0 ? n : 1));
+    return p;
+  }
+};
+
+struct Plan {
+  int64_t T, D, V, cap;
+  int n_splits;
+  int64_t split_len;
+};
+
+Plan make_plan(int64_t T, int64_t D, int64_t V, int64_t cap) {
+  Plan pl{T, D, V, cap, 1, 0};
+  const int64_t nsb = (T + 127) / 128;
+  int64_t ns = nsb > 0 ? (1024 + nsb - 1) / nsb : 1;
+  const int64_t max_ns = (V + 31) / 32;
+  if (ns > max_ns) ns = max_ns;
+  if (ns > 256) ns = 256;
+  if (ns >= 8) ns = ns / 8 * 8;
+  if (ns < 1) ns = 1;
+  int64_t sl = (V + ns - 1) / ns;
+  sl = (sl + 31) / 32 * 32;
+  pl.n_splits = (int)ns;
+  pl.split_len = sl;
+  return pl;
+}
+
+struct Ws {
+  unsigned long long* err;
+  cl::TargetsWs tw;
+  float* w;
+  float* part_a;
+  float* part_b;
+  float* part_dA;
+  float* S_u;
+  size_t bytes;
+};
+
+// op: 0 fwd (loss partials), 1 bwd (dA partials + S_u), 2 CE fwd (two partial arrays)
+Ws carve(void* base, const Plan& pl, bool need_dA, bool need_Su, bool two_partials) {
+  Carver c(base);
+  Ws w{};
+  w.err = c.take<unsigned long long>(4);
+  const int64_t T = pl.T, cap = pl.cap;
+  const size_t nblk = cl::targets_radix_blocks(cap);
+  cl::TargetsWs& t = w.tw;
+  t.err = w.err;
+  t.counts = c.take<int32_t>(4);
+  t.cnt = c.take<int32_t>(T + 1);
+  t.off = c.take<int32_t>(T + 1);
+  t.keyA = c.take<int32_t>(cap);
+  t.valA = c.take<int32_t>(cap);
+  t.keyB = c.take<int32_t>(cap);
+  t.valB = c.take<int32_t>(cap);
+  t.flags = c.take<int32_t>(cap + 1);
+  t.fscan = c.take<int32_t>(cap + 1);
+  t.hist = c.take<int32_t>(256 * nblk);
+  t.hscan = c.take<int32_t>(256 * nblk + 1);
+  t.csc_items = c.take<int32_t>(cap);
+  t.csc_rows = c.take<int32_t>(cap);
+  t.uitems = c.take<int32_t>(cap);
+  t.useg = c.take<int32_t>(cap + 1);
+  t.crow = c.take<int32_t>(T + 1);
+  t.cids = c.take<int32_t>(cap);
+  w.w = c.take<float>(T);
+  w.part_a = c.take<float>((size_t)pl.n_splits * T);
+  w.part_b = two_partials ? c.take<float>((size_t)pl.n_splits * T) : nullptr;
+  w.part_dA = need_dA ? c.take<float>((size_t)pl.n_splits * T * pl.D) : nullptr;
+  w.S_u = need_Su ? c.take<float>((size_t)cap * pl.D) : nullptr;
+  w.bytes = c.off;
+  return w;
+}
+
+cutloss_status check_common(int64_t T, int64_t D, int64_t V, const void* A, const void* E, int e_dtype) {
+  if (T < 0 || D <= 0 || V <= 0) return fail(CUTLOSS_ERR_INVALID_ARG, "bad sizes T=%lld D=%lld V=%lld", (long long)T, (long long)D, (long long)V);
+  if (T >= (1ll << 31) || V >= (1ll << 31)) return fail(CUTLOSS_ERR_INVALID_ARG, "T and V must be < 2^31");
+  if (D % 64 != 0) return fail(CUTLOSS_ERR_UNSUPPORTED, "D=%lld must be a multiple of 64", (long long)D);
+  if (D > 2304 * 4) return fail(CUTLOSS_ERR_UNSUPPORTED, "D=%lld too large", (long long)D);
+  if (e_dtype != CUTLOSS_BF16 && e_dtype != CUTLOSS_FP8_E4M3) return fail(CUTLOSS_ERR_INVALID_ARG, "unknown e_dtype %d", e_dtype);
+  if (T > 0 && (A == nullptr || !aligned(A, 16))) return fail(CUTLOSS_ERR_INVALID_ARG, "A must be a non-NULL 16-byte aligned device pointer");
+  if (E == nullptr || !aligned(E, 16)) return fail(CUTLOSS_ERR_INVALID_ARG, "E must be a non-NULL 16-byte aligned device pointer");
+  if (!cl::sweep_supported(D)) return fail(CUTLOSS_ERR_UNSUPPORTED, "D=%lld not supported by this build (64, 128, 256, 512)", (long long)D);
+  return CUTLOSS_OK;
+}
+
+cutloss_status check_bce(const cutloss_bce_problem* p) {
+  if (p == nullptr) return fail(CUTLOSS_ERR_INVALID_ARG, "problem is NULL");
+  cutloss_status s = check_common(p->T, p->D, p->V, p->A, p->E, p->e_dtype);
+  if (s != CUTLOSS_OK) return s;
+  if (p->nnz < 0 || p->nnz >= (1ll << 31)) return fail(CUTLOSS_ERR_INVALID_ARG, "bad nnz %lld", (long long)p->nnz);
+  if (p->T > 0 && (p->pos_row_ptr == nullptr || !aligned(p->pos_row_ptr, 4))) return fail(CUTLOSS_ERR_INVALID_ARG, "pos_row_ptr must be a non-NULL aligned device pointer");
+  if (p->nnz > 0 && (p->pos_ids == nullptr || !aligned(p->pos_ids, 4))) return fail(CUTLOSS_ERR_INVALID_ARG, "pos_ids must be a non-NULL aligned device pointer");
+  return CUTLOSS_OK;
+}
+
+cutloss_status check_ce(const cutloss_ce_problem* p) {
+  if (p == nullptr) return fail(CUTLOSS_ERR_INVALID_ARG, "problem is NULL");
+  cutloss_status s = check_common(p->T, p->D, p->V, p->A, p->E, p->e_dtype);
+  if (s != CUTLOSS_OK) return s;
+  if (p->T > 0 && (p->target == nullptr || !aligned(p->target, 8))) return fail(CUTLOSS_ERR_INVALID_ARG, "target must be a non-NULL 8-byte aligned device pointer");
+  return CUTLOSS_OK;
+}
+
+cutloss_status check_ws(void* ws, size_t have, size_t need) {
+  if (have < need) return fail(CUTLOSS_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", have, need);
+  if (need > 0 && (ws == nullptr || !aligned(ws, kAlign))) return fail(CUTLOSS_ERR_INVALID_ARG, "workspace must be a non-NULL 256-byte aligned device pointer");
+  return CUTLOSS_OK;
+}
+
+cutloss_status check_out(const void* ptr, size_t align, const char* name, bool required) {
+  if (ptr == nullptr) return required ? fail(CUTLOSS_ERR_INVALID_ARG, "%s is NULL", name) : CUTLOSS_OK;
+  if (!aligned(ptr, align)) return fail(CUTLOSS_ERR_INVALID_ARG, "%s must be %zu-byte aligned", name, align);
+  return CUTLOSS_OK;
+}
+
+#define CL_TRY(expr)                      \
+  do {                                    \
+    cutloss_status _s = (expr);           \
+    if (_s != CUTLOSS_OK) return _s;      \
+  } while (0)
+#define CL_HIP(expr, where) CL_TRY(hip_check((expr), where))
+
+// BCE pipeline shared by fwd / bwd / bwd_sgd.
+// want_loss: emit loss; want_dA; dE_mode: 0 none, 1 write dE, 2 SGD in place
+cutloss_status bce_run(const cutloss_bce_problem* p, const float* dloss, float* loss, void* dA, void* dE,
+                       int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st) {
+  const Plan pl = make_plan(p->T, p->D, p->V, p->nnz);
+  const bool rows_grad = dA != nullptr;
+  const bool need_Su = dE_mode != 0;
+  const Ws w = carve(ws, pl, rows_grad, need_Su, false);
+  CL_TRY(check_ws(ws, ws_bytes, w.bytes));
+  const int e_fp8 = p->e_dtype == CUTLOSS_FP8_E4M3;
+
+  {
+    Phase ph(CUTLOSS_PHASE_TARGETS, st);
+    CL_HIP(cl::launch_zero_u64(w.err, 4, st), "zero counters");
+    CL_HIP(cl::launch_targets(w.tw, p->T, p->V, p->nnz, p->pos_row_ptr, p->pos_ids, p->row_mask, p->pad_id,
+                              nullptr, 0, st), "targets");
+  }
+
+  cl::FinalizeParams fp{};
+  fp.T = p->T; fp.D = p->D; fp.V = p->V; fp.A = p->A; fp.E = p->E; fp.e_fp8 = e_fp8;
+  fp.crow = w.tw.crow; fp.cids = w.tw.cids; fp.dloss = dloss; fp.mask = p->row_mask;
+  fp.n_splits = pl.n_splits; fp.part_a = w.part_a; fp.part_dA = w.part_dA;
+  fp.loss = loss; fp.dA = dA; fp.w_out = w.w;
+
+  cl::SweepParams sp{};
+  sp.T = p->T; sp.D = p->D; sp.V = p->V; sp.A = p->A; sp.E = p->E; sp.e_fp8 = e_fp8;
+  sp.n_splits = pl.n_splits; sp.split_len = pl.split_len;
+  sp.part_a = w.part_a; sp.part_dA = w.part_dA;
+  sp.w = w.w; sp.uitems = w.tw.uitems; sp.counts = w.tw.counts; sp.S_u = w.S_u;
+  sp.dE = dE_mode == 1 ? dE : nullptr; sp.E_inplace = dE_mode == 2 ? (void*)p->E : nullptr; sp.lr = lr;
+
+  if (p->T > 0 && (loss != nullptr || rows_grad)) {
+    const int mode = rows_grad ? (loss ? 2 : 1) : 0;
+    {
+      Phase ph(CUTLOSS_PHASE_ROWS, st);
+      CL_HIP(cl::launch_sweep_rows(sp, mode, st), "rows sweep");
+    }
+    Phase ph(CUTLOSS_PHASE_FINALIZE, st);
+    CL_HIP(cl::launch_finalize_rows(fp, 0, loss != nullptr, rows_grad, st), "finalize rows");
+  }
+  if (dE_mode != 0) {
+    {
+      Phase ph(CUTLOSS_PHASE_ITEM_SUMS, st);
+      CL_HIP(cl::launch_row_weights(fp, 0, st), "row weights");
+      CL_HIP(cl::launch_item_sums(p->D, pl.cap, p->A, w.w, w.tw.csc_rows, w.tw.useg, w.tw.counts, w.S_u, st), "item sums");
+    }
+    Phase ph(CUTLOSS_PHASE_COLS, st);
+    CL_HIP(cl::launch_sweep_cols(sp, 0, dE_mode == 2 ? 1 : 0, st), "cols sweep");
+  }
+  return CUTLOSS_OK;
+}
+
+cutloss_status ce_run(const cutloss_ce_problem* p, const float* lse_in, const float* dloss, float* loss, float* lse,
+                      void* dA, void* dE, void* ws, size_t ws_bytes, hipStream_t st) {
+  const bool fwd = loss != nullptr;
+  const Plan pl = make_plan(p->T, p->D, p->V, p->T);
+  const Ws w = carve(ws, pl, dA != nullptr, dE != nullptr, fwd);
+  CL_TRY(check_ws(ws, ws_bytes, w.bytes));
+  const int e_fp8 = p->e_dtype == CUTLOSS_FP8_E4M3;
+
+  {
+    Phase ph(CUTLOSS_PHASE_TARGETS, st);
+    CL_HIP(cl::launch_zero_u64(w.err, 4, st), "zero counters");
+    CL_HIP(cl::launch_targets(w.tw, p->T, p->V, p->T, nullptr, nullptr, nullptr, -1, p->target, p->ignore_index, st), "targets");
+  }
+
+  cl::FinalizeParams fp{};
+  fp.T = p->T; fp.D = p->D; fp.V = p->V; fp.A = p->A; fp.E = p->E; fp.e_fp8 = e_fp8;
+  fp.crow = w.tw.crow; fp.cids = w.tw.cids; fp.dloss = dloss; fp.ce_target = p->target; fp.ignore_index = p->ignore_index;
+  fp.n_splits = pl.n_splits; fp.part_a = w.part_a; fp.part_b = w.part_b; fp.part_dA = w.part_dA;
+  fp.loss = loss; fp.lse = lse; fp.dA = dA; fp.w_out = w.w; fp.lse_in = lse_in;
+
+  cl::SweepParams sp{};
+  sp.T = p->T; sp.D = p->D; sp.V = p->V; sp.A = p->A; sp.E = p->E; sp.e_fp8 = e_fp8;
+  sp.n_splits = pl.n_splits; sp.split_len = pl.split_len;
+  sp.part_a = w.part_a; sp.part_b = w.part_b; sp.part_dA = w.part_dA;
+  sp.w = w.w; sp.lse = lse_in; sp.uitems = w.tw.uitems; sp.counts = w.tw.counts; sp.S_u = w.S_u; sp.dE = dE;
+
+  if (fwd) {
+    if (p->T > 0) {
+      {
+        Phase ph(CUTLOSS_PHASE_ROWS, st);
+        CL_HIP(cl::launch_sweep_rows(sp, 3, st), "rows sweep");
+      }
+      Phase ph(CUTLOSS_PHASE_FINALIZE, st);
+      CL_HIP(cl::launch_finalize_rows(fp, 1, 1, 0, st), "finalize rows");
+    }
+    return CUTLOSS_OK;
+  }
+  if (dA != nullptr && p->T > 0) {
+    {
+      Phase ph(CUTLOSS_PHASE_ROWS, st);
+      CL_HIP(cl::launch_sweep_rows(sp, 4, st), "rows sweep");
+    }
+    Phase ph(CUTLOSS_PHASE_FINALIZE, st);
+    CL_HIP(cl::launch_finalize_rows(fp, 1, 0, 1, st), "finalize rows");
+  }
+  if (dE != nullptr) {
+    {
+      Phase ph(CUTLOSS_PHASE_ITEM_SUMS, st);
+      CL_HIP(cl::launch_row_weights(fp, 1, st), "row weights");
+      CL_HIP(cl::launch_item_sums(p->D, pl.cap, p->A, w.w, w.tw.csc_rows, w.tw.useg, w.tw.counts, w.S_u, st), "item sums");
+    }
+    Phase ph(CUTLOSS_PHASE_COLS, st);
+    CL_HIP(cl::launch_sweep_cols(sp, 1, 0, st), "cols sweep");
+  }
+  return CUTLOSS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t cutloss_bce_workspace_size(const cutloss_bce_problem* p, int32_t op) {
+  if (check_bce(p) != CUTLOSS_OK) return 0;
+  const Plan pl = make_plan(p->T, p->D, p->V, p->nnz);
+  const bool bwd = op != CUTLOSS_OP_FWD;
+  return carve(nullptr, pl, bwd, bwd, false).bytes;
+}
+
+size_t cutloss_ce_workspace_size(const cutloss_ce_problem* p, int32_t op) {
+  if (check_ce(p) != CUTLOSS_OK) return 0;
+  const Plan pl = make_plan(p->T, p->D, p->V, p->T);
+  const bool bwd = op != CUTLOSS_OP_FWD;
+  return carve(nullptr, pl, bwd, bwd, !bwd).bytes;
+}
+
+cutloss_status cutloss_bce_fwd(const cutloss_bce_problem* p, float* loss, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  CL_TRY(check_bce(p));
+  CL_TRY(check_out(loss, 4, "loss", p->T > 0));
+  return bce_run(p, nullptr, loss, nullptr, nullptr, 0, 0.0f, ws, ws_bytes, (hipStream_t)stream);
+}
+
+cutloss_status cutloss_bce_bwd(const cutloss_bce_problem* p, const float* dloss, void* dA, void* dE, float* loss_out,
+                               void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  CL_TRY(check_bce(p));
+  CL_TRY(check_out(dloss, 4, "dloss", false));
+  CL_TRY(check_out(dA, 16, "dA", false));
+  CL_TRY(check_out(dE, 16, "dE", false));
+  CL_TRY(check_out(loss_out, 4, "loss_out", false));
+  return bce_run(p, dloss, loss_out, dA, dE, dE ? 1 : 0, 0.0f, ws, ws_bytes, (hipStream_t)stream);
+}
+
+cutloss_status cutloss_bce_bwd_sgd(const cutloss_bce_problem* p, const float* dloss, float lr, void* dA, float* loss_out,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  CL_TRY(check_bce(p));
+  CL_TRY(check_out(dloss, 4, "dloss", false));
+  CL_TRY(check_out(dA, 16, "dA", false));
+  CL_TRY(check_out(loss_out, 4, "loss_out", false));
+  if (!(lr == lr)) return fail(CUTLOSS_ERR_INVALID_ARG, "lr is NaN");
+  return bce_run(p, dloss, loss_out, dA, nullptr, 2, lr, ws, ws_bytes, (hipStream_t)stream);
+}
+
+cutloss_status cutloss_ce_fwd(const cutloss_ce_problem* p, float* loss, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  CL_TRY(check_ce(p));
+  CL_TRY(check_out(loss, 4, "loss", p->T > 0));
+  CL_TRY(check_out(lse, 4, "lse", p->T > 0));
+  return ce_run(p, nullptr, nullptr, loss, lse, nullptr, nullptr, ws, ws_bytes, (hipStream_t)stream);
+}
+
+cutloss_status cutloss_ce_bwd(const cutloss_ce_problem* p, const float* lse, const float* dloss, void* dA, void* dE,
+                              void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  CL_TRY(check_ce(p));
+  CL_TRY(check_out(lse, 4, "lse", p->T > 0));
+  CL_TRY(check_out(dloss, 4, "dloss", false));
+  CL_TRY(check_out(dA, 16, "dA", false));
+  CL_TRY(check_out(dE, 16, "dE", false));
+  return ce_run(p, lse, dloss, nullptr, nullptr, dA, dE, ws, ws_bytes, (hipStream_t)stream);
+}
+
+cutloss_status cutloss_read_data_errors(const void* ws, void* stream, int64_t* n_errors) {
+  g_last_error.clear();
+  if (ws == nullptr || n_errors == nullptr) return fail(CUTLOSS_ERR_INVALID_ARG, "NULL argument");
+  unsigned long long v = 0;
+  CL_HIP(hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, (hipStream_t)stream), "read error counter");
+  CL_HIP(hipStreamSynchronize((hipStream_t)stream), "synchronize");
+  *n_errors = (int64_t)v;
+  return CUTLOSS_OK;
+}
+
+cutloss_status cutloss_bce_canonical_targets(const cutloss_bce_problem* p, int32_t* crow, int32_t* cids, int32_t* items,
+                                             int32_t* rows, int64_t* n_unique_pairs, void* ws, size_t ws_bytes,
+                                             void* stream) {
+  g_last_error.clear();
+  CL_TRY(check_bce(p));
+  if (crow == nullptr || n_unique_pairs == nullptr || (p->nnz > 0 && (cids == nullptr || items == nullptr || rows == nullptr)))
+    return fail(CUTLOSS_ERR_INVALID_ARG, "NULL output");
+  hipStream_t st = (hipStream_t)stream;
+  const Plan pl = make_plan(p->T, p->D, p->V, p->nnz);
+  const Ws w = carve(ws, pl, false, false, false);
+  CL_TRY(check_ws(ws, ws_bytes, w.bytes));
+  CL_HIP(cl::launch_zero_u64(w.err, 4, st), "zero counters");
+  CL_HIP(cl::launch_targets(w.tw, p->T, p->V, p->nnz, p->pos_row_ptr, p->pos_ids, p->row_mask, p->pad_id, nullptr, 0, st), "targets");
+  int32_t n = 0;
+  CL_HIP(hipMemcpyAsync(&n, w.tw.counts + 1, sizeof(n), hipMemcpyDeviceToHost, st), "copy count");
+  CL_HIP(hipMemcpyAsync(crow, w.tw.crow, sizeof(int32_t) * (p->T + 1), hipMemcpyDeviceToDevice, st), "copy crow");
+  CL_HIP(hipStreamSynchronize(st), "synchronize");
+  if (n > 0) {
+    CL_HIP(hipMemcpyAsync(cids, w.tw.cids, sizeof(int32_t) * n, hipMemcpyDeviceToDevice, st), "copy cids");
+    CL_HIP(hipMemcpyAsync(items, w.tw.csc_items, sizeof(int32_t) * n, hipMemcpyDeviceToDevice, st), "copy items");
+    CL_HIP(hipMemcpyAsync(rows, w.tw.csc_rows, sizeof(int32_t) * n, hipMemcpyDeviceToDevice, st), "copy rows");
+    CL_HIP(hipStreamSynchronize(st), "synchronize");
+  }
+  *n_unique_pairs = n;
+  return CUTLOSS_OK;
+}
+
+cutloss_status cutloss_profile_enable(int32_t enable) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  g_prof_on = enable != 0;
+  return CUTLOSS_OK;
+}
+
+cutloss_status cutloss_profile_read(float* ms, int32_t* launches, int32_t n) {
+  g_last_error.clear();
+  if (n < 0 || (n > 0 && (ms == nullptr || launches == nullptr))) return fail(CUTLOSS_ERR_INVALID_ARG, "bad output arrays");
+  std::vector<PhaseRec> recs;
+  {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    recs.swap(g_prof);
+  }
+  for (int i = 0; i < n; ++i) { ms[i] = 0.0f; launches[i] = 0; }
+  cutloss_status st = CUTLOSS_OK;
+  for (const PhaseRec& r : recs) {
+    if (st == CUTLOSS_OK) {
+      hipError_t e = hipEventSynchronize(r.b);
+      float t = 0.0f;
+      if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
+      if (e != hipSuccess) st = hip_check(e, "profile events");
+      else if (r.phase < n) { ms[r.phase] += t; launches[r.phase] += 1; }
+    }
+  }
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  for (const PhaseRec& r : recs) { g_event_pool.push_back(r.a); g_event_pool.push_back(r.b); }
+  return st;
+}
+
+const char* cutloss_status_string(cutloss_status s) {
+  switch (s) {
+    case CUTLOSS_OK: return "ok";
+    case CUTLOSS_ERR_INVALID_ARG: return "invalid argument";
+    case CUTLOSS_ERR_UNSUPPORTED: return "unsupported";
+    case CUTLOSS_ERR_WORKSPACE: return "workspace too small";
+    case CUTLOSS_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* cutloss_last_error(void) { return g_last_error.c_str(); }
+
+const char* cutloss_version(void) { return "cutloss 0.1.0 gfx950"; }
+
+}  // extern "C"

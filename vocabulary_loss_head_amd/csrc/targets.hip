@@ -1,0 +1,343 @@
+// Canonical positive sets on the device.
+//
+// Cut Binary Cross Entropy (paperpeel) keeps only the sparse target IDs of each row
+// (§III-B), pads target lists and trains non-padding positions (§III-E), and tests
+// padded and duplicate IDs (§IV-A). The label y_tv is 1 exactly when v is in row t's
+// list, is not the padding ID and row t is valid; repeats count once. IDs outside
+// [0, V) are counted as data errors and ignored. For softmax CE the single target of
+// each non-ignored row is the one positive.
+//
+// Pipeline (every step deterministic, any row length):
+//   1. count valid entries per row, scan, compact (item, row) pairs in row order;
+//   2. stable LSD radix sort by item (8-bit digits) -> item-major order with
+//      repeats adjacent; keep the first of each (item, row) run -> CSC pairs;
+//   3. unique item list and its segment starts (for the dE sparse term);
+//   4. stable radix sort of the unique pairs by row -> canonical CSR (items
+//      ascending within a row).
+#include "common.h"
+
+namespace cl {
+
+constexpr int RS_TILE = 1024;
+
+size_t targets_radix_blocks(int64_t nnz) { return nnz <= 0 ? 1 : (size_t)((nnz + RS_TILE - 1) / RS_TILE); }
+
+__global__ void k_zero_u64(unsigned long long* p, int n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0ull;
+}
+
+hipError_t launch_zero_u64(unsigned long long* p, int n, hipStream_t st) {
+  k_zero_u64<<<(n + 255) / 256, 256, 0, st>>>(p, n);
+  return hipGetLastError();
+}
+
+// ---- step 1 -------------------------------------------------------------------------
+__global__ void k_row_count(int64_t T, int64_t V, int64_t nnz, const int32_t* __restrict__ row_ptr,
+                            const int32_t* __restrict__ ids, const uint8_t* __restrict__ mask, int32_t pad,
+                            int32_t* __restrict__ cnt, unsigned long long* err) {
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  int64_t b = row_ptr[t], e = row_ptr[t + 1];
+  if (b < 0 || e > nnz || e < b) {            // malformed row: a data error, no positives
+    atomicAdd(err, 1ull);
+    cnt[t] = 0;
+    return;
+  }
+  if (mask != nullptr && mask[t] == 0) { cnt[t] = 0; return; }
+  int c = 0;
+  unsigned long long bad = 0;
+  for (int64_t i = b; i < e; ++i) {
+    int32_t v = ids[i];
+    if (pad >= 0 && v == pad) continue;
+    if (v < 0 || (int64_t)v >= V) { ++bad; continue; }
+    ++c;
+  }
+  if (bad) atomicAdd(err, bad);
+  cnt[t] = c;
+}
+
+__global__ void k_row_count_ce(int64_t T, int64_t V, const int64_t* __restrict__ target, int64_t ignore,
+                               int32_t* __restrict__ cnt, unsigned long long* err) {
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  int64_t y = target[t];
+  int c = 0;
+  if (y != ignore) {
+    if (y >= 0 && y < V) c = 1;
+    else atomicAdd(err, 1ull);
+  }
+  cnt[t] = c;
+}
+
+__global__ void k_row_compact(int64_t T, int64_t V, int64_t nnz, const int32_t* __restrict__ row_ptr,
+                              const int32_t* __restrict__ ids, const int32_t* __restrict__ cnt,
+                              const int32_t* __restrict__ off, int32_t pad,
+                              int32_t* __restrict__ key, int32_t* __restrict__ val) {
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  if (cnt[t] == 0) return;                    // masked, malformed or no valid entries
+  int64_t b = row_ptr[t], e = row_ptr[t + 1];
+  int64_t o = off[t];
+  for (int64_t i = b; i < e; ++i) {
+    int32_t v = ids[i];
+    if (pad >= 0 && v == pad) continue;
+    if (v < 0 || (int64_t)v >= V) continue;
+    if (o >= nnz) break;                      // overlapping rows of a non-monotone row_ptr
+    key[o] = v;
+    val[o] = (int32_t)t;
+    ++o;
+  }
+}
+
+// Overlapping rows (a non-monotone row_ptr) can count more valid entries than nnz: the
+// excess is a data error and the pair count is clamped to the array capacity.
+__global__ void k_clamp_count(int32_t* counts, int64_t cap, unsigned long long* err) {
+  if (threadIdx.x == 0 && blockIdx.x == 0 && (int64_t)counts[0] > cap) {
+    atomicAdd(err, (unsigned long long)((int64_t)counts[0] - cap));
+    counts[0] = (int32_t)cap;
+  }
+}
+
+__global__ void k_row_compact_ce(int64_t T, const int64_t* __restrict__ target, const int32_t* __restrict__ cnt,
+                                 const int32_t* __restrict__ off, int32_t* __restrict__ key, int32_t* __restrict__ val) {
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  if (cnt[t] == 0) return;
+  key[off[t]] = (int32_t)target[t];
+  val[off[t]] = (int32_t)t;
+}
+
+// Single-workgroup exclusive scan: out[i] = sum in[0..i), out[n] = total.
+// If n_dev != NULL the length is min(n, *n_dev) and entries past it read as 0.
+__global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ in, int64_t n, const int32_t* n_dev,
+                                               int32_t* __restrict__ out, int32_t* total_out) {
+  __shared__ int32_t s[1024];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x;
+  int64_t m = n;
+  if (n_dev != nullptr) m = min((int64_t)*n_dev, n);
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int64_t base = 0; base < n; base += 4096) {
+    int v[4];
+    int64_t i0 = base + (int64_t)tid * 4;
+    int local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = (i0 + j < m) ? in[i0 + j] : 0;
+      local += v[j];
+    }
+    s[tid] = local;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+      int t = tid >= o ? s[tid - o] : 0;
+      __syncthreads();
+      s[tid] += t;
+      __syncthreads();
+    }
+    int run = s[tid] - local + carry;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (i0 + j < n) out[i0 + j] = run;
+      run += v[j];
+    }
+    __syncthreads();
+    if (tid == 1023) carry += s[1023];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    out[n] = carry;
+    if (total_out != nullptr) *total_out = carry;
+  }
+}
+
+// ---- radix sort (stable, 8-bit digits) ------------------------------------------------
+__global__ __launch_bounds__(256) void k_rs_hist(const int32_t* __restrict__ kin, const int32_t* n_dev, int shift,
+                                                 int32_t* __restrict__ hist, int nblk) {
+  __shared__ int32_t h[256];
+  const int tid = threadIdx.x;
+  h[tid] = 0;
+  __syncthreads();
+  const int64_t n = *n_dev;
+  const int64_t b = blockIdx.x;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int64_t i = b * RS_TILE + j * 256 + tid;
+    if (i < n) atomicAdd(&h[((uint32_t)kin[i] >> shift) & 255u], 1);
+  }
+  __syncthreads();
+  hist[(int64_t)tid * nblk + b] = h[tid];
+}
+
+__global__ __launch_bounds__(256) void k_rs_scatter(const int32_t* __restrict__ kin, const int32_t* __restrict__ vin,
+                                                    int32_t* __restrict__ kout, int32_t* __restrict__ vout,
+                                                    const int32_t* n_dev, int shift,
+                                                    const int32_t* __restrict__ hscan, int nblk) {
+  __shared__ int32_t run[256];
+  __shared__ int32_t wcnt[4][256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t b = blockIdx.x;
+  const int64_t n = *n_dev;
+  run[tid] = hscan[(int64_t)tid * nblk + b];
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) wcnt[k][tid] = 0;
+    __syncthreads();
+    const int64_t i = b * RS_TILE + j * 256 + tid;
+    const bool act = i < n;
+    const int32_t key = act ? kin[i] : 0;
+    const int32_t val = act ? vin[i] : 0;
+    const uint32_t d = ((uint32_t)key >> shift) & 255u;
+    unsigned long long peers = __ballot(act);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool on = (d >> bit) & 1u;
+      const unsigned long long bb = __ballot(on);
+      peers &= on ? bb : ~bb;
+    }
+    const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+    if (act && rank == 0) wcnt[w][d] = __popcll(peers);
+    __syncthreads();
+    if (act) {
+      int pre = 0;
+      for (int k = 0; k < w; ++k) pre += wcnt[k][d];
+      const int pos = run[d] + pre + rank;
+      kout[pos] = key;
+      vout[pos] = val;
+    }
+    __syncthreads();
+    run[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
+    __syncthreads();
+  }
+}
+
+// ---- dedupe / unique items / row pointers ------------------------------------------------
+__global__ void k_flag_pairs(const int32_t* __restrict__ key, const int32_t* __restrict__ val, const int32_t* n_dev,
+                             int64_t cap, int32_t* __restrict__ flags) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= cap) return;
+  const int64_t n = *n_dev;
+  int f = 0;
+  if (i < n) f = (i == 0 || key[i] != key[i - 1] || val[i] != val[i - 1]) ? 1 : 0;
+  flags[i] = f;
+}
+
+__global__ void k_compact_pairs(const int32_t* __restrict__ key, const int32_t* __restrict__ val,
+                                const int32_t* __restrict__ flags, const int32_t* __restrict__ fscan,
+                                const int32_t* n_dev, int64_t cap,
+                                int32_t* __restrict__ items, int32_t* __restrict__ rows) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= cap || i >= *n_dev) return;
+  if (flags[i]) {
+    items[fscan[i]] = key[i];
+    rows[fscan[i]] = val[i];
+  }
+}
+
+__global__ void k_flag_items(const int32_t* __restrict__ items, const int32_t* n_dev, int64_t cap,
+                             int32_t* __restrict__ flags) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= cap) return;
+  const int64_t n = *n_dev;
+  flags[i] = (i < n && (i == 0 || items[i] != items[i - 1])) ? 1 : 0;
+}
+
+__global__ void k_compact_items(const int32_t* __restrict__ items, const int32_t* __restrict__ flags,
+                                const int32_t* __restrict__ fscan, const int32_t* n_dev, const int32_t* nu_dev,
+                                int64_t cap, int32_t* __restrict__ uitems, int32_t* __restrict__ useg) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = *n_dev;
+  if (i == 0) useg[*nu_dev] = (int32_t)n;
+  if (i >= cap || i >= n) return;
+  if (flags[i]) {
+    uitems[fscan[i]] = items[i];
+    useg[fscan[i]] = (int32_t)i;
+  }
+}
+
+__global__ void k_copy2(const int32_t* __restrict__ a, const int32_t* __restrict__ b, const int32_t* n_dev,
+                        int64_t cap, int32_t* __restrict__ a2, int32_t* __restrict__ b2) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= cap || i >= *n_dev) return;
+  a2[i] = a[i];
+  b2[i] = b[i];
+}
+
+__global__ void k_row_ptr(const int32_t* __restrict__ rows_sorted, const int32_t* n_dev, int64_t cap, int64_t T,
+                          int32_t* __restrict__ crow) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = *n_dev;
+  if (i > cap || i > n) return;
+  const int64_t r_prev = (i == 0) ? -1 : rows_sorted[i - 1];
+  const int64_t r_cur = (i == n) ? T : rows_sorted[i];
+  for (int64_t r = r_prev + 1; r <= r_cur; ++r) crow[r] = (int32_t)i;
+}
+
+static int bits_for(int64_t n) {  // bits needed for values in [0, n)
+  int b = 0;
+  while (b < 62 && ((int64_t)1 << b) < n) ++b;
+  return b;
+}
+
+static inline unsigned grid_for(int64_t n, int bs) { return (unsigned)((n + bs - 1) / bs > 0 ? (n + bs - 1) / bs : 1); }
+
+// Radix-sort (key, val) pairs held in (kA, vA) by key bits [0, nbits); returns true if the
+// result ended in (kB, vB).
+static bool radix_sort(const TargetsWs& w, int32_t* kA, int32_t* vA, int32_t* kB, int32_t* vB,
+                       const int32_t* n_dev, int64_t cap, int nbits, hipStream_t st) {
+  const int nblk = (int)targets_radix_blocks(cap);
+  bool inB = false;
+  for (int shift = 0; shift < nbits; shift += 8) {
+    const int32_t* ki = inB ? kB : kA;
+    const int32_t* vi = inB ? vB : vA;
+    int32_t* ko = inB ? kA : kB;
+    int32_t* vo = inB ? vA : vB;
+    k_rs_hist<<<nblk, 256, 0, st>>>(ki, n_dev, shift, w.hist, nblk);
+    k_scan<<<1, 1024, 0, st>>>(w.hist, (int64_t)256 * nblk, nullptr, w.hscan, nullptr);
+    k_rs_scatter<<<nblk, 256, 0, st>>>(ki, vi, ko, vo, n_dev, shift, w.hscan, nblk);
+    inB = !inB;
+  }
+  return inB;
+}
+
+hipError_t launch_targets(const TargetsWs& w, int64_t T, int64_t V, int64_t nnz,
+                          const int32_t* row_ptr, const int32_t* ids, const uint8_t* mask, int32_t pad_id,
+                          const int64_t* ce_target, int64_t ignore_index, hipStream_t st) {
+  const int64_t cap = ce_target ? T : nnz;     // capacity of every pair array
+  // 1. valid entries per row, their offsets, compacted (item, row) pairs in row order
+  if (ce_target) {
+    k_row_count_ce<<<grid_for(T, 256), 256, 0, st>>>(T, V, ce_target, ignore_index, w.cnt, w.err);
+  } else {
+    k_row_count<<<grid_for(T, 256), 256, 0, st>>>(T, V, nnz, row_ptr, ids, mask, pad_id, w.cnt, w.err);
+  }
+  k_scan<<<1, 1024, 0, st>>>(w.cnt, T, nullptr, w.off, w.counts + 0);
+  k_clamp_count<<<1, 64, 0, st>>>(w.counts, cap, w.err);
+  if (ce_target) {
+    k_row_compact_ce<<<grid_for(T, 256), 256, 0, st>>>(T, ce_target, w.cnt, w.off, w.keyA, w.valA);
+  } else {
+    k_row_compact<<<grid_for(T, 256), 256, 0, st>>>(T, V, nnz, row_ptr, ids, w.cnt, w.off, pad_id, w.keyA, w.valA);
+  }
+  // 2. item-major order, repeats removed
+  const bool inB = radix_sort(w, w.keyA, w.valA, w.keyB, w.valB, w.counts + 0, cap, bits_for(V), st);
+  const int32_t* ks = inB ? w.keyB : w.keyA;
+  const int32_t* vs = inB ? w.valB : w.valA;
+  const unsigned g = grid_for(cap + 1, 256);
+  k_flag_pairs<<<g, 256, 0, st>>>(ks, vs, w.counts + 0, cap, w.flags);
+  k_scan<<<1, 1024, 0, st>>>(w.flags, cap, nullptr, w.fscan, w.counts + 1);
+  k_compact_pairs<<<g, 256, 0, st>>>(ks, vs, w.flags, w.fscan, w.counts + 0, cap, w.csc_items, w.csc_rows);
+  // 3. unique items and segment starts
+  k_flag_items<<<g, 256, 0, st>>>(w.csc_items, w.counts + 1, cap, w.flags);
+  k_scan<<<1, 1024, 0, st>>>(w.flags, cap, nullptr, w.fscan, w.counts + 2);
+  k_compact_items<<<g, 256, 0, st>>>(w.csc_items, w.flags, w.fscan, w.counts + 1, w.counts + 2, cap, w.uitems, w.useg);
+  // 4. canonical CSR: stable sort of the unique pairs by row
+  k_copy2<<<g, 256, 0, st>>>(w.csc_rows, w.csc_items, w.counts + 1, cap, w.keyA, w.valA);
+  const bool inB2 = radix_sort(w, w.keyA, w.valA, w.keyB, w.valB, w.counts + 1, cap, bits_for(T), st);
+  const int32_t* rs = inB2 ? w.keyB : w.keyA;
+  const int32_t* is = inB2 ? w.valB : w.valA;
+  k_copy2<<<g, 256, 0, st>>>(is, is, w.counts + 1, cap, w.cids, w.cids);
+  k_row_ptr<<<grid_for(cap + 1, 256), 256, 0, st>>>(rs, w.counts + 1, cap, T, w.crow);
+  return hipGetLastError();
+}
+
+}  // namespace cl
