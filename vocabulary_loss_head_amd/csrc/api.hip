@@ -12,6 +12,16 @@
 
 namespace {
 
+hipError_t rows_sweep(const cl::SweepParams& sp, int mode, hipStream_t st) {
+  if (cl::sweep2_rows_supported(sp.D, sp.e_fp8)) return cl::launch_sweep2_rows(sp, mode, st);
+  return cl::launch_sweep_rows(sp, mode, st);
+}
+
+hipError_t cols_sweep(const cl::SweepParams& sp, int kind, int epi, hipStream_t st) {
+  if (cl::sweep2_cols_supported(sp.D)) return cl::launch_sweep2_cols(sp, kind, epi, st);
+  return cl::launch_sweep_cols(sp, kind, epi, st);
+}
+
 // ---- phase profiling (cutloss_profile_enable / cutloss_profile_read)
 struct PhaseRec {
   int phase;
@@ -95,10 +105,15 @@ struct Plan {
   int64_t split_len;
 };
 
-Plan make_plan(int64_t T, int64_t D, int64_t V, int64_t cap) {
+// Vocabulary splits of the rows sweep: enough (row block, split) workgroups to fill the
+// chip about twice; a multiple of 8 so each split maps to one XCD.
+Plan make_plan(int64_t T, int64_t D, int64_t V, int64_t cap, int e_fp8) {
   Plan pl{T, D, V, cap, 1, 0};
-  const int64_t nsb = (T + 127) / 128;
-  int64_t ns = nsb > 0 ? (1024 + nsb - 1) / nsb : 1;
+  const bool v2 = cl::sweep2_rows_supported(D, e_fp8);
+  const int64_t rpb = v2 ? cl::sweep2_rows_per_block(D) : 128;
+  const int64_t target = 1024;
+  const int64_t nsb = (T + rpb - 1) / rpb;
+  int64_t ns = nsb > 0 ? (target + nsb - 1) / nsb : 1;
   const int64_t max_ns = (V + 31) / 32;
   if (ns > max_ns) ns = max_ns;
   if (ns > 256) ns = 256;
@@ -210,7 +225,7 @@ cutloss_status check_out(const void* ptr, size_t align, const char* name, bool r
 // want_loss: emit loss; want_dA; dE_mode: 0 none, 1 write dE, 2 SGD in place
 cutloss_status bce_run(const cutloss_bce_problem* p, const float* dloss, float* loss, void* dA, void* dE,
                        int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st) {
-  const Plan pl = make_plan(p->T, p->D, p->V, p->nnz);
+  const Plan pl = make_plan(p->T, p->D, p->V, p->nnz, p->e_dtype == CUTLOSS_FP8_E4M3);
   const bool rows_grad = dA != nullptr;
   const bool need_Su = dE_mode != 0;
   const Ws w = carve(ws, pl, rows_grad, need_Su, false);
@@ -241,7 +256,7 @@ cutloss_status bce_run(const cutloss_bce_problem* p, const float* dloss, float* 
     const int mode = rows_grad ? (loss ? 2 : 1) : 0;
     {
       Phase ph(CUTLOSS_PHASE_ROWS, st);
-      CL_HIP(cl::launch_sweep_rows(sp, mode, st), "rows sweep");
+      CL_HIP(rows_sweep(sp, mode, st), "rows sweep");
     }
     Phase ph(CUTLOSS_PHASE_FINALIZE, st);
     CL_HIP(cl::launch_finalize_rows(fp, 0, loss != nullptr, rows_grad, st), "finalize rows");
@@ -253,7 +268,7 @@ cutloss_status bce_run(const cutloss_bce_problem* p, const float* dloss, float* 
       CL_HIP(cl::launch_item_sums(p->D, pl.cap, p->A, w.w, w.tw.csc_rows, w.tw.useg, w.tw.counts, w.S_u, st), "item sums");
     }
     Phase ph(CUTLOSS_PHASE_COLS, st);
-    CL_HIP(cl::launch_sweep_cols(sp, 0, dE_mode == 2 ? 1 : 0, st), "cols sweep");
+    CL_HIP(cols_sweep(sp, 0, dE_mode == 2 ? 1 : 0, st), "cols sweep");
   }
   return CUTLOSS_OK;
 }
@@ -261,7 +276,7 @@ cutloss_status bce_run(const cutloss_bce_problem* p, const float* dloss, float* 
 cutloss_status ce_run(const cutloss_ce_problem* p, const float* lse_in, const float* dloss, float* loss, float* lse,
                       void* dA, void* dE, void* ws, size_t ws_bytes, hipStream_t st) {
   const bool fwd = loss != nullptr;
-  const Plan pl = make_plan(p->T, p->D, p->V, p->T);
+  const Plan pl = make_plan(p->T, p->D, p->V, p->T, p->e_dtype == CUTLOSS_FP8_E4M3);
   const Ws w = carve(ws, pl, dA != nullptr, dE != nullptr, fwd);
   CL_TRY(check_ws(ws, ws_bytes, w.bytes));
   const int e_fp8 = p->e_dtype == CUTLOSS_FP8_E4M3;
@@ -288,7 +303,7 @@ cutloss_status ce_run(const cutloss_ce_problem* p, const float* lse_in, const fl
     if (p->T > 0) {
       {
         Phase ph(CUTLOSS_PHASE_ROWS, st);
-        CL_HIP(cl::launch_sweep_rows(sp, 3, st), "rows sweep");
+        CL_HIP(rows_sweep(sp, 3, st), "rows sweep");
       }
       Phase ph(CUTLOSS_PHASE_FINALIZE, st);
       CL_HIP(cl::launch_finalize_rows(fp, 1, 1, 0, st), "finalize rows");
@@ -298,7 +313,7 @@ cutloss_status ce_run(const cutloss_ce_problem* p, const float* lse_in, const fl
   if (dA != nullptr && p->T > 0) {
     {
       Phase ph(CUTLOSS_PHASE_ROWS, st);
-      CL_HIP(cl::launch_sweep_rows(sp, 4, st), "rows sweep");
+      CL_HIP(rows_sweep(sp, 4, st), "rows sweep");
     }
     Phase ph(CUTLOSS_PHASE_FINALIZE, st);
     CL_HIP(cl::launch_finalize_rows(fp, 1, 0, 1, st), "finalize rows");
@@ -310,7 +325,7 @@ cutloss_status ce_run(const cutloss_ce_problem* p, const float* lse_in, const fl
       CL_HIP(cl::launch_item_sums(p->D, pl.cap, p->A, w.w, w.tw.csc_rows, w.tw.useg, w.tw.counts, w.S_u, st), "item sums");
     }
     Phase ph(CUTLOSS_PHASE_COLS, st);
-    CL_HIP(cl::launch_sweep_cols(sp, 1, 0, st), "cols sweep");
+    CL_HIP(cols_sweep(sp, 1, 0, st), "cols sweep");
   }
   return CUTLOSS_OK;
 }
@@ -321,14 +336,14 @@ extern "C" {
 
 size_t cutloss_bce_workspace_size(const cutloss_bce_problem* p, int32_t op) {
   if (check_bce(p) != CUTLOSS_OK) return 0;
-  const Plan pl = make_plan(p->T, p->D, p->V, p->nnz);
+  const Plan pl = make_plan(p->T, p->D, p->V, p->nnz, p->e_dtype == CUTLOSS_FP8_E4M3);
   const bool bwd = op != CUTLOSS_OP_FWD;
   return carve(nullptr, pl, bwd, bwd, false).bytes;
 }
 
 size_t cutloss_ce_workspace_size(const cutloss_ce_problem* p, int32_t op) {
   if (check_ce(p) != CUTLOSS_OK) return 0;
-  const Plan pl = make_plan(p->T, p->D, p->V, p->T);
+  const Plan pl = make_plan(p->T, p->D, p->V, p->T, p->e_dtype == CUTLOSS_FP8_E4M3);
   const bool bwd = op != CUTLOSS_OP_FWD;
   return carve(nullptr, pl, bwd, bwd, !bwd).bytes;
 }
@@ -399,7 +414,7 @@ cutloss_status cutloss_bce_canonical_targets(const cutloss_bce_problem* p, int32
   if (crow == nullptr || n_unique_pairs == nullptr || (p->nnz > 0 && (cids == nullptr || items == nullptr || rows == nullptr)))
     return fail(CUTLOSS_ERR_INVALID_ARG, "NULL output");
   hipStream_t st = (hipStream_t)stream;
-  const Plan pl = make_plan(p->T, p->D, p->V, p->nnz);
+  const Plan pl = make_plan(p->T, p->D, p->V, p->nnz, p->e_dtype == CUTLOSS_FP8_E4M3);
   const Ws w = carve(ws, pl, false, false, false);
   CL_TRY(check_ws(ws, ws_bytes, w.bytes));
   CL_HIP(cl::launch_zero_u64(w.err, 4, st), "zero counters");

@@ -144,13 +144,19 @@ struct SweepParams {
   float lr;
 };
 
-// mode: 0 = BCE forward only (loss partials), 1 = BCE backward rows (dA partials,
-// optional loss partials when part_a != NULL), 2 = CE forward (max/sum partials),
-// 3 = CE backward rows (dA partials)
+// Rows sweep modes: 0 = BCE loss partials, 1 = BCE dA partials, 2 = BCE dA + loss partials,
+// 3 = CE (max, sum) partials, 4 = CE dA partials.
+// Cols sweep: kind 0 = BCE, 1 = CE; epi 0 = write dE (bf16), 1 = SGD step on E in place.
+// sweep.hip: register-staged sweeps (any supported D, bf16 or fp8 streamed E);
+// sweep2.hip: LDS-DMA sweeps at two workgroups per CU (bf16 streamed operand, D <= 256).
 hipError_t launch_sweep_rows(const SweepParams& p, int mode, hipStream_t st);
-// kind: 0 = BCE, 1 = CE; epi: 0 = write dE bf16, 1 = SGD in place
 hipError_t launch_sweep_cols(const SweepParams& p, int kind, int epi, hipStream_t st);
 bool sweep_supported(int64_t D);
+hipError_t launch_sweep2_rows(const SweepParams& p, int mode, hipStream_t st);
+hipError_t launch_sweep2_cols(const SweepParams& p, int kind, int epi, hipStream_t st);
+bool sweep2_rows_supported(int64_t D, int e_fp8);
+bool sweep2_cols_supported(int64_t D);
+int sweep2_rows_per_block(int64_t D);   // stationary rows per workgroup of the LDS-DMA rows sweep
 
 struct FinalizeParams {
   int64_t T, D, V;

@@ -1,0 +1,660 @@
+// Logit-tile sweeps for bf16 streamed operands and D in {64, 128, 256} (gfx950).
+//
+// Same computation as the register-staged sweeps in sweep.hip (derivation from Cut
+// Binary Cross Entropy §III-A..C and the Cut Your Losses article there), arranged for
+// measured CDNA4 limits:
+//  * each wave holds MT 32-row tiles of the stationary matrix (64 rows for D = 256), so
+//    every LDS read of a streamed chunk feeds MT MFMAs in the logit product and in the
+//    gradient product: half the LDS traffic per MFMA of a one-tile wave;
+//  * gradient modes overlap VALU and matrix work inside each wave: the sigmoid/exp
+//    epilogue of chunk c is issued in one basic block with the gradient MFMAs of chunk
+//    c-1 (shaped by sched_group_barrier), so the epilogue hides under matrix work;
+//  * streamed 32-row chunks go HBM/L2 -> LDS by global_load_lds_dwordx4 (no staging
+//    registers, no ds_write) into a 4-buffer ring inside one LDS array. Each step waits
+//    for its own DMA with an explicit vmcnt, one s_barrier publishes the chunk to the
+//    workgroup and retires the oldest buffer, and the next DMA is issued right after;
+//  * rows past the end of a range are fetched as copies of the last valid row (never
+//    out of bounds) and their logits are set to -inf, which makes every epilogue
+//    (softplus, sigmoid, exp) contribute exactly zero.
+//
+// LDS layout of a chunk: row r, 16-byte piece c stored at piece c ^ f(r) (swz in
+// common.h). A DMA instruction writes 1 KB lane-linearly, so lane i of block kb fetches
+// the logical piece that belongs at physical byte kb*1024 + 16 i. The XOR touches the
+// same address bits as the per-iteration steps of both read patterns, so every read
+// address is one per-lane base XOR a constant, plus the ring offset.
+#include "common.h"
+
+#define CL_GAS __attribute__((address_space(1)))
+
+namespace cl {
+
+namespace {
+
+constexpr int kRC = 32;          // streamed rows per chunk
+constexpr int kRing = 4;         // LDS buffers
+constexpr float kNegInf = -__builtin_inff();
+
+template <int D>
+struct Geo {
+  static constexpr int NCH = D / 8;             // 16-byte pieces per row
+  static constexpr int ROW = 2 * D;             // bytes per row
+  static constexpr int BYTES = kRC * ROW;       // one chunk
+  static constexpr int KB = BYTES / 1024;       // 1 KB DMA blocks per chunk
+  static constexpr int LPW = KB / 4;            // DMA instructions per wave
+  static_assert(KB % 4 == 0 && LPW >= 1, "unsupported D");
+};
+
+// tiles per wave and waves per SIMD for each D
+template <int D> struct Tiling;
+template <> struct Tiling<64> { static constexpr int MT = 2, WPE = 2; };
+template <> struct Tiling<128> { static constexpr int MT = 2, WPE = 1; };
+template <> struct Tiling<256> { static constexpr int MT = 1, WPE = 2; };
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+template <class T>
+__device__ __forceinline__ const CL_LDS T* lds_ptr(uint32_t a) { return (const CL_LDS T*)(uintptr_t)a; }
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt[3:0], expcnt[6:4] = 7, lgkmcnt[11:8] = 15).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0xF70 | N);
+}
+
+__device__ __forceinline__ void block_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// Fetch rows [row0, row0 + 32) of a row-major bf16 [*, D] matrix into the LDS buffer at
+// byte address `buf`; rows at or past `row_end` (> row0) are fetched as copies of
+// row_end - 1. `wv` is wave-uniform, so each instruction's LDS destination is scalar.
+template <int D>
+__device__ __forceinline__ void dma_chunk(const uint16_t* base, int64_t row0, int64_t row_end, uint32_t buf, int wv,
+                                          int lane) {
+  using G = Geo<D>;
+  const char* cbase = (const char*)(base + row0 * D);       // wave-uniform
+  const int lim = (int)min((int64_t)(kRC - 1), row_end - 1 - row0);
+  // the per-lane offsets are a few VALU ops: recompute them at every issue instead of
+  // keeping them live across the loop (an opaque copy of the lane id stops hoisting)
+  asm volatile("" : "+v"(lane));
+#pragma unroll
+  for (int j = 0; j < G::LPW; ++j) {
+    const int kb = wv * G::LPW + j;
+    const int byte = kb * 1024 + lane * 16;
+    const int r = byte / G::ROW;
+    const int pc = (byte % G::ROW) / 16;
+    const int lc = swz<G::NCH>(pc, r);          // swz is an involution
+    const uint32_t off = (uint32_t)((min(r, lim) * D + lc * 8) * 2);
+    __builtin_amdgcn_global_load_lds((const CL_GAS void*)(cbase + off), (CL_LDS void*)(uintptr_t)(buf + kb * 1024),
+                                     16, 0, 0);
+  }
+}
+
+// 32 floats [row0, row0 + 32) of v (clamped to n - 1) into LDS at `buf` (lanes 0..31).
+__device__ __forceinline__ void dma_vec(const float* v, int64_t row0, int64_t n, uint32_t buf, int lane) {
+  int64_t r = row0 + (lane & 31);
+  r = r < n ? r : n - 1;
+  if (lane < 32) __builtin_amdgcn_global_load_lds((const CL_GAS void*)(v + r), (CL_LDS void*)(uintptr_t)buf, 4, 0, 0);
+}
+
+template <int D, bool FP8>
+__device__ __forceinline__ void load_stationary(bf16x8 (&sf)[D / 16], const void* base, int64_t row, bool ok, int h) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    if (!ok) { sf[ks] = bf16x8{}; continue; }
+    if constexpr (FP8) {
+      const uint2 q = *(const uint2*)((const uint8_t*)base + row * D + 16 * ks + 8 * h);
+      sf[ks] = fp8x8_to_bf16x8(q);
+    } else {
+      sf[ks] = *(const bf16x8*)((const uint16_t*)base + row * D + 16 * ks + 8 * h);
+    }
+  }
+}
+
+// chunk row held in result register i of a lane with half h
+__device__ __forceinline__ int res_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+
+__device__ __forceinline__ int swz_f(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+// Per-lane LDS read bases of a chunk at ring offset 0.
+//  rowb: 16-byte read of logical piece 2ks+h of row l32 = rowb ^ (32 ks)
+//  trA/trB: transposed 8-byte reads of column tile nt, rows 4h+rsub (+8) = tr ^ (64 nt),
+//           plus 16 rows (kk = 1) = + 16 * ROW
+template <int D>
+struct ReadBase {
+  uint32_t rowb, trA, trB;
+  __device__ __forceinline__ void init(uint32_t ring, int lane) {
+    using G = Geo<D>;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int fm = swz_f(l32) & (G::NCH - 1);
+    rowb = ring + l32 * G::ROW + 16 * ((fm & ~1) | (h ^ (fm & 1)));
+    const int rsub = (lane & 15) >> 2;
+    const int c0 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int co = 8 * (lane & 1);
+    const int rA = 4 * h + rsub, rB = rA + 8;
+    trA = ring + rA * G::ROW + co + 16 * (c0 ^ (swz_f(rA) & (G::NCH - 1)));
+    trB = ring + rB * G::ROW + co + 16 * (c0 ^ (swz_f(rB) & (G::NCH - 1)));
+  }
+};
+
+template <int D>
+__device__ __forceinline__ bf16x8 read_row_piece(const ReadBase<D>& rb, uint32_t boff, int ks) {
+  return *lds_ptr<bf16x8>((rb.rowb ^ (uint32_t)(32 * ks)) + boff);
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 read_col_piece(const ReadBase<D>& rb, uint32_t boff, int nt, int kk) {
+  const uint32_t o = boff + (uint32_t)(kk * 16 * Geo<D>::ROW);
+  const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CL_LDS s16x4*)(uintptr_t)((rb.trA ^ (uint32_t)(64 * nt)) + o));
+  const s16x4 b2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CL_LDS s16x4*)(uintptr_t)((rb.trB ^ (uint32_t)(64 * nt)) + o));
+  return cat_bf16(b1, b2);
+}
+
+// Logits of chunk rows at or past `lim` (chunk-relative, wave-uniform) become -inf.
+template <int MT>
+__device__ __forceinline__ void mask_tail(f32x16 (&y)[MT], int lim, int h) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) y[mt][i] = (res_row(i, h) < lim) ? y[mt][i] : kNegInf;
+}
+
+// ------------------------------------------------------------------------------------
+// Epilogue of one chunk for MT tiles, visited element by element so that a caller can
+// interleave it with matrix work.
+//   RM 0: BCE softplus sum + sigmoid (F)      RM 1: sigmoid only
+//   RM 2: BCE softplus sum only                RM 3: CE running (max, sum)
+//   RM 4: exp(x - lse_row) (CE rows gradient)  RM 5: w_r * sigmoid(x) (BCE cols)
+//   RM 6: w_r * exp(x - lse_r) (CE cols)
+// ------------------------------------------------------------------------------------
+template <int MT, int RM>
+struct Epi {
+  float relu[MT], lg[MT], prod[MT];
+  float run_m[MT], run_s[MT], mb[MT];
+  float lse_s[MT];
+  uint32_t vb = 0;          // LDS address of the chunk's per-row vectors (cols kinds)
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      relu[mt] = 0.0f; lg[mt] = 0.0f; prod[mt] = 1.0f;
+      run_m[mt] = kNegInf; run_s[mt] = 0.0f; mb[mt] = 0.0f; lse_s[mt] = 0.0f;
+    }
+  }
+  // before the elements of a chunk (CE needs the chunk max first)
+  __device__ __forceinline__ void begin(const f32x16 (&y)[MT]) {
+    if constexpr (RM == 3) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        float xm = y[mt][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) xm = __builtin_fmaxf(xm, y[mt][i]);
+        const float mn = __builtin_fmaxf(run_m[mt], xm);
+        // rescale the running sum to the new max (0 while nothing finite has been seen)
+        run_s[mt] = mn == kNegInf ? 0.0f : run_s[mt] * __builtin_amdgcn_exp2f((run_m[mt] - mn) * kLog2e);
+        run_m[mt] = mn;
+        mb[mt] = mn == kNegInf ? 0.0f : mn * kLog2e;
+      }
+    }
+  }
+  // per-row weight (and CE logsumexp) of result registers i, i+1 (adjacent chunk rows),
+  // read from LDS where they are used
+  __device__ __forceinline__ f32x2 row_pair(int i, int h, int which) const {
+    return *lds_ptr<f32x2>(vb + 4 * (which * kRC + res_row(i, h)));
+  }
+  __device__ __forceinline__ void elem2(int mt, int i, int h, float x0, float x1, float& f0, float& f1) {
+    if constexpr (RM == 5) {
+      const f32x2 w = row_pair(i, h, 0);
+      f0 = w[0] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x0 * kLog2e));
+      f1 = w[1] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x1 * kLog2e));
+    } else if constexpr (RM == 6) {
+      const f32x2 w = row_pair(i, h, 0);
+      const f32x2 l = row_pair(i, h, 1);
+      const float e0 = __builtin_amdgcn_exp2f((x0 - l[0]) * kLog2e);
+      const float e1 = __builtin_amdgcn_exp2f((x1 - l[1]) * kLog2e);
+      f0 = w[0] != 0.0f ? w[0] * e0 : 0.0f;           // ignored rows: exactly 0
+      f1 = w[1] != 0.0f ? w[1] * e1 : 0.0f;
+    } else {
+      f0 = elem(mt, i, x0);
+      f1 = elem(mt, i + 1, x1);
+    }
+  }
+  __device__ __forceinline__ float elem(int mt, int i, float x) {
+    if constexpr (RM == 0 || RM == 2) {
+      const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * kLog2e);   // e^-|x| in [0, 1]
+      const float q = 1.0f + e;
+      relu[mt] += __builtin_fmaxf(x, 0.0f);
+      prod[mt] *= q;
+      if constexpr (RM == 0) {
+        const float r = __builtin_amdgcn_rcpf(q);
+        return x >= 0.0f ? r : e * r;
+      }
+      return 0.0f;
+    } else if constexpr (RM == 1) {
+      // 1 / (1 + 2^(-x log2 e)): the exp overflows to +inf for x << 0, giving 0
+      return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
+    } else if constexpr (RM == 3) {
+      run_s[mt] += __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -mb[mt]));
+      return 0.0f;
+    } else if constexpr (RM == 4) {
+      return __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -lse_s[mt]));
+    }
+    return 0.0f;    // RM 5, 6 go through elem2
+  }
+  __device__ __forceinline__ void end() {
+    if constexpr (RM == 0 || RM == 2) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        lg[mt] += __builtin_amdgcn_logf(prod[mt]);   // log2 of a product of 16 factors in [1, 2]
+        prod[mt] = 1.0f;
+      }
+    }
+  }
+};
+
+template <int RM> struct EpiHasF { static constexpr bool value = (RM == 0 || RM == 1 || RM >= 4); };
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100;
+#ifndef CL_SCHED_GROUPS
+#define CL_SCHED_GROUPS 1
+#endif
+constexpr bool kUseSchedGroups = CL_SCHED_GROUPS;
+#ifndef CL_PIPE_GRAD
+#define CL_PIPE_GRAD 0
+#endif
+constexpr bool kPipeGrad = CL_PIPE_GRAD;
+
+// packed bf16 operand of the gradient product: pw[mt][kk][j] = bf16 pair (F[8kk+2j], F[8kk+2j+1])
+template <int MT>
+struct FPack {
+  uint32_t pw[MT][2][4];
+  __device__ __forceinline__ bf16x8 op(int mt, int kk) const {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = {pw[mt][kk][0], pw[mt][kk][1], pw[mt][kk][2], pw[mt][kk][3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2 v = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// y = logits of the chunk in buffer `boff` for the MT stationary tiles.
+template <int D, int MT>
+__device__ __forceinline__ void chunk_logits(const bf16x8 (&sf)[MT][D / 16], f32x16 (&y)[MT], const ReadBase<D>& rb,
+                                             uint32_t boff) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) y[mt] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8 ra = read_row_piece<D>(rb, boff, ks);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) y[mt] = mfma32(ra, sf[mt][ks], y[mt]);
+  }
+}
+
+// Epilogue of the chunk whose logits are y, producing the packed operand `fo`, issued
+// together with the gradient product of the previous chunk (operand `fi`, buffer
+// `boff_prev`) when DO_GRAD.
+template <int D, int MT, int RM, bool DO_GRAD>
+__device__ __forceinline__ void epi_and_grad(f32x16 (&acc)[MT][D / 32], const f32x16 (&y)[MT], Epi<MT, RM>& ep,
+                                             FPack<MT>& fo, const FPack<MT>& fi, const ReadBase<D>& rb,
+                                             uint32_t boff_prev, int h) {
+  constexpr int NT = D / 32;
+  constexpr int NIT = 2 * NT;                   // (nt, kk) pairs
+  constexpr int NP = MT * 8;                    // element pairs per chunk
+  constexpr int PPI = (NP + NIT - 1) / NIT;     // pairs per iteration
+  constexpr bool HAS_F = EpiHasF<RM>::value;
+  ep.begin(y);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    if constexpr (DO_GRAD) {
+      const int nt = it >> 1, kk = it & 1;
+      const bf16x8 b = read_col_piece<D>(rb, boff_prev, nt, kk);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt][nt] = mfma32(fi.op(mt, kk), b, acc[mt][nt]);
+    }
+#pragma unroll
+    for (int j = 0; j < PPI; ++j) {
+      const int e = it * PPI + j;
+      if (e < NP) {
+        const int mt = e / 8, i = 2 * (e % 8);
+        float f0, f1;
+        ep.elem2(mt, i, h, y[mt][i], y[mt][i + 1], f0, f1);
+        if constexpr (HAS_F) fo.pw[mt][i / 8][(i % 8) / 2] = pack_bf16x2(f0, f1);
+      }
+    }
+  }
+  if constexpr (DO_GRAD && kUseSchedGroups) {
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, MT, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgValu, 10 * PPI, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  ep.end();
+}
+
+template <int D, int MT>
+__device__ __forceinline__ void grad_only(f32x16 (&acc)[MT][D / 32], const FPack<MT>& fi, const ReadBase<D>& rb,
+                                          uint32_t boff) {
+#pragma unroll
+  for (int it = 0; it < 2 * (D / 32); ++it) {
+    const int nt = it >> 1, kk = it & 1;
+    const bf16x8 b = read_col_piece<D>(rb, boff, nt, kk);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt][nt] = mfma32(fi.op(mt, kk), b, acc[mt][nt]);
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// The chunk loop shared by both sweeps. issue(c, boff) enqueues the DMA of chunk c into
+// the buffer at ring offset boff (NPER instructions per wave); prep(c, boff) loads the
+// per-chunk epilogue inputs. Gradient modes overlap the epilogue of chunk c with the
+// gradient of chunk c-1 (buffer c-1 stays live, prefetch distance 2); other modes
+// prefetch 3 chunks ahead.
+// ------------------------------------------------------------------------------------
+template <int D, int MT, int RM, int NPER, class Issue, class Prep>
+__device__ __forceinline__ void sweep_loop(int nch, int64_t rows_left0, const bf16x8 (&sf)[MT][D / 16],
+                                           f32x16 (&acc)[MT][D / 32], Epi<MT, RM>& ep, const ReadBase<D>& rb,
+                                           int h, Issue issue, Prep prep) {
+  using G = Geo<D>;
+  constexpr bool HAS_F = EpiHasF<RM>::value;
+  constexpr int AHEAD = (HAS_F && kPipeGrad) ? 2 : 3;   // chunks in flight beyond the current one
+  if (nch <= 0) return;
+#pragma unroll
+  for (int k = 0; k < AHEAD; ++k)
+    if (k < nch) issue(k, (uint32_t)(k * G::BYTES));
+  FPack<MT> fprev, fcur;
+  f32x16 y[MT];
+  for (int c = 0; c < nch; ++c) {
+    const uint32_t boff = (uint32_t)((c & (kRing - 1)) * G::BYTES);
+    // chunk c in LDS: own DMAs of later chunks (up to AHEAD - 1) may stay in flight
+    const int later = min(nch - 1 - c, AHEAD - 1);
+    if constexpr (AHEAD == 3) {
+      if (later >= 2) wait_vm<2 * NPER>(); else if (later == 1) wait_vm<NPER>(); else wait_vm<0>();
+    } else {
+      if (later >= 1) wait_vm<NPER>(); else wait_vm<0>();
+    }
+    block_sync();
+    if (c + AHEAD < nch) issue(c + AHEAD, (uint32_t)(((c + AHEAD) & (kRing - 1)) * G::BYTES));
+    prep(c, boff);
+    chunk_logits<D, MT>(sf, y, rb, boff);
+    const int64_t left = rows_left0 - (int64_t)c * kRC;
+    if (left < kRC) mask_tail<MT>(y, (int)left, h);
+    if constexpr (HAS_F && kPipeGrad) {
+      const uint32_t bprev = (uint32_t)(((c - 1) & (kRing - 1)) * G::BYTES);
+      if (c > 0) epi_and_grad<D, MT, RM, true>(acc, y, ep, fcur, fprev, rb, bprev, h);
+      else epi_and_grad<D, MT, RM, false>(acc, y, ep, fcur, fprev, rb, bprev, h);
+      fprev = fcur;
+    } else {
+      epi_and_grad<D, MT, RM, false>(acc, y, ep, fcur, fprev, rb, 0, h);
+      if constexpr (HAS_F) grad_only<D, MT>(acc, fcur, rb, boff);
+    }
+  }
+  if constexpr (HAS_F && kPipeGrad) grad_only<D, MT>(acc, fprev, rb, (uint32_t)(((nch - 1) & (kRing - 1)) * G::BYTES));
+}
+
+// ------------------------------------------------------------------------------------
+// rows sweep. MODE: 0 BCE loss partials, 1 BCE dA partials, 2 BCE dA + loss partials,
+// 3 CE (max, sum) partials, 4 CE dA partials.
+// ------------------------------------------------------------------------------------
+template <int MODE> struct RowsRM;
+template <> struct RowsRM<0> { static constexpr int RM = 2; };
+template <> struct RowsRM<1> { static constexpr int RM = 1; };
+template <> struct RowsRM<2> { static constexpr int RM = 0; };
+template <> struct RowsRM<3> { static constexpr int RM = 3; };
+template <> struct RowsRM<4> { static constexpr int RM = 4; };
+
+template <int D, int MODE>
+__global__ __launch_bounds__(256, Tiling<D>::WPE) void k_rows2(const SweepParams p) {
+  using G = Geo<D>;
+  constexpr int MT = Tiling<D>::MT;
+  constexpr int RM = RowsRM<MODE>::RM;
+  constexpr bool HAS_F = EpiHasF<RM>::value;
+  constexpr int KS = D / 16, NT = D / 32;
+  constexpr int SB = 128 * MT;                  // stationary rows per workgroup
+  __shared__ __attribute__((aligned(1024))) char ring[kRing * G::BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nsb = (int)((p.T + SB - 1) / SB);
+  const int g = blockIdx.x;
+  int split, sb;
+  if ((p.n_splits & 7) == 0) {          // workgroup g runs on XCD g % 8: one split per XCD
+    const int loc = g >> 3;
+    split = (g & 7) + 8 * (loc / nsb);
+    sb = loc % nsb;
+  } else {
+    split = g / nsb;
+    sb = g % nsb;
+  }
+  const int64_t s_wave = (int64_t)sb * SB + wv * 32 * MT;
+  const int64_t r_begin = (int64_t)split * p.split_len;
+  const int64_t r_end = min(p.V, r_begin + p.split_len);
+  const int nch = r_end > r_begin ? (int)((r_end - r_begin + kRC - 1) / kRC) : 0;
+  const uint16_t* E = (const uint16_t*)p.E;
+  const uint32_t ring0 = lds_addr(ring);
+
+  bf16x8 sf[MT][KS];
+  Epi<MT, RM> ep;
+  ep.init();
+  f32x16 acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int64_t srow = s_wave + 32 * mt + l32;
+    load_stationary<D, false>(sf[mt], p.A, srow, srow < p.T, h);
+    if constexpr (RM == 4) ep.lse_s[mt] = srow < p.T ? p.lse[srow] * kLog2e : 0.0f;
+    if constexpr (HAS_F) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x16{};
+    }
+  }
+  ReadBase<D> rb;
+  rb.init(ring0, lane);
+
+  auto issue = [&](int c, uint32_t boff) {
+    dma_chunk<D>(E, r_begin + (int64_t)c * kRC, r_end, ring0 + boff, wv, lane);
+  };
+  auto prep = [&](int, uint32_t) {};
+  sweep_loop<D, MT, RM, G::LPW>(nch, r_end - r_begin, sf, acc, ep, rb, h, issue, prep);
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int64_t srow = s_wave + 32 * mt + l32;
+    const bool s_ok = srow < p.T;
+    if constexpr (RM == 0 || RM == 2) {
+      float v = ep.relu[mt] + ep.lg[mt] * kLn2;
+      v += __shfl_xor(v, 32, 64);
+      if (h == 0 && s_ok) p.part_a[(int64_t)split * p.T + srow] = v;
+    }
+    if constexpr (RM == 3) {
+      const float m1 = ep.run_m[mt], s1 = ep.run_s[mt];
+      const float m2 = __shfl_xor(m1, 32, 64);
+      const float s2 = __shfl_xor(s1, 32, 64);
+      const float mn = __builtin_fmaxf(m1, m2);
+      float s = 0.0f;
+      if (mn != kNegInf) s = s1 * __builtin_amdgcn_exp2f((m1 - mn) * kLog2e) + s2 * __builtin_amdgcn_exp2f((m2 - mn) * kLog2e);
+      if (h == 0 && s_ok) {
+        p.part_a[(int64_t)split * p.T + srow] = mn;
+        p.part_b[(int64_t)split * p.T + srow] = s;
+      }
+    }
+    if constexpr (HAS_F) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int64_t s = s_wave + 32 * mt + res_row(i, h);
+          if (s < p.T) p.part_dA[((int64_t)split * p.T + s) * D + 32 * nt + l32] = acc[mt][nt][i];
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// cols sweep: 128*MT stationary E rows per workgroup, A streamed with the row weights
+// (and the CE logsumexp). KIND 0 BCE, 1 CE. EPI 0 writes dE (bf16), EPI 1 applies
+// E <- round(E - lr dE) in place.
+// ------------------------------------------------------------------------------------
+template <int D, int KIND, int EPI, bool SFP8>
+__global__ __launch_bounds__(256, Tiling<D>::WPE) void k_cols2(const SweepParams p) {
+  using G = Geo<D>;
+  constexpr int MT = Tiling<D>::MT;
+  constexpr int RM = KIND == 0 ? 5 : 6;
+  constexpr int NT = D / 32, KS = D / 16;
+  constexpr int NV = KIND == 1 ? 2 : 1;     // per-row vectors streamed with A: w (and lse)
+  constexpr int SB = 128 * MT;
+  __shared__ __attribute__((aligned(1024))) char ring[kRing * G::BYTES];
+  __shared__ __attribute__((aligned(256))) float vecs[kRing][NV][kRC];
+  __shared__ int uix[SB];
+
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t v_blk = (int64_t)blockIdx.x * SB;
+  const int64_t s_wave = v_blk + wv * 32 * MT;
+  const int nch = (int)((p.T + kRC - 1) / kRC);
+  const uint16_t* A = (const uint16_t*)p.A;
+  const uint32_t ring0 = lds_addr(ring);
+  const uint32_t vec0 = lds_addr(vecs);
+
+  bf16x8 sf[MT][KS];
+  f32x16 acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int64_t srow = s_wave + 32 * mt + l32;
+    load_stationary<D, SFP8>(sf[mt], p.E, srow, srow < p.V, h);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x16{};
+  }
+  Epi<MT, RM> ep;
+  ep.init();
+  ReadBase<D> rb;
+  rb.init(ring0, lane);
+
+  auto issue = [&](int c, uint32_t boff) {
+    const int64_t r0 = (int64_t)c * kRC;
+    const uint32_t vb = vec0 + (boff / G::BYTES) * (NV * kRC * 4);
+    dma_chunk<D>(A, r0, p.T, ring0 + boff, wv, lane);
+    dma_vec(p.w, r0, p.T, vb, lane);
+    if constexpr (KIND == 1) dma_vec(p.lse, r0, p.T, vb + kRC * 4, lane);
+  };
+  auto prep = [&](int, uint32_t boff) { ep.vb = vec0 + (boff / G::BYTES) * (NV * kRC * 4); };
+  sweep_loop<D, MT, RM, G::LPW + NV>(nch, p.T, sf, acc, ep, rb, h, issue, prep);
+
+  // sparse positive term: index of each item of the block in the sorted unique-item list
+  for (int k = tid; k < SB; k += 256) {
+    const int64_t v = v_blk + k;
+    const int nu = p.counts[2];
+    int lo = 0, hi = nu;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)p.uitems[mid] < v) lo = mid + 1;
+      else hi = mid;
+    }
+    uix[k] = (lo < nu && (int64_t)p.uitems[lo] == v) ? lo : -1;
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = wv * 32 * MT + 32 * mt + res_row(i, h);
+      const int64_t v = v_blk + m;
+      if (v >= p.V) continue;
+      const int u = uix[m];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int d = 32 * nt + l32;
+        float gv = acc[mt][nt][i];
+        if (u >= 0) gv -= p.S_u[(int64_t)u * D + d];
+        if constexpr (EPI == 0) {
+          ((uint16_t*)p.dE)[v * D + d] = (uint16_t)f32_to_bf16_bits(gv);
+        } else if constexpr (SFP8) {
+          uint8_t* e8 = (uint8_t*)p.E_inplace + v * D + d;
+          *e8 = (uint8_t)f32_to_fp8_sat(fp8_to_f32(*e8) - p.lr * gv);
+        } else {
+          uint16_t* e16 = (uint16_t*)p.E_inplace + v * D + d;
+          *e16 = (uint16_t)f32_to_bf16_bits(bf16_bits_to_f32(*e16) - p.lr * gv);
+        }
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t rows2_d(const SweepParams& p, int mode, hipStream_t st) {
+  const int nsb = (int)((p.T + 128 * Tiling<D>::MT - 1) / (128 * Tiling<D>::MT));
+  const dim3 grid((unsigned)(nsb * p.n_splits)), block(256);
+  switch (mode) {
+    case 0: k_rows2<D, 0><<<grid, block, 0, st>>>(p); break;
+    case 1: k_rows2<D, 1><<<grid, block, 0, st>>>(p); break;
+    case 2: k_rows2<D, 2><<<grid, block, 0, st>>>(p); break;
+    case 3: k_rows2<D, 3><<<grid, block, 0, st>>>(p); break;
+    case 4: k_rows2<D, 4><<<grid, block, 0, st>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t cols2_d(const SweepParams& p, int kind, int epi, hipStream_t st) {
+  const int64_t sb = 128 * Tiling<D>::MT;
+  const dim3 grid((unsigned)((p.V + sb - 1) / sb)), block(256);
+  const int key = kind * 4 + epi * 2 + (p.e_fp8 ? 1 : 0);
+  switch (key) {
+    case 0: k_cols2<D, 0, 0, false><<<grid, block, 0, st>>>(p); break;
+    case 1: k_cols2<D, 0, 0, true><<<grid, block, 0, st>>>(p); break;
+    case 2: k_cols2<D, 0, 1, false><<<grid, block, 0, st>>>(p); break;
+    case 3: k_cols2<D, 0, 1, true><<<grid, block, 0, st>>>(p); break;
+    case 4: k_cols2<D, 1, 0, false><<<grid, block, 0, st>>>(p); break;
+    case 5: k_cols2<D, 1, 0, true><<<grid, block, 0, st>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool sweep2_rows_supported(int64_t D, int e_fp8) { return !e_fp8 && (D == 64 || D == 128 || D == 256); }
+bool sweep2_cols_supported(int64_t D) { return D == 64 || D == 128 || D == 256; }
+int sweep2_rows_per_block(int64_t D) {
+  switch (D) {
+    case 64: return 128 * Tiling<64>::MT;
+    case 128: return 128 * Tiling<128>::MT;
+    case 256: return 128 * Tiling<256>::MT;
+    default: return 128;
+  }
+}
+
+hipError_t launch_sweep2_rows(const SweepParams& p, int mode, hipStream_t st) {
+  switch (p.D) {
+    case 64: return rows2_d<64>(p, mode, st);
+    case 128: return rows2_d<128>(p, mode, st);
+    case 256: return rows2_d<256>(p, mode, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_sweep2_cols(const SweepParams& p, int kind, int epi, hipStream_t st) {
+  switch (p.D) {
+    case 64: return cols2_d<64>(p, kind, epi, st);
+    case 128: return cols2_d<128>(p, kind, epi, st);
+    case 256: return cols2_d<256>(p, kind, epi, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace cl
