@@ -25,7 +25,7 @@
  *    space comes from the caller's workspace, sized by the *_workspace_size query.
  *  - Matrices are row-major and dense: A is [T, D] bf16; E is [V, D] bf16 or OCP FP8
  *    E4M3FN (1 byte); dA is [T, D] bf16; dE is [V, D] bf16. D must be a positive
- *    multiple of 64. loss/lse/dloss are [T] float32.
+ *    multiple of 64 (at most 9216). loss/lse/dloss are [T] float32.
  *  - All work is enqueued on `stream` (a hipStream_t, NULL = default stream);
  *    no call synchronizes except cutloss_read_data_errors.
  *  - Host-detectable errors (bad sizes, NULL or misaligned pointers, too small a
@@ -38,6 +38,12 @@
  *  - Masked (BCE) and ignored (CE) rows give loss 0, a zero dA row and no dE
  *    contribution.
  *  - Results are deterministic: every reduction runs in a fixed order.
+ *  - Paths: heads with D in {64, 128, 256} and bf16 E run fused logit-tile sweeps that
+ *    never write a logit; every other head (any D that is a multiple of 64, or FP8 E)
+ *    runs a chunked path that keeps one vocabulary chunk's bf16 gradient tile
+ *    (T x Vc, at most 512 MiB by default) in the workspace. The environment variable
+ *    CUTLOSS_MAX_CHUNK_ITEMS caps Vc (read when a call or size query plans the work,
+ *    so set it before both).
  */
 #ifndef CUTLOSS_H
 #define CUTLOSS_H

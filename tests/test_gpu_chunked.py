@@ -1,0 +1,142 @@
+"""GPU parity of the chunked path (heads with D outside {64, 128, 256}, or FP8 E)
+against the fp64 CPU oracle, with the chunk size capped so that every case spans
+several vocabulary chunks and a ragged last chunk (CUTLOSS_MAX_CHUNK_ITEMS).
+Tolerances are those of tests/gpu_util.py.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import head_loss as H
+from workloads import make
+from workloads.gen import Workload
+
+from gpu_util import (bf16_to_f64, canonical, check_grad, check_loss, decode_inputs, run_bce, run_ce, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    from vocabulary_loss_head_amd import binding
+    return binding
+
+
+@pytest.fixture(autouse=True)
+def small_chunks(monkeypatch):
+    monkeypatch.setenv("CUTLOSS_MAX_CHUNK_ITEMS", "512")
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _bce_check(B, inp, pad_id, dloss=None):
+    w = inp["workload"]
+    A64, E64 = decode_inputs(inp)
+    crow, cids, n_bad = canonical(inp, w.V, pad_id)
+    g = upload(inp)
+    dl = None if dloss is None else torch.from_numpy(dloss).to(g["A"].device)
+    out = run_bce(B, g, pad_id, dloss=dl)
+    ref_loss = H.bce_loss(A64, E64, crow, cids, inp["mask"])
+    check_loss(out["loss"].cpu().numpy(), ref_loss, what="fwd loss")
+    check_loss(out["floss"].cpu().numpy(), ref_loss, what="fused loss")
+    assert out["n_err"] == n_bad
+    dA, dE = H.bce_grads(A64, E64, crow, cids, inp["mask"], dloss)
+    check_grad(bf16_to_f64(out["dA"]), dA, "dA")
+    check_grad(bf16_to_f64(out["dE"]), dE, "dE")
+    m = inp["mask"] == 0
+    if m.any():
+        assert np.all(out["loss"].cpu().numpy()[m] == 0)
+        assert np.all(bf16_to_f64(out["dA"])[m] == 0)
+    return out
+
+
+@pytest.mark.parametrize("T,D,V", [(70, 320, 3001), (129, 512, 1001), (33, 768, 700), (300, 384, 2100)])
+def test_bce_chunked_ragged(B, T, D, V):
+    _say(f"chunked bce T={T} D={D} V={V}")
+    w = Workload("chunk", "bce", T, D, V, "bf16", None, None, "uniform_any", L=10, pad_id=0, mask_frac=0.15,
+                 seed=200 + T)
+    inp = make(w, with_dloss=True)
+    _bce_check(B, inp, 0, dloss=inp["dloss"])
+
+
+def test_bce_chunked_stress_scale(B):
+    # A, E ~ N(0, I) as in the Cut BCE mini-benchmark (§IV-A): saturated sigmoids
+    _say("chunked bce stress N(0,1) T=64 D=384 V=1500")
+    w = Workload("chunk_stress", "bce", 64, 384, 1500, "bf16", 1.0, 1.0, "uniform_any", L=8, pad_id=0, seed=21)
+    _bce_check(B, make(w), 0)
+
+
+def test_bce_chunked_closed_forms(B):
+    w = Workload("chunk_cf", "bce", 50, 384, 1300, "bf16", None, None, "uniform_any", L=6, pad_id=0, mask_frac=0.1,
+                 seed=22)
+    inp = make(w)
+    for zero in ("A", "E"):
+        _say(f"chunked closed form {zero}=0")
+        z = dict(inp)
+        z[zero] = np.zeros_like(inp[zero])
+        out = _bce_check(B, z, 0)
+        valid = z["mask"] != 0
+        np.testing.assert_allclose(out["loss"].cpu().numpy()[valid], w.V * math.log(2.0), rtol=1e-5)
+
+
+def _sgd_case(B, T, D, V, seed):
+    w = Workload("sgd", "bce", T, D, V, "fp8", None, 0.05, "poisson_distinct", L=5, pad_id=-1, lr=0.01, seed=seed)
+    inp = make(w)
+    A64, E64 = decode_inputs(inp)
+    crow, cids, _ = canonical(inp, w.V, -1)
+    g = upload(inp)
+    dev = g["A"].device
+    prob = B.bce_problem(g["A"], g["E"], g["row_ptr"], g["ids"], g["mask"], -1)
+    ws = B.workspace(B.cutloss_bce_workspace_size(prob, B.OP_BWD_SGD), dev)
+    dE = torch.empty(w.V, w.D, dtype=torch.bfloat16, device=dev)
+    dA = torch.empty(w.T, w.D, dtype=torch.bfloat16, device=dev)
+    B.cutloss_bce_bwd(prob, None, dA, dE, None, ws)
+    loss = torch.empty(w.T, dtype=torch.float32, device=dev)
+    dA2 = torch.empty(w.T, w.D, dtype=torch.bfloat16, device=dev)
+    B.cutloss_bce_bwd_sgd(prob, None, w.lr, dA2, loss, ws)
+    torch.cuda.synchronize()
+    dA_ref, dE_ref = H.bce_grads(A64, E64, crow, cids, inp["mask"])
+    check_grad(bf16_to_f64(dE), dE_ref, "dE (fp8 E)")
+    check_grad(bf16_to_f64(dA), dA_ref, "dA (fp8 E)")
+    # the fused call reads E before updating it: its dA and loss are those of the old E
+    check_grad(bf16_to_f64(dA2), dA_ref, "dA (fused SGD call)")
+    check_loss(loss.cpu().numpy(), H.bce_loss(A64, E64, crow, cids, inp["mask"]), what="sgd fused loss")
+    from test_gpu_parity import _check_sgd
+    _check_sgd(g["E"].cpu().numpy(), inp["E"], dE_ref, w.lr)
+
+
+def test_sgd_fp8_chunked_wide(B):
+    _say("chunked fp8 SGD T=40 D=768 V=2000")
+    _sgd_case(B, 40, 768, 2000, 31)
+
+
+def test_sgd_fp8_chunked_ragged(B):
+    _say("chunked fp8 SGD T=130 D=192 V=1537")
+    _sgd_case(B, 130, 192, 1537, 32)
+
+
+@pytest.mark.parametrize("T,D,V", [(70, 384, 3001), (33, 2304, 700), (257, 512, 1300)])
+def test_ce_chunked(B, T, D, V):
+    _say(f"chunked ce T={T} D={D} V={V}")
+    w = Workload("ce_chunk", "ce", T, D, V, "bf16", None, None, "ce_uniform", L=1, pad_id=-1, ignore_frac=0.1,
+                 seed=300 + T)
+    inp = make(w, with_dloss=True)
+    tgt = inp["target"].copy()
+    tgt[1] = V + 7          # out of range: counted, row ignored
+    inp["target"] = tgt
+    g = upload(inp)
+    A64, E64 = decode_inputs(inp)
+    out = run_ce(B, g, dloss=g["dloss"])
+    loss, lse = H.ce_forward(A64, E64, tgt)
+    check_loss(out["lse"].cpu().numpy(), lse, what="lse")
+    check_loss(out["loss"].cpu().numpy(), loss, what="loss")
+    dA, dE = H.ce_grads(A64, E64, tgt, dloss=inp["dloss"])
+    check_grad(bf16_to_f64(out["dA"]), dA, "dA")
+    check_grad(bf16_to_f64(out["dE"]), dE, "dE")
+    assert out["n_err"] == 1

@@ -1,8 +1,10 @@
 // C ABI of the cutloss library: argument validation, workspace layout and kernel order.
 // Every entry point validates on the host and returns before launching anything if a
 // check fails; all work is then enqueued on the caller's stream without synchronizing.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -12,14 +14,12 @@
 
 namespace {
 
-hipError_t rows_sweep(const cl::SweepParams& sp, int mode, hipStream_t st) {
-  if (cl::sweep2_rows_supported(sp.D, sp.e_fp8)) return cl::launch_sweep2_rows(sp, mode, st);
-  return cl::launch_sweep_rows(sp, mode, st);
-}
+// Heads with D in {64, 128, 256} and bf16 E run the fused LDS-DMA sweeps (sweep2.hip);
+// every other supported head runs the chunked GEMM path (gemm.hip).
+hipError_t rows_sweep(const cl::SweepParams& sp, int mode, hipStream_t st) { return cl::launch_sweep2_rows(sp, mode, st); }
 
 hipError_t cols_sweep(const cl::SweepParams& sp, int kind, int epi, hipStream_t st) {
-  if (cl::sweep2_cols_supported(sp.D)) return cl::launch_sweep2_cols(sp, kind, epi, st);
-  return cl::launch_sweep_cols(sp, kind, epi, st);
+  return cl::launch_sweep2_cols(sp, kind, epi, st);
 }
 
 // ---- phase profiling (cutloss_profile_enable / cutloss_profile_read)
@@ -109,8 +109,7 @@ struct Plan {
 // chip about twice; a multiple of 8 so each split maps to one XCD.
 Plan make_plan(int64_t T, int64_t D, int64_t V, int64_t cap, int e_fp8) {
   Plan pl{T, D, V, cap, 1, 0};
-  const bool v2 = cl::sweep2_rows_supported(D, e_fp8);
-  const int64_t rpb = v2 ? cl::sweep2_rows_per_block(D) : 128;
+  const int64_t rpb = cl::sweep2_rows_supported(D, e_fp8) ? cl::sweep2_rows_per_block(D) : 128;
   const int64_t target = 1024;
   const int64_t nsb = (T + rpb - 1) / rpb;
   int64_t ns = nsb > 0 ? (target + nsb - 1) / nsb : 1;
@@ -134,6 +133,7 @@ struct Ws {
   float* part_b;
   float* part_dA;
   float* S_u;
+  float* S_part;
   size_t bytes;
 };
 
@@ -168,8 +168,118 @@ Ws carve(void* base, const Plan& pl, bool need_dA, bool need_Su, bool two_partia
   w.part_b = two_partials ? c.take<float>((size_t)pl.n_splits * T) : nullptr;
   w.part_dA = need_dA ? c.take<float>((size_t)pl.n_splits * T * pl.D) : nullptr;
   w.S_u = need_Su ? c.take<float>((size_t)cap * pl.D) : nullptr;
+  w.S_part = need_Su ? c.take<float>(2 * cl::item_sum_parts(cap) * pl.D) : nullptr;
   w.bytes = c.off;
   return w;
+}
+
+// ---------------------------------------------------------------------------------
+// Chunked path (wide heads, FP8 E): see gemm.hip.
+// ---------------------------------------------------------------------------------
+bool use_chunked(int64_t D, int e_fp8) {
+  return !(cl::sweep2_rows_supported(D, e_fp8) && cl::sweep2_cols_supported(D));
+}
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+int64_t ceil_div(int64_t x, int64_t a) { return (x + a - 1) / a; }
+
+struct ChunkPlan {
+  int64_t T, D, V, cap;
+  int64_t Tp;         // rows padded to 128: row stride of the P buffer
+  int64_t Vc;         // items per chunk (multiple of the item tile)
+  int64_t n_chunks;
+  int64_t n_splits;   // loss / lse partials: item tiles x waves along the item dimension
+  int64_t sk;         // split-K slices of the dA product
+  int64_t kps;        // items per slice
+};
+
+constexpr int64_t kChunkPBytes = 512ll << 20;   // P buffer budget
+
+ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap) {
+  ChunkPlan c{};
+  c.T = T; c.D = D; c.V = V; c.cap = cap;
+  const int64_t bm = cl::gemm_tile_m();
+  c.Tp = round_up(T > 0 ? T : 1, 128);
+  int64_t vc = kChunkPBytes / (c.Tp * 2) / bm * bm;
+  // CUTLOSS_MAX_CHUNK_ITEMS caps the chunk (rounded down to the item tile): a tuning knob,
+  // and the way tests exercise several chunks on small problems
+  if (const char* env = std::getenv("CUTLOSS_MAX_CHUNK_ITEMS")) {
+    const long long cap_items = std::atoll(env);
+    if (cap_items > 0 && cap_items / bm * bm < vc) vc = cap_items / bm * bm;
+  }
+  if (vc < bm) vc = bm;
+  if (vc > round_up(V, bm)) vc = round_up(V, bm);
+  c.Vc = vc;
+  c.n_chunks = ceil_div(V, vc);
+  c.n_splits = ceil_div(V, bm) * cl::gemm_warps_m(c.Tp);
+  // dA product: (row tiles) x (D tiles) x slices, about 1024 workgroups
+  const int64_t tiles = ceil_div(T > 0 ? T : 1, bm) * ceil_div(D, cl::gemm_tile_n(D));
+  int64_t sk = ceil_div(1024, tiles);
+  if (sk > vc / 32) sk = vc / 32;
+  if (sk < 1) sk = 1;
+  c.kps = round_up(ceil_div(vc, sk), 32);
+  c.sk = ceil_div(vc, c.kps);
+  return c;
+}
+
+struct Ws2 {
+  unsigned long long* err;
+  cl::TargetsWs tw;
+  float* w;
+  float* part_a;
+  float* part_b;
+  uint16_t* P;
+  float* part_dA;
+  float* pos_dot;
+  float* pos_sum;
+  float* S_u;
+  float* S_part;
+  size_t bytes;
+};
+
+Ws2 carve_chunked(void* base, const ChunkPlan& pl, bool need_P, bool need_dA, bool need_Su, bool two_partials,
+                  bool need_pos) {
+  Carver c(base);
+  Ws2 w{};
+  w.err = c.take<unsigned long long>(4);
+  const int64_t T = pl.T, cap = pl.cap;
+  const size_t nblk = cl::targets_radix_blocks(cap);
+  cl::TargetsWs& t = w.tw;
+  t.err = w.err;
+  t.counts = c.take<int32_t>(4);
+  t.cnt = c.take<int32_t>(T + 1);
+  t.off = c.take<int32_t>(T + 1);
+  t.keyA = c.take<int32_t>(cap);
+  t.valA = c.take<int32_t>(cap);
+  t.keyB = c.take<int32_t>(cap);
+  t.valB = c.take<int32_t>(cap);
+  t.flags = c.take<int32_t>(cap + 1);
+  t.fscan = c.take<int32_t>(cap + 1);
+  t.hist = c.take<int32_t>(256 * nblk);
+  t.hscan = c.take<int32_t>(256 * nblk + 1);
+  t.csc_items = c.take<int32_t>(cap);
+  t.csc_rows = c.take<int32_t>(cap);
+  t.uitems = c.take<int32_t>(cap);
+  t.useg = c.take<int32_t>(cap + 1);
+  t.crow = c.take<int32_t>(T + 1);
+  t.cids = c.take<int32_t>(cap);
+  w.w = c.take<float>(T);
+  w.part_a = c.take<float>((size_t)pl.n_splits * T);
+  w.part_b = two_partials ? c.take<float>((size_t)pl.n_splits * T) : nullptr;
+  w.P = need_P ? c.take<uint16_t>((size_t)pl.Vc * pl.Tp) : nullptr;
+  w.part_dA = need_dA ? c.take<float>((size_t)pl.sk * T * pl.D) : nullptr;
+  w.pos_dot = need_pos ? c.take<float>(T) : nullptr;
+  w.pos_sum = need_pos && need_dA ? c.take<float>((size_t)T * pl.D) : nullptr;
+  w.S_u = need_Su ? c.take<float>((size_t)cap * pl.D) : nullptr;
+  w.S_part = need_Su ? c.take<float>(2 * cl::item_sum_parts(cap) * pl.D) : nullptr;
+  w.bytes = c.off;
+  return w;
+}
+
+cl::GemmOperand operand(const void* p, int64_t ld, int64_t rows_valid, int64_t cols_valid, int kc, int fp8) {
+  cl::GemmOperand o;
+  o.p = p; o.ld = ld; o.rows_valid = rows_valid; o.cols_valid = cols_valid; o.kc = kc; o.fp8 = fp8;
+  return o;
 }
 
 cutloss_status check_common(int64_t T, int64_t D, int64_t V, const void* A, const void* E, int e_dtype) {
@@ -180,7 +290,6 @@ cutloss_status check_common(int64_t T, int64_t D, int64_t V, const void* A, cons
   if (e_dtype != CUTLOSS_BF16 && e_dtype != CUTLOSS_FP8_E4M3) return fail(CUTLOSS_ERR_INVALID_ARG, "unknown e_dtype %d", e_dtype);
   if (T > 0 && (A == nullptr || !aligned(A, 16))) return fail(CUTLOSS_ERR_INVALID_ARG, "A must be a non-NULL 16-byte aligned device pointer");
   if (E == nullptr || !aligned(E, 16)) return fail(CUTLOSS_ERR_INVALID_ARG, "E must be a non-NULL 16-byte aligned device pointer");
-  if (!cl::sweep_supported(D)) return fail(CUTLOSS_ERR_UNSUPPORTED, "D=%lld not supported by this build (64, 128, 256, 512)", (long long)D);
   return CUTLOSS_OK;
 }
 
@@ -223,8 +332,15 @@ cutloss_status check_out(const void* ptr, size_t align, const char* name, bool r
 
 // BCE pipeline shared by fwd / bwd / bwd_sgd.
 // want_loss: emit loss; want_dA; dE_mode: 0 none, 1 write dE, 2 SGD in place
+cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss, float* loss, void* dA, void* dE,
+                               int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st);
+cutloss_status ce_run_chunked(const cutloss_ce_problem* p, const float* lse_in, const float* dloss, float* loss,
+                              float* lse, void* dA, void* dE, void* ws, size_t ws_bytes, hipStream_t st);
+
 cutloss_status bce_run(const cutloss_bce_problem* p, const float* dloss, float* loss, void* dA, void* dE,
                        int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (use_chunked(p->D, p->e_dtype == CUTLOSS_FP8_E4M3))
+    return bce_run_chunked(p, dloss, loss, dA, dE, dE_mode, lr, ws, ws_bytes, st);
   const Plan pl = make_plan(p->T, p->D, p->V, p->nnz, p->e_dtype == CUTLOSS_FP8_E4M3);
   const bool rows_grad = dA != nullptr;
   const bool need_Su = dE_mode != 0;
@@ -242,7 +358,7 @@ cutloss_status bce_run(const cutloss_bce_problem* p, const float* dloss, float* 
   cl::FinalizeParams fp{};
   fp.T = p->T; fp.D = p->D; fp.V = p->V; fp.A = p->A; fp.E = p->E; fp.e_fp8 = e_fp8;
   fp.crow = w.tw.crow; fp.cids = w.tw.cids; fp.dloss = dloss; fp.mask = p->row_mask;
-  fp.n_splits = pl.n_splits; fp.part_a = w.part_a; fp.part_dA = w.part_dA;
+  fp.n_splits = pl.n_splits; fp.n_splits_dA = pl.n_splits; fp.part_a = w.part_a; fp.part_dA = w.part_dA;
   fp.loss = loss; fp.dA = dA; fp.w_out = w.w;
 
   cl::SweepParams sp{};
@@ -265,7 +381,7 @@ cutloss_status bce_run(const cutloss_bce_problem* p, const float* dloss, float* 
     {
       Phase ph(CUTLOSS_PHASE_ITEM_SUMS, st);
       CL_HIP(cl::launch_row_weights(fp, 0, st), "row weights");
-      CL_HIP(cl::launch_item_sums(p->D, pl.cap, p->A, w.w, w.tw.csc_rows, w.tw.useg, w.tw.counts, w.S_u, st), "item sums");
+      CL_HIP(cl::launch_item_sums(p->D, pl.cap, p->A, w.w, w.tw.csc_rows, w.tw.useg, w.tw.counts, w.S_u, w.S_part, st), "item sums");
     }
     Phase ph(CUTLOSS_PHASE_COLS, st);
     CL_HIP(cols_sweep(sp, 0, dE_mode == 2 ? 1 : 0, st), "cols sweep");
@@ -275,6 +391,8 @@ cutloss_status bce_run(const cutloss_bce_problem* p, const float* dloss, float* 
 
 cutloss_status ce_run(const cutloss_ce_problem* p, const float* lse_in, const float* dloss, float* loss, float* lse,
                       void* dA, void* dE, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (use_chunked(p->D, p->e_dtype == CUTLOSS_FP8_E4M3))
+    return ce_run_chunked(p, lse_in, dloss, loss, lse, dA, dE, ws, ws_bytes, st);
   const bool fwd = loss != nullptr;
   const Plan pl = make_plan(p->T, p->D, p->V, p->T, p->e_dtype == CUTLOSS_FP8_E4M3);
   const Ws w = carve(ws, pl, dA != nullptr, dE != nullptr, fwd);
@@ -290,7 +408,7 @@ cutloss_status ce_run(const cutloss_ce_problem* p, const float* lse_in, const fl
   cl::FinalizeParams fp{};
   fp.T = p->T; fp.D = p->D; fp.V = p->V; fp.A = p->A; fp.E = p->E; fp.e_fp8 = e_fp8;
   fp.crow = w.tw.crow; fp.cids = w.tw.cids; fp.dloss = dloss; fp.ce_target = p->target; fp.ignore_index = p->ignore_index;
-  fp.n_splits = pl.n_splits; fp.part_a = w.part_a; fp.part_b = w.part_b; fp.part_dA = w.part_dA;
+  fp.n_splits = pl.n_splits; fp.n_splits_dA = pl.n_splits; fp.part_a = w.part_a; fp.part_b = w.part_b; fp.part_dA = w.part_dA;
   fp.loss = loss; fp.lse = lse; fp.dA = dA; fp.w_out = w.w; fp.lse_in = lse_in;
 
   cl::SweepParams sp{};
@@ -322,10 +440,167 @@ cutloss_status ce_run(const cutloss_ce_problem* p, const float* lse_in, const fl
     {
       Phase ph(CUTLOSS_PHASE_ITEM_SUMS, st);
       CL_HIP(cl::launch_row_weights(fp, 1, st), "row weights");
-      CL_HIP(cl::launch_item_sums(p->D, pl.cap, p->A, w.w, w.tw.csc_rows, w.tw.useg, w.tw.counts, w.S_u, st), "item sums");
+      CL_HIP(cl::launch_item_sums(p->D, pl.cap, p->A, w.w, w.tw.csc_rows, w.tw.useg, w.tw.counts, w.S_u, w.S_part, st), "item sums");
     }
     Phase ph(CUTLOSS_PHASE_COLS, st);
     CL_HIP(cols_sweep(sp, 1, 0, st), "cols sweep");
+  }
+  return CUTLOSS_OK;
+}
+
+// One vocabulary chunk of the chunked path: K1 (logits + epilogue), then K2 (dA) and
+// K3 (dE / SGD) on the chunk's P. Stream order keeps K2 reading E_c before K3 updates it.
+struct ChunkJob {
+  const ChunkPlan* pl;
+  const void* A; const void* E; int e_fp8;
+  int k1_epi;            // GEMM_EPI_*
+  const float* w; const float* lse;
+  uint16_t* P; float* part_a; float* part_b;
+  float* part_dA;        // NULL: no dA
+  int k3_epi;            // -1: none, GEMM_EPI_DE or GEMM_EPI_SGD
+  const int32_t* uitems; const int32_t* counts; const float* S_u;
+  void* dE; float lr;
+};
+
+cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
+  const ChunkPlan& pl = *j.pl;
+  const int64_t bm = cl::gemm_tile_m();
+  const int64_t esz = j.e_fp8 ? 1 : 2;
+  for (int64_t c = 0; c < pl.n_chunks; ++c) {
+    const int64_t v0 = c * pl.Vc;
+    const int64_t vlen = std::min(pl.Vc, pl.V - v0);
+    const int64_t mc = round_up(vlen, bm);
+    const void* Ec = (const char*)j.E + v0 * pl.D * esz;
+    {
+      Phase ph(CUTLOSS_PHASE_ROWS, st);
+      cl::GemmParams g{};
+      g.a = operand(Ec, pl.D, vlen, pl.D, 1, j.e_fp8);
+      g.b = operand(j.A, pl.D, pl.T, pl.D, 1, 0);
+      g.M = mc; g.N = pl.Tp; g.K = pl.D; g.k_per_split = pl.D;
+      g.epi = j.k1_epi;
+      g.v0 = v0; g.V = pl.V; g.T = pl.T; g.D = pl.D;
+      g.w = j.w; g.lse = j.lse; g.P = j.P; g.ldp = pl.Tp;
+      g.part_a = j.part_a; g.part_b = j.part_b;
+      g.part_base = (v0 / bm) * cl::gemm_warps_m(pl.Tp);
+      CL_HIP(cl::launch_gemm(g, st), "chunk logits");
+    }
+    if (j.part_dA != nullptr) {
+      Phase ph(CUTLOSS_PHASE_ROWS, st);
+      cl::GemmParams g{};
+      g.a = operand(j.P, pl.Tp, mc, pl.Tp, 0, 0);
+      g.b = operand(Ec, pl.D, vlen, pl.D, 0, j.e_fp8);
+      g.M = pl.T; g.N = pl.D; g.K = mc; g.k_per_split = pl.kps;
+      g.epi = cl::GEMM_EPI_ACC;
+      g.T = pl.T; g.D = pl.D;
+      g.acc = j.part_dA; g.ldacc = pl.D; g.acc_slice = pl.T * pl.D; g.acc_first = c == 0;
+      CL_HIP(cl::launch_gemm(g, st), "chunk dA");
+    }
+    if (j.k3_epi >= 0) {
+      Phase ph(CUTLOSS_PHASE_COLS, st);
+      cl::GemmParams g{};
+      g.a = operand(j.P, pl.Tp, mc, pl.Tp, 1, 0);
+      g.b = operand(j.A, pl.D, pl.T, pl.D, 0, 0);
+      g.M = mc; g.N = pl.D; g.K = pl.Tp; g.k_per_split = pl.Tp;
+      g.epi = j.k3_epi;
+      g.v0 = v0; g.V = pl.V; g.T = pl.T; g.D = pl.D;
+      g.uitems = j.uitems; g.counts = j.counts; g.S_u = j.S_u;
+      g.dE = j.dE; g.E_inplace = (void*)j.E; g.e_fp8 = j.e_fp8; g.lr = j.lr;
+      CL_HIP(cl::launch_gemm(g, st), "chunk dE");
+    }
+  }
+  return CUTLOSS_OK;
+}
+
+cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss, float* loss, void* dA, void* dE,
+                               int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st) {
+  const ChunkPlan pl = make_chunk_plan(p->T, p->D, p->V, p->nnz);
+  const bool grad = dA != nullptr || dE_mode != 0;
+  const Ws2 w = carve_chunked(ws, pl, grad, dA != nullptr, dE_mode != 0, false, true);
+  CL_TRY(check_ws(ws, ws_bytes, w.bytes));
+  const int e_fp8 = p->e_dtype == CUTLOSS_FP8_E4M3;
+  {
+    Phase ph(CUTLOSS_PHASE_TARGETS, st);
+    CL_HIP(cl::launch_zero_u64(w.err, 4, st), "zero counters");
+    CL_HIP(cl::launch_targets(w.tw, p->T, p->V, p->nnz, p->pos_row_ptr, p->pos_ids, p->row_mask, p->pad_id,
+                              nullptr, 0, st), "targets");
+  }
+  if (p->T == 0) return CUTLOSS_OK;
+  cl::FinalizeParams fp{};
+  fp.T = p->T; fp.D = p->D; fp.V = p->V; fp.A = p->A; fp.E = p->E; fp.e_fp8 = e_fp8;
+  fp.crow = w.tw.crow; fp.cids = w.tw.cids; fp.dloss = dloss; fp.mask = p->row_mask;
+  fp.n_splits = (int)pl.n_splits; fp.n_splits_dA = (int)pl.sk; fp.dA_weighted = 1;
+  fp.part_a = w.part_a; fp.part_dA = w.part_dA; fp.loss = loss; fp.dA = dA; fp.w_out = w.w;
+  fp.pos_dot = w.pos_dot; fp.pos_sum = w.pos_sum;
+  {
+    Phase ph(CUTLOSS_PHASE_ITEM_SUMS, st);
+    CL_HIP(cl::launch_row_weights(fp, 0, st), "row weights");
+    // positive-row terms read E before any chunk's SGD step changes it
+    CL_HIP(cl::launch_row_positives(fp, st), "row positives");
+    if (dE_mode != 0)
+      CL_HIP(cl::launch_item_sums(p->D, pl.cap, p->A, w.w, w.tw.csc_rows, w.tw.useg, w.tw.counts, w.S_u, w.S_part, st),
+             "item sums");
+  }
+  ChunkJob j{};
+  j.pl = &pl; j.A = p->A; j.E = p->E; j.e_fp8 = e_fp8;
+  j.k1_epi = grad ? cl::GEMM_EPI_BCE_P : cl::GEMM_EPI_BCE_LOSS;
+  j.w = w.w; j.P = w.P; j.part_a = w.part_a; j.part_dA = w.part_dA;
+  j.k3_epi = dE_mode == 0 ? -1 : (dE_mode == 1 ? cl::GEMM_EPI_DE : cl::GEMM_EPI_SGD);
+  j.uitems = w.tw.uitems; j.counts = w.tw.counts; j.S_u = w.S_u; j.dE = dE; j.lr = lr;
+  CL_TRY(run_chunks(j, st));
+  if (loss != nullptr || dA != nullptr) {
+    Phase ph(CUTLOSS_PHASE_FINALIZE, st);
+    CL_HIP(cl::launch_finalize_rows(fp, 0, loss != nullptr, dA != nullptr, st), "finalize rows");
+  }
+  return CUTLOSS_OK;
+}
+
+cutloss_status ce_run_chunked(const cutloss_ce_problem* p, const float* lse_in, const float* dloss, float* loss,
+                              float* lse, void* dA, void* dE, void* ws, size_t ws_bytes, hipStream_t st) {
+  const bool fwd = loss != nullptr;
+  const ChunkPlan pl = make_chunk_plan(p->T, p->D, p->V, p->T);
+  const bool grad = !fwd && (dA != nullptr || dE != nullptr);
+  const Ws2 w = carve_chunked(ws, pl, grad, !fwd && dA != nullptr, !fwd && dE != nullptr, fwd, false);
+  CL_TRY(check_ws(ws, ws_bytes, w.bytes));
+  const int e_fp8 = p->e_dtype == CUTLOSS_FP8_E4M3;
+  {
+    Phase ph(CUTLOSS_PHASE_TARGETS, st);
+    CL_HIP(cl::launch_zero_u64(w.err, 4, st), "zero counters");
+    CL_HIP(cl::launch_targets(w.tw, p->T, p->V, p->T, nullptr, nullptr, nullptr, -1, p->target, p->ignore_index, st),
+           "targets");
+  }
+  if (p->T == 0 || (!fwd && !grad)) return CUTLOSS_OK;
+  cl::FinalizeParams fp{};
+  fp.T = p->T; fp.D = p->D; fp.V = p->V; fp.A = p->A; fp.E = p->E; fp.e_fp8 = e_fp8;
+  fp.crow = w.tw.crow; fp.cids = w.tw.cids; fp.dloss = dloss; fp.ce_target = p->target; fp.ignore_index = p->ignore_index;
+  fp.n_splits = (int)pl.n_splits; fp.n_splits_dA = (int)pl.sk; fp.dA_weighted = 1;
+  fp.part_a = w.part_a; fp.part_b = w.part_b; fp.part_dA = w.part_dA;
+  fp.loss = loss; fp.lse = lse; fp.dA = dA; fp.w_out = w.w; fp.lse_in = lse_in;
+  ChunkJob j{};
+  j.pl = &pl; j.A = p->A; j.E = p->E; j.e_fp8 = e_fp8;
+  j.w = w.w; j.lse = lse_in; j.P = w.P; j.part_a = w.part_a; j.part_b = w.part_b;
+  j.uitems = w.tw.uitems; j.counts = w.tw.counts; j.S_u = w.S_u; j.dE = dE;
+  if (fwd) {
+    j.k1_epi = cl::GEMM_EPI_CE_LSE;
+    j.k3_epi = -1;
+    CL_TRY(run_chunks(j, st));
+    Phase ph(CUTLOSS_PHASE_FINALIZE, st);
+    CL_HIP(cl::launch_finalize_rows(fp, 1, 1, 0, st), "finalize rows");
+    return CUTLOSS_OK;
+  }
+  {
+    Phase ph(CUTLOSS_PHASE_ITEM_SUMS, st);
+    CL_HIP(cl::launch_row_weights(fp, 1, st), "row weights");
+    if (dE != nullptr)
+      CL_HIP(cl::launch_item_sums(p->D, pl.cap, p->A, w.w, w.tw.csc_rows, w.tw.useg, w.tw.counts, w.S_u, w.S_part, st),
+             "item sums");
+  }
+  j.k1_epi = cl::GEMM_EPI_CE_P;
+  j.part_dA = w.part_dA;
+  j.k3_epi = dE != nullptr ? cl::GEMM_EPI_DE : -1;
+  CL_TRY(run_chunks(j, st));
+  if (dA != nullptr) {
+    Phase ph(CUTLOSS_PHASE_FINALIZE, st);
+    CL_HIP(cl::launch_finalize_rows(fp, 1, 0, 1, st), "finalize rows");
   }
   return CUTLOSS_OK;
 }
@@ -336,15 +611,23 @@ extern "C" {
 
 size_t cutloss_bce_workspace_size(const cutloss_bce_problem* p, int32_t op) {
   if (check_bce(p) != CUTLOSS_OK) return 0;
-  const Plan pl = make_plan(p->T, p->D, p->V, p->nnz, p->e_dtype == CUTLOSS_FP8_E4M3);
   const bool bwd = op != CUTLOSS_OP_FWD;
+  if (use_chunked(p->D, p->e_dtype == CUTLOSS_FP8_E4M3)) {
+    const ChunkPlan cp = make_chunk_plan(p->T, p->D, p->V, p->nnz);
+    return carve_chunked(nullptr, cp, bwd, bwd, bwd, false, true).bytes;
+  }
+  const Plan pl = make_plan(p->T, p->D, p->V, p->nnz, p->e_dtype == CUTLOSS_FP8_E4M3);
   return carve(nullptr, pl, bwd, bwd, false).bytes;
 }
 
 size_t cutloss_ce_workspace_size(const cutloss_ce_problem* p, int32_t op) {
   if (check_ce(p) != CUTLOSS_OK) return 0;
-  const Plan pl = make_plan(p->T, p->D, p->V, p->T, p->e_dtype == CUTLOSS_FP8_E4M3);
   const bool bwd = op != CUTLOSS_OP_FWD;
+  if (use_chunked(p->D, p->e_dtype == CUTLOSS_FP8_E4M3)) {
+    const ChunkPlan cp = make_chunk_plan(p->T, p->D, p->V, p->T);
+    return carve_chunked(nullptr, cp, bwd, bwd, bwd, !bwd, false).bytes;
+  }
+  const Plan pl = make_plan(p->T, p->D, p->V, p->T, p->e_dtype == CUTLOSS_FP8_E4M3);
   return carve(nullptr, pl, bwd, bwd, !bwd).bytes;
 }
 

@@ -147,16 +147,61 @@ struct SweepParams {
 // Rows sweep modes: 0 = BCE loss partials, 1 = BCE dA partials, 2 = BCE dA + loss partials,
 // 3 = CE (max, sum) partials, 4 = CE dA partials.
 // Cols sweep: kind 0 = BCE, 1 = CE; epi 0 = write dE (bf16), 1 = SGD step on E in place.
-// sweep.hip: register-staged sweeps (any supported D, bf16 or fp8 streamed E);
-// sweep2.hip: LDS-DMA sweeps at two workgroups per CU (bf16 streamed operand, D <= 256).
-hipError_t launch_sweep_rows(const SweepParams& p, int mode, hipStream_t st);
-hipError_t launch_sweep_cols(const SweepParams& p, int kind, int epi, hipStream_t st);
-bool sweep_supported(int64_t D);
+// sweep2.hip: LDS-DMA sweeps (bf16 streamed operand, D in {64, 128, 256}).
 hipError_t launch_sweep2_rows(const SweepParams& p, int mode, hipStream_t st);
 hipError_t launch_sweep2_cols(const SweepParams& p, int kind, int epi, hipStream_t st);
 bool sweep2_rows_supported(int64_t D, int e_fp8);
 bool sweep2_cols_supported(int64_t D);
 int sweep2_rows_per_block(int64_t D);   // stationary rows per workgroup of the LDS-DMA rows sweep
+
+// ----------------------------------------------------------------------------------
+// Chunked path for wide heads (gemm.hip): three MFMA GEMMs per vocabulary chunk.
+// An operand is stored row-major as [rows][cols] with leading dimension ld (elements):
+// kc = 1 if its cols are the GEMM's K index (k contiguous), 0 if its rows are (k rows).
+// Rows at or past rows_valid and column groups past cols_valid are read as copies of
+// the last valid ones (never out of bounds); the GEMM masks or zero-pads them.
+// ----------------------------------------------------------------------------------
+struct GemmOperand {
+  const void* p;
+  int64_t ld, rows_valid, cols_valid;
+  int kc;      // 1: [M or N][K]; 0: [K][M or N]
+  int fp8;     // OCP E4M3FN storage (widened to bf16 when staged)
+};
+
+enum {
+  GEMM_EPI_BCE_P = 0,     // logits (M = chunk items, N = rows): P = w sigmoid(x), softplus partials
+  GEMM_EPI_BCE_LOSS = 1,  // softplus partials only
+  GEMM_EPI_CE_LSE = 2,    // running (max, sum) partials
+  GEMM_EPI_CE_P = 3,      // P = w exp(x - lse)
+  GEMM_EPI_ACC = 4,       // C (+)= acc into fp32 [M][N] (split-K slice per blockIdx.z)
+  GEMM_EPI_DE = 5,        // dE rows of the chunk: acc - S_u, bf16
+  GEMM_EPI_SGD = 6        // E <- round(E - lr (acc - S_u)) in place
+};
+
+struct GemmParams {
+  GemmOperand a, b;
+  int64_t M, N, K;          // K a multiple of 32
+  int64_t k_per_split;      // K range of one blockIdx.z slice (multiple of 32)
+  int epi;
+  // logits epilogues: chunk rows m map to items v0 + m (< V), cols n to rows t (< T)
+  int64_t v0, V, T;
+  const float* w;           // [T] row weights
+  const float* lse;         // [T] CE logsumexp
+  uint16_t* P;              // [M][ldp] bf16 gradient tile of the chunk
+  int64_t ldp;
+  float* part_a; float* part_b;  // [n_splits][T] row partials
+  int64_t part_base;        // split index of this chunk's first item tile
+  // ACC epilogue
+  float* acc; int64_t ldacc; int64_t acc_slice;   // acc + z * acc_slice
+  int acc_first;            // 1: store, 0: add to the previous value
+  // DE / SGD epilogues
+  const int32_t* uitems; const int32_t* counts; const float* S_u; int64_t D;
+  void* dE; void* E_inplace; int e_fp8; float lr;
+};
+hipError_t launch_gemm(const GemmParams& p, hipStream_t st);
+int gemm_tile_m();                     // 256
+int gemm_tile_n(int64_t N);            // 128 or 256
+int gemm_warps_m(int64_t N);           // waves along M (row partials per item tile)
 
 struct FinalizeParams {
   int64_t T, D, V;
@@ -164,17 +209,26 @@ struct FinalizeParams {
   const int32_t* crow; const int32_t* cids;   // canonical positives / targets
   const float* dloss; const uint8_t* mask;     // BCE
   const int64_t* ce_target; int64_t ignore_index;  // CE
-  int n_splits;
+  int n_splits;             // loss / lse partials
+  int n_splits_dA;          // dA partials
+  int dA_weighted;          // 1: dA partials already carry w_t (chunked path)
   const float* part_a; const float* part_b; const float* part_dA;
   float* loss; float* lse; void* dA;
   const float* lse_in;      // CE backward: lse from the forward
   float* w_out;             // [T] weights for the cols sweep
+  // positive-row terms computed before E changes (chunked path): if set, finalize reads
+  // them instead of E: pos_dot[t] = sum_p A_t . E_p, pos_sum[t][d] = sum_p E_p[d]
+  float* pos_dot; float* pos_sum;
 };
+hipError_t launch_row_positives(const FinalizeParams& p, hipStream_t st);
 // kind: 0 = BCE, 1 = CE
 hipError_t launch_finalize_rows(const FinalizeParams& p, int kind, int want_loss, int want_dA, hipStream_t st);
 hipError_t launch_row_weights(const FinalizeParams& p, int kind, hipStream_t st);
+// Sparse dE term S_u (one row per unique positive item); `part` holds
+// 2 * item_sum_parts(nnz_cap) * D floats of piece partials.
+size_t item_sum_parts(int64_t nnz_cap);
 hipError_t launch_item_sums(int64_t D, int64_t nnz_cap, const void* A, const float* w,
                             const int32_t* csc_rows, const int32_t* useg, const int32_t* counts,
-                            float* S_u, hipStream_t st);
+                            float* S_u, float* part, hipStream_t st);
 
 }  // namespace cl

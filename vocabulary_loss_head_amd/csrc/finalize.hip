@@ -37,9 +37,7 @@ __device__ __forceinline__ float row_weight(const FinalizeParams& p, int kind, i
   return p.dloss ? p.dloss[t] : 1.0f;
 }
 
-constexpr int kMaxDPerLane = 2304 / 64;
-
-// One wave per row.
+// One wave per row; lanes over d (d = lane + 64 k).
 __global__ __launch_bounds__(256) void k_finalize_rows(const FinalizeParams p, int kind, int want_loss, int want_dA) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -48,25 +46,21 @@ __global__ __launch_bounds__(256) void k_finalize_rows(const FinalizeParams p, i
   const int nd = (int)(D / 64);
   const bool valid = row_valid(p, kind, t);
   const uint16_t* A = (const uint16_t*)p.A;
-
-  // positives: x_tp and the sum of E_p
-  float corr[kMaxDPerLane];
-  for (int k = 0; k < nd; ++k) corr[k] = 0.0f;
-  float sum_x = 0.0f;
   const int32_t pb = p.crow[t], pe = p.crow[t + 1];
-  for (int32_t e = pb; e < pe; ++e) {
-    const int64_t v = p.cids[e];
-    float part = 0.0f;
-    for (int k = 0; k < nd; ++k) {
-      const int64_t d = lane + 64 * k;
-      const float ev = load_e(p.E, p.e_fp8, v * D + d);
-      part += bf16_bits_to_f32(A[t * D + d]) * ev;
-      corr[k] += ev;
-    }
-    sum_x += wave_sum(part);
-  }
 
   if (want_loss) {
+    // positive logits x_tp = A_t . E_p (indexed dot products), summed in positive order
+    float sum_x = 0.0f;
+    if (p.pos_dot != nullptr) sum_x = p.pos_dot[t];
+    else for (int32_t e = pb; e < pe; ++e) {
+      const int64_t v = p.cids[e];
+      float part = 0.0f;
+      for (int k = 0; k < nd; ++k) {
+        const int64_t d = lane + 64 * k;
+        part += bf16_bits_to_f32(A[t * D + d]) * load_e(p.E, p.e_fp8, v * D + d);
+      }
+      sum_x += wave_sum(part);
+    }
     if (kind == 0) {
       float part = 0.0f;
       for (int j = lane; j < p.n_splits; j += 64) part += p.part_a[(int64_t)j * p.T + t];
@@ -98,11 +92,44 @@ __global__ __launch_bounds__(256) void k_finalize_rows(const FinalizeParams p, i
       float g = 0.0f;
       if (valid) {
         float acc = 0.0f;
-        for (int j = 0; j < p.n_splits; ++j) acc += p.part_dA[((int64_t)j * p.T + t) * D + d];
-        g = w * (acc - corr[k]);
+        for (int j = 0; j < p.n_splits_dA; ++j) acc += p.part_dA[((int64_t)j * p.T + t) * D + d];
+        float corr = 0.0f;                       // sum of E_p over the row's positives
+        if (p.pos_sum != nullptr) corr = p.pos_sum[t * D + d];
+        else for (int32_t e = pb; e < pe; ++e) corr += load_e(p.E, p.e_fp8, (int64_t)p.cids[e] * D + d);
+        g = p.dA_weighted ? acc - w * corr : w * (acc - corr);
       }
       dA[t * D + d] = (uint16_t)f32_to_bf16_bits(g);
     }
+  }
+}
+
+// pos_dot[t] = sum_p A_t . E_p and pos_sum[t][d] = sum_p E_p[d], one wave per row, in
+// positive order (the same order finalize uses when it reads E directly).
+__global__ __launch_bounds__(256) void k_row_positives(const FinalizeParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= p.T) return;
+  const int64_t D = p.D;
+  const int nd = (int)(D / 64);
+  const uint16_t* A = (const uint16_t*)p.A;
+  const int32_t pb = p.crow[t], pe = p.crow[t + 1];
+  float sum_x = 0.0f;
+  for (int32_t e = pb; e < pe; ++e) {
+    const int64_t v = p.cids[e];
+    float part = 0.0f;
+    for (int k = 0; k < nd; ++k) {
+      const int64_t d = lane + 64 * k;
+      part += bf16_bits_to_f32(A[t * D + d]) * load_e(p.E, p.e_fp8, v * D + d);
+    }
+    sum_x += wave_sum(part);
+  }
+  if (lane == 0) p.pos_dot[t] = sum_x;
+  if (p.pos_sum == nullptr) return;          // no dA requested
+  for (int k = 0; k < nd; ++k) {
+    const int64_t d = lane + 64 * k;
+    float corr = 0.0f;
+    for (int32_t e = pb; e < pe; ++e) corr += load_e(p.E, p.e_fp8, (int64_t)p.cids[e] * D + d);
+    p.pos_sum[t * D + d] = corr;
   }
 }
 
@@ -111,21 +138,74 @@ __global__ void k_row_weights(const FinalizeParams p, int kind) {
   if (t < p.T) p.w_out[t] = row_weight(p, kind, t);
 }
 
-// S_u[d] = sum over the item's pairs (in row order) of w_t A_t[d]
-__global__ __launch_bounds__(256) void k_item_sums(int64_t D, const uint16_t* __restrict__ A, const float* __restrict__ w,
-                                                   const int32_t* __restrict__ csc_rows, const int32_t* __restrict__ useg,
-                                                   const int32_t* __restrict__ counts, float* __restrict__ S_u) {
-  const int nu = counts[2];
-  for (int u = blockIdx.x; u < nu; u += gridDim.x) {
-    const int32_t b = useg[u], e = useg[u + 1];
-    for (int64_t d = threadIdx.x; d < D; d += 256) {
+// Sparse dE term S_u = sum over the item's pairs (in row order) of w_t A_t, as a
+// segmented sum over the item-major pairs. Pairs are cut into fixed pieces of kPiece;
+// one wave sums each piece, lanes over d. An item lying inside one piece is finished
+// there; an item crossing piece boundaries leaves its run at the end of its first
+// piece in part[j][1], its runs covering or starting later pieces in part[j][0], and
+// k_item_fixup adds them in piece order. Every sum runs in a fixed order.
+constexpr int kPiece = 32;
+
+// index of the unique item that holds pair i (useg ascending, useg[0] = 0)
+__device__ __forceinline__ int item_of(const int32_t* useg, int nu, int32_t i) {
+  int lo = 0, hi = nu;          // first index with useg[idx] > i, minus one
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (useg[mid] <= i) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo - 1;
+}
+
+__global__ __launch_bounds__(256) void k_item_pieces(int64_t D, const uint16_t* __restrict__ A, const float* __restrict__ w,
+                                                     const int32_t* __restrict__ csc_rows, const int32_t* __restrict__ useg,
+                                                     const int32_t* __restrict__ counts, float* __restrict__ S_u,
+                                                     float* __restrict__ part) {
+  const int lane = threadIdx.x & 63;
+  const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int32_t n = counts[1], nu = counts[2];
+  const int64_t a = j * kPiece;
+  if (a >= n) return;
+  const int64_t b = min(a + kPiece, (int64_t)n);
+  const int nd = (int)(D / 64);
+  int64_t i = a;
+  while (i < b) {
+    const int u = item_of(useg, nu, (int32_t)i);
+    const int64_t s = useg[u], e = useg[u + 1];
+    const int64_t r1 = min(e, b);
+    float* dst;
+    if (s >= a && e <= b) dst = S_u + (int64_t)u * D;          // complete inside this piece
+    else if (s < a) dst = part + (j * 2 + 0) * D;               // began in an earlier piece
+    else dst = part + (j * 2 + 1) * D;                          // continues into later pieces
+    for (int k = 0; k < nd; ++k) {
       float acc = 0.0f;
-      for (int32_t i = b; i < e; ++i) {
-        const int64_t t = csc_rows[i];
-        acc += w[t] * bf16_bits_to_f32(A[t * D + d]);
+      for (int64_t q = i; q < r1; ++q) {
+        const int64_t t = csc_rows[q];
+        acc += w[t] * bf16_bits_to_f32(A[t * D + lane + 64 * k]);
       }
-      S_u[(int64_t)u * D + d] = acc;
+      dst[lane + 64 * k] = acc;
     }
+    i = r1;
+  }
+}
+
+// One block per piece: if an item starts in piece j and continues past it, finish it.
+__global__ __launch_bounds__(256) void k_item_fixup(int64_t D, const int32_t* __restrict__ useg,
+                                                    const int32_t* __restrict__ counts, float* __restrict__ S_u,
+                                                    const float* __restrict__ part) {
+  const int64_t j = blockIdx.x;
+  const int32_t n = counts[1], nu = counts[2];
+  const int64_t a = j * kPiece;
+  if (a >= n) return;
+  const int64_t b = min(a + kPiece, (int64_t)n);
+  const int u = item_of(useg, nu, (int32_t)(b - 1));
+  const int64_t s = useg[u], e = useg[u + 1];
+  if (!(e > b && s >= a)) return;
+  const int64_t j1 = (e - 1) / kPiece;
+  for (int64_t d = threadIdx.x; d < D; d += 256) {
+    float acc = part[(j * 2 + 1) * D + d];
+    for (int64_t jj = j + 1; jj <= j1; ++jj) acc += part[(jj * 2 + 0) * D + d];
+    S_u[(int64_t)u * D + d] = acc;
   }
 }
 
@@ -133,8 +213,13 @@ __global__ __launch_bounds__(256) void k_item_sums(int64_t D, const uint16_t* __
 
 hipError_t launch_finalize_rows(const FinalizeParams& p, int kind, int want_loss, int want_dA, hipStream_t st) {
   if (p.T == 0) return hipSuccess;
-  if (p.D / 64 > kMaxDPerLane) return hipErrorInvalidValue;
   k_finalize_rows<<<(unsigned)((p.T + 3) / 4), 256, 0, st>>>(p, kind, want_loss, want_dA);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_positives(const FinalizeParams& p, hipStream_t st) {
+  if (p.T == 0) return hipSuccess;
+  k_row_positives<<<(unsigned)((p.T + 3) / 4), 256, 0, st>>>(p);
   return hipGetLastError();
 }
 
@@ -144,11 +229,14 @@ hipError_t launch_row_weights(const FinalizeParams& p, int kind, hipStream_t st)
   return hipGetLastError();
 }
 
+size_t item_sum_parts(int64_t nnz_cap) { return (size_t)((nnz_cap + kPiece - 1) / kPiece); }
+
 hipError_t launch_item_sums(int64_t D, int64_t nnz_cap, const void* A, const float* w, const int32_t* csc_rows,
-                            const int32_t* useg, const int32_t* counts, float* S_u, hipStream_t st) {
+                            const int32_t* useg, const int32_t* counts, float* S_u, float* part, hipStream_t st) {
   if (nnz_cap <= 0) return hipSuccess;
-  const unsigned grid = (unsigned)(nnz_cap < 4096 ? nnz_cap : 4096);
-  k_item_sums<<<grid, 256, 0, st>>>(D, (const uint16_t*)A, w, csc_rows, useg, counts, S_u);
+  const int64_t np = (int64_t)item_sum_parts(nnz_cap);
+  k_item_pieces<<<(unsigned)((np + 3) / 4), 256, 0, st>>>(D, (const uint16_t*)A, w, csc_rows, useg, counts, S_u, part);
+  k_item_fixup<<<(unsigned)np, 256, 0, st>>>(D, useg, counts, S_u, part);
   return hipGetLastError();
 }
 
