@@ -72,3 +72,24 @@ def test_generator_bf16_rounding_matches_torch():
     x = (rng.normal(0, 1, 100000) * np.exp2(rng.integers(-20, 20, 100000))).astype(np.float32)
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(_bf16_bits(x), ref)
+
+
+def test_generator_fp8_encoder_matches_nearest_even_table():
+    """The input generator's fast E4M3FN rounding equals a brute-force nearest-value
+    search over the 127 finite codes with ties to the even code, saturating at 448
+    (including every code, every midpoint and its float32 neighbours)."""
+    from workloads.gen import _fp8_bytes, fp8_e4m3fn_values
+    vals = fp8_e4m3fn_values()[:127]
+    rng = np.random.default_rng(0)
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)
+    x = np.concatenate([np.concatenate([rng.normal(0, s, 4000) for s in (0.01, 0.05, 1.0, 100.0, 500.0)]).astype(np.float32),
+                        vals.astype(np.float32), -vals.astype(np.float32), mids, -mids,
+                        np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9)),
+                        np.float32([448, 449, 463.9, 464, 465, 1e6, -1e6, 0.0, 1e-30])])
+    a = np.minimum(np.abs(x.astype(np.float64)), 448.0)
+    d = np.abs(a[:, None] - vals[None, :])
+    cand = d == d.min(1, keepdims=True)
+    even = np.arange(127)[None, :] % 2 == 0
+    idx = np.where(cand.sum(1) > 1, np.argmax(cand & even, axis=1), np.argmin(d, axis=1))
+    ref = idx.astype(np.uint8) | ((np.signbit(x) & (idx != 0)).astype(np.uint8) << 7)
+    assert np.array_equal(_fp8_bytes(x), ref)

@@ -114,21 +114,25 @@ def fp8_e4m3fn_values() -> np.ndarray:
     return vals
 
 
-_FP8_POS = fp8_e4m3fn_values()[:127]  # finite, strictly increasing
-
-
 def _fp8_bytes(x: np.ndarray) -> np.ndarray:
-    """float -> E4M3FN byte: nearest finite code, ties to the even code, |x| > 448 saturates."""
-    x = np.asarray(x, dtype=np.float64)
-    a = np.minimum(np.abs(x), _FP8_POS[-1])
-    hi = np.searchsorted(_FP8_POS, a, side="left")          # first code >= a
-    hi = np.minimum(hi, 126)
-    lo = np.maximum(hi - 1, 0)
-    d_lo = a - _FP8_POS[lo]
-    d_hi = _FP8_POS[hi] - a
-    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
-    code = np.where(pick_hi, hi, lo).astype(np.uint8)
-    code = np.where(a == _FP8_POS[hi], hi, code).astype(np.uint8)
+    """float32 -> E4M3FN byte: nearest, ties to the even code, |x| > 448 saturates to 448.
+
+    Normal codes (|x| >= 2^-6): round the float32 mantissa to 3 bits (nearest, ties to
+    even) by integer arithmetic on the bit pattern, then re-bias the exponent (127 -> 7).
+    Subnormal codes (|x| < 2^-6): the code is |x| / 2^-9 rounded to nearest even.
+    A negative input sets the sign bit unless it rounds to zero.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    a = np.minimum(np.abs(x), np.float32(448.0))
+    u = a.view(np.uint32)
+    lsb = (u >> np.uint32(20)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFFF) + lsb) & np.uint32(0xFFF00000)
+    e = (r >> np.uint32(23)).astype(np.int32) - 127 + 7
+    m = ((r >> np.uint32(20)) & np.uint32(7)).astype(np.int32)
+    normal = (e << 3) | m
+    normal = np.minimum(normal, 0x7E)                       # 464 would round to 480: saturate
+    sub = np.rint(a * np.float32(512.0)).astype(np.int32)   # multiples of 2^-9, 0..8
+    code = np.where(a >= np.float32(2.0 ** -6), normal, sub).astype(np.uint8)
     neg = np.signbit(x) & (code != 0)
     return (code | (neg.astype(np.uint8) << 7)).astype(np.uint8)
 
@@ -137,43 +141,36 @@ def _fp8_bytes(x: np.ndarray) -> np.ndarray:
 # samplers
 # ----------------------------------------------------------------------------
 
-_CHUNK_ROWS = 1 << 16
+_CHUNK_ELEMS = 1 << 22
+
+
+def _normal_matrix(seq: np.random.SeedSequence, rows: int, cols: int, std: float, encode, dtype) -> np.ndarray:
+    """rows x cols normals (fp32 draws scaled by std) in chunks of whole rows, each chunk
+    with its own spawned stream, encoded by `encode`."""
+    out = np.empty((rows, cols), dtype=dtype)
+    step = max(1, _CHUNK_ELEMS // max(cols, 1))
+    starts = list(range(0, rows, step))
+    seqs = seq.spawn(len(starts))
+
+    def fill(i):
+        r0 = starts[i]
+        r1 = min(rows, r0 + step)
+        g = np.random.Generator(np.random.PCG64(seqs[i]))
+        z = g.standard_normal((r1 - r0, cols), dtype=np.float32)
+        z *= np.float32(std)
+        out[r0:r1] = encode(z)
+
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        list(ex.map(fill, range(len(starts))))
+    return out
 
 
 def _normal_bf16(seq: np.random.SeedSequence, rows: int, cols: int, std: float) -> np.ndarray:
-    out = np.empty((rows, cols), dtype=np.uint16)
-    starts = list(range(0, rows, _CHUNK_ROWS))
-    seqs = seq.spawn(len(starts))
-
-    def fill(i):
-        r0 = starts[i]
-        r1 = min(rows, r0 + _CHUNK_ROWS)
-        g = np.random.Generator(np.random.PCG64(seqs[i]))
-        z = g.standard_normal((r1 - r0, cols), dtype=np.float32)
-        z *= np.float32(std)
-        out[r0:r1] = _bf16_bits(z)
-
-    with ThreadPoolExecutor(max_workers=8) as ex:
-        list(ex.map(fill, range(len(starts))))
-    return out
+    return _normal_matrix(seq, rows, cols, std, _bf16_bits, np.uint16)
 
 
 def _normal_fp8(seq: np.random.SeedSequence, rows: int, cols: int, std: float) -> np.ndarray:
-    out = np.empty((rows, cols), dtype=np.uint8)
-    starts = list(range(0, rows, _CHUNK_ROWS))
-    seqs = seq.spawn(len(starts))
-
-    def fill(i):
-        r0 = starts[i]
-        r1 = min(rows, r0 + _CHUNK_ROWS)
-        g = np.random.Generator(np.random.PCG64(seqs[i]))
-        z = g.standard_normal((r1 - r0, cols), dtype=np.float32)
-        z *= np.float32(std)
-        out[r0:r1] = _fp8_bytes(z)
-
-    with ThreadPoolExecutor(max_workers=8) as ex:
-        list(ex.map(fill, range(len(starts))))
-    return out
+    return _normal_matrix(seq, rows, cols, std, _fp8_bytes, np.uint8)
 
 
 def _distinct_rows(draw, T: int, counts: np.ndarray) -> list[np.ndarray]:
