@@ -158,7 +158,8 @@ def time_calls(fn, steps, warmup, profile=False):
     phases = {}
     if profile:
         B.cutloss_profile_enable(False)
-        phases = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in B.cutloss_profile_read().items()}
+        # {phase: (ms per step, launches per step)}
+        phases = {k: (v[0] / steps, v[1] / steps) for k, v in B.cutloss_profile_read().items() if v[1]}
     return ev0.elapsed_time(ev1) / steps, phases
 
 
@@ -179,10 +180,9 @@ def record(name, steps, warmup, with_cpu):
     T, D, V = w.T, w.D, w.V
     tflops = 8.0 * T * V * D / (ms * 1e-3) / 1e12
     n_valid = int(inp["mask"].sum()) if "mask" in inp else int((inp["target"] != -100).sum())
-    # dominant kernel phase. Fused sweeps (D <= 256): the rows sweep executes
-    # 4TVD per launch (recompute + dA). Chunked path: one logits or dA GEMM launch per
-    # chunk, 2 T Vc D each; the mean launch is reported with 2TVD / chunks.
-    dom = max(("rows_sweep", "cols_sweep"), key=lambda k: phases.get(k, 0.0))
+    # dominant kernel phase of the fused sweeps (D <= 256): one launch per step each;
+    # the rows sweep executes 4TVD per launch (logit recompute + dA)
+    dom = max(("rows_sweep", "cols_sweep"), key=lambda k: phases.get(k, (0.0, 0))[0])
     rec = {
         "metric": METRIC if name == "seqrec_bce" else f"{name}: fused fwd+bwd TFLOP/s (8TVD counted)",
         "value": round(tflops, 2),
@@ -201,14 +201,15 @@ def record(name, steps, warmup, with_cpu):
         "rows_per_s": round(T / (ms * 1e-3), 1),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "tflops_valid_rows": round(8.0 * n_valid * V * D / (ms * 1e-3) / 1e12, 2),
-        "phase_ms": {k: round(v, 4) for k, v in phases.items()},
+        "phase_ms": {k: round(v[0], 4) for k, v in phases.items()},
+        "phase_launches": {k: round(v[1], 2) for k, v in phases.items()},
         "peak_hbm_bytes": int(peak),
         "workspace_bytes": h.ws_bytes,
         "logits_fp32_bytes": 4 * T * V,
     }
     if name == "seqrec_bce":
         dom_flops = 4.0 * T * V * D
-        achieved = dom_flops / (phases[dom] * 1e-3) / 1e12
+        achieved = dom_flops / (phases[dom][0] / phases[dom][1] * 1e-3) / 1e12
         rec["roofline"] = {"kernel": f"k_{dom.split('_')[0]}2 (fused {dom.replace('_', ' ')})", "bound": "mfma",
                            "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}

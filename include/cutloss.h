@@ -41,7 +41,7 @@
  *  - Paths: heads with D in {64, 128, 256} and bf16 E run fused logit-tile sweeps that
  *    never write a logit; every other head (any D that is a multiple of 64, or FP8 E)
  *    runs a chunked path that keeps one vocabulary chunk's bf16 gradient tile
- *    (T x Vc, at most 512 MiB by default) in the workspace. The environment variable
+ *    (T x Vc, at most 1 GiB by default) in the workspace. The environment variable
  *    CUTLOSS_MAX_CHUNK_ITEMS caps Vc (read when a call or size query plans the work,
  *    so set it before both).
  */
@@ -176,13 +176,16 @@ cutloss_status cutloss_bce_canonical_targets(const cutloss_bce_problem* p,
  * pair on the caller's stream around each of its kernel phases:
  *   0 target canonicalization, 1 rows sweep (loss/LSE partials, dA partials),
  *   2 row finalization (loss, lse, dA), 3 row weights + sparse item sums,
- *   4 cols sweep (dE or the fused SGD step).
+ *   4 cols sweep (dE or the fused SGD step); the chunked path records its three
+ *   products per chunk as 5 logits + epilogue, 6 dA product, 7 dE product (or the
+ *   fused SGD step).
  * cutloss_profile_read synchronizes on the recorded events, writes the summed
  * milliseconds and the number of recorded launches per phase (arrays of n entries),
  * and clears the records. Enabling costs one event record per phase boundary.
  */
 enum { CUTLOSS_PHASE_TARGETS = 0, CUTLOSS_PHASE_ROWS = 1, CUTLOSS_PHASE_FINALIZE = 2,
-       CUTLOSS_PHASE_ITEM_SUMS = 3, CUTLOSS_PHASE_COLS = 4, CUTLOSS_N_PHASES = 5 };
+       CUTLOSS_PHASE_ITEM_SUMS = 3, CUTLOSS_PHASE_COLS = 4, CUTLOSS_PHASE_CHUNK_LOGITS = 5,
+       CUTLOSS_PHASE_CHUNK_DA = 6, CUTLOSS_PHASE_CHUNK_DE = 7, CUTLOSS_N_PHASES = 8 };
 cutloss_status cutloss_profile_enable(int32_t enable);
 cutloss_status cutloss_profile_read(float* ms, int32_t* launches, int32_t n);
 

@@ -52,7 +52,8 @@ EXPORTED = [
     "cutloss_profile_enable", "cutloss_profile_read",
     "cutloss_status_string", "cutloss_last_error", "cutloss_version",
 ]
-PHASES = ["targets", "rows_sweep", "finalize_rows", "item_sums", "cols_sweep"]
+PHASES = ["targets", "rows_sweep", "finalize_rows", "item_sums", "cols_sweep", "chunk_logits", "chunk_dA",
+          "chunk_dE"]
 
 
 def _load() -> ctypes.CDLL:

@@ -185,15 +185,15 @@ int64_t ceil_div(int64_t x, int64_t a) { return (x + a - 1) / a; }
 
 struct ChunkPlan {
   int64_t T, D, V, cap;
-  int64_t Tp;         // rows padded to 128: row stride of the P buffer
-  int64_t Vc;         // items per chunk (multiple of the item tile)
+  int64_t Tp;         // rows padded to 128: rows of the P buffer P[t][item]
+  int64_t Vc;         // items per chunk (multiple of the item tile): row stride of P
   int64_t n_chunks;
   int64_t n_splits;   // loss / lse partials: item tiles x waves along the item dimension
   int64_t sk;         // split-K slices of the dA product
   int64_t kps;        // items per slice
 };
 
-constexpr int64_t kChunkPBytes = 512ll << 20;   // P buffer budget
+constexpr int64_t kChunkPBytes = 1ll << 30;     // P buffer budget
 
 ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap) {
   ChunkPlan c{};
@@ -234,6 +234,7 @@ struct Ws2 {
   float* pos_sum;
   float* S_u;
   float* S_part;
+  float* red;         // staging of the split reductions
   size_t bytes;
 };
 
@@ -272,6 +273,9 @@ Ws2 carve_chunked(void* base, const ChunkPlan& pl, bool need_P, bool need_dA, bo
   w.pos_sum = need_pos && need_dA ? c.take<float>((size_t)T * pl.D) : nullptr;
   w.S_u = need_Su ? c.take<float>((size_t)cap * pl.D) : nullptr;
   w.S_part = need_Su ? c.take<float>(2 * cl::item_sum_parts(cap) * pl.D) : nullptr;
+  const size_t red_loss = cl::reduce_splits_tmp_floats(pl.n_splits, T, two_partials ? 1 : 0);
+  const size_t red_dA = need_dA ? cl::reduce_splits_tmp_floats(pl.sk, T * pl.D, 0) : 0;
+  w.red = c.take<float>(std::max<size_t>(1, std::max(red_loss, red_dA)));
   w.bytes = c.off;
   return w;
 }
@@ -472,22 +476,22 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
     const int64_t mc = round_up(vlen, bm);
     const void* Ec = (const char*)j.E + v0 * pl.D * esz;
     {
-      Phase ph(CUTLOSS_PHASE_ROWS, st);
+      Phase ph(CUTLOSS_PHASE_CHUNK_LOGITS, st);
       cl::GemmParams g{};
       g.a = operand(Ec, pl.D, vlen, pl.D, 1, j.e_fp8);
       g.b = operand(j.A, pl.D, pl.T, pl.D, 1, 0);
       g.M = mc; g.N = pl.Tp; g.K = pl.D; g.k_per_split = pl.D;
       g.epi = j.k1_epi;
       g.v0 = v0; g.V = pl.V; g.T = pl.T; g.D = pl.D;
-      g.w = j.w; g.lse = j.lse; g.P = j.P; g.ldp = pl.Tp;
+      g.w = j.w; g.lse = j.lse; g.P = j.P; g.ldp = pl.Vc; g.p_rows = pl.Tp;
       g.part_a = j.part_a; g.part_b = j.part_b;
       g.part_base = (v0 / bm) * cl::gemm_warps_m(pl.Tp);
       CL_HIP(cl::launch_gemm(g, st), "chunk logits");
     }
     if (j.part_dA != nullptr) {
-      Phase ph(CUTLOSS_PHASE_ROWS, st);
+      Phase ph(CUTLOSS_PHASE_CHUNK_DA, st);
       cl::GemmParams g{};
-      g.a = operand(j.P, pl.Tp, mc, pl.Tp, 0, 0);
+      g.a = operand(j.P, pl.Vc, pl.Tp, mc, 1, 0);
       g.b = operand(Ec, pl.D, vlen, pl.D, 0, j.e_fp8);
       g.M = pl.T; g.N = pl.D; g.K = mc; g.k_per_split = pl.kps;
       g.epi = cl::GEMM_EPI_ACC;
@@ -496,9 +500,9 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
       CL_HIP(cl::launch_gemm(g, st), "chunk dA");
     }
     if (j.k3_epi >= 0) {
-      Phase ph(CUTLOSS_PHASE_COLS, st);
+      Phase ph(CUTLOSS_PHASE_CHUNK_DE, st);
       cl::GemmParams g{};
-      g.a = operand(j.P, pl.Tp, mc, pl.Tp, 1, 0);
+      g.a = operand(j.P, pl.Vc, pl.Tp, mc, 0, 0);
       g.b = operand(j.A, pl.D, pl.T, pl.D, 0, 0);
       g.M = mc; g.N = pl.D; g.K = pl.Tp; g.k_per_split = pl.Tp;
       g.epi = j.k3_epi;
@@ -549,6 +553,14 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
   CL_TRY(run_chunks(j, st));
   if (loss != nullptr || dA != nullptr) {
     Phase ph(CUTLOSS_PHASE_FINALIZE, st);
+    if (loss != nullptr) {
+      CL_HIP(cl::launch_reduce_splits(w.part_a, nullptr, pl.n_splits, p->T, w.red, 0, st), "loss partials");
+      fp.n_splits = 1;
+    }
+    if (dA != nullptr) {
+      CL_HIP(cl::launch_reduce_splits(w.part_dA, nullptr, pl.sk, p->T * p->D, w.red, 0, st), "dA partials");
+      fp.n_splits_dA = 1;
+    }
     CL_HIP(cl::launch_finalize_rows(fp, 0, loss != nullptr, dA != nullptr, st), "finalize rows");
   }
   return CUTLOSS_OK;
@@ -584,6 +596,8 @@ cutloss_status ce_run_chunked(const cutloss_ce_problem* p, const float* lse_in, 
     j.k3_epi = -1;
     CL_TRY(run_chunks(j, st));
     Phase ph(CUTLOSS_PHASE_FINALIZE, st);
+    CL_HIP(cl::launch_reduce_splits(w.part_a, w.part_b, pl.n_splits, p->T, w.red, 1, st), "lse partials");
+    fp.n_splits = 1;
     CL_HIP(cl::launch_finalize_rows(fp, 1, 1, 0, st), "finalize rows");
     return CUTLOSS_OK;
   }
@@ -600,6 +614,8 @@ cutloss_status ce_run_chunked(const cutloss_ce_problem* p, const float* lse_in, 
   CL_TRY(run_chunks(j, st));
   if (dA != nullptr) {
     Phase ph(CUTLOSS_PHASE_FINALIZE, st);
+    CL_HIP(cl::launch_reduce_splits(w.part_dA, nullptr, pl.sk, p->T * p->D, w.red, 0, st), "dA partials");
+    fp.n_splits_dA = 1;
     CL_HIP(cl::launch_finalize_rows(fp, 1, 0, 1, st), "finalize rows");
   }
   return CUTLOSS_OK;

@@ -187,8 +187,8 @@ struct GemmParams {
   int64_t v0, V, T;
   const float* w;           // [T] row weights
   const float* lse;         // [T] CE logsumexp
-  uint16_t* P;              // [M][ldp] bf16 gradient tile of the chunk
-  int64_t ldp;
+  uint16_t* P;              // [p_rows][ldp] bf16 gradient tile of the chunk: P[t][item]
+  int64_t ldp, p_rows;
   float* part_a; float* part_b;  // [n_splits][T] row partials
   int64_t part_base;        // split index of this chunk's first item tile
   // ACC epilogue
@@ -223,6 +223,11 @@ struct FinalizeParams {
 hipError_t launch_row_positives(const FinalizeParams& p, hipStream_t st);
 // kind: 0 = BCE, 1 = CE
 hipError_t launch_finalize_rows(const FinalizeParams& p, int kind, int want_loss, int want_dA, hipStream_t st);
+// Reduces split partials pa (and pb) [S][N] into their split-0 slice in a fixed order
+// (groups of 64 splits, then groups of group sums). mode 1 merges logsumexp (max, sum)
+// pairs. tmp holds reduce_splits_tmp_floats(S, N, mode) floats.
+size_t reduce_splits_tmp_floats(int64_t S, int64_t N, int mode);
+hipError_t launch_reduce_splits(float* pa, float* pb, int64_t S, int64_t N, float* tmp, int mode, hipStream_t st);
 hipError_t launch_row_weights(const FinalizeParams& p, int kind, hipStream_t st);
 // Sparse dE term S_u (one row per unique positive item); `part` holds
 // 2 * item_sum_parts(nnz_cap) * D floats of piece partials.

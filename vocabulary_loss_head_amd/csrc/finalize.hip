@@ -209,7 +209,67 @@ __global__ __launch_bounds__(256) void k_item_fixup(int64_t D, const int32_t* __
   }
 }
 
+// Fixed-order reduction of split partials [S][N] (row-major by split), one thread per
+// column n: group g sums splits [64 g, 64 g + 64) in split order. mode 0: plain sums;
+// mode 1: logsumexp pairs (a = running max, b = sum of exp(x - max)), merged to the
+// group max. Reading and writing the same buffer is allowed: each thread reads all of
+// its column before it writes it.
+constexpr int kRedGroup = 64;
+
+__global__ __launch_bounds__(256) void k_reduce_splits(const float* pa, const float* pb, int64_t S, int64_t N, float* oa,
+                                                       float* ob, int mode) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t g = blockIdx.y;
+  if (n >= N) return;
+  const int64_t s0 = g * kRedGroup, s1 = min(S, s0 + kRedGroup);
+  if (mode == 0) {
+    float acc = 0.0f;
+    for (int64_t s = s0; s < s1; ++s) acc += pa[s * N + n];
+    oa[g * N + n] = acc;
+  } else {
+    float m = -__builtin_inff();
+    for (int64_t s = s0; s < s1; ++s) m = __builtin_fmaxf(m, pa[s * N + n]);
+    float sum = 0.0f;
+    if (m != -__builtin_inff()) {
+      for (int64_t s = s0; s < s1; ++s) {
+        const float ms = pa[s * N + n];
+        if (ms != -__builtin_inff()) sum += pb[s * N + n] * __builtin_amdgcn_exp2f((ms - m) * kLog2e);
+      }
+    }
+    oa[g * N + n] = m;
+    ob[g * N + n] = sum;
+  }
+}
+
+int64_t red_groups(int64_t S) { return (S + kRedGroup - 1) / kRedGroup; }
+
 }  // namespace
+
+size_t reduce_splits_tmp_floats(int64_t S, int64_t N, int mode) {
+  size_t f = 0;
+  for (int64_t s = S; s > kRedGroup; s = red_groups(s)) f += (size_t)red_groups(s) * (size_t)N;
+  return mode ? 2 * f : f;
+}
+
+hipError_t launch_reduce_splits(float* pa, float* pb, int64_t S, int64_t N, float* tmp, int mode, hipStream_t st) {
+  if (S <= 1 || N <= 0) return hipSuccess;
+  const unsigned bx = (unsigned)((N + 255) / 256);
+  const float* ca = pa;
+  const float* cb = pb;
+  int64_t cs = S;
+  while (cs > kRedGroup) {
+    const int64_t g = red_groups(cs);
+    float* ta = tmp;
+    float* tb = mode ? tmp + g * N : nullptr;
+    k_reduce_splits<<<dim3(bx, (unsigned)g), 256, 0, st>>>(ca, cb, cs, N, ta, tb, mode);
+    tmp += (mode ? 2 : 1) * g * N;
+    ca = ta;
+    cb = tb;
+    cs = g;
+  }
+  k_reduce_splits<<<dim3(bx, 1), 256, 0, st>>>(ca, cb, cs, N, pa, pb, mode);
+  return hipGetLastError();
+}
 
 hipError_t launch_finalize_rows(const FinalizeParams& p, int kind, int want_loss, int want_dA, hipStream_t st) {
   if (p.T == 0) return hipSuccess;

@@ -2,10 +2,10 @@
 // chunk of Vc items, three MFMA GEMMs with fused epilogues.
 //
 //   K1  X^T = E_c A^T          (M = chunk items, N = rows, K = D)
-//       BCE: P = w sigmoid(X) -> bf16 [Vc][T] buffer, softplus row partials;
+//       BCE: P = w sigmoid(X) -> bf16 P[t][v] buffer, softplus row partials;
 //       CE forward: (max, sum) row partials; CE backward: P = w exp(X - lse).
-//   K2  dA (+)= P^T-chunk E_c   (M = rows, N = D, K = Vc), fp32 split-K partials
-//   K3  dE_c = P A - S          (M = chunk items, N = D, K = rows): bf16 dE, or the
+//   K2  dA (+)= P E_c          (M = rows, N = D, K = Vc), fp32 split-K partials
+//   K3  dE_c = P^T A - S       (M = chunk items, N = D, K = rows): bf16 dE, or the
 //       SGD step on E in place (ELMO summary, Key Contributions 2: gradient fused with
 //       the update, never stored).
 //
@@ -15,11 +15,16 @@
 // (no recompute), and at D >= 512 each GEMM stays compute-bound with P in HBM.
 //
 // Kernel: 8 waves, 256 x (256 | 128) output tile, K stages of 32 in a 4-deep LDS ring.
-// bf16 operands arrive by global_load_lds_dwordx4 (lane-linear 1 KB blocks); FP8
-// operands go through registers and are widened to bf16 exactly on the way to LDS.
-// An operand tile is either k-contiguous ([rows][32 k], read with ds_read_b128) or
-// k-major ([32 k][cols], read transposed with ds_read_b64_tr_b16); both read patterns
-// give lane (l, h) the k values 16 kk + 8 h + 0..7, so any pair of modes composes.
+// bf16 operands arrive by global_load_lds_dwordx4 (lane-linear 1 KB blocks) from a
+// wave-uniform tile origin plus per-lane offsets fixed at kernel start; FP8 operands go
+// through registers and are widened to bf16 exactly on the way to LDS. An operand tile
+// is either k-contiguous ([rows][32 k], read with ds_read_b128) or k-major
+// ([32 k][cols], read transposed with ds_read_b64_tr_b16); both read patterns give lane
+// (l, h) the k values 16 kk + 8 h + 0..7, so any pair of modes composes.
+//
+// Workgroups take output tiles in an order that keeps each XCD (blockIdx % 8) on a
+// contiguous run of tiles: 8 row tiles by all column tiles, so the 32 workgroups an XCD
+// runs at once share their A and B tiles through that XCD's L2.
 #include "common.h"
 
 #define CL_GAS __attribute__((address_space(1)))
@@ -32,10 +37,17 @@ constexpr int kBK = 32;
 constexpr int kNst = 4;
 constexpr int kBM = 256;
 constexpr int kThreads = 512;
+constexpr int kGroupM = 8;
 constexpr float kNegInf = -__builtin_inff();
 
-__device__ __forceinline__ int swz_f(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 __device__ __forceinline__ int res_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+
+// Swizzle of k-major tiles. One transposed read touches 4 rows at 64 logical bytes for
+// each half wave, rows q..q+3 and q+8..q+11 (q = 0 or 4, + 16 for the second k16 half).
+// s(r) sends rows with different r & 3 to different 64-byte groups of the 256-byte bank
+// window and the two row quads to alternate 32-byte groups, so every 16- or 32-lane
+// subset of the instruction reads distinct banks.
+__device__ __forceinline__ int swz_kr(int r) { return ((r & 3) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1); }
 
 template <class T>
 __device__ __forceinline__ const CL_LDS T* lds_ptr(uint32_t a) { return (const CL_LDS T*)(uintptr_t)a; }
@@ -67,48 +79,100 @@ struct Tile {
   static_assert(PER_WAVE >= 1 && PIECES >= 1, "tile");
   __device__ __forceinline__ static int phys(int lp, int r) {   // an involution in lp
     if constexpr (KC) return lp ^ ((r >> 2) & 3);
-    else return lp ^ (swz_f(r) & (NCH - 1));
+    else return lp ^ (swz_kr(r) & (NCH - 1));
   }
-  // storage element offset of the 8-element group that belongs at LDS byte `byte`
-  __device__ __forceinline__ static int64_t src(const GemmOperand& op, int64_t outer0, int64_t k0, int byte) {
-    const int r = byte / ROW;
-    const int lp = phys((byte % ROW) / 16, r);
+};
+
+// Where the 8-element groups of one stage come from. The LDS byte of group j is fixed
+// per lane; its source is origin(k0) + off[j] elements, origin(k0) being the wave-uniform
+// address of element (outer0, k0) (KC) or (k0, outer0) (KR). Offsets clamp the outer
+// index into the valid range once; a stage that reaches past the valid k range (only the
+// last stages of some products) recomputes them with the k clamp as well.
+template <int R, bool KC, bool F8>
+struct Loader {
+  using TL = Tile<R, KC>;
+  static constexpr int N = F8 ? TL::PIECES : TL::PER_WAVE;
+  static constexpr int ESZ = F8 ? 1 : 2;
+  uint32_t off[N];
+
+  __device__ __forceinline__ static int byte_of(int j, int wv, int lane, int tid) {
+    return F8 ? 16 * (tid + kThreads * j) : (wv * TL::PER_WAVE + j) * 1024 + 16 * lane;
+  }
+  __device__ __forceinline__ static void rc(int byte, int& r, int& c) {
+    r = byte / TL::ROW;
+    c = 8 * TL::phys((byte % TL::ROW) / 16, r);
+  }
+  __device__ __forceinline__ void init(const GemmOperand& op, int64_t outer0, int wv, int lane, int tid) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      int r, c;
+      rc(byte_of(j, wv, lane, tid), r, c);
+      if constexpr (KC) {
+        const int64_t row = min(outer0 + r, op.rows_valid - 1) - outer0;
+        off[j] = (uint32_t)(row * op.ld + c);
+      } else {
+        const int64_t col = min(outer0 + c, op.cols_valid - 8) - outer0;
+        off[j] = (uint32_t)(r * op.ld + col);
+      }
+    }
+  }
+  __device__ __forceinline__ static const char* origin(const GemmOperand& op, int64_t outer0, int64_t k0) {
+    return (const char*)op.p + (KC ? outer0 * op.ld + k0 : k0 * op.ld + outer0) * ESZ;
+  }
+  __device__ __forceinline__ static bool tail(const GemmOperand& op, int64_t k0) {
+    return KC ? k0 + kBK > op.cols_valid : k0 + kBK > op.rows_valid;
+  }
+  // element offset from origin(k0) with every index clamped
+  __device__ __forceinline__ static int64_t clamped(const GemmOperand& op, int64_t outer0, int64_t k0, int byte) {
+    int r, c;
+    rc(byte, r, c);
     int64_t row, col;
     if constexpr (KC) {
-      row = outer0 + r;
-      col = k0 + 8 * lp;
+      row = min(outer0 + r, op.rows_valid - 1);
+      col = min(k0 + c, op.cols_valid - 8);
+      return (row - outer0) * op.ld + (col - k0);
     } else {
-      row = k0 + r;
-      col = outer0 + 8 * lp;
+      row = min(k0 + r, op.rows_valid - 1);
+      col = min(outer0 + c, op.cols_valid - 8);
+      return (row - k0) * op.ld + (col - outer0);
     }
-    row = row < op.rows_valid ? row : op.rows_valid - 1;
-    col = col <= op.cols_valid - 8 ? col : op.cols_valid - 8;
-    return row * op.ld + col;
   }
 };
 
 template <int R, bool KC>
-__device__ __forceinline__ void dma_tile(const GemmOperand& op, int64_t outer0, int64_t k0, uint32_t lds, int wv,
-                                         int lane) {
+__device__ __forceinline__ void dma_stage(const Loader<R, KC, false>& ld, const GemmOperand& op, int64_t outer0,
+                                          int64_t k0, uint32_t lds, int wv, int lane) {
   using TL = Tile<R, KC>;
-  asm volatile("" : "+v"(lane));     // recompute the cheap per-lane offsets at every issue
+  const char* org = Loader<R, KC, false>::origin(op, outer0, k0);
+  if (!Loader<R, KC, false>::tail(op, k0)) {
 #pragma unroll
-  for (int j = 0; j < TL::PER_WAVE; ++j) {
-    const int kb = wv * TL::PER_WAVE + j;
-    const int64_t off = TL::src(op, outer0, k0, kb * 1024 + 16 * lane);
-    __builtin_amdgcn_global_load_lds((const CL_GAS void*)((const uint16_t*)op.p + off),
-                                     (CL_LDS void*)(uintptr_t)(lds + kb * 1024), 16, 0, 0);
+    for (int j = 0; j < TL::PER_WAVE; ++j)
+      __builtin_amdgcn_global_load_lds((const CL_GAS void*)(org + 2 * (size_t)ld.off[j]),
+                                       (CL_LDS void*)(uintptr_t)(lds + (wv * TL::PER_WAVE + j) * 1024), 16, 0, 0);
+  } else {
+#pragma unroll
+    for (int j = 0; j < TL::PER_WAVE; ++j) {
+      const int kb = wv * TL::PER_WAVE + j;
+      const int64_t o = Loader<R, KC, false>::clamped(op, outer0, k0, kb * 1024 + 16 * lane);
+      __builtin_amdgcn_global_load_lds((const CL_GAS void*)(org + 2 * o), (CL_LDS void*)(uintptr_t)(lds + kb * 1024),
+                                       16, 0, 0);
+    }
   }
 }
 
 template <int R, bool KC>
 struct Fp8Stage {
   uint2 q[Tile<R, KC>::PIECES];
-  __device__ __forceinline__ void load(const GemmOperand& op, int64_t outer0, int64_t k0, int tid) {
+  __device__ __forceinline__ void load(const Loader<R, KC, true>& ld, const GemmOperand& op, int64_t outer0, int64_t k0,
+                                       int tid) {
+    const char* org = Loader<R, KC, true>::origin(op, outer0, k0);
+    if (!Loader<R, KC, true>::tail(op, k0)) {
 #pragma unroll
-    for (int i = 0; i < Tile<R, KC>::PIECES; ++i) {
-      const int64_t off = Tile<R, KC>::src(op, outer0, k0, 16 * (tid + kThreads * i));
-      q[i] = *(const uint2*)((const uint8_t*)op.p + off);
+      for (int i = 0; i < Tile<R, KC>::PIECES; ++i) q[i] = *(const uint2*)(org + ld.off[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < Tile<R, KC>::PIECES; ++i)
+        q[i] = *(const uint2*)(org + Loader<R, KC, true>::clamped(op, outer0, k0, 16 * (tid + kThreads * i)));
     }
   }
   __device__ __forceinline__ void store(uint32_t lds, int tid) const {
@@ -136,8 +200,8 @@ struct Frag {
       const int c0 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
       const int co = 8 * (lane & 1);
       const int rA = 8 * h + rsub, rB = rA + 4;
-      base0 = blk0_off + rA * TL::ROW + co + 16 * (c0 ^ (swz_f(rA) & (TL::NCH - 1)));
-      base1 = blk0_off + rB * TL::ROW + co + 16 * (c0 ^ (swz_f(rB) & (TL::NCH - 1)));
+      base0 = blk0_off + rA * TL::ROW + co + 16 * (c0 ^ (swz_kr(rA) & (TL::NCH - 1)));
+      base1 = blk0_off + rB * TL::ROW + co + 16 * (c0 ^ (swz_kr(rB) & (TL::NCH - 1)));
     }
   }
   // blk: 32-wide block index within the tile's R; kk: 16-k half of the stage
@@ -158,7 +222,28 @@ template <int BN> struct WaveGrid;
 template <> struct WaveGrid<256> { static constexpr int WM = 2, WN = 4; };
 template <> struct WaveGrid<128> { static constexpr int WM = 4, WN = 2; };
 
-__device__ __forceinline__ uint16_t bf16_bits(float x) { return (uint16_t)f32_to_bf16_bits(x); }
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const bf16x2 v = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Output tile of workgroup blockIdx.x (grid padded to a multiple of 8). Returns false for
+// padding workgroups.
+__device__ __forceinline__ bool map_tile(int gm, int gn, int gz, int& tm, int& tn, int& tz) {
+  const int g = blockIdx.x;
+  const int per = (int)(gridDim.x >> 3);
+  const int L = (g & 7) * per + (g >> 3);
+  const int plane = gm * gn;
+  if (L >= plane * gz) return false;
+  tz = L / plane;
+  const int r = L - tz * plane;
+  const int grp = r / (kGroupM * gn);
+  const int rem = r - grp * (kGroupM * gn);
+  const int gsz = min(kGroupM, gm - grp * kGroupM);
+  tn = rem / gsz;
+  tm = grp * kGroupM + (rem - tn * gsz);
+  return true;
+}
 
 template <int BN, bool AKC, bool BKC, bool AF8, bool BF8, int EPI>
 __global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
@@ -171,14 +256,24 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
   constexpr int NPER = (AF8 ? TA::PIECES : TA::PER_WAVE) + (BF8 ? TB::PIECES : TB::PER_WAVE);
   __shared__ __attribute__((aligned(1024))) char ring[kNst * STAGE];
 
+  int tm, tn, tz;
+  if (!map_tile((int)((p.M + kBM - 1) / kBM), (int)((p.N + BN - 1) / BN),
+                (int)((p.K + p.k_per_split - 1) / p.k_per_split), tm, tn, tz))
+    return;
+
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv % WM, wn = wv / WM;
-  const int64_t m0 = (int64_t)blockIdx.x * kBM, n0 = (int64_t)blockIdx.y * BN;
-  const int64_t kz0 = (int64_t)blockIdx.z * p.k_per_split;
+  const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * BN;
+  const int64_t kz0 = (int64_t)tz * p.k_per_split;
   const int64_t klen = min(p.k_per_split, p.K - kz0);
   const int nk = klen > 0 ? (int)(klen / kBK) : 0;
   const uint32_t ring0 = (uint32_t)(uintptr_t)ring;
+
+  Loader<kBM, AKC, AF8> la;
+  Loader<BN, BKC, BF8> lb;
+  la.init(p.a, m0, wv, lane, tid);
+  lb.init(p.b, n0, wv, lane, tid);
 
   Frag<kBM, AKC> fa;
   Frag<BN, BKC> fb;
@@ -199,10 +294,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
   auto issue = [&](int s) {
     const uint32_t so = ring0 + (uint32_t)((s % kNst) * STAGE);
     const int64_t k0 = kz0 + (int64_t)s * kBK;
-    if constexpr (AF8) sa.load(p.a, m0, k0, tid);
-    if constexpr (BF8) sb.load(p.b, n0, k0, tid);
-    if constexpr (!AF8) dma_tile<kBM, AKC>(p.a, m0, k0, so, wv, lane);
-    if constexpr (!BF8) dma_tile<BN, BKC>(p.b, n0, k0, so + TA::BYTES, wv, lane);
+    if constexpr (AF8) sa.load(la, p.a, m0, k0, tid);
+    if constexpr (BF8) sb.load(lb, p.b, n0, k0, tid);
+    if constexpr (!AF8) dma_stage<kBM, AKC>(la, p.a, m0, k0, so, wv, lane);
+    if constexpr (!BF8) dma_stage<BN, BKC>(lb, p.b, n0, k0, so + TA::BYTES, wv, lane);
   };
   auto store_fp8 = [&](int s) {
     const uint32_t so = ring0 + (uint32_t)((s % kNst) * STAGE);
@@ -242,21 +337,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
 
   // ---------------------------------------------------------------- epilogues
   if constexpr (EPI == GEMM_EPI_BCE_P || EPI == GEMM_EPI_BCE_LOSS || EPI == GEMM_EPI_CE_LSE || EPI == GEMM_EPI_CE_P) {
-    const int64_t split = p.part_base + (int64_t)blockIdx.x * WM + wm;
+    constexpr bool WRITES_P = EPI == GEMM_EPI_BCE_P || EPI == GEMM_EPI_CE_P;
+    const int64_t split = p.part_base + (int64_t)tm * WM + wm;
+    const int64_t mw = m0 + wm * TM;          // chunk-relative first item of the wave
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
       const int64_t t = n0 + wn * TN + 32 * nt + l32;
       const bool t_ok = t < p.T;
+      const bool t_st = t < p.p_rows;          // the P buffer has this row
       float wt = 0.0f, lt = 0.0f;
-      if constexpr (EPI == GEMM_EPI_BCE_P || EPI == GEMM_EPI_CE_P) wt = t_ok ? p.w[t] : 0.0f;
+      if constexpr (WRITES_P) wt = t_ok ? p.w[t] : 0.0f;
       if constexpr (EPI == GEMM_EPI_CE_P) lt = t_ok ? p.lse[t] * kLog2e : 0.0f;
+      uint16_t* prow = nullptr;
+      if constexpr (WRITES_P) prow = p.P + (t_st ? t : 0) * p.ldp + mw + 4 * h;
       float relu = 0.0f, prod = 1.0f, lg = 0.0f, mx = kNegInf, sm = 0.0f;
       if constexpr (EPI == GEMM_EPI_CE_LSE) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int64_t v = p.v0 + m0 + wm * TM + 32 * mt + res_row(i, h);
+            const int64_t v = p.v0 + mw + 32 * mt + res_row(i, h);
             mx = (v < p.V && t_ok) ? __builtin_fmaxf(mx, acc[mt][nt][i]) : mx;
           }
       }
@@ -264,31 +364,44 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int64_t ml = m0 + wm * TM + 32 * mt + res_row(i, h);
-          const int64_t v = p.v0 + ml;
-          const bool ok = v < p.V && t_ok;
-          const float x = acc[mt][nt][i];
-          if constexpr (EPI == GEMM_EPI_BCE_P || EPI == GEMM_EPI_BCE_LOSS) {
-            const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * kLog2e);
-            const float q = 1.0f + e;
-            relu += ok ? __builtin_fmaxf(x, 0.0f) : 0.0f;
-            prod *= ok ? q : 1.0f;
-            if constexpr (EPI == GEMM_EPI_BCE_P) {
-              const float r = __builtin_amdgcn_rcpf(q);
-              const float sig = x >= 0.0f ? r : e * r;
-              if (t < p.ldp) p.P[ml * p.ldp + t] = bf16_bits(ok ? wt * sig : 0.0f);
+        for (int j = 0; j < 4; ++j) {
+          float f[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int i = 4 * j + q;
+            const int64_t v = p.v0 + mw + 32 * mt + res_row(i, h);
+            const bool ok = v < p.V && t_ok;
+            const float x = acc[mt][nt][i];
+            f[q] = 0.0f;
+            if constexpr (EPI == GEMM_EPI_BCE_P || EPI == GEMM_EPI_BCE_LOSS) {
+              const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * kLog2e);
+              const float qv = 1.0f + e;
+              relu += ok ? __builtin_fmaxf(x, 0.0f) : 0.0f;
+              prod *= ok ? qv : 1.0f;
+              if constexpr (EPI == GEMM_EPI_BCE_P) {
+                const float r = __builtin_amdgcn_rcpf(qv);
+                const float sig = x >= 0.0f ? r : e * r;
+                f[q] = ok ? wt * sig : 0.0f;
+              }
+            } else if constexpr (EPI == GEMM_EPI_CE_LSE) {
+              sm += ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -mb)) : 0.0f;
+            } else {  // CE_P
+              const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -lt));
+              f[q] = ok && wt != 0.0f ? wt * e : 0.0f;
             }
-            if ((i & 15) == 15) {      // log2 of a product of 16 factors in [1, 2]
-              lg += __builtin_amdgcn_logf(prod);
-              prod = 1.0f;
-            }
-          } else if constexpr (EPI == GEMM_EPI_CE_LSE) {
-            sm += ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -mb)) : 0.0f;
-          } else {  // CE_P
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -lt));
-            if (t < p.ldp) p.P[ml * p.ldp + t] = bf16_bits(ok && wt != 0.0f ? wt * e : 0.0f);
           }
+          if constexpr (WRITES_P) {
+            if (t_st) {
+              uint2 pk;
+              pk.x = pack2(f[0], f[1]);
+              pk.y = pack2(f[2], f[3]);
+              *(uint2*)(prow + 32 * mt + 8 * j) = pk;
+            }
+          }
+        }
+        if constexpr (EPI == GEMM_EPI_BCE_P || EPI == GEMM_EPI_BCE_LOSS) {
+          lg += __builtin_amdgcn_logf(prod);   // log2 of a product of 16 factors in [1, 2]
+          prod = 1.0f;
         }
         __builtin_amdgcn_sched_barrier(0);     // one 32-row slice at a time
       }
@@ -310,7 +423,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
       }
     }
   } else if constexpr (EPI == GEMM_EPI_ACC) {
-    float* out = p.acc + (int64_t)blockIdx.z * p.acc_slice;
+    float* out = p.acc + (int64_t)tz * p.acc_slice;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -325,9 +438,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
           }
         }
       }
-  } else {  // DE / SGD
-    block_sync();                              // the ring is free: reuse it for item indices
-    int* uix = (int*)ring;
+  } else {  // DE / SGD: rows of the tile go through LDS so that each lane owns 16 adjacent d
+    __shared__ int uix[kBM];
+    block_sync();                              // every wave is done with the ring
     for (int k = tid; k < kBM; k += kThreads) {
       const int64_t v = p.v0 + m0 + k;
       const int nu = p.counts[2];
@@ -339,39 +452,98 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
       }
       uix[k] = (lo < nu && (int64_t)p.uitems[lo] == v) ? lo : -1;
     }
-    __syncthreads();
+    constexpr int WREG = kNst * STAGE / 8;     // LDS bytes per wave
+    constexpr int RS = TN * 4 + 16;            // fp32 row stride: 16 B pad spreads the 16-lane reads
+    constexpr int MG = (WREG / (32 * RS)) < MT ? (WREG / (32 * RS)) : MT;
+    constexpr int SEGS = TN / 16;
+    static_assert(MG >= 1 && MT % MG == 0 && TN % 16 == 0, "epilogue staging");
+    char* wbuf = ring + wv * WREG;
+    const uint32_t wb = ring0 + (uint32_t)(wv * WREG);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int g0 = 0; g0 < MT; g0 += MG) {
+      __syncthreads();
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int ml = wm * TM + 32 * mt + res_row(i, h);
+      for (int mq = 0; mq < MG; ++mq)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            *(float*)(wbuf + (32 * mq + res_row(i, h)) * RS + 4 * (32 * nt + l32)) = acc[g0 + mq][nt][i];
+      __syncthreads();
+      for (int s = lane; s < 32 * MG * SEGS; s += 64) {
+        const int row = s / SEGS, seg = s - row * SEGS;
+        const int ml = wm * TM + 32 * g0 + row;
         const int64_t v = p.v0 + m0 + ml;
-        if (v >= p.V) continue;
-        const int u = uix[ml];
+        const int64_t d0 = n0 + wn * TN + 16 * seg;
+        if (v >= p.V || d0 >= p.D) continue;
+        float g[16];
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-          const int64_t d = n0 + wn * TN + 32 * nt + l32;
-          if (d >= p.D) continue;
-          float g = acc[mt][nt][i];
-          if (u >= 0) g -= p.S_u[(int64_t)u * p.D + d];
-          if constexpr (EPI == GEMM_EPI_DE) {
-            ((uint16_t*)p.dE)[v * p.D + d] = bf16_bits(g);
-          } else if (p.e_fp8) {
-            uint8_t* e8 = (uint8_t*)p.E_inplace + v * p.D + d;
-            *e8 = (uint8_t)f32_to_fp8_sat(fp8_to_f32(*e8) - p.lr * g);
-          } else {
-            uint16_t* e16 = (uint16_t*)p.E_inplace + v * p.D + d;
-            *e16 = bf16_bits(bf16_bits_to_f32(*e16) - p.lr * g);
+        for (int q = 0; q < 4; ++q) {
+          typedef float f32x4 __attribute__((ext_vector_type(4)));
+          const f32x4 x = *lds_ptr<f32x4>(wb + (uint32_t)(row * RS + 64 * seg + 16 * q));
+          g[4 * q] = x[0]; g[4 * q + 1] = x[1]; g[4 * q + 2] = x[2]; g[4 * q + 3] = x[3];
+        }
+        const int u = uix[ml];
+        if (u >= 0) {
+          const float4* su = (const float4*)(p.S_u + (int64_t)u * p.D + d0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 x = su[q];
+            g[4 * q] -= x.x; g[4 * q + 1] -= x.y; g[4 * q + 2] -= x.z; g[4 * q + 3] -= x.w;
+          }
+        }
+        if constexpr (EPI == GEMM_EPI_DE) {
+          uint4 o0, o1;
+          o0.x = pack2(g[0], g[1]); o0.y = pack2(g[2], g[3]); o0.z = pack2(g[4], g[5]); o0.w = pack2(g[6], g[7]);
+          o1.x = pack2(g[8], g[9]); o1.y = pack2(g[10], g[11]); o1.z = pack2(g[12], g[13]); o1.w = pack2(g[14], g[15]);
+          uint4* dst = (uint4*)((uint16_t*)p.dE + v * p.D + d0);
+          dst[0] = o0;
+          dst[1] = o1;
+        } else if (p.e_fp8) {
+          uint4* ep = (uint4*)((uint8_t*)p.E_inplace + v * p.D + d0);
+          const uint4 e = *ep;
+          const uint32_t w[4] = {e.x, e.y, e.z, e.w};
+          uint32_t o[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            // two E4M3 values per conversion; the clamp to +-448 keeps the hardware
+            // conversion from turning |x| > 464 into NaN (saturating RNE)
+            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], false);
+            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], true);
+            const float e0 = __builtin_amdgcn_fmed3f(__builtin_fmaf(-p.lr, g[4 * q], lo[0]), -kFp8Max, kFp8Max);
+            const float e1 = __builtin_amdgcn_fmed3f(__builtin_fmaf(-p.lr, g[4 * q + 1], lo[1]), -kFp8Max, kFp8Max);
+            const float e2 = __builtin_amdgcn_fmed3f(__builtin_fmaf(-p.lr, g[4 * q + 2], hi[0]), -kFp8Max, kFp8Max);
+            const float e3 = __builtin_amdgcn_fmed3f(__builtin_fmaf(-p.lr, g[4 * q + 3], hi[1]), -kFp8Max, kFp8Max);
+            int r = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+            r = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, r, true);
+            o[q] = (uint32_t)r;
+          }
+          *ep = uint4{o[0], o[1], o[2], o[3]};
+        } else {
+          uint4* ep = (uint4*)((uint16_t*)p.E_inplace + v * p.D + d0);
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const uint4 e = ep[q];
+            const uint32_t w[4] = {e.x, e.y, e.z, e.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              const float lo = bf16_bits_to_f32(w[b] & 0xffffu) - p.lr * g[8 * q + 2 * b];
+              const float hi = bf16_bits_to_f32(w[b] >> 16) - p.lr * g[8 * q + 2 * b + 1];
+              o[b] = pack2(lo, hi);
+            }
+            ep[q] = uint4{o[0], o[1], o[2], o[3]};
           }
         }
       }
+    }
   }
 }
 
 // The three operand combinations the chunked path uses:
 //   K1: A = E chunk (k-contiguous, bf16 or fp8), B = activations (k-contiguous)
-//   K2: A = P (k-major), B = E chunk (k-major, bf16 or fp8)
-//   K3: A = P (k-contiguous), B = activations (k-major)
+//   K2: A = P (k-contiguous), B = E chunk (k-major, bf16 or fp8)
+//   K3: A = P (k-major), B = activations (k-major)
 template <int BN>
 hipError_t gemm_bn(const GemmParams& p, dim3 grid, hipStream_t st) {
   const bool akc = p.a.kc, bkc = p.b.kc, af8 = p.a.fp8, bf8 = p.b.fp8;
@@ -383,12 +555,12 @@ hipError_t gemm_bn(const GemmParams& p, dim3 grid, hipStream_t st) {
 #undef CL_K1
       default: return hipErrorInvalidValue;
     }
-  } else if (!akc && !bkc && !af8 && p.epi == GEMM_EPI_ACC) {   // K2
-    if (bf8) CL_G(false, false, false, true, GEMM_EPI_ACC);
-    else CL_G(false, false, false, false, GEMM_EPI_ACC);
-  } else if (akc && !bkc && !af8 && !bf8) {    // K3
-    if (p.epi == GEMM_EPI_DE) CL_G(true, false, false, false, GEMM_EPI_DE);
-    else if (p.epi == GEMM_EPI_SGD) CL_G(true, false, false, false, GEMM_EPI_SGD);
+  } else if (akc && !bkc && !af8 && p.epi == GEMM_EPI_ACC) {    // K2
+    if (bf8) CL_G(true, false, false, true, GEMM_EPI_ACC);
+    else CL_G(true, false, false, false, GEMM_EPI_ACC);
+  } else if (!akc && !bkc && !af8 && !bf8) {   // K3
+    if (p.epi == GEMM_EPI_DE) CL_G(false, false, false, false, GEMM_EPI_DE);
+    else if (p.epi == GEMM_EPI_SGD) CL_G(false, false, false, false, GEMM_EPI_SGD);
     else return hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;
@@ -407,8 +579,17 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t st) {
   if (p.M <= 0 || p.N <= 0 || p.K <= 0 || p.K % kBK != 0 || p.k_per_split % kBK != 0 || p.k_per_split <= 0)
     return hipErrorInvalidValue;
   const int bn = gemm_tile_n(p.N);
-  const dim3 grid((unsigned)((p.M + kBM - 1) / kBM), (unsigned)((p.N + bn - 1) / bn),
-                  (unsigned)((p.K + p.k_per_split - 1) / p.k_per_split));
+  const int64_t gm = (p.M + kBM - 1) / kBM, gn = (p.N + bn - 1) / bn, gz = (p.K + p.k_per_split - 1) / p.k_per_split;
+  // every tile's outer origin lies inside its operand (the loaders clamp relative to it);
+  // operands have at least one row and one 8-element group per row
+  const int64_t a_outer = p.a.kc ? p.a.rows_valid : p.a.cols_valid;
+  const int64_t b_outer = p.b.kc ? p.b.rows_valid : p.b.cols_valid;
+  if ((gm - 1) * kBM >= a_outer || (gn - 1) * bn >= b_outer || p.a.rows_valid < 1 || p.b.rows_valid < 1 ||
+      p.a.cols_valid < 8 || p.b.cols_valid < 8)
+    return hipErrorInvalidValue;
+  const int64_t tiles = gm * gn * gz;
+  if (tiles > ((int64_t)1 << 30)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((tiles + 7) / 8 * 8));
   return bn == 128 ? gemm_bn<128>(p, grid, st) : gemm_bn<256>(p, grid, st);
 }
 
