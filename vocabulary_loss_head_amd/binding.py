@@ -4,7 +4,9 @@ Argument marshalling only: every function takes torch tensors that already live 
 the GPU, passes their device pointers and the current HIP stream to the library
 entry point of the same name, and raises ``CutlossError`` on a non-OK status. No
 step of the computation runs here. If the shared library is missing the import of
-this module fails loudly: there is no fallback path.
+this module fails loudly: there is no fallback path. The environment variable
+CUTLOSS_LIBRARY names another build of the same library to load instead (for
+comparing kernel builds).
 """
 from __future__ import annotations
 
@@ -14,7 +16,7 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libcutloss.so")
+LIB_PATH = os.environ.get("CUTLOSS_LIBRARY") or os.path.join(_HERE, "libcutloss.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 BF16, FP8_E4M3 = 0, 1

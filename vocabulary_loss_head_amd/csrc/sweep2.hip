@@ -15,13 +15,17 @@
 //    workgroup and retires the oldest buffer, and the next DMA is issued right after;
 //  * rows past the end of a range are fetched as copies of the last valid row (never
 //    out of bounds) and their logits are set to -inf, which makes every epilogue
-//    (softplus, sigmoid, exp) contribute exactly zero.
+//    (softplus, sigmoid, exp) contribute exactly zero; only the last chunk of a range
+//    can hold such rows, so only that chunk runs the masked epilogue.
 //
-// LDS layout of a chunk: row r, 16-byte piece c stored at piece c ^ f(r) (swz in
-// common.h). A DMA instruction writes 1 KB lane-linearly, so lane i of block kb fetches
-// the logical piece that belongs at physical byte kb*1024 + 16 i. The XOR touches the
-// same address bits as the per-iteration steps of both read patterns, so every read
-// address is one per-lane base XOR a constant, plus the ring offset.
+// LDS layout of a chunk: rows at a stride of ROW + 16 bytes, so row r starts at bank
+// slot r (mod 16) of the 256-byte bank window. A DMA instruction writes 1 KB
+// lane-linearly: lane i of block kb fetches the piece that belongs at byte
+// kb*1024 + 16 i (pad slots fetch a harmless copy), and a chunk takes 4 n + 1 blocks.
+// Reads need no swizzle: a logits read (one 16-byte piece of 16 rows per 16 lanes)
+// hits 16 distinct slots, and a transposed read touches rows 4 apart (4 q + 2 h + b,
+// see pi_row) whose 64-byte windows tile the bank window. Every read address is a
+// per-lane base plus an immediate offset.
 #include "common.h"
 
 #define CL_GAS __attribute__((address_space(1)))
@@ -37,18 +41,22 @@ constexpr float kNegInf = -__builtin_inff();
 template <int D>
 struct Geo {
   static constexpr int NCH = D / 8;             // 16-byte pieces per row
-  static constexpr int ROW = 2 * D;             // bytes per row
-  static constexpr int BYTES = kRC * ROW;       // one chunk
-  static constexpr int KB = BYTES / 1024;       // 1 KB DMA blocks per chunk
-  static constexpr int LPW = KB / 4;            // DMA instructions per wave
-  static_assert(KB % 4 == 0 && LPW >= 1, "unsupported D");
+  static constexpr int ROW = 2 * D;             // bytes of row data
+  static constexpr int ROWP = ROW + 16;         // LDS row stride
+  static constexpr int KBP = (kRC * ROWP + 1023) / 1024;   // DMA blocks per chunk (4 n + 1)
+  static constexpr int BUF = KBP * 1024;        // LDS bytes per ring buffer
+  static constexpr int LPWP = KBP / 4;          // blocks of every wave; wave 0 also takes the last
+  static_assert(KBP % 4 == 1, "padded chunk layout");
 };
 
 // tiles per wave and waves per SIMD for each D
 template <int D> struct Tiling;
 template <> struct Tiling<64> { static constexpr int MT = 2, WPE = 2; };
 template <> struct Tiling<128> { static constexpr int MT = 2, WPE = 1; };
-template <> struct Tiling<256> { static constexpr int MT = 1, WPE = 2; };
+#ifndef CL_T256_WPE
+#define CL_T256_WPE 2
+#endif
+template <> struct Tiling<256> { static constexpr int MT = 1, WPE = CL_T256_WPE; };
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 template <class T>
@@ -69,34 +77,71 @@ __device__ __forceinline__ void block_sync() {
   asm volatile("" ::: "memory");
 }
 
+// Chunk position of streamed row r: the logits read of lane l32 takes LDS row
+// pi_row(l32), so the logit in result register i of half h belongs to LDS row
+// pi_row(res_row(i, h)) = 16 (i >> 3) + 4 (i & 3) + 2 h + ((i >> 2) & 1), and the
+// k-block of the gradient product that a transposed read serves is rows 4 q + 2 h + b.
+__device__ __forceinline__ int pi_row(int r) {
+  return (r & 16) | ((r & 3) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
+}
+
+// Source offsets (bf16 elements from the chunk's first row) of this lane's DMA blocks:
+// blocks wv * LPWP + j, and for wave 0 also the last block. Pad slots and bytes past the
+// chunk fetch element 0. `lim` clamps rows (the last valid row of a short chunk).
+template <int D>
+struct DmaOffsets {
+  int32_t off[Geo<D>::LPWP + 1];
+  __device__ __forceinline__ static int32_t at(int kb, int lane, int lim) {
+    using G = Geo<D>;
+    const int byte = kb * 1024 + 16 * lane;
+    const int r = byte / G::ROWP;
+    const int w = byte - r * G::ROWP;
+    if (r >= kRC || w >= G::ROW) return 0;
+    return min(r, lim) * D + (w >> 4) * 8;
+  }
+  __device__ __forceinline__ static int block(int j, int wv) {
+    return j < Geo<D>::LPWP ? wv * Geo<D>::LPWP + j : Geo<D>::KBP - 1;
+  }
+  __device__ __forceinline__ void init(int wv, int lane) {
+#pragma unroll
+    for (int j = 0; j <= Geo<D>::LPWP; ++j) off[j] = at(block(j, wv), lane, kRC - 1);
+  }
+};
+
 // Fetch rows [row0, row0 + 32) of a row-major bf16 [*, D] matrix into the LDS buffer at
 // byte address `buf`; rows at or past `row_end` (> row0) are fetched as copies of
 // row_end - 1. `wv` is wave-uniform, so each instruction's LDS destination is scalar.
 template <int D>
-__device__ __forceinline__ void dma_chunk(const uint16_t* base, int64_t row0, int64_t row_end, uint32_t buf, int wv,
-                                          int lane) {
+__device__ __forceinline__ void dma_chunk(const DmaOffsets<D>& dof, const uint16_t* base, int64_t row0,
+                                          int64_t row_end, uint32_t buf, int wv, int lane) {
   using G = Geo<D>;
   const char* cbase = (const char*)(base + row0 * D);       // wave-uniform
   const int lim = (int)min((int64_t)(kRC - 1), row_end - 1 - row0);
-  // the per-lane offsets are a few VALU ops: recompute them at every issue instead of
-  // keeping them live across the loop (an opaque copy of the lane id stops hoisting)
-  asm volatile("" : "+v"(lane));
+  const int nb = G::LPWP + (wv == 0 ? 1 : 0);
+  if (lim == kRC - 1) {
 #pragma unroll
-  for (int j = 0; j < G::LPW; ++j) {
-    const int kb = wv * G::LPW + j;
-    const int byte = kb * 1024 + lane * 16;
-    const int r = byte / G::ROW;
-    const int pc = (byte % G::ROW) / 16;
-    const int lc = swz<G::NCH>(pc, r);          // swz is an involution
-    const uint32_t off = (uint32_t)((min(r, lim) * D + lc * 8) * 2);
-    __builtin_amdgcn_global_load_lds((const CL_GAS void*)(cbase + off), (CL_LDS void*)(uintptr_t)(buf + kb * 1024),
-                                     16, 0, 0);
+    for (int j = 0; j <= G::LPWP; ++j) {
+      if (j == G::LPWP && nb == G::LPWP) break;
+      const int kb = DmaOffsets<D>::block(j, wv);
+      __builtin_amdgcn_global_load_lds((const CL_GAS void*)(cbase + 2 * (uint32_t)dof.off[j]),
+                                       (CL_LDS void*)(uintptr_t)(buf + kb * 1024), 16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j <= G::LPWP; ++j) {
+      if (j == G::LPWP && nb == G::LPWP) break;
+      const int kb = DmaOffsets<D>::block(j, wv);
+      const int32_t o = DmaOffsets<D>::at(kb, lane, lim);
+      __builtin_amdgcn_global_load_lds((const CL_GAS void*)(cbase + 2 * (uint32_t)o),
+                                       (CL_LDS void*)(uintptr_t)(buf + kb * 1024), 16, 0, 0);
+    }
   }
 }
 
-// 32 floats [row0, row0 + 32) of v (clamped to n - 1) into LDS at `buf` (lanes 0..31).
+// 32 floats of v for the rows of a chunk (clamped to n - 1) into LDS at `buf`: slot j
+// holds row row0 + pi_row(j), the row whose logits sit where result row j would be.
 __device__ __forceinline__ void dma_vec(const float* v, int64_t row0, int64_t n, uint32_t buf, int lane) {
-  int64_t r = row0 + (lane & 31);
+  int64_t r = row0 + pi_row(lane & 31);
   r = r < n ? r : n - 1;
   if (lane < 32) __builtin_amdgcn_global_load_lds((const CL_GAS void*)(v + r), (CL_LDS void*)(uintptr_t)buf, 4, 0, 0);
 }
@@ -118,39 +163,33 @@ __device__ __forceinline__ void load_stationary(bf16x8 (&sf)[D / 16], const void
 // chunk row held in result register i of a lane with half h
 __device__ __forceinline__ int res_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 
-__device__ __forceinline__ int swz_f(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-
 // Per-lane LDS read bases of a chunk at ring offset 0.
-//  rowb: 16-byte read of logical piece 2ks+h of row l32 = rowb ^ (32 ks)
-//  trA/trB: transposed 8-byte reads of column tile nt, rows 4h+rsub (+8) = tr ^ (64 nt),
-//           plus 16 rows (kk = 1) = + 16 * ROW
+//  rowb: 16-byte read of piece 2 ks + h of LDS row pi_row(l32) = rowb + 32 ks
+//  tr0/tr1: transposed 8-byte reads of column tile nt, LDS rows 4 q + 2 h (+ 1) with
+//           q = (lane & 15) >> 2 = trX + 64 nt, plus 16 rows (kk = 1) = + 16 * ROWP
 template <int D>
 struct ReadBase {
-  uint32_t rowb, trA, trB;
+  uint32_t rowb, tr0, tr1;
   __device__ __forceinline__ void init(uint32_t ring, int lane) {
     using G = Geo<D>;
     const int h = lane >> 5, l32 = lane & 31;
-    const int fm = swz_f(l32) & (G::NCH - 1);
-    rowb = ring + l32 * G::ROW + 16 * ((fm & ~1) | (h ^ (fm & 1)));
-    const int rsub = (lane & 15) >> 2;
-    const int c0 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    const int co = 8 * (lane & 1);
-    const int rA = 4 * h + rsub, rB = rA + 8;
-    trA = ring + rA * G::ROW + co + 16 * (c0 ^ (swz_f(rA) & (G::NCH - 1)));
-    trB = ring + rB * G::ROW + co + 16 * (c0 ^ (swz_f(rB) & (G::NCH - 1)));
+    rowb = ring + pi_row(l32) * G::ROWP + 16 * h;
+    const int q = (lane & 15) >> 2;
+    tr0 = ring + (4 * q + 2 * h) * G::ROWP + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+    tr1 = tr0 + G::ROWP;
   }
 };
 
 template <int D>
 __device__ __forceinline__ bf16x8 read_row_piece(const ReadBase<D>& rb, uint32_t boff, int ks) {
-  return *lds_ptr<bf16x8>((rb.rowb ^ (uint32_t)(32 * ks)) + boff);
+  return *lds_ptr<bf16x8>(rb.rowb + boff + (uint32_t)(32 * ks));
 }
 
 template <int D>
 __device__ __forceinline__ bf16x8 read_col_piece(const ReadBase<D>& rb, uint32_t boff, int nt, int kk) {
-  const uint32_t o = boff + (uint32_t)(kk * 16 * Geo<D>::ROW);
-  const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CL_LDS s16x4*)(uintptr_t)((rb.trA ^ (uint32_t)(64 * nt)) + o));
-  const s16x4 b2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CL_LDS s16x4*)(uintptr_t)((rb.trB ^ (uint32_t)(64 * nt)) + o));
+  const uint32_t o = boff + (uint32_t)(64 * nt + kk * 16 * Geo<D>::ROWP);
+  const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CL_LDS s16x4*)(uintptr_t)(rb.tr0 + o));
+  const s16x4 b2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CL_LDS s16x4*)(uintptr_t)(rb.tr1 + o));
   return cat_bf16(b1, b2);
 }
 
@@ -160,7 +199,7 @@ __device__ __forceinline__ void mask_tail(f32x16 (&y)[MT], int lim, int h) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) y[mt][i] = (res_row(i, h) < lim) ? y[mt][i] : kNegInf;
+    for (int i = 0; i < 16; ++i) y[mt][i] = (pi_row(res_row(i, h)) < lim) ? y[mt][i] : kNegInf;
 }
 
 // ------------------------------------------------------------------------------------
@@ -174,6 +213,7 @@ __device__ __forceinline__ void mask_tail(f32x16 (&y)[MT], int lim, int h) {
 template <int MT, int RM>
 struct Epi {
   float relu[MT], lg[MT], prod[MT];
+  float sx[MT], sa[MT];     // sums of x and |x| over full chunks: relu = (sx + sa) / 2
   float run_m[MT], run_s[MT], mb[MT];
   float lse_s[MT];
   uint32_t vb = 0;          // LDS address of the chunk's per-row vectors (cols kinds)
@@ -181,7 +221,7 @@ struct Epi {
   __device__ __forceinline__ void init() {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      relu[mt] = 0.0f; lg[mt] = 0.0f; prod[mt] = 1.0f;
+      relu[mt] = 0.0f; lg[mt] = 0.0f; prod[mt] = 1.0f; sx[mt] = 0.0f; sa[mt] = 0.0f;
       run_m[mt] = kNegInf; run_s[mt] = 0.0f; mb[mt] = 0.0f; lse_s[mt] = 0.0f;
     }
   }
@@ -206,6 +246,7 @@ struct Epi {
   __device__ __forceinline__ f32x2 row_pair(int i, int h, int which) const {
     return *lds_ptr<f32x2>(vb + 4 * (which * kRC + res_row(i, h)));
   }
+  template <bool TAIL>
   __device__ __forceinline__ void elem2(int mt, int i, int h, float x0, float x1, float& f0, float& f1) {
     if constexpr (RM == 5) {
       const f32x2 w = row_pair(i, h, 0);
@@ -219,15 +260,23 @@ struct Epi {
       f0 = w[0] != 0.0f ? w[0] * e0 : 0.0f;           // ignored rows: exactly 0
       f1 = w[1] != 0.0f ? w[1] * e1 : 0.0f;
     } else {
-      f0 = elem(mt, i, x0);
-      f1 = elem(mt, i + 1, x1);
+      f0 = elem<TAIL>(mt, i, x0);
+      f1 = elem<TAIL>(mt, i + 1, x1);
     }
   }
+  // TAIL: the chunk may hold -inf logits (rows past the range), which the sums of x and
+  // |x| cannot take; other chunks hold finite logits only
+  template <bool TAIL>
   __device__ __forceinline__ float elem(int mt, int i, float x) {
     if constexpr (RM == 0 || RM == 2) {
       const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * kLog2e);   // e^-|x| in [0, 1]
       const float q = 1.0f + e;
-      relu[mt] += __builtin_fmaxf(x, 0.0f);
+      if constexpr (TAIL) {
+        relu[mt] += __builtin_fmaxf(x, 0.0f);
+      } else {
+        sx[mt] += x;
+        sa[mt] += __builtin_fabsf(x);
+      }
       prod[mt] *= q;
       if constexpr (RM == 0) {
         const float r = __builtin_amdgcn_rcpf(q);
@@ -257,17 +306,6 @@ struct Epi {
 };
 
 template <int RM> struct EpiHasF { static constexpr bool value = (RM == 0 || RM == 1 || RM >= 4); };
-
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100;
-#ifndef CL_SCHED_GROUPS
-#define CL_SCHED_GROUPS 1
-#endif
-constexpr bool kUseSchedGroups = CL_SCHED_GROUPS;
-#ifndef CL_PIPE_GRAD
-#define CL_PIPE_GRAD 0
-#endif
-constexpr bool kPipeGrad = CL_PIPE_GRAD;
 
 // packed bf16 operand of the gradient product: pw[mt][kk][j] = bf16 pair (F[8kk+2j], F[8kk+2j+1])
 template <int MT>
@@ -299,49 +337,19 @@ __device__ __forceinline__ void chunk_logits(const bf16x8 (&sf)[MT][D / 16], f32
   }
 }
 
-// Epilogue of the chunk whose logits are y, producing the packed operand `fo`, issued
-// together with the gradient product of the previous chunk (operand `fi`, buffer
-// `boff_prev`) when DO_GRAD.
-template <int D, int MT, int RM, bool DO_GRAD>
-__device__ __forceinline__ void epi_and_grad(f32x16 (&acc)[MT][D / 32], const f32x16 (&y)[MT], Epi<MT, RM>& ep,
-                                             FPack<MT>& fo, const FPack<MT>& fi, const ReadBase<D>& rb,
-                                             uint32_t boff_prev, int h) {
-  constexpr int NT = D / 32;
-  constexpr int NIT = 2 * NT;                   // (nt, kk) pairs
+// Epilogue of the chunk whose logits are y, producing the packed gradient operand fo.
+template <int MT, int RM, bool TAIL>
+__device__ __forceinline__ void epilogue(const f32x16 (&y)[MT], Epi<MT, RM>& ep, FPack<MT>& fo, int h) {
   constexpr int NP = MT * 8;                    // element pairs per chunk
-  constexpr int PPI = (NP + NIT - 1) / NIT;     // pairs per iteration
   constexpr bool HAS_F = EpiHasF<RM>::value;
   ep.begin(y);
-  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    if constexpr (DO_GRAD) {
-      const int nt = it >> 1, kk = it & 1;
-      const bf16x8 b = read_col_piece<D>(rb, boff_prev, nt, kk);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt][nt] = mfma32(fi.op(mt, kk), b, acc[mt][nt]);
-    }
-#pragma unroll
-    for (int j = 0; j < PPI; ++j) {
-      const int e = it * PPI + j;
-      if (e < NP) {
-        const int mt = e / 8, i = 2 * (e % 8);
-        float f0, f1;
-        ep.elem2(mt, i, h, y[mt][i], y[mt][i + 1], f0, f1);
-        if constexpr (HAS_F) fo.pw[mt][i / 8][(i % 8) / 2] = pack_bf16x2(f0, f1);
-      }
-    }
+  for (int e = 0; e < NP; ++e) {
+    const int mt = e / 8, i = 2 * (e % 8);
+    float f0, f1;
+    ep.template elem2<TAIL>(mt, i, h, y[mt][i], y[mt][i + 1], f0, f1);
+    if constexpr (HAS_F) fo.pw[mt][i / 8][(i % 8) / 2] = pack_bf16x2(f0, f1);
   }
-  if constexpr (DO_GRAD && kUseSchedGroups) {
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, MT, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgValu, 10 * PPI, 0);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
   ep.end();
 }
 
@@ -359,50 +367,46 @@ __device__ __forceinline__ void grad_only(f32x16 (&acc)[MT][D / 32], const FPack
 
 // ------------------------------------------------------------------------------------
 // The chunk loop shared by both sweeps. issue(c, boff) enqueues the DMA of chunk c into
-// the buffer at ring offset boff (NPER instructions per wave); prep(c, boff) loads the
-// per-chunk epilogue inputs. Gradient modes overlap the epilogue of chunk c with the
-// gradient of chunk c-1 (buffer c-1 stays live, prefetch distance 2); other modes
-// prefetch 3 chunks ahead.
+// the buffer at ring offset boff (NPER0 instructions on wave 0, NPER on the others);
+// prep(c, boff) points the epilogue at the chunk's per-row inputs. Three chunks are in
+// flight beyond the current one.
 // ------------------------------------------------------------------------------------
-template <int D, int MT, int RM, int NPER, class Issue, class Prep>
+template <int D, int MT, int RM, int NPER0, int NPER, class Issue, class Prep>
 __device__ __forceinline__ void sweep_loop(int nch, int64_t rows_left0, const bf16x8 (&sf)[MT][D / 16],
                                            f32x16 (&acc)[MT][D / 32], Epi<MT, RM>& ep, const ReadBase<D>& rb,
-                                           int h, Issue issue, Prep prep) {
+                                           int h, int wv, Issue issue, Prep prep) {
   using G = Geo<D>;
   constexpr bool HAS_F = EpiHasF<RM>::value;
-  constexpr int AHEAD = (HAS_F && kPipeGrad) ? 2 : 3;   // chunks in flight beyond the current one
+  constexpr int AHEAD = 3;
+  static_assert(2 * NPER0 < 16 && kRing == 4, "vmcnt / ring");
   if (nch <= 0) return;
 #pragma unroll
   for (int k = 0; k < AHEAD; ++k)
-    if (k < nch) issue(k, (uint32_t)(k * G::BYTES));
-  FPack<MT> fprev, fcur;
+    if (k < nch) issue(k, (uint32_t)(k * G::BUF));
+  FPack<MT> f;
   f32x16 y[MT];
   for (int c = 0; c < nch; ++c) {
-    const uint32_t boff = (uint32_t)((c & (kRing - 1)) * G::BYTES);
+    const uint32_t boff = (uint32_t)((c & (kRing - 1)) * G::BUF);
     // chunk c in LDS: own DMAs of later chunks (up to AHEAD - 1) may stay in flight
     const int later = min(nch - 1 - c, AHEAD - 1);
-    if constexpr (AHEAD == 3) {
-      if (later >= 2) wait_vm<2 * NPER>(); else if (later == 1) wait_vm<NPER>(); else wait_vm<0>();
+    if (wv == 0) {
+      if (later >= 2) wait_vm<2 * NPER0>(); else if (later == 1) wait_vm<NPER0>(); else wait_vm<0>();
     } else {
-      if (later >= 1) wait_vm<NPER>(); else wait_vm<0>();
+      if (later >= 2) wait_vm<2 * NPER>(); else if (later == 1) wait_vm<NPER>(); else wait_vm<0>();
     }
     block_sync();
-    if (c + AHEAD < nch) issue(c + AHEAD, (uint32_t)(((c + AHEAD) & (kRing - 1)) * G::BYTES));
+    if (c + AHEAD < nch) issue(c + AHEAD, (uint32_t)(((c + AHEAD) & (kRing - 1)) * G::BUF));
     prep(c, boff);
     chunk_logits<D, MT>(sf, y, rb, boff);
     const int64_t left = rows_left0 - (int64_t)c * kRC;
-    if (left < kRC) mask_tail<MT>(y, (int)left, h);
-    if constexpr (HAS_F && kPipeGrad) {
-      const uint32_t bprev = (uint32_t)(((c - 1) & (kRing - 1)) * G::BYTES);
-      if (c > 0) epi_and_grad<D, MT, RM, true>(acc, y, ep, fcur, fprev, rb, bprev, h);
-      else epi_and_grad<D, MT, RM, false>(acc, y, ep, fcur, fprev, rb, bprev, h);
-      fprev = fcur;
+    if (left < kRC) {
+      mask_tail<MT>(y, (int)left, h);
+      epilogue<MT, RM, true>(y, ep, f, h);
     } else {
-      epi_and_grad<D, MT, RM, false>(acc, y, ep, fcur, fprev, rb, 0, h);
-      if constexpr (HAS_F) grad_only<D, MT>(acc, fcur, rb, boff);
+      epilogue<MT, RM, false>(y, ep, f, h);
     }
+    if constexpr (HAS_F) grad_only<D, MT>(acc, f, rb, boff);
   }
-  if constexpr (HAS_F && kPipeGrad) grad_only<D, MT>(acc, fprev, rb, (uint32_t)(((nch - 1) & (kRing - 1)) * G::BYTES));
 }
 
 // ------------------------------------------------------------------------------------
@@ -424,7 +428,7 @@ __global__ __launch_bounds__(256, Tiling<D>::WPE) void k_rows2(const SweepParams
   constexpr bool HAS_F = EpiHasF<RM>::value;
   constexpr int KS = D / 16, NT = D / 32;
   constexpr int SB = 128 * MT;                  // stationary rows per workgroup
-  __shared__ __attribute__((aligned(1024))) char ring[kRing * G::BYTES];
+  __shared__ __attribute__((aligned(1024))) char ring[kRing * G::BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -462,19 +466,21 @@ __global__ __launch_bounds__(256, Tiling<D>::WPE) void k_rows2(const SweepParams
   }
   ReadBase<D> rb;
   rb.init(ring0, lane);
+  DmaOffsets<D> dof;
+  dof.init(wv, lane);
 
   auto issue = [&](int c, uint32_t boff) {
-    dma_chunk<D>(E, r_begin + (int64_t)c * kRC, r_end, ring0 + boff, wv, lane);
+    dma_chunk<D>(dof, E, r_begin + (int64_t)c * kRC, r_end, ring0 + boff, wv, lane);
   };
   auto prep = [&](int, uint32_t) {};
-  sweep_loop<D, MT, RM, G::LPW>(nch, r_end - r_begin, sf, acc, ep, rb, h, issue, prep);
+  sweep_loop<D, MT, RM, G::LPWP + 1, G::LPWP>(nch, r_end - r_begin, sf, acc, ep, rb, h, wv, issue, prep);
 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int64_t srow = s_wave + 32 * mt + l32;
     const bool s_ok = srow < p.T;
     if constexpr (RM == 0 || RM == 2) {
-      float v = ep.relu[mt] + ep.lg[mt] * kLn2;
+      float v = ep.relu[mt] + 0.5f * (ep.sx[mt] + ep.sa[mt]) + ep.lg[mt] * kLn2;
       v += __shfl_xor(v, 32, 64);
       if (h == 0 && s_ok) p.part_a[(int64_t)split * p.T + srow] = v;
     }
@@ -516,7 +522,7 @@ __global__ __launch_bounds__(256, Tiling<D>::WPE) void k_cols2(const SweepParams
   constexpr int NT = D / 32, KS = D / 16;
   constexpr int NV = KIND == 1 ? 2 : 1;     // per-row vectors streamed with A: w (and lse)
   constexpr int SB = 128 * MT;
-  __shared__ __attribute__((aligned(1024))) char ring[kRing * G::BYTES];
+  __shared__ __attribute__((aligned(1024))) char ring[kRing * G::BUF];
   __shared__ __attribute__((aligned(256))) float vecs[kRing][NV][kRC];
   __shared__ int uix[SB];
 
@@ -542,16 +548,18 @@ __global__ __launch_bounds__(256, Tiling<D>::WPE) void k_cols2(const SweepParams
   ep.init();
   ReadBase<D> rb;
   rb.init(ring0, lane);
+  DmaOffsets<D> dof;
+  dof.init(wv, lane);
 
   auto issue = [&](int c, uint32_t boff) {
     const int64_t r0 = (int64_t)c * kRC;
-    const uint32_t vb = vec0 + (boff / G::BYTES) * (NV * kRC * 4);
-    dma_chunk<D>(A, r0, p.T, ring0 + boff, wv, lane);
+    const uint32_t vb = vec0 + (boff / G::BUF) * (NV * kRC * 4);
+    dma_chunk<D>(dof, A, r0, p.T, ring0 + boff, wv, lane);
     dma_vec(p.w, r0, p.T, vb, lane);
     if constexpr (KIND == 1) dma_vec(p.lse, r0, p.T, vb + kRC * 4, lane);
   };
-  auto prep = [&](int, uint32_t boff) { ep.vb = vec0 + (boff / G::BYTES) * (NV * kRC * 4); };
-  sweep_loop<D, MT, RM, G::LPW + NV>(nch, p.T, sf, acc, ep, rb, h, issue, prep);
+  auto prep = [&](int, uint32_t boff) { ep.vb = vec0 + (boff / G::BUF) * (NV * kRC * 4); };
+  sweep_loop<D, MT, RM, G::LPWP + 1 + NV, G::LPWP + NV>(nch, p.T, sf, acc, ep, rb, h, wv, issue, prep);
 
   // sparse positive term: index of each item of the block in the sorted unique-item list
   for (int k = tid; k < SB; k += 256) {
