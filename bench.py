@@ -13,10 +13,18 @@ workload.
 cutloss_bce_bwd with loss; softmax CE cutloss_ce_fwd + cutloss_ce_bwd; the FP8 XMC head
 cutloss_bce_bwd_sgd with loss). --all prints one JSON line per configuration with the
 forward-only and fused-step timings (a report, not the benchmark contract line).
+
+roofline.traffic is the HBM byte count per launch of the dominant kernel measured with
+rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, each scaled by the factor a plain copy of
+known size reads on the same counter), stored in profiles/ with the SHA-256 of the
+kernel sources it was taken on; it is null when those sources have changed since.
+--copy-calibration BYTES runs only that plain copy (torch's device copy kernel), for the
+counter runs.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +40,41 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "fused fwd+bwd BCE head TFLOP/s & rows/s at V=876,939; % of bf16 MFMA peak"
 ALL = ["tiny_bce", "seqrec_bce", "seqrec_bce_large", "llm_ce", "xmc_sgd"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "seqrec_bce_sweeps_hbm_traffic.json")
+SWEEP_SOURCES = ["vocabulary_loss_head_amd/csrc/sweep2.hip", "vocabulary_loss_head_amd/csrc/common.h"]
+
+
+def sweep_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for rel in SWEEP_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the stored counter summary, or None when it is
+    missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_sha256") != sweep_sources_sha256():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(nbytes: int, reps: int = 5) -> None:
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": 4 * n, "reps": reps}), flush=True)
 
 
 def _cpu_threads() -> int:
@@ -210,9 +253,10 @@ def record(name, steps, warmup, with_cpu):
     if name == "seqrec_bce":
         dom_flops = 4.0 * T * V * D
         achieved = dom_flops / (phases[dom][0] / phases[dom][1] * 1e-3) / 1e12
-        rec["roofline"] = {"kernel": f"k_{dom.split('_')[0]}2 (fused {dom.replace('_', ' ')})", "bound": "mfma",
+        kname = f"k_{dom.split('_')[0]}2"
+        rec["roofline"] = {"kernel": f"{kname} (fused {dom.replace('_', ' ')})", "bound": "mfma",
                            "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                           "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(kname)}
     if w.lr > 0:
         # fused SGD step: E is read and written once at the least
         rec["e_traffic_GBps"] = round(2 * e_bytes(w) / (ms * 1e-3) / 1e9, 1)
@@ -244,7 +288,12 @@ def main():
     ap.add_argument("--workload", default="seqrec_bce", choices=ALL)
     ap.add_argument("--all", action="store_true", help="one report line per configuration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the vocabulary-parallel design is described in DESIGN.md)", file=sys.stderr)

@@ -72,26 +72,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
 
-// LDS row swizzle of the sweeps: the 16-byte piece c of row r is stored at piece
-// c ^ f(r), f(r) = 4 (r & 3) + 2 ((r >> 2) & 1) + ((r >> 3) & 1), a bijection on the 16
-// rows of a group. The 16 lanes of a ds_read_b128 that read one piece of 16 consecutive
-// rows hit 16 distinct 16-byte bank slots. A transposed read covers rows q..q+3 (one half
-// wave) and q+4..q+7 (the other) at 64 logical bytes each: the r & 3 term sends the four
-// rows of a half wave to distinct 64-byte groups of the 256-byte bank window, and the
-// (r >> 2) term puts the two halves on alternate 32-byte groups, so any 16- or 32-lane
-// subset of the instruction reads distinct banks.
-__device__ __forceinline__ int swz_row(int r) {
-#if defined(CL_SWZ_OLD) && CL_SWZ_OLD
-  return ((r & 7) << 1) | ((r >> 3) & 1);
-#else
-  return ((r & 3) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
-#endif
-}
-template <int NCHUNK>
-__device__ __forceinline__ int swz(int c, int r) {
-  return c ^ (swz_row(r) & (NCHUNK - 1));
-}
-
 __device__ __forceinline__ float wave_sum(float v) {
   // fixed butterfly order: deterministic
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

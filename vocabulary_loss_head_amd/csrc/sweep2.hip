@@ -56,7 +56,10 @@ template <> struct Tiling<128> { static constexpr int MT = 2, WPE = 1; };
 #ifndef CL_T256_WPE
 #define CL_T256_WPE 2
 #endif
-template <> struct Tiling<256> { static constexpr int MT = 1, WPE = CL_T256_WPE; };
+#ifndef CL_T256_MT
+#define CL_T256_MT 1
+#endif
+template <> struct Tiling<256> { static constexpr int MT = CL_T256_MT, WPE = CL_T256_WPE; };
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 template <class T>
