@@ -156,6 +156,15 @@ class Head:
         self.ws = B.workspace(nb, dev)
         self.ws_bytes = int(nb)
 
+    def fwd_metrics(self):
+        """BCE forward with the Cut Metrics counts (a separately measured option)."""
+        import torch
+        B = self.B
+        if getattr(self, "mws", None) is None:
+            self.mws = B.workspace(B.cutloss_bce_workspace_size(self.prob, B.OP_FWD_METRICS), self.A.device)
+            self.counts = torch.empty(self.w.T, 4, dtype=torch.int32, device=self.A.device)
+        B.cutloss_bce_fwd_metrics(self.prob, self.loss, self.counts, self.mws)
+
     def fwd(self):
         B = self.B
         if self.w.kind == "ce":
@@ -275,6 +284,9 @@ def report_all(steps, warmup):
         rec["fwd_tflops"] = round(2.0 * w.T * w.V * w.D / (fwd_ms * 1e-3) / 1e12, 2)
         rec["fwd_pct_bf16_peak"] = round(100.0 * rec["fwd_tflops"] / PEAK_BF16_TFLOPS, 2)
         rec["fwd_e_read_GBps"] = round(e_bytes(w) / (fwd_ms * 1e-3) / 1e9, 1)
+        if w.kind == "bce":
+            m_ms, _ = time_calls(h.fwd_metrics, steps, warmup)
+            rec["fwd_cut_metrics_ms"] = round(m_ms, 4)
         print(json.dumps(rec), flush=True)
         del h
         torch.cuda.empty_cache()

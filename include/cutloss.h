@@ -72,7 +72,8 @@ typedef enum {
 typedef enum {
   CUTLOSS_OP_FWD = 0,
   CUTLOSS_OP_BWD = 1,
-  CUTLOSS_OP_BWD_SGD = 2
+  CUTLOSS_OP_BWD_SGD = 2,
+  CUTLOSS_OP_FWD_METRICS = 3
 } cutloss_op;
 
 /*
@@ -115,6 +116,20 @@ size_t cutloss_ce_workspace_size(const cutloss_ce_problem* p, int32_t op);
  */
 cutloss_status cutloss_bce_fwd(const cutloss_bce_problem* p, float* loss,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * BCE forward with Cut Metrics (Cut Binary Cross Entropy, paperpeel, §III-D): besides
+ * loss (as cutloss_bce_fwd), counts[t] = (TP, FP, FN, TN) for row t, the confusion
+ * counts over the V items of the predictions sigmoid(x_tv) > 0.5, i.e. x_tv > 0, against
+ * the canonical positive set P_t. Computed in the same pass as the loss; no logits are
+ * stored. Masked rows give (0, 0, 0, 0). counts: int32 [T][4], device, 16-byte aligned.
+ * A logit within fp32 rounding of 0 may be decided either way, and a positive's decision
+ * may differ between the dense count and the indexed dot product (FP is kept >= 0).
+ * Requires V < 2^24 (CUTLOSS_ERR_UNSUPPORTED otherwise).
+ * Workspace: cutloss_bce_workspace_size(p, CUTLOSS_OP_FWD_METRICS).
+ */
+cutloss_status cutloss_bce_fwd_metrics(const cutloss_bce_problem* p, float* loss, int32_t* counts,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * BCE backward: with G = w (sigmoid(X) - Y), w_t = dloss_t * mask_t,

@@ -20,7 +20,7 @@ LIB_PATH = os.environ.get("CUTLOSS_LIBRARY") or os.path.join(_HERE, "libcutloss.
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 BF16, FP8_E4M3 = 0, 1
-OP_FWD, OP_BWD, OP_BWD_SGD = 0, 1, 2
+OP_FWD, OP_BWD, OP_BWD_SGD, OP_FWD_METRICS = 0, 1, 2, 3
 
 
 class CutlossError(RuntimeError):
@@ -48,7 +48,7 @@ class CeProblem(ctypes.Structure):
 
 EXPORTED = [
     "cutloss_bce_workspace_size", "cutloss_ce_workspace_size",
-    "cutloss_bce_fwd", "cutloss_bce_bwd", "cutloss_bce_bwd_sgd",
+    "cutloss_bce_fwd", "cutloss_bce_fwd_metrics", "cutloss_bce_bwd", "cutloss_bce_bwd_sgd",
     "cutloss_ce_fwd", "cutloss_ce_bwd",
     "cutloss_read_data_errors", "cutloss_bce_canonical_targets",
     "cutloss_profile_enable", "cutloss_profile_read",
@@ -71,6 +71,7 @@ def _load() -> ctypes.CDLL:
         "cutloss_bce_workspace_size": (sz, [pb, ctypes.c_int32]),
         "cutloss_ce_workspace_size": (sz, [pc, ctypes.c_int32]),
         "cutloss_bce_fwd": (st, [pb, P, P, sz, P]),
+        "cutloss_bce_fwd_metrics": (st, [pb, P, P, P, sz, P]),
         "cutloss_bce_bwd": (st, [pb, P, P, P, P, P, sz, P]),
         "cutloss_bce_bwd_sgd": (st, [pb, P, ctypes.c_float, P, P, P, sz, P]),
         "cutloss_ce_fwd": (st, [pc, P, P, P, sz, P]),
@@ -161,6 +162,12 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 
 def cutloss_bce_fwd(problem: BceProblem, loss, ws: torch.Tensor, stream=None) -> None:
     _check(_lib.cutloss_bce_fwd(ctypes.byref(problem), _ptr(loss), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def cutloss_bce_fwd_metrics(problem: BceProblem, loss, counts, ws: torch.Tensor, stream=None) -> None:
+    """loss [T] fp32 and counts [T, 4] int32 = (TP, FP, FN, TN) per row."""
+    _check(_lib.cutloss_bce_fwd_metrics(ctypes.byref(problem), _ptr(loss), _ptr(counts), _ptr(ws), ws.numel(),
+                                        _stream(stream)))
 
 
 def cutloss_bce_bwd(problem: BceProblem, dloss, dA, dE, loss_out, ws: torch.Tensor, stream=None) -> None:

@@ -232,6 +232,7 @@ struct Ws2 {
   float* part_dA;
   float* pos_dot;
   float* pos_sum;
+  int32_t* pos_tp;
   float* S_u;
   float* S_part;
   float* red;         // staging of the split reductions
@@ -271,6 +272,7 @@ Ws2 carve_chunked(void* base, const ChunkPlan& pl, bool need_P, bool need_dA, bo
   w.part_dA = need_dA ? c.take<float>((size_t)pl.sk * T * pl.D) : nullptr;
   w.pos_dot = need_pos ? c.take<float>(T) : nullptr;
   w.pos_sum = need_pos && need_dA ? c.take<float>((size_t)T * pl.D) : nullptr;
+  w.pos_tp = need_pos ? c.take<int32_t>(T) : nullptr;
   w.S_u = need_Su ? c.take<float>((size_t)cap * pl.D) : nullptr;
   w.S_part = need_Su ? c.take<float>(2 * cl::item_sum_parts(cap) * pl.D) : nullptr;
   const size_t red_loss = cl::reduce_splits_tmp_floats(pl.n_splits, T, two_partials ? 1 : 0);
@@ -337,18 +339,19 @@ cutloss_status check_out(const void* ptr, size_t align, const char* name, bool r
 // BCE pipeline shared by fwd / bwd / bwd_sgd.
 // want_loss: emit loss; want_dA; dE_mode: 0 none, 1 write dE, 2 SGD in place
 cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss, float* loss, void* dA, void* dE,
-                               int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st);
+                               int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st, int32_t* counts);
 cutloss_status ce_run_chunked(const cutloss_ce_problem* p, const float* lse_in, const float* dloss, float* loss,
                               float* lse, void* dA, void* dE, void* ws, size_t ws_bytes, hipStream_t st);
 
+// counts != NULL (forward only): Cut Metrics in the same pass as the loss
 cutloss_status bce_run(const cutloss_bce_problem* p, const float* dloss, float* loss, void* dA, void* dE,
-                       int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st) {
+                       int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st, int32_t* counts = nullptr) {
   if (use_chunked(p->D, p->e_dtype == CUTLOSS_FP8_E4M3))
-    return bce_run_chunked(p, dloss, loss, dA, dE, dE_mode, lr, ws, ws_bytes, st);
+    return bce_run_chunked(p, dloss, loss, dA, dE, dE_mode, lr, ws, ws_bytes, st, counts);
   const Plan pl = make_plan(p->T, p->D, p->V, p->nnz, p->e_dtype == CUTLOSS_FP8_E4M3);
   const bool rows_grad = dA != nullptr;
   const bool need_Su = dE_mode != 0;
-  const Ws w = carve(ws, pl, rows_grad, need_Su, false);
+  const Ws w = carve(ws, pl, rows_grad, need_Su, counts != nullptr);
   CL_TRY(check_ws(ws, ws_bytes, w.bytes));
   const int e_fp8 = p->e_dtype == CUTLOSS_FP8_E4M3;
 
@@ -364,16 +367,17 @@ cutloss_status bce_run(const cutloss_bce_problem* p, const float* dloss, float* 
   fp.crow = w.tw.crow; fp.cids = w.tw.cids; fp.dloss = dloss; fp.mask = p->row_mask;
   fp.n_splits = pl.n_splits; fp.n_splits_dA = pl.n_splits; fp.part_a = w.part_a; fp.part_dA = w.part_dA;
   fp.loss = loss; fp.dA = dA; fp.w_out = w.w;
+  fp.part_c = w.part_b; fp.counts = counts;
 
   cl::SweepParams sp{};
   sp.T = p->T; sp.D = p->D; sp.V = p->V; sp.A = p->A; sp.E = p->E; sp.e_fp8 = e_fp8;
   sp.n_splits = pl.n_splits; sp.split_len = pl.split_len;
-  sp.part_a = w.part_a; sp.part_dA = w.part_dA;
+  sp.part_a = w.part_a; sp.part_b = w.part_b; sp.part_dA = w.part_dA;
   sp.w = w.w; sp.uitems = w.tw.uitems; sp.counts = w.tw.counts; sp.S_u = w.S_u;
   sp.dE = dE_mode == 1 ? dE : nullptr; sp.E_inplace = dE_mode == 2 ? (void*)p->E : nullptr; sp.lr = lr;
 
   if (p->T > 0 && (loss != nullptr || rows_grad)) {
-    const int mode = rows_grad ? (loss ? 2 : 1) : 0;
+    const int mode = rows_grad ? (loss ? 2 : 1) : (counts ? 5 : 0);
     {
       Phase ph(CUTLOSS_PHASE_ROWS, st);
       CL_HIP(rows_sweep(sp, mode, st), "rows sweep");
@@ -516,10 +520,10 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
 }
 
 cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss, float* loss, void* dA, void* dE,
-                               int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st) {
+                               int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st, int32_t* counts) {
   const ChunkPlan pl = make_chunk_plan(p->T, p->D, p->V, p->nnz);
   const bool grad = dA != nullptr || dE_mode != 0;
-  const Ws2 w = carve_chunked(ws, pl, grad, dA != nullptr, dE_mode != 0, false, true);
+  const Ws2 w = carve_chunked(ws, pl, grad, dA != nullptr, dE_mode != 0, counts != nullptr, true);
   CL_TRY(check_ws(ws, ws_bytes, w.bytes));
   const int e_fp8 = p->e_dtype == CUTLOSS_FP8_E4M3;
   {
@@ -535,6 +539,7 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
   fp.n_splits = (int)pl.n_splits; fp.n_splits_dA = (int)pl.sk; fp.dA_weighted = 1;
   fp.part_a = w.part_a; fp.part_dA = w.part_dA; fp.loss = loss; fp.dA = dA; fp.w_out = w.w;
   fp.pos_dot = w.pos_dot; fp.pos_sum = w.pos_sum;
+  fp.part_c = w.part_b; fp.counts = counts; fp.pos_tp = counts ? w.pos_tp : nullptr;
   {
     Phase ph(CUTLOSS_PHASE_ITEM_SUMS, st);
     CL_HIP(cl::launch_row_weights(fp, 0, st), "row weights");
@@ -546,8 +551,8 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
   }
   ChunkJob j{};
   j.pl = &pl; j.A = p->A; j.E = p->E; j.e_fp8 = e_fp8;
-  j.k1_epi = grad ? cl::GEMM_EPI_BCE_P : cl::GEMM_EPI_BCE_LOSS;
-  j.w = w.w; j.P = w.P; j.part_a = w.part_a; j.part_dA = w.part_dA;
+  j.k1_epi = grad ? cl::GEMM_EPI_BCE_P : (counts ? cl::GEMM_EPI_BCE_METRICS : cl::GEMM_EPI_BCE_LOSS);
+  j.w = w.w; j.P = w.P; j.part_a = w.part_a; j.part_b = w.part_b; j.part_dA = w.part_dA;
   j.k3_epi = dE_mode == 0 ? -1 : (dE_mode == 1 ? cl::GEMM_EPI_DE : cl::GEMM_EPI_SGD);
   j.uitems = w.tw.uitems; j.counts = w.tw.counts; j.S_u = w.S_u; j.dE = dE; j.lr = lr;
   CL_TRY(run_chunks(j, st));
@@ -555,6 +560,8 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
     Phase ph(CUTLOSS_PHASE_FINALIZE, st);
     if (loss != nullptr) {
       CL_HIP(cl::launch_reduce_splits(w.part_a, nullptr, pl.n_splits, p->T, w.red, 0, st), "loss partials");
+      if (counts != nullptr)
+        CL_HIP(cl::launch_reduce_splits(w.part_b, nullptr, pl.n_splits, p->T, w.red, 0, st), "count partials");
       fp.n_splits = 1;
     }
     if (dA != nullptr) {
@@ -627,13 +634,14 @@ extern "C" {
 
 size_t cutloss_bce_workspace_size(const cutloss_bce_problem* p, int32_t op) {
   if (check_bce(p) != CUTLOSS_OK) return 0;
-  const bool bwd = op != CUTLOSS_OP_FWD;
+  const bool metrics = op == CUTLOSS_OP_FWD_METRICS;
+  const bool bwd = op != CUTLOSS_OP_FWD && !metrics;
   if (use_chunked(p->D, p->e_dtype == CUTLOSS_FP8_E4M3)) {
     const ChunkPlan cp = make_chunk_plan(p->T, p->D, p->V, p->nnz);
-    return carve_chunked(nullptr, cp, bwd, bwd, bwd, false, true).bytes;
+    return carve_chunked(nullptr, cp, bwd, bwd, bwd, metrics, true).bytes;
   }
   const Plan pl = make_plan(p->T, p->D, p->V, p->nnz, p->e_dtype == CUTLOSS_FP8_E4M3);
-  return carve(nullptr, pl, bwd, bwd, false).bytes;
+  return carve(nullptr, pl, bwd, bwd, metrics).bytes;
 }
 
 size_t cutloss_ce_workspace_size(const cutloss_ce_problem* p, int32_t op) {
@@ -652,6 +660,16 @@ cutloss_status cutloss_bce_fwd(const cutloss_bce_problem* p, float* loss, void* 
   CL_TRY(check_bce(p));
   CL_TRY(check_out(loss, 4, "loss", p->T > 0));
   return bce_run(p, nullptr, loss, nullptr, nullptr, 0, 0.0f, ws, ws_bytes, (hipStream_t)stream);
+}
+
+cutloss_status cutloss_bce_fwd_metrics(const cutloss_bce_problem* p, float* loss, int32_t* counts, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  CL_TRY(check_bce(p));
+  CL_TRY(check_out(loss, 4, "loss", p->T > 0));
+  CL_TRY(check_out(counts, 16, "counts", p->T > 0));
+  if (p->V >= (int64_t)1 << 24) return fail(CUTLOSS_ERR_UNSUPPORTED, "Cut Metrics need V < 2^24 (V = %lld)", (long long)p->V);
+  return bce_run(p, nullptr, loss, nullptr, nullptr, 0, 0.0f, ws, ws_bytes, (hipStream_t)stream, counts);
 }
 
 cutloss_status cutloss_bce_bwd(const cutloss_bce_problem* p, const float* dloss, void* dA, void* dE, float* loss_out,

@@ -165,7 +165,8 @@ enum {
   GEMM_EPI_CE_P = 3,      // P = w exp(x - lse)
   GEMM_EPI_ACC = 4,       // C (+)= acc into fp32 [M][N] (split-K slice per blockIdx.z)
   GEMM_EPI_DE = 5,        // dE rows of the chunk: acc - S_u, bf16
-  GEMM_EPI_SGD = 6        // E <- round(E - lr (acc - S_u)) in place
+  GEMM_EPI_SGD = 6,       // E <- round(E - lr (acc - S_u)) in place
+  GEMM_EPI_BCE_METRICS = 7  // softplus partials + counts of logits > 0 (as floats) in part_b
 };
 
 struct GemmParams {
@@ -209,6 +210,10 @@ struct FinalizeParams {
   // positive-row terms computed before E changes (chunked path): if set, finalize reads
   // them instead of E: pos_dot[t] = sum_p A_t . E_p, pos_sum[t][d] = sum_p E_p[d]
   float* pos_dot; float* pos_sum;
+  // Cut Metrics: per-split counts of logits > 0 (floats, exact below 2^24) in part_c, the
+  // per-row positives with a positive logit (pos_tp, from k_row_positives when set), and
+  // the output counts[T][4] = (TP, FP, FN, TN)
+  const float* part_c; int32_t* pos_tp; int32_t* counts;
 };
 hipError_t launch_row_positives(const FinalizeParams& p, hipStream_t st);
 // kind: 0 = BCE, 1 = CE

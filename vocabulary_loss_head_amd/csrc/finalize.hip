@@ -49,23 +49,53 @@ __global__ __launch_bounds__(256) void k_finalize_rows(const FinalizeParams p, i
   const int32_t pb = p.crow[t], pe = p.crow[t + 1];
 
   if (want_loss) {
-    // positive logits x_tp = A_t . E_p (indexed dot products), summed in positive order
+    // positive logits x_tp = A_t . E_p (indexed dot products), summed in positive order;
+    // tp counts the positives with x_tp > 0 (Cut Metrics)
     float sum_x = 0.0f;
-    if (p.pos_dot != nullptr) sum_x = p.pos_dot[t];
-    else for (int32_t e = pb; e < pe; ++e) {
-      const int64_t v = p.cids[e];
-      float part = 0.0f;
-      for (int k = 0; k < nd; ++k) {
-        const int64_t d = lane + 64 * k;
-        part += bf16_bits_to_f32(A[t * D + d]) * load_e(p.E, p.e_fp8, v * D + d);
+    int tp = 0;
+    if (p.pos_dot != nullptr) {
+      sum_x = p.pos_dot[t];
+      if (p.pos_tp != nullptr) tp = p.pos_tp[t];
+    } else {
+      for (int32_t e = pb; e < pe; ++e) {
+        const int64_t v = p.cids[e];
+        float part = 0.0f;
+        for (int k = 0; k < nd; ++k) {
+          const int64_t d = lane + 64 * k;
+          part += bf16_bits_to_f32(A[t * D + d]) * load_e(p.E, p.e_fp8, v * D + d);
+        }
+        const float x = wave_sum(part);
+        sum_x += x;
+        tp += x > 0.0f ? 1 : 0;
       }
-      sum_x += wave_sum(part);
     }
     if (kind == 0) {
       float part = 0.0f;
       for (int j = lane; j < p.n_splits; j += 64) part += p.part_a[(int64_t)j * p.T + t];
       const float dense = wave_sum(part);
       if (lane == 0) p.loss[t] = valid ? dense - sum_x : 0.0f;
+      if (p.counts != nullptr) {
+        // confusion counts of the predictions x > 0 against the positive set; the dense
+        // count sums integer-valued partials (exact in fp32 below 2^24)
+        float c = 0.0f;
+        for (int j = lane; j < p.n_splits; j += 64) c += p.part_c[(int64_t)j * p.T + t];
+        const int64_t npos = (int64_t)(pe - pb);
+        const int64_t pos_pred = (int64_t)wave_sum(c);
+        if (lane == 0) {
+          int32_t* o = p.counts + 4 * t;
+          if (!valid) {
+            o[0] = o[1] = o[2] = o[3] = 0;
+          } else {
+            // a positive whose logit sits within rounding of 0 can be decided differently
+            // by the dense pass and the indexed dot product: keep FP >= 0
+            const int64_t fp = pos_pred > tp ? pos_pred - tp : 0;
+            o[0] = tp;
+            o[1] = (int32_t)fp;
+            o[2] = (int32_t)(npos - tp);
+            o[3] = (int32_t)(p.V - npos - fp);
+          }
+        }
+      }
     } else {
       float m = -__builtin_inff();
       for (int j = lane; j < p.n_splits; j += 64) m = __builtin_fmaxf(m, p.part_a[(int64_t)j * p.T + t]);
@@ -114,6 +144,7 @@ __global__ __launch_bounds__(256) void k_row_positives(const FinalizeParams p) {
   const uint16_t* A = (const uint16_t*)p.A;
   const int32_t pb = p.crow[t], pe = p.crow[t + 1];
   float sum_x = 0.0f;
+  int tp = 0;
   for (int32_t e = pb; e < pe; ++e) {
     const int64_t v = p.cids[e];
     float part = 0.0f;
@@ -121,9 +152,12 @@ __global__ __launch_bounds__(256) void k_row_positives(const FinalizeParams p) {
       const int64_t d = lane + 64 * k;
       part += bf16_bits_to_f32(A[t * D + d]) * load_e(p.E, p.e_fp8, v * D + d);
     }
-    sum_x += wave_sum(part);
+    const float x = wave_sum(part);
+    sum_x += x;
+    tp += x > 0.0f ? 1 : 0;
   }
   if (lane == 0) p.pos_dot[t] = sum_x;
+  if (lane == 0 && p.pos_tp != nullptr) p.pos_tp[t] = tp;
   if (p.pos_sum == nullptr) return;          // no dA requested
   for (int k = 0; k < nd; ++k) {
     const int64_t d = lane + 64 * k;

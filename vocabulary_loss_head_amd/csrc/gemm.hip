@@ -336,7 +336,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
   }
 
   // ---------------------------------------------------------------- epilogues
-  if constexpr (EPI == GEMM_EPI_BCE_P || EPI == GEMM_EPI_BCE_LOSS || EPI == GEMM_EPI_CE_LSE || EPI == GEMM_EPI_CE_P) {
+  if constexpr (EPI == GEMM_EPI_BCE_P || EPI == GEMM_EPI_BCE_LOSS || EPI == GEMM_EPI_CE_LSE || EPI == GEMM_EPI_CE_P ||
+                EPI == GEMM_EPI_BCE_METRICS) {
+    constexpr bool BCE_SUM = EPI == GEMM_EPI_BCE_P || EPI == GEMM_EPI_BCE_LOSS || EPI == GEMM_EPI_BCE_METRICS;
     constexpr bool WRITES_P = EPI == GEMM_EPI_BCE_P || EPI == GEMM_EPI_CE_P;
     const int64_t split = p.part_base + (int64_t)tm * WM + wm;
     const int64_t mw = m0 + wm * TM;          // chunk-relative first item of the wave
@@ -350,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
       if constexpr (EPI == GEMM_EPI_CE_P) lt = t_ok ? p.lse[t] * kLog2e : 0.0f;
       uint16_t* prow = nullptr;
       if constexpr (WRITES_P) prow = p.P + (t_st ? t : 0) * p.ldp + mw + 4 * h;
-      float relu = 0.0f, prod = 1.0f, lg = 0.0f, mx = kNegInf, sm = 0.0f;
+      float relu = 0.0f, prod = 1.0f, lg = 0.0f, mx = kNegInf, sm = 0.0f, cnt = 0.0f;
       if constexpr (EPI == GEMM_EPI_CE_LSE) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -373,7 +375,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
             const bool ok = v < p.V && t_ok;
             const float x = acc[mt][nt][i];
             f[q] = 0.0f;
-            if constexpr (EPI == GEMM_EPI_BCE_P || EPI == GEMM_EPI_BCE_LOSS) {
+            if constexpr (EPI == GEMM_EPI_BCE_METRICS) cnt += (ok && x > 0.0f) ? 1.0f : 0.0f;
+            if constexpr (BCE_SUM) {
               const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * kLog2e);
               const float qv = 1.0f + e;
               relu += ok ? __builtin_fmaxf(x, 0.0f) : 0.0f;
@@ -399,16 +402,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
             }
           }
         }
-        if constexpr (EPI == GEMM_EPI_BCE_P || EPI == GEMM_EPI_BCE_LOSS) {
+        if constexpr (BCE_SUM) {
           lg += __builtin_amdgcn_logf(prod);   // log2 of a product of 16 factors in [1, 2]
           prod = 1.0f;
         }
         __builtin_amdgcn_sched_barrier(0);     // one 32-row slice at a time
       }
-      if constexpr (EPI == GEMM_EPI_BCE_P || EPI == GEMM_EPI_BCE_LOSS) {
+      if constexpr (BCE_SUM) {
         float vsum = relu + lg * kLn2;
         vsum += __shfl_xor(vsum, 32, 64);
         if (h == 0 && t_ok) p.part_a[split * p.T + t] = vsum;
+      }
+      if constexpr (EPI == GEMM_EPI_BCE_METRICS) {
+        cnt += __shfl_xor(cnt, 32, 64);
+        if (h == 0 && t_ok) p.part_b[split * p.T + t] = cnt;
       }
       if constexpr (EPI == GEMM_EPI_CE_LSE) {
         const float m2 = __shfl_xor(mx, 32, 64);
@@ -552,6 +559,7 @@ hipError_t gemm_bn(const GemmParams& p, dim3 grid, hipStream_t st) {
     switch (p.epi) {
 #define CL_K1(E) case E: if (af8) CL_G(true, true, true, false, E); else CL_G(true, true, false, false, E); break;
       CL_K1(GEMM_EPI_BCE_P) CL_K1(GEMM_EPI_BCE_LOSS) CL_K1(GEMM_EPI_CE_LSE) CL_K1(GEMM_EPI_CE_P)
+      CL_K1(GEMM_EPI_BCE_METRICS)
 #undef CL_K1
       default: return hipErrorInvalidValue;
     }

@@ -211,12 +211,13 @@ __device__ __forceinline__ void mask_tail(f32x16 (&y)[MT], int lim, int h) {
 //   RM 0: BCE softplus sum + sigmoid (F)      RM 1: sigmoid only
 //   RM 2: BCE softplus sum only                RM 3: CE running (max, sum)
 //   RM 4: exp(x - lse_row) (CE rows gradient)  RM 5: w_r * sigmoid(x) (BCE cols)
-//   RM 6: w_r * exp(x - lse_r) (CE cols)
+//   RM 6: w_r * exp(x - lse_r) (CE cols)       RM 7: RM 2 + count of logits > 0
 // ------------------------------------------------------------------------------------
 template <int MT, int RM>
 struct Epi {
   float relu[MT], lg[MT], prod[MT];
   float sx[MT], sa[MT];     // sums of x and |x| over full chunks: relu = (sx + sa) / 2
+  float cnt[MT];            // RM 7: logits > 0 (exact in fp32 below 2^24)
   float run_m[MT], run_s[MT], mb[MT];
   float lse_s[MT];
   uint32_t vb = 0;          // LDS address of the chunk's per-row vectors (cols kinds)
@@ -224,7 +225,7 @@ struct Epi {
   __device__ __forceinline__ void init() {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      relu[mt] = 0.0f; lg[mt] = 0.0f; prod[mt] = 1.0f; sx[mt] = 0.0f; sa[mt] = 0.0f;
+      relu[mt] = 0.0f; lg[mt] = 0.0f; prod[mt] = 1.0f; sx[mt] = 0.0f; sa[mt] = 0.0f; cnt[mt] = 0.0f;
       run_m[mt] = kNegInf; run_s[mt] = 0.0f; mb[mt] = 0.0f; lse_s[mt] = 0.0f;
     }
   }
@@ -271,7 +272,8 @@ struct Epi {
   // |x| cannot take; other chunks hold finite logits only
   template <bool TAIL>
   __device__ __forceinline__ float elem(int mt, int i, float x) {
-    if constexpr (RM == 0 || RM == 2) {
+    if constexpr (RM == 7) cnt[mt] += x > 0.0f ? 1.0f : 0.0f;
+    if constexpr (RM == 0 || RM == 2 || RM == 7) {
       const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * kLog2e);   // e^-|x| in [0, 1]
       const float q = 1.0f + e;
       if constexpr (TAIL) {
@@ -298,7 +300,7 @@ struct Epi {
     return 0.0f;    // RM 5, 6 go through elem2
   }
   __device__ __forceinline__ void end() {
-    if constexpr (RM == 0 || RM == 2) {
+    if constexpr (RM == 0 || RM == 2 || RM == 7) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         lg[mt] += __builtin_amdgcn_logf(prod[mt]);   // log2 of a product of 16 factors in [1, 2]
@@ -308,7 +310,7 @@ struct Epi {
   }
 };
 
-template <int RM> struct EpiHasF { static constexpr bool value = (RM == 0 || RM == 1 || RM >= 4); };
+template <int RM> struct EpiHasF { static constexpr bool value = (RM == 0 || RM == 1 || (RM >= 4 && RM <= 6)); };
 
 // packed bf16 operand of the gradient product: pw[mt][kk][j] = bf16 pair (F[8kk+2j], F[8kk+2j+1])
 template <int MT>
@@ -414,7 +416,8 @@ __device__ __forceinline__ void sweep_loop(int nch, int64_t rows_left0, const bf
 
 // ------------------------------------------------------------------------------------
 // rows sweep. MODE: 0 BCE loss partials, 1 BCE dA partials, 2 BCE dA + loss partials,
-// 3 CE (max, sum) partials, 4 CE dA partials.
+// 3 CE (max, sum) partials, 4 CE dA partials, 5 BCE loss partials + counts of logits > 0
+// (the dense part of the Cut Metrics, Cut Binary Cross Entropy §III-D).
 // ------------------------------------------------------------------------------------
 template <int MODE> struct RowsRM;
 template <> struct RowsRM<0> { static constexpr int RM = 2; };
@@ -422,6 +425,7 @@ template <> struct RowsRM<1> { static constexpr int RM = 1; };
 template <> struct RowsRM<2> { static constexpr int RM = 0; };
 template <> struct RowsRM<3> { static constexpr int RM = 3; };
 template <> struct RowsRM<4> { static constexpr int RM = 4; };
+template <> struct RowsRM<5> { static constexpr int RM = 7; };
 
 template <int D, int MODE>
 __global__ __launch_bounds__(256, Tiling<D>::WPE) void k_rows2(const SweepParams p) {
@@ -482,10 +486,15 @@ __global__ __launch_bounds__(256, Tiling<D>::WPE) void k_rows2(const SweepParams
   for (int mt = 0; mt < MT; ++mt) {
     const int64_t srow = s_wave + 32 * mt + l32;
     const bool s_ok = srow < p.T;
-    if constexpr (RM == 0 || RM == 2) {
+    if constexpr (RM == 0 || RM == 2 || RM == 7) {
       float v = ep.relu[mt] + 0.5f * (ep.sx[mt] + ep.sa[mt]) + ep.lg[mt] * kLn2;
       v += __shfl_xor(v, 32, 64);
       if (h == 0 && s_ok) p.part_a[(int64_t)split * p.T + srow] = v;
+    }
+    if constexpr (RM == 7) {
+      float c = ep.cnt[mt];
+      c += __shfl_xor(c, 32, 64);
+      if (h == 0 && s_ok) p.part_b[(int64_t)split * p.T + srow] = c;
     }
     if constexpr (RM == 3) {
       const float m1 = ep.run_m[mt], s1 = ep.run_s[mt];
@@ -615,6 +624,7 @@ hipError_t rows2_d(const SweepParams& p, int mode, hipStream_t st) {
     case 2: k_rows2<D, 2><<<grid, block, 0, st>>>(p); break;
     case 3: k_rows2<D, 3><<<grid, block, 0, st>>>(p); break;
     case 4: k_rows2<D, 4><<<grid, block, 0, st>>>(p); break;
+    case 5: k_rows2<D, 5><<<grid, block, 0, st>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
