@@ -185,8 +185,9 @@ int64_t ceil_div(int64_t x, int64_t a) { return (x + a - 1) / a; }
 
 struct ChunkPlan {
   int64_t T, D, V, cap;
-  int64_t Tp;         // rows padded to 128: rows of the P buffer P[t][item]
-  int64_t Vc;         // items per chunk (multiple of the item tile): row stride of P
+  int64_t Tp;         // rows of the P buffer P[t][item], a multiple of bt
+  int64_t bt;         // P row-block height: 128 for T <= 128, else 256 (blocks of bt x 32)
+  int64_t Vc;         // items per chunk (multiple of the item tile)
   int64_t n_chunks;
   int64_t n_splits;   // loss / lse partials: item tiles x waves along the item dimension
   int64_t sk;         // split-K slices of the dA product
@@ -199,7 +200,8 @@ ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap) {
   ChunkPlan c{};
   c.T = T; c.D = D; c.V = V; c.cap = cap;
   const int64_t bm = cl::gemm_tile_m();
-  c.Tp = round_up(T > 0 ? T : 1, 128);
+  c.bt = round_up(T > 0 ? T : 1, 128) <= 128 ? 128 : 256;
+  c.Tp = round_up(T > 0 ? T : 1, c.bt);
   int64_t vc = kChunkPBytes / (c.Tp * 2) / bm * bm;
   // CUTLOSS_MAX_CHUNK_ITEMS caps the chunk (rounded down to the item tile): a tuning knob,
   // and the way tests exercise several chunks on small problems
@@ -282,9 +284,11 @@ Ws2 carve_chunked(void* base, const ChunkPlan& pl, bool need_P, bool need_dA, bo
   return w;
 }
 
-cl::GemmOperand operand(const void* p, int64_t ld, int64_t rows_valid, int64_t cols_valid, int kc, int fp8) {
+cl::GemmOperand operand(const void* p, int64_t ld, int64_t rows_valid, int64_t cols_valid, int kc, int fp8,
+                        int bt = 0, int64_t nvb = 0) {
   cl::GemmOperand o;
   o.p = p; o.ld = ld; o.rows_valid = rows_valid; o.cols_valid = cols_valid; o.kc = kc; o.fp8 = fp8;
+  o.bt = bt; o.nvb = nvb;
   return o;
 }
 
@@ -487,7 +491,7 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
       g.M = mc; g.N = pl.Tp; g.K = pl.D; g.k_per_split = pl.D;
       g.epi = j.k1_epi;
       g.v0 = v0; g.V = pl.V; g.T = pl.T; g.D = pl.D;
-      g.w = j.w; g.lse = j.lse; g.P = j.P; g.ldp = pl.Vc; g.p_rows = pl.Tp;
+      g.w = j.w; g.lse = j.lse; g.P = j.P; g.p_bt = (int)pl.bt; g.p_nvb = pl.Vc / 32; g.p_rows = pl.Tp;
       g.part_a = j.part_a; g.part_b = j.part_b;
       g.part_base = (v0 / bm) * cl::gemm_warps_m(pl.Tp);
       CL_HIP(cl::launch_gemm(g, st), "chunk logits");
@@ -495,7 +499,7 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
     if (j.part_dA != nullptr) {
       Phase ph(CUTLOSS_PHASE_CHUNK_DA, st);
       cl::GemmParams g{};
-      g.a = operand(j.P, pl.Vc, pl.Tp, mc, 1, 0);
+      g.a = operand(j.P, 0, pl.Tp, mc, 1, 0, (int)pl.bt, pl.Vc / 32);
       g.b = operand(Ec, pl.D, vlen, pl.D, 0, j.e_fp8);
       g.M = pl.T; g.N = pl.D; g.K = mc; g.k_per_split = pl.kps;
       g.epi = cl::GEMM_EPI_ACC;
@@ -506,7 +510,7 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
     if (j.k3_epi >= 0) {
       Phase ph(CUTLOSS_PHASE_CHUNK_DE, st);
       cl::GemmParams g{};
-      g.a = operand(j.P, pl.Vc, pl.Tp, mc, 0, 0);
+      g.a = operand(j.P, 0, pl.Tp, mc, 0, 0, (int)pl.bt, pl.Vc / 32);
       g.b = operand(j.A, pl.D, pl.T, pl.D, 0, 0);
       g.M = mc; g.N = pl.D; g.K = pl.Tp; g.k_per_split = pl.Tp;
       g.epi = j.k3_epi;

@@ -156,6 +156,11 @@ struct GemmOperand {
   int64_t ld, rows_valid, cols_valid;
   int kc;      // 1: [M or N][K]; 0: [K][M or N]
   int fp8;     // OCP E4M3FN storage (widened to bf16 when staged)
+  // bt > 0: blocked bf16 storage of the chunk's gradient tile P[t][v] (t = the stored row
+  // index, v = the column): element (t, v) at ((t / bt) * nvb + v / 32) * bt * 32
+  // + (t % bt) * 32 + v % 32, i.e. bt x 32 blocks, contiguous, ld unused
+  int bt;
+  int64_t nvb;
 };
 
 enum {
@@ -178,8 +183,9 @@ struct GemmParams {
   int64_t v0, V, T;
   const float* w;           // [T] row weights
   const float* lse;         // [T] CE logsumexp
-  uint16_t* P;              // [p_rows][ldp] bf16 gradient tile of the chunk: P[t][item]
-  int64_t ldp, p_rows;
+  uint16_t* P;              // bf16 gradient tile of the chunk P[t][item], blocked as for a
+  int p_bt;                 // GemmOperand with bt = p_bt, nvb = p_nvb; rows t < p_rows
+  int64_t p_nvb, p_rows;
   float* part_a; float* part_b;  // [n_splits][T] row partials
   int64_t part_base;        // split index of this chunk's first item tile
   // ACC epilogue

@@ -107,7 +107,18 @@ struct Loader {
     for (int j = 0; j < N; ++j) {
       int r, c;
       rc(byte_of(j, wv, lane, tid), r, c);
-      if constexpr (KC) {
+      if (op.bt > 0) {
+        // blocked P: the stage's k range is one 32-column block; KC: rows t of the tile
+        // (clamped), KR: columns v of the tile, rows k0 + r inside one row block
+        const int64_t bsz = (int64_t)op.bt * 32;
+        if constexpr (KC) {
+          const int64_t t = min(outer0 + r, op.rows_valid - 1);
+          off[j] = (uint32_t)((t / op.bt) * op.nvb * bsz + (t % op.bt) * 32 + c);
+        } else {
+          const int64_t v = outer0 + c;
+          off[j] = (uint32_t)((v >> 5) * bsz + r * 32 + (v & 31));
+        }
+      } else if constexpr (KC) {
         const int64_t row = min(outer0 + r, op.rows_valid - 1) - outer0;
         off[j] = (uint32_t)(row * op.ld + c);
       } else {
@@ -117,9 +128,15 @@ struct Loader {
     }
   }
   __device__ __forceinline__ static const char* origin(const GemmOperand& op, int64_t outer0, int64_t k0) {
+    if (op.bt > 0) {
+      if constexpr (KC) return (const char*)op.p + k0 * op.bt * ESZ;          // column block k0 / 32
+      else return (const char*)op.p + ((k0 / op.bt) * op.nvb * op.bt * 32 + (k0 % op.bt) * 32) * ESZ;
+    }
     return (const char*)op.p + (KC ? outer0 * op.ld + k0 : k0 * op.ld + outer0) * ESZ;
   }
+  // blocked operands are fully valid over the k range (checked by the launcher)
   __device__ __forceinline__ static bool tail(const GemmOperand& op, int64_t k0) {
+    if (op.bt > 0) return false;
     return KC ? k0 + kBK > op.cols_valid : k0 + kBK > op.rows_valid;
   }
   // element offset from origin(k0) with every index clamped
@@ -350,8 +367,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
       float wt = 0.0f, lt = 0.0f;
       if constexpr (WRITES_P) wt = t_ok ? p.w[t] : 0.0f;
       if constexpr (EPI == GEMM_EPI_CE_P) lt = t_ok ? p.lse[t] * kLog2e : 0.0f;
+      // blocked P: row t, columns mw + 32 mt + 8 j + 4 h + 0..3 = 8 contiguous bytes
       uint16_t* prow = nullptr;
-      if constexpr (WRITES_P) prow = p.P + (t_st ? t : 0) * p.ldp + mw + 4 * h;
+      const int64_t pbs = (int64_t)p.p_bt * 32;
+      if constexpr (WRITES_P) {
+        const int64_t ts = t_st ? t : 0;
+        prow = p.P + ((ts / p.p_bt) * p.p_nvb + (mw >> 5)) * pbs + (ts % p.p_bt) * 32 + 4 * h;
+      }
       float relu = 0.0f, prod = 1.0f, lg = 0.0f, mx = kNegInf, sm = 0.0f, cnt = 0.0f;
       if constexpr (EPI == GEMM_EPI_CE_LSE) {
 #pragma unroll
@@ -398,7 +420,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
               uint2 pk;
               pk.x = pack2(f[0], f[1]);
               pk.y = pack2(f[2], f[3]);
-              *(uint2*)(prow + 32 * mt + 8 * j) = pk;
+              *(uint2*)(prow + mt * pbs + 8 * j) = pk;
             }
           }
         }
@@ -595,6 +617,16 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t st) {
   if ((gm - 1) * kBM >= a_outer || (gn - 1) * bn >= b_outer || p.a.rows_valid < 1 || p.b.rows_valid < 1 ||
       p.a.cols_valid < 8 || p.b.cols_valid < 8)
     return hipErrorInvalidValue;
+  // blocked operands (bf16 only): bt a multiple of 32 (a k stage of 32 stored rows stays in
+  // one row block), the whole k range valid, and every column of a tile stored
+  for (const GemmOperand* op : {&p.a, &p.b}) {
+    if (op->bt <= 0) continue;
+    const int64_t tile = op == &p.a ? kBM : bn;
+    const int64_t outer_tiles = op == &p.a ? gm : gn;
+    if (op->fp8 || op->bt % 32 != 0 || (op->kc ? p.K > op->cols_valid : p.K > op->rows_valid) ||
+        (!op->kc && outer_tiles * tile > op->cols_valid))
+      return hipErrorInvalidValue;
+  }
   const int64_t tiles = gm * gn * gz;
   if (tiles > ((int64_t)1 << 30)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((tiles + 7) / 8 * 8));
