@@ -41,7 +41,7 @@
  *  - Paths: heads with D in {64, 128, 256} and bf16 E run fused logit-tile sweeps that
  *    never write a logit; every other head (any D that is a multiple of 64, or FP8 E)
  *    runs a chunked path that keeps one vocabulary chunk's bf16 gradient tile
- *    (T x Vc, at most 1 GiB by default) in the workspace. The environment variable
+ *    (T x Vc, at most 2 GiB by default) in the workspace. The environment variable
  *    CUTLOSS_MAX_CHUNK_ITEMS caps Vc (read when a call or size query plans the work,
  *    so set it before both).
  */

@@ -194,7 +194,7 @@ struct ChunkPlan {
   int64_t kps;        // items per slice
 };
 
-constexpr int64_t kChunkPBytes = 1ll << 30;     // P buffer budget
+constexpr int64_t kChunkPBytes = 2ll << 30;     // P buffer budget
 
 ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap) {
   ChunkPlan c{};
@@ -213,9 +213,9 @@ ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap) {
   if (vc > round_up(V, bm)) vc = round_up(V, bm);
   c.Vc = vc;
   c.n_chunks = ceil_div(V, vc);
-  c.n_splits = ceil_div(V, bm) * cl::gemm_warps_m(c.Tp);
+  c.n_splits = ceil_div(V, bm) * cl::gemm_k1_warps_m(T, D);
   // dA product: (row tiles) x (D tiles) x slices, about 1024 workgroups
-  const int64_t tiles = ceil_div(T > 0 ? T : 1, bm) * ceil_div(D, cl::gemm_tile_n(D));
+  const int64_t tiles = ceil_div(T > 0 ? T : 1, bm) * ceil_div(D, cl::gemm_tile_n_of(cl::GEMM_EPI_ACC, T, D, D));
   int64_t sk = ceil_div(1024, tiles);
   if (sk > vc / 32) sk = vc / 32;
   if (sk < 1) sk = 1;
@@ -488,12 +488,13 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
       cl::GemmParams g{};
       g.a = operand(Ec, pl.D, vlen, pl.D, 1, j.e_fp8);
       g.b = operand(j.A, pl.D, pl.T, pl.D, 1, 0);
-      g.M = mc; g.N = pl.Tp; g.K = pl.D; g.k_per_split = pl.D;
+      // columns t < T (tiles past T would start outside A); P rows T .. tile end are written as 0
+      g.M = mc; g.N = pl.T; g.K = pl.D; g.k_per_split = pl.D;
       g.epi = j.k1_epi;
       g.v0 = v0; g.V = pl.V; g.T = pl.T; g.D = pl.D;
       g.w = j.w; g.lse = j.lse; g.P = j.P; g.p_bt = (int)pl.bt; g.p_nvb = pl.Vc / 32; g.p_rows = pl.Tp;
       g.part_a = j.part_a; g.part_b = j.part_b;
-      g.part_base = (v0 / bm) * cl::gemm_warps_m(pl.Tp);
+      g.part_base = (v0 / bm) * cl::gemm_k1_warps_m(pl.T, pl.D);
       CL_HIP(cl::launch_gemm(g, st), "chunk logits");
     }
     if (j.part_dA != nullptr) {
@@ -512,7 +513,8 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
       cl::GemmParams g{};
       g.a = operand(j.P, 0, pl.Tp, mc, 0, 0, (int)pl.bt, pl.Vc / 32);
       g.b = operand(j.A, pl.D, pl.T, pl.D, 0, 0);
-      g.M = mc; g.N = pl.D; g.K = pl.Tp; g.k_per_split = pl.Tp;
+      // k = t over the rows the logits product wrote (T rounded up to the k stage)
+      g.M = mc; g.N = pl.D; g.K = round_up(pl.T, 32); g.k_per_split = g.K;
       g.epi = j.k3_epi;
       g.v0 = v0; g.V = pl.V; g.T = pl.T; g.D = pl.D;
       g.uitems = j.uitems; g.counts = j.counts; g.S_u = j.S_u;

@@ -197,8 +197,9 @@ struct GemmParams {
 };
 hipError_t launch_gemm(const GemmParams& p, hipStream_t st);
 int gemm_tile_m();                     // 256
-int gemm_tile_n(int64_t N);            // 128 or 256
-int gemm_warps_m(int64_t N);           // waves along M (row partials per item tile)
+int gemm_tile_n_of(int epi, int64_t M, int64_t N, int64_t D);   // 128 or 256 for that product
+// waves along M of the logits product (row partials per item tile) for T rows, head D
+int gemm_k1_warps_m(int64_t T, int64_t D);
 
 struct FinalizeParams {
   int64_t T, D, V;

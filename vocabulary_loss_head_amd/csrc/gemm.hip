@@ -34,9 +34,14 @@ namespace cl {
 namespace {
 
 constexpr int kBK = 32;
-constexpr int kNst = 4;
+// Two workgroup shapes: NW = 8 waves with a 4-deep ring (one workgroup per CU), and NW = 4
+// waves with 256 x 128 tiles and a 3-deep ring (72 KB of LDS, two workgroups per CU, so one
+// can run its MFMAs while the other is in its epilogue).
+template <int NW> struct Cfg {
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int NST = NW == 4 ? 3 : 4;
+};
 constexpr int kBM = 256;
-constexpr int kThreads = 512;
 constexpr int kGroupM = 8;
 constexpr float kNegInf = -__builtin_inff();
 
@@ -52,10 +57,11 @@ __device__ __forceinline__ int swz_kr(int r) { return ((r & 3) << 2) | (((r >> 3
 template <class T>
 __device__ __forceinline__ const CL_LDS T* lds_ptr(uint32_t a) { return (const CL_LDS T*)(uintptr_t)a; }
 
+// s_waitcnt vmcnt(N): gfx9 encoding, vmcnt[3:0] at bits 3:0 and vmcnt[5:4] at 15:14
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 16, "vmcnt");
-  __builtin_amdgcn_s_waitcnt(0xF70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0xF70 | (N & 15) | ((N >> 4) << 14));
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
@@ -68,14 +74,14 @@ __device__ __forceinline__ void block_sync() {
 }
 
 // One stage of one operand: R rows (KC) or R columns (KR) by 32 k, bf16 in LDS.
-template <int R, bool KC>
+template <int NW, int R, bool KC>
 struct Tile {
   static constexpr int BYTES = 64 * R;
   static constexpr int KB = BYTES / 1024;
-  static constexpr int PER_WAVE = KB / 8;             // DMA blocks per wave
+  static constexpr int PER_WAVE = KB / NW;            // DMA blocks per wave
   static constexpr int ROW = KC ? 64 : 2 * R;         // bytes per LDS row
   static constexpr int NCH = ROW / 16;
-  static constexpr int PIECES = BYTES / 16 / kThreads;  // staged pieces per thread
+  static constexpr int PIECES = BYTES / 16 / (64 * NW);  // staged pieces per thread
   static_assert(PER_WAVE >= 1 && PIECES >= 1, "tile");
   __device__ __forceinline__ static int phys(int lp, int r) {   // an involution in lp
     if constexpr (KC) return lp ^ ((r >> 2) & 3);
@@ -88,15 +94,15 @@ struct Tile {
 // address of element (outer0, k0) (KC) or (k0, outer0) (KR). Offsets clamp the outer
 // index into the valid range once; a stage that reaches past the valid k range (only the
 // last stages of some products) recomputes them with the k clamp as well.
-template <int R, bool KC, bool F8>
+template <int NW, int R, bool KC, bool F8>
 struct Loader {
-  using TL = Tile<R, KC>;
+  using TL = Tile<NW, R, KC>;
   static constexpr int N = F8 ? TL::PIECES : TL::PER_WAVE;
   static constexpr int ESZ = F8 ? 1 : 2;
   uint32_t off[N];
 
   __device__ __forceinline__ static int byte_of(int j, int wv, int lane, int tid) {
-    return F8 ? 16 * (tid + kThreads * j) : (wv * TL::PER_WAVE + j) * 1024 + 16 * lane;
+    return F8 ? 16 * (tid + 64 * NW * j) : (wv * TL::PER_WAVE + j) * 1024 + 16 * lane;
   }
   __device__ __forceinline__ static void rc(int byte, int& r, int& c) {
     r = byte / TL::ROW;
@@ -156,12 +162,13 @@ struct Loader {
   }
 };
 
-template <int R, bool KC>
-__device__ __forceinline__ void dma_stage(const Loader<R, KC, false>& ld, const GemmOperand& op, int64_t outer0,
+template <int NW, int R, bool KC>
+__device__ __forceinline__ void dma_stage(const Loader<NW, R, KC, false>& ld, const GemmOperand& op, int64_t outer0,
                                           int64_t k0, uint32_t lds, int wv, int lane) {
-  using TL = Tile<R, KC>;
-  const char* org = Loader<R, KC, false>::origin(op, outer0, k0);
-  if (!Loader<R, KC, false>::tail(op, k0)) {
+  using TL = Tile<NW, R, KC>;
+  using LD = Loader<NW, R, KC, false>;
+  const char* org = LD::origin(op, outer0, k0);
+  if (!LD::tail(op, k0)) {
 #pragma unroll
     for (int j = 0; j < TL::PER_WAVE; ++j)
       __builtin_amdgcn_global_load_lds((const CL_GAS void*)(org + 2 * (size_t)ld.off[j]),
@@ -170,42 +177,43 @@ __device__ __forceinline__ void dma_stage(const Loader<R, KC, false>& ld, const 
 #pragma unroll
     for (int j = 0; j < TL::PER_WAVE; ++j) {
       const int kb = wv * TL::PER_WAVE + j;
-      const int64_t o = Loader<R, KC, false>::clamped(op, outer0, k0, kb * 1024 + 16 * lane);
+      const int64_t o = LD::clamped(op, outer0, k0, kb * 1024 + 16 * lane);
       __builtin_amdgcn_global_load_lds((const CL_GAS void*)(org + 2 * o), (CL_LDS void*)(uintptr_t)(lds + kb * 1024),
                                        16, 0, 0);
     }
   }
 }
 
-template <int R, bool KC>
+template <int NW, int R, bool KC>
 struct Fp8Stage {
-  uint2 q[Tile<R, KC>::PIECES];
-  __device__ __forceinline__ void load(const Loader<R, KC, true>& ld, const GemmOperand& op, int64_t outer0, int64_t k0,
-                                       int tid) {
-    const char* org = Loader<R, KC, true>::origin(op, outer0, k0);
-    if (!Loader<R, KC, true>::tail(op, k0)) {
+  using TL = Tile<NW, R, KC>;
+  using LD = Loader<NW, R, KC, true>;
+  uint2 q[TL::PIECES];
+  __device__ __forceinline__ void load(const LD& ld, const GemmOperand& op, int64_t outer0, int64_t k0, int tid) {
+    const char* org = LD::origin(op, outer0, k0);
+    if (!LD::tail(op, k0)) {
 #pragma unroll
-      for (int i = 0; i < Tile<R, KC>::PIECES; ++i) q[i] = *(const uint2*)(org + ld.off[i]);
+      for (int i = 0; i < TL::PIECES; ++i) q[i] = *(const uint2*)(org + ld.off[i]);
     } else {
 #pragma unroll
-      for (int i = 0; i < Tile<R, KC>::PIECES; ++i)
-        q[i] = *(const uint2*)(org + Loader<R, KC, true>::clamped(op, outer0, k0, 16 * (tid + kThreads * i)));
+      for (int i = 0; i < TL::PIECES; ++i)
+        q[i] = *(const uint2*)(org + LD::clamped(op, outer0, k0, 16 * (tid + 64 * NW * i)));
     }
   }
   __device__ __forceinline__ void store(uint32_t lds, int tid) const {
 #pragma unroll
-    for (int i = 0; i < Tile<R, KC>::PIECES; ++i)
-      *(CL_LDS bf16x8*)(uintptr_t)(lds + 16 * (tid + kThreads * i)) = fp8x8_to_bf16x8(q[i]);
+    for (int i = 0; i < TL::PIECES; ++i)
+      *(CL_LDS bf16x8*)(uintptr_t)(lds + 16 * (tid + 64 * NW * i)) = fp8x8_to_bf16x8(q[i]);
   }
 };
 
 // MFMA operand fragments of a stage tile: lane (l32, h) gets index l32 of the 32-wide
 // block `blk` and k = 16 kk + 8 h + 0..7.
-template <int R, bool KC>
+template <int NW, int R, bool KC>
 struct Frag {
   uint32_t base0, base1;   // KC: row-read base; KR: transposed-read bases (k rows +0..3, +4..7)
   __device__ __forceinline__ void init(uint32_t blk0_off, int lane) {
-    using TL = Tile<R, KC>;
+    using TL = Tile<NW, R, KC>;
     const int h = lane >> 5, l32 = lane & 31;
     if constexpr (KC) {
       const int r = l32;                         // + 32 blk: does not change (r >> 2) & 3
@@ -223,7 +231,7 @@ struct Frag {
   }
   // blk: 32-wide block index within the tile's R; kk: 16-k half of the stage
   __device__ __forceinline__ bf16x8 read(uint32_t stage_off, int blk, int kk) const {
-    using TL = Tile<R, KC>;
+    using TL = Tile<NW, R, KC>;
     if constexpr (KC) {
       return *lds_ptr<bf16x8>(((base0 ^ (uint32_t)(32 * kk)) + (uint32_t)(blk * 32 * TL::ROW)) + stage_off);
     } else {
@@ -235,9 +243,10 @@ struct Frag {
   }
 };
 
-template <int BN> struct WaveGrid;
-template <> struct WaveGrid<256> { static constexpr int WM = 2, WN = 4; };
-template <> struct WaveGrid<128> { static constexpr int WM = 4, WN = 2; };
+template <int NW, int BN> struct WaveGrid;
+template <> struct WaveGrid<8, 256> { static constexpr int WM = 2, WN = 4; };
+template <> struct WaveGrid<8, 128> { static constexpr int WM = 4, WN = 2; };
+template <> struct WaveGrid<4, 128> { static constexpr int WM = 2, WN = 2; };
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   const bf16x2 v = __builtin_convertvector(f32x2{a, b}, bf16x2);
@@ -262,11 +271,12 @@ __device__ __forceinline__ bool map_tile(int gm, int gn, int gz, int& tm, int& t
   return true;
 }
 
-template <int BN, bool AKC, bool BKC, bool AF8, bool BF8, int EPI>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
-  using TA = Tile<kBM, AKC>;
-  using TB = Tile<BN, BKC>;
-  constexpr int WM = WaveGrid<BN>::WM, WN = WaveGrid<BN>::WN;
+template <int NW, int BN, bool AKC, bool BKC, bool AF8, bool BF8, int EPI>
+__global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
+  constexpr int kThreads = Cfg<NW>::THREADS, kNst = Cfg<NW>::NST;
+  using TA = Tile<NW, kBM, AKC>;
+  using TB = Tile<NW, BN, BKC>;
+  constexpr int WM = WaveGrid<NW, BN>::WM, WN = WaveGrid<NW, BN>::WN;
   constexpr int TM = kBM / WM, TN = BN / WN;
   constexpr int MT = TM / 32, NTW = TN / 32;
   constexpr int STAGE = TA::BYTES + TB::BYTES;
@@ -287,13 +297,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
   const int nk = klen > 0 ? (int)(klen / kBK) : 0;
   const uint32_t ring0 = (uint32_t)(uintptr_t)ring;
 
-  Loader<kBM, AKC, AF8> la;
-  Loader<BN, BKC, BF8> lb;
+  Loader<NW, kBM, AKC, AF8> la;
+  Loader<NW, BN, BKC, BF8> lb;
   la.init(p.a, m0, wv, lane, tid);
   lb.init(p.b, n0, wv, lane, tid);
 
-  Frag<kBM, AKC> fa;
-  Frag<BN, BKC> fb;
+  Frag<NW, kBM, AKC> fa;
+  Frag<NW, BN, BKC> fb;
   fa.init(ring0, lane);
   fb.init(ring0 + TA::BYTES, lane);
   const int ablk0 = (wm * TM) / 32, bblk0 = (wn * TN) / 32;
@@ -304,8 +314,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = f32x16{};
 
-  Fp8Stage<kBM, AKC> sa;
-  Fp8Stage<BN, BKC> sb;
+  Fp8Stage<NW, kBM, AKC> sa;
+  Fp8Stage<NW, BN, BKC> sb;
   // fp8 register loads are issued before the stage's DMAs, so waiting for them at the
   // next step does not wait for those DMAs.
   auto issue = [&](int s) {
@@ -313,8 +323,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
     const int64_t k0 = kz0 + (int64_t)s * kBK;
     if constexpr (AF8) sa.load(la, p.a, m0, k0, tid);
     if constexpr (BF8) sb.load(lb, p.b, n0, k0, tid);
-    if constexpr (!AF8) dma_stage<kBM, AKC>(la, p.a, m0, k0, so, wv, lane);
-    if constexpr (!BF8) dma_stage<BN, BKC>(lb, p.b, n0, k0, so + TA::BYTES, wv, lane);
+    if constexpr (!AF8) dma_stage<NW, kBM, AKC>(la, p.a, m0, k0, so, wv, lane);
+    if constexpr (!BF8) dma_stage<NW, BN, BKC>(lb, p.b, n0, k0, so + TA::BYTES, wv, lane);
   };
   auto store_fp8 = [&](int s) {
     const uint32_t so = ring0 + (uint32_t)((s % kNst) * STAGE);
@@ -481,7 +491,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
       }
       uix[k] = (lo < nu && (int64_t)p.uitems[lo] == v) ? lo : -1;
     }
-    constexpr int WREG = kNst * STAGE / 8;     // LDS bytes per wave
+    constexpr int WREG = kNst * STAGE / NW;    // LDS bytes per wave
     constexpr int RS = TN * 4 + 16;            // fp32 row stride: 16 B pad spreads the 16-lane reads
     constexpr int MG = (WREG / (32 * RS)) < MT ? (WREG / (32 * RS)) : MT;
     constexpr int SEGS = TN / 16;
@@ -573,10 +583,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const GemmParams p) {
 //   K1: A = E chunk (k-contiguous, bf16 or fp8), B = activations (k-contiguous)
 //   K2: A = P (k-contiguous), B = E chunk (k-major, bf16 or fp8)
 //   K3: A = P (k-major), B = activations (k-major)
-template <int BN>
+template <int NW, int BN>
 hipError_t gemm_bn(const GemmParams& p, dim3 grid, hipStream_t st) {
   const bool akc = p.a.kc, bkc = p.b.kc, af8 = p.a.fp8, bf8 = p.b.fp8;
-#define CL_G(AKC, BKC, AF8, BF8, E) k_gemm<BN, AKC, BKC, AF8, BF8, E><<<grid, kThreads, 0, st>>>(p)
+#define CL_G(AKC, BKC, AF8, BF8, E) k_gemm<NW, BN, AKC, BKC, AF8, BF8, E><<<grid, 64 * NW, 0, st>>>(p)
   if (akc && bkc && !bf8) {                    // K1
     switch (p.epi) {
 #define CL_K1(E) case E: if (af8) CL_G(true, true, true, false, E); else CL_G(true, true, false, false, E); break;
@@ -601,14 +611,35 @@ hipError_t gemm_bn(const GemmParams& p, dim3 grid, hipStream_t st) {
 
 }  // namespace
 
+// Workgroup shape of a product: 4 waves (two workgroups per CU) for heads up to D = 1024,
+// where the logits epilogue and the short k loops gain most from the overlap, except the
+// dA product of very few rows (one row tile), which keeps 8 waves.
+int gemm_waves(const GemmParams& p) {
+  if (p.D > 1024) return 8;
+  if (p.epi == GEMM_EPI_ACC && p.M <= 128) return 8;
+  return 4;
+}
+int tile_n_for(int nw, int64_t N) { return (nw == 4 || N <= 128) ? 128 : 256; }
+
 int gemm_tile_m() { return kBM; }
-int gemm_tile_n(int64_t N) { return N <= 128 ? 128 : 256; }
-int gemm_warps_m(int64_t N) { return N <= 128 ? WaveGrid<128>::WM : WaveGrid<256>::WM; }
+int gemm_tile_n_of(int epi, int64_t M, int64_t N, int64_t D) {
+  GemmParams q{};
+  q.epi = epi; q.M = M; q.N = N; q.D = D;
+  return tile_n_for(gemm_waves(q), N);
+}
+int gemm_k1_warps_m(int64_t T, int64_t D) {
+  GemmParams q{};
+  q.D = D; q.epi = GEMM_EPI_BCE_LOSS; q.M = kBM; q.N = T;
+  const int nw = gemm_waves(q);
+  const int bn = tile_n_for(nw, T);
+  return nw == 4 ? WaveGrid<4, 128>::WM : (bn == 128 ? WaveGrid<8, 128>::WM : WaveGrid<8, 256>::WM);
+}
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t st) {
   if (p.M <= 0 || p.N <= 0 || p.K <= 0 || p.K % kBK != 0 || p.k_per_split % kBK != 0 || p.k_per_split <= 0)
     return hipErrorInvalidValue;
-  const int bn = gemm_tile_n(p.N);
+  const int nw = gemm_waves(p);
+  const int bn = tile_n_for(nw, p.N);
   const int64_t gm = (p.M + kBM - 1) / kBM, gn = (p.N + bn - 1) / bn, gz = (p.K + p.k_per_split - 1) / p.k_per_split;
   // every tile's outer origin lies inside its operand (the loaders clamp relative to it);
   // operands have at least one row and one 8-element group per row
@@ -630,7 +661,8 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t st) {
   const int64_t tiles = gm * gn * gz;
   if (tiles > ((int64_t)1 << 30)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((tiles + 7) / 8 * 8));
-  return bn == 128 ? gemm_bn<128>(p, grid, st) : gemm_bn<256>(p, grid, st);
+  if (nw == 4) return gemm_bn<4, 128>(p, grid, st);
+  return bn == 128 ? gemm_bn<8, 128>(p, grid, st) : gemm_bn<8, 256>(p, grid, st);
 }
 
 }  // namespace cl
