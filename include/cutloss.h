@@ -169,6 +169,22 @@ cutloss_status cutloss_ce_bwd(const cutloss_ce_problem* p, const float* lse, con
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Softmax CE backward with the gradient filter (Cut Your Losses article, the note that the
+ * softmax tail below numerical precision contributes negligibly to the gradient and its
+ * computation may be skipped). As cutloss_ce_bwd, except that the matrix work of a logit
+ * tile whose entries all have |w_t softmax_tv| < grad_filter_eps is skipped for both dA and
+ * dE (the tile's dense terms are dropped; the -1 target terms never are). Tiles are 32 x 32
+ * per wave on the fused-sweep path (D in {64, 128, 256}) and the products' stage tiles on
+ * the chunked path. An approximation by design: the dropped sum is bounded by
+ * sum over entries below eps of |w_t softmax_tv| |E_v| (dA) or |A_t| (dE).
+ * grad_filter_eps in [0, 1]; 0 gives the exact cutloss_ce_bwd result.
+ * Workspace: cutloss_ce_workspace_size(p, CUTLOSS_OP_BWD).
+ */
+cutloss_status cutloss_ce_bwd_filtered(const cutloss_ce_problem* p, const float* lse, const float* dloss,
+                                       void* dA, void* dE, float grad_filter_eps,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Number of data errors counted by the last call that used this workspace
  * (positive IDs / targets outside [0, V), malformed CSR rows). Synchronizes `stream`.
  */

@@ -212,6 +212,22 @@ def ce_items(A, E, target, items, lse_all, ignore_index=-100, dloss=None):
     return (w[:, None] * P).T @ A
 
 
+def ce_filter_bounds(A, E, target, eps, ignore_index=-100, dloss=None):
+    """Largest change the CE gradient filter can make (Cut Your Losses article, the note on
+    skipping the softmax tail below numerical precision): with Q = w softmax(X) (the dense
+    part of G), dropping any set of entries with |Q_tv| < eps moves dA_td by at most
+    sum_{v: |Q_tv| < eps} |Q_tv| |E_vd| and dE_vd by at most sum_{t: |Q_tv| < eps} |Q_tv| |A_td|.
+    Returns (bound_dA [T, D], bound_dE [V, D])."""
+    T, V = A.shape[0], E.shape[0]
+    X = A @ E.T
+    lse = logsumexp_rows(X)
+    valid = _ce_valid(target, V, ignore_index)
+    w = _weights(T, valid, dloss)
+    Q = np.abs(w[:, None] * np.exp(X - lse[:, None]))
+    Q = np.where(Q < eps, Q, 0.0)
+    return Q @ np.abs(E), Q.T @ np.abs(A)
+
+
 # ----------------------------------------------------------------------------
 # fused SGD on FP8 weights
 # ----------------------------------------------------------------------------

@@ -277,3 +277,31 @@ def test_sgd_fp8_matches_torch_rounding():
     pre = decode_fp8_e4m3fn(E_codes) - lr * dE
     ref = torch.from_numpy(pre).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(ours, ref)
+
+
+def test_ce_filter_bound_limits():
+    # eps above every probability: the bound covers dropping the whole dense part, i.e. the
+    # gap between the full gradient and the target-only gradient; eps = 0 bounds nothing
+    rng = np.random.default_rng(11)
+    T, D, V = 6, 5, 40
+    A = rng.standard_normal((T, D))
+    E = rng.standard_normal((V, D))
+    target = rng.integers(0, V, size=T)
+    target[2] = -100
+    b_dA, b_dE = H.ce_filter_bounds(A, E, target, 2.0)
+    dA, dE = H.ce_grads(A, E, target)
+    valid = target != -100
+    only_dA = np.zeros_like(dA)
+    only_dE = np.zeros_like(dE)
+    for t in np.nonzero(valid)[0]:
+        only_dA[t] = -E[target[t]]
+        only_dE[target[t]] -= A[t]
+    assert np.all(np.abs(dA - only_dA) <= b_dA + 1e-12)
+    assert np.all(np.abs(dE - only_dE) <= b_dE + 1e-12)
+    # the bound is the triangle inequality of that gap: equal where all terms share a sign
+    P = np.exp(A @ E.T - H.logsumexp_rows(A @ E.T)[:, None]) * valid[:, None]
+    assert np.allclose(b_dA, P @ np.abs(E)) and np.allclose(b_dE, P.T @ np.abs(A))
+    z_dA, z_dE = H.ce_filter_bounds(A, E, target, 0.0)
+    assert not z_dA.any() and not z_dE.any()
+    m_dA, _ = H.ce_filter_bounds(A, E, target, 0.05)
+    assert np.all(m_dA <= b_dA + 1e-15)

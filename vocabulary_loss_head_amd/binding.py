@@ -49,7 +49,7 @@ class CeProblem(ctypes.Structure):
 EXPORTED = [
     "cutloss_bce_workspace_size", "cutloss_ce_workspace_size",
     "cutloss_bce_fwd", "cutloss_bce_fwd_metrics", "cutloss_bce_bwd", "cutloss_bce_bwd_sgd",
-    "cutloss_ce_fwd", "cutloss_ce_bwd",
+    "cutloss_ce_fwd", "cutloss_ce_bwd", "cutloss_ce_bwd_filtered",
     "cutloss_read_data_errors", "cutloss_bce_canonical_targets",
     "cutloss_profile_enable", "cutloss_profile_read",
     "cutloss_status_string", "cutloss_last_error", "cutloss_version",
@@ -76,6 +76,7 @@ def _load() -> ctypes.CDLL:
         "cutloss_bce_bwd_sgd": (st, [pb, P, ctypes.c_float, P, P, P, sz, P]),
         "cutloss_ce_fwd": (st, [pc, P, P, P, sz, P]),
         "cutloss_ce_bwd": (st, [pc, P, P, P, P, P, sz, P]),
+        "cutloss_ce_bwd_filtered": (st, [pc, P, P, P, P, ctypes.c_float, P, sz, P]),
         "cutloss_read_data_errors": (st, [P, P, ctypes.POINTER(ctypes.c_int64)]),
         "cutloss_bce_canonical_targets": (st, [pb, P, P, P, P, ctypes.POINTER(ctypes.c_int64), P, sz, P]),
         "cutloss_profile_enable": (st, [ctypes.c_int32]),
@@ -187,6 +188,12 @@ def cutloss_ce_fwd(problem: CeProblem, loss, lse, ws: torch.Tensor, stream=None)
 def cutloss_ce_bwd(problem: CeProblem, lse, dloss, dA, dE, ws: torch.Tensor, stream=None) -> None:
     _check(_lib.cutloss_ce_bwd(ctypes.byref(problem), _ptr(lse), _ptr(dloss), _ptr(dA), _ptr(dE),
                                _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def cutloss_ce_bwd_filtered(problem: CeProblem, lse, dloss, dA, dE, grad_filter_eps: float, ws: torch.Tensor,
+                            stream=None) -> None:
+    _check(_lib.cutloss_ce_bwd_filtered(ctypes.byref(problem), _ptr(lse), _ptr(dloss), _ptr(dA), _ptr(dE),
+                                        float(grad_filter_eps), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def cutloss_read_data_errors(ws: torch.Tensor, stream=None) -> int:

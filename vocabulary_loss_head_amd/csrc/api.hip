@@ -192,6 +192,7 @@ struct ChunkPlan {
   int64_t n_splits;   // loss / lse partials: item tiles x waves along the item dimension
   int64_t sk;         // split-K slices of the dA product
   int64_t kps;        // items per slice
+  int64_t flag_bn, flag_ld;   // gradient filter flags: row tile of the logits product, row tiles
 };
 
 constexpr int64_t kChunkPBytes = 2ll << 30;     // P buffer budget
@@ -221,6 +222,8 @@ ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap) {
   if (sk < 1) sk = 1;
   c.kps = round_up(ceil_div(vc, sk), 32);
   c.sk = ceil_div(vc, c.kps);
+  c.flag_bn = cl::gemm_tile_n_of(cl::GEMM_EPI_CE_P, vc, T > 0 ? T : 1, D);
+  c.flag_ld = ceil_div(T > 0 ? T : 1, c.flag_bn);
   return c;
 }
 
@@ -238,6 +241,7 @@ struct Ws2 {
   float* S_u;
   float* S_part;
   float* red;         // staging of the split reductions
+  int32_t* flags;     // gradient filter: [Vc / 256][flag_ld]
   size_t bytes;
 };
 
@@ -280,6 +284,7 @@ Ws2 carve_chunked(void* base, const ChunkPlan& pl, bool need_P, bool need_dA, bo
   const size_t red_loss = cl::reduce_splits_tmp_floats(pl.n_splits, T, two_partials ? 1 : 0);
   const size_t red_dA = need_dA ? cl::reduce_splits_tmp_floats(pl.sk, T * pl.D, 0) : 0;
   w.red = c.take<float>(std::max<size_t>(1, std::max(red_loss, red_dA)));
+  w.flags = need_P ? c.take<int32_t>((size_t)(pl.Vc / 256) * pl.flag_ld) : nullptr;
   w.bytes = c.off;
   return w;
 }
@@ -345,7 +350,17 @@ cutloss_status check_out(const void* ptr, size_t align, const char* name, bool r
 cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss, float* loss, void* dA, void* dE,
                                int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st, int32_t* counts);
 cutloss_status ce_run_chunked(const cutloss_ce_problem* p, const float* lse_in, const float* dloss, float* loss,
-                              float* lse, void* dA, void* dE, void* ws, size_t ws_bytes, hipStream_t st);
+                              float* lse, void* dA, void* dE, void* ws, size_t ws_bytes, hipStream_t st,
+                              float filter_eps);
+
+// smallest bf16 bit pattern whose value is >= eps (eps > 0, finite); 0 = filter off
+uint32_t filter_bits_of(float eps) {
+  if (!(eps > 0.0f)) return 0u;
+  uint32_t u;
+  std::memcpy(&u, &eps, 4);
+  const uint32_t hi = u >> 16;
+  return (u & 0xFFFFu) ? hi + 1 : hi;
+}
 
 // counts != NULL (forward only): Cut Metrics in the same pass as the loss
 cutloss_status bce_run(const cutloss_bce_problem* p, const float* dloss, float* loss, void* dA, void* dE,
@@ -401,10 +416,11 @@ cutloss_status bce_run(const cutloss_bce_problem* p, const float* dloss, float* 
   return CUTLOSS_OK;
 }
 
+// filter_eps > 0 (backward only): the CE gradient filter
 cutloss_status ce_run(const cutloss_ce_problem* p, const float* lse_in, const float* dloss, float* loss, float* lse,
-                      void* dA, void* dE, void* ws, size_t ws_bytes, hipStream_t st) {
+                      void* dA, void* dE, void* ws, size_t ws_bytes, hipStream_t st, float filter_eps = 0.0f) {
   if (use_chunked(p->D, p->e_dtype == CUTLOSS_FP8_E4M3))
-    return ce_run_chunked(p, lse_in, dloss, loss, lse, dA, dE, ws, ws_bytes, st);
+    return ce_run_chunked(p, lse_in, dloss, loss, lse, dA, dE, ws, ws_bytes, st, filter_eps);
   const bool fwd = loss != nullptr;
   const Plan pl = make_plan(p->T, p->D, p->V, p->T, p->e_dtype == CUTLOSS_FP8_E4M3);
   const Ws w = carve(ws, pl, dA != nullptr, dE != nullptr, fwd);
@@ -428,6 +444,7 @@ cutloss_status ce_run(const cutloss_ce_problem* p, const float* lse_in, const fl
   sp.n_splits = pl.n_splits; sp.split_len = pl.split_len;
   sp.part_a = w.part_a; sp.part_b = w.part_b; sp.part_dA = w.part_dA;
   sp.w = w.w; sp.lse = lse_in; sp.uitems = w.tw.uitems; sp.counts = w.tw.counts; sp.S_u = w.S_u; sp.dE = dE;
+  sp.filter_bits = fwd ? 0u : filter_bits_of(filter_eps);
 
   if (fwd) {
     if (p->T > 0) {
@@ -472,6 +489,7 @@ struct ChunkJob {
   int k3_epi;            // -1: none, GEMM_EPI_DE or GEMM_EPI_SGD
   const int32_t* uitems; const int32_t* counts; const float* S_u;
   void* dE; float lr;
+  int32_t* flags; int64_t flag_ld; int flag_bn; float filter_eps;   // gradient filter (flags NULL: off)
 };
 
 cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
@@ -495,6 +513,8 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
       g.w = j.w; g.lse = j.lse; g.P = j.P; g.p_bt = (int)pl.bt; g.p_nvb = pl.Vc / 32; g.p_rows = pl.Tp;
       g.part_a = j.part_a; g.part_b = j.part_b;
       g.part_base = (v0 / bm) * cl::gemm_k1_warps_m(pl.T, pl.D);
+      g.flags = j.flags; g.flag_ld = j.flag_ld; g.flag_bn = j.flag_bn; g.flag_gen = (int)(c + 1);
+      g.filter_eps = j.filter_eps;
       CL_HIP(cl::launch_gemm(g, st), "chunk logits");
     }
     if (j.part_dA != nullptr) {
@@ -506,6 +526,7 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
       g.epi = cl::GEMM_EPI_ACC;
       g.T = pl.T; g.D = pl.D;
       g.acc = j.part_dA; g.ldacc = pl.D; g.acc_slice = pl.T * pl.D; g.acc_first = c == 0;
+      g.flags = j.flags; g.flag_ld = j.flag_ld; g.flag_bn = j.flag_bn; g.flag_gen = (int)(c + 1);
       CL_HIP(cl::launch_gemm(g, st), "chunk dA");
     }
     if (j.k3_epi >= 0) {
@@ -519,6 +540,7 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
       g.v0 = v0; g.V = pl.V; g.T = pl.T; g.D = pl.D;
       g.uitems = j.uitems; g.counts = j.counts; g.S_u = j.S_u;
       g.dE = j.dE; g.E_inplace = (void*)j.E; g.e_fp8 = j.e_fp8; g.lr = j.lr;
+      g.flags = j.flags; g.flag_ld = j.flag_ld; g.flag_bn = j.flag_bn; g.flag_gen = (int)(c + 1);
       CL_HIP(cl::launch_gemm(g, st), "chunk dE");
     }
   }
@@ -580,7 +602,8 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
 }
 
 cutloss_status ce_run_chunked(const cutloss_ce_problem* p, const float* lse_in, const float* dloss, float* loss,
-                              float* lse, void* dA, void* dE, void* ws, size_t ws_bytes, hipStream_t st) {
+                              float* lse, void* dA, void* dE, void* ws, size_t ws_bytes, hipStream_t st,
+                              float filter_eps) {
   const bool fwd = loss != nullptr;
   const ChunkPlan pl = make_chunk_plan(p->T, p->D, p->V, p->T);
   const bool grad = !fwd && (dA != nullptr || dE != nullptr);
@@ -623,6 +646,11 @@ cutloss_status ce_run_chunked(const cutloss_ce_problem* p, const float* lse_in, 
   }
   j.k1_epi = cl::GEMM_EPI_CE_P;
   j.part_dA = w.part_dA;
+  // the filtered products list at most 1024 k stages per workgroup: beyond that the call
+  // runs unfiltered (exact)
+  if (filter_eps > 0.0f && pl.kps / 32 <= 1024 && round_up(pl.T, 32) / 32 <= 1024) {
+    j.flags = w.flags; j.flag_ld = pl.flag_ld; j.flag_bn = (int)pl.flag_bn; j.filter_eps = filter_eps;
+  }
   j.k3_epi = dE != nullptr ? cl::GEMM_EPI_DE : -1;
   CL_TRY(run_chunks(j, st));
   if (dA != nullptr) {
@@ -706,6 +734,19 @@ cutloss_status cutloss_ce_fwd(const cutloss_ce_problem* p, float* loss, float* l
   CL_TRY(check_out(loss, 4, "loss", p->T > 0));
   CL_TRY(check_out(lse, 4, "lse", p->T > 0));
   return ce_run(p, nullptr, nullptr, loss, lse, nullptr, nullptr, ws, ws_bytes, (hipStream_t)stream);
+}
+
+cutloss_status cutloss_ce_bwd_filtered(const cutloss_ce_problem* p, const float* lse, const float* dloss, void* dA,
+                                       void* dE, float grad_filter_eps, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!(grad_filter_eps >= 0.0f) || grad_filter_eps > 1.0f)
+    return fail(CUTLOSS_ERR_INVALID_ARG, "grad_filter_eps must lie in [0, 1]");
+  CL_TRY(check_ce(p));
+  CL_TRY(check_out(lse, 4, "lse", p->T > 0));
+  CL_TRY(check_out(dloss, 4, "dloss", false));
+  CL_TRY(check_out(dA, 16, "dA", false));
+  CL_TRY(check_out(dE, 16, "dE", false));
+  return ce_run(p, lse, dloss, nullptr, nullptr, dA, dE, ws, ws_bytes, (hipStream_t)stream, grad_filter_eps);
 }
 
 cutloss_status cutloss_ce_bwd(const cutloss_ce_problem* p, const float* lse, const float* dloss, void* dA, void* dE,

@@ -132,6 +132,9 @@ struct SweepParams {
   void* dE;                 // bf16 [V, D] output or NULL
   void* E_inplace;          // SGD target (== E) or NULL
   float lr;
+  // CE gradient filter: a wave skips its gradient product for a chunk whose |P| values
+  // (bf16 bit patterns) are all below filter_bits; 0 = off
+  uint32_t filter_bits;
 };
 
 // Rows sweep modes: 0 = BCE loss partials, 1 = BCE dA partials, 2 = BCE dA + loss partials,
@@ -194,6 +197,11 @@ struct GemmParams {
   // DE / SGD epilogues
   const int32_t* uitems; const int32_t* counts; const float* S_u; int64_t D;
   void* dE; void* E_inplace; int e_fp8; float lr;
+  // CE gradient filter: the CE_P epilogue sets flags[tm * flag_ld + tn] = flag_gen for an
+  // output tile (item tile tm, row tile tn of flag_bn rows) holding some |P| >= filter_eps;
+  // the dA and dE products skip the matrix work of a k stage whose P tiles are unflagged.
+  // flags == NULL: off.
+  int32_t* flags; int64_t flag_ld; int flag_bn; int flag_gen; float filter_eps;
 };
 hipError_t launch_gemm(const GemmParams& p, hipStream_t st);
 int gemm_tile_m();                     // 256

@@ -43,6 +43,7 @@ template <int NW> struct Cfg {
 };
 constexpr int kBM = 256;
 constexpr int kGroupM = 8;
+constexpr int kMaxStages = 1024;      // k stages of one filtered dA / dE workgroup
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ int res_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
@@ -314,13 +315,49 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = f32x16{};
 
+  // Gradient filter (dA and dE products): wave 0 lists, in order, the k stages whose P tile
+  // the logits product flagged; the pipeline then runs over that list only.
+  __shared__ int slist[kMaxStages];
+  __shared__ int scount;
+  bool filt = false;
+  int nk_run = nk;
+  if constexpr (EPI == GEMM_EPI_ACC || EPI == GEMM_EPI_DE) {
+    if (p.flags != nullptr) {
+      filt = true;
+      if (wv == 0) {
+        int cnt = 0;
+        for (int b = 0; b < nk; b += 64) {
+          const int st = b + lane;
+          bool act = false;
+          if (st < nk) {
+            const int64_t k0 = kz0 + (int64_t)st * kBK;
+            if constexpr (EPI == GEMM_EPI_ACC) {   // k = items, M tile = rows t
+              const int64_t it = k0 >> 8;
+              const int64_t t0 = m0 / p.flag_bn, t1 = min((m0 + kBM - 1) / p.flag_bn, p.flag_ld - 1);
+              act = p.flags[it * p.flag_ld + t0] == p.flag_gen || p.flags[it * p.flag_ld + t1] == p.flag_gen;
+            } else {                               // M tile = items, k = rows t
+              act = p.flags[(m0 >> 8) * p.flag_ld + k0 / p.flag_bn] == p.flag_gen;
+            }
+          }
+          const uint64_t m = __builtin_amdgcn_ballot_w64(act);
+          if (act) slist[cnt + __builtin_popcountll(m & ((1ull << lane) - 1))] = st;
+          cnt += __builtin_popcountll(m);
+        }
+        if (lane == 0) scount = cnt;
+      }
+      __syncthreads();
+      nk_run = scount;
+    }
+  }
+  auto stage_k = [&](int s) -> int64_t { return kz0 + (int64_t)(filt ? slist[s] : s) * kBK; };
+
   Fp8Stage<NW, kBM, AKC> sa;
   Fp8Stage<NW, BN, BKC> sb;
   // fp8 register loads are issued before the stage's DMAs, so waiting for them at the
   // next step does not wait for those DMAs.
   auto issue = [&](int s) {
     const uint32_t so = ring0 + (uint32_t)((s % kNst) * STAGE);
-    const int64_t k0 = kz0 + (int64_t)s * kBK;
+    const int64_t k0 = stage_k(s);
     if constexpr (AF8) sa.load(la, p.a, m0, k0, tid);
     if constexpr (BF8) sb.load(lb, p.b, n0, k0, tid);
     if constexpr (!AF8) dma_stage<NW, kBM, AKC>(la, p.a, m0, k0, so, wv, lane);
@@ -333,20 +370,20 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
   };
 
   for (int s = 0; s < kNst - 1; ++s) {
-    if (s < nk) {
+    if (s < nk_run) {
       issue(s);
       store_fp8(s);
     }
   }
-  for (int s = 0; s < nk; ++s) {
+  for (int s = 0; s < nk_run; ++s) {
     if constexpr (AF8 || BF8) {
-      if (s >= 1 && s + kNst - 2 < nk) store_fp8(s + kNst - 2);   // loaded at step s - 1
+      if (s >= 1 && s + kNst - 2 < nk_run) store_fp8(s + kNst - 2);   // loaded at step s - 1
       wait_lgkm0();
     }
-    const int later = min(nk - 1 - s, kNst - 2);
+    const int later = min(nk_run - 1 - s, kNst - 2);
     if (later >= 2) wait_vm<2 * NPER>(); else if (later == 1) wait_vm<NPER>(); else wait_vm<0>();
     block_sync();
-    if (s + kNst - 1 < nk) issue(s + kNst - 1);
+    if (s + kNst - 1 < nk_run) issue(s + kNst - 1);
     const uint32_t so = (uint32_t)((s % kNst) * STAGE);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -369,6 +406,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
     constexpr bool WRITES_P = EPI == GEMM_EPI_BCE_P || EPI == GEMM_EPI_CE_P;
     const int64_t split = p.part_base + (int64_t)tm * WM + wm;
     const int64_t mw = m0 + wm * TM;          // chunk-relative first item of the wave
+    float pabs = 0.0f;                         // CE_P: largest |P| of the wave (gradient filter)
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
       const int64_t t = n0 + wn * TN + 32 * nt + l32;
@@ -423,6 +461,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
             } else {  // CE_P
               const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -lt));
               f[q] = ok && wt != 0.0f ? wt * e : 0.0f;
+              pabs = __builtin_fmaxf(pabs, __builtin_fabsf(f[q]));
             }
           }
           if constexpr (WRITES_P) {
@@ -460,6 +499,11 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
           p.part_b[split * p.T + t] = s;
         }
       }
+    }
+    if constexpr (EPI == GEMM_EPI_CE_P) {
+      // gradient filter: flag the output tile when some |P| of any wave reaches the threshold
+      if (p.flags != nullptr && __builtin_amdgcn_ballot_w64(pabs >= p.filter_eps) != 0 && lane == 0)
+        p.flags[(int64_t)tm * p.flag_ld + tn] = p.flag_gen;
     }
   } else if constexpr (EPI == GEMM_EPI_ACC) {
     float* out = p.acc + (int64_t)tz * p.acc_slice;
@@ -658,6 +702,8 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t st) {
         (!op->kc && outer_tiles * tile > op->cols_valid))
       return hipErrorInvalidValue;
   }
+  if (p.flags != nullptr && (p.epi == GEMM_EPI_ACC || p.epi == GEMM_EPI_DE) && p.k_per_split / kBK > kMaxStages)
+    return hipErrorInvalidValue;
   const int64_t tiles = gm * gn * gz;
   if (tiles > ((int64_t)1 << 30)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((tiles + 7) / 8 * 8));

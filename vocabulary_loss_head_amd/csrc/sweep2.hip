@@ -376,10 +376,28 @@ __device__ __forceinline__ void grad_only(f32x16 (&acc)[MT][D / 32], const FPack
 // prep(c, boff) points the epilogue at the chunk's per-row inputs. Three chunks are in
 // flight beyond the current one.
 // ------------------------------------------------------------------------------------
+// CE gradient filter (Cut Your Losses article, the note on the softmax tail below numerical
+// precision): true when some |P| of the wave's chunk tile is at least the bf16 pattern
+// `bits`; wave-uniform.
+template <int MT>
+__device__ __forceinline__ bool wave_any_at_least(const FPack<MT>& f, uint32_t bits) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t v = f.pw[mt][kk][j] & 0x7FFF7FFFu;
+        m = max(m, max(v & 0xFFFFu, v >> 16));
+      }
+  return __builtin_amdgcn_ballot_w64(m >= bits) != 0;
+}
+
 template <int D, int MT, int RM, int NPER0, int NPER, class Issue, class Prep>
 __device__ __forceinline__ void sweep_loop(int nch, int64_t rows_left0, const bf16x8 (&sf)[MT][D / 16],
                                            f32x16 (&acc)[MT][D / 32], Epi<MT, RM>& ep, const ReadBase<D>& rb,
-                                           int h, int wv, Issue issue, Prep prep) {
+                                           int h, int wv, uint32_t filter_bits, Issue issue, Prep prep) {
   using G = Geo<D>;
   constexpr bool HAS_F = EpiHasF<RM>::value;
   constexpr int AHEAD = 3;
@@ -410,7 +428,11 @@ __device__ __forceinline__ void sweep_loop(int nch, int64_t rows_left0, const bf
     } else {
       epilogue<MT, RM, false>(y, ep, f, h);
     }
-    if constexpr (HAS_F) grad_only<D, MT>(acc, f, rb, boff);
+    if constexpr (HAS_F) {
+      bool keep = true;
+      if constexpr (RM == 4 || RM == 6) keep = filter_bits == 0 || wave_any_at_least(f, filter_bits);
+      if (keep) grad_only<D, MT>(acc, f, rb, boff);
+    }
   }
 }
 
@@ -480,7 +502,7 @@ __global__ __launch_bounds__(256, Tiling<D>::WPE) void k_rows2(const SweepParams
     dma_chunk<D>(dof, E, r_begin + (int64_t)c * kRC, r_end, ring0 + boff, wv, lane);
   };
   auto prep = [&](int, uint32_t) {};
-  sweep_loop<D, MT, RM, G::LPWP + 1, G::LPWP>(nch, r_end - r_begin, sf, acc, ep, rb, h, wv, issue, prep);
+  sweep_loop<D, MT, RM, G::LPWP + 1, G::LPWP>(nch, r_end - r_begin, sf, acc, ep, rb, h, wv, p.filter_bits, issue, prep);
 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -571,7 +593,7 @@ __global__ __launch_bounds__(256, Tiling<D>::WPE) void k_cols2(const SweepParams
     if constexpr (KIND == 1) dma_vec(p.lse, r0, p.T, vb + kRC * 4, lane);
   };
   auto prep = [&](int, uint32_t boff) { ep.vb = vec0 + (boff / G::BUF) * (NV * kRC * 4); };
-  sweep_loop<D, MT, RM, G::LPWP + 1 + NV, G::LPWP + NV>(nch, p.T, sf, acc, ep, rb, h, wv, issue, prep);
+  sweep_loop<D, MT, RM, G::LPWP + 1 + NV, G::LPWP + NV>(nch, p.T, sf, acc, ep, rb, h, wv, p.filter_bits, issue, prep);
 
   // sparse positive term: index of each item of the block in the sorted unique-item list
   for (int k = tid; k < SB; k += 256) {
