@@ -242,11 +242,12 @@ struct Ws2 {
   float* S_part;
   float* red;         // staging of the split reductions
   int32_t* flags;     // gradient filter: [Vc / 256][flag_ld]
+  uint16_t* Et;       // the chunk's bf16 E transposed, [D][Vc] (the dA product's k-contiguous operand)
   size_t bytes;
 };
 
 Ws2 carve_chunked(void* base, const ChunkPlan& pl, bool need_P, bool need_dA, bool need_Su, bool two_partials,
-                  bool need_pos) {
+                  bool need_pos, bool need_Et) {
   Carver c(base);
   Ws2 w{};
   w.err = c.take<unsigned long long>(4);
@@ -285,6 +286,7 @@ Ws2 carve_chunked(void* base, const ChunkPlan& pl, bool need_P, bool need_dA, bo
   const size_t red_dA = need_dA ? cl::reduce_splits_tmp_floats(pl.sk, T * pl.D, 0) : 0;
   w.red = c.take<float>(std::max<size_t>(1, std::max(red_loss, red_dA)));
   w.flags = need_P ? c.take<int32_t>((size_t)(pl.Vc / 256) * pl.flag_ld) : nullptr;
+  w.Et = need_dA && need_Et ? c.take<uint16_t>((size_t)pl.Vc * pl.D) : nullptr;
   w.bytes = c.off;
   return w;
 }
@@ -486,6 +488,7 @@ struct ChunkJob {
   const float* w; const float* lse;
   uint16_t* P; float* part_a; float* part_b;
   float* part_dA;        // NULL: no dA
+  uint16_t* Et;          // bf16 E: workspace for the transposed chunk
   int k3_epi;            // -1: none, GEMM_EPI_DE or GEMM_EPI_SGD
   const int32_t* uitems; const int32_t* counts; const float* S_u;
   void* dE; float lr;
@@ -521,7 +524,14 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
       Phase ph(CUTLOSS_PHASE_CHUNK_DA, st);
       cl::GemmParams g{};
       g.a = operand(j.P, 0, pl.Tp, mc, 1, 0, (int)pl.bt, pl.Vc / 32);
-      g.b = operand(Ec, pl.D, vlen, pl.D, 0, j.e_fp8);
+      if (j.e_fp8) {
+        g.b = operand(Ec, pl.D, vlen, pl.D, 0, 1);
+      } else {
+        // k-contiguous copy of the chunk (zero past vlen): the product reads it with full-width
+        // LDS reads instead of transposing reads
+        CL_HIP(cl::launch_transpose_chunk((const uint16_t*)Ec, vlen, mc, pl.D, j.Et, pl.Vc, st), "chunk transpose");
+        g.b = operand(j.Et, pl.Vc, pl.D, mc, 1, 0);
+      }
       g.M = pl.T; g.N = pl.D; g.K = mc; g.k_per_split = pl.kps;
       g.epi = cl::GEMM_EPI_ACC;
       g.T = pl.T; g.D = pl.D;
@@ -551,9 +561,9 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
                                int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st, int32_t* counts) {
   const ChunkPlan pl = make_chunk_plan(p->T, p->D, p->V, p->nnz);
   const bool grad = dA != nullptr || dE_mode != 0;
-  const Ws2 w = carve_chunked(ws, pl, grad, dA != nullptr, dE_mode != 0, counts != nullptr, true);
-  CL_TRY(check_ws(ws, ws_bytes, w.bytes));
   const int e_fp8 = p->e_dtype == CUTLOSS_FP8_E4M3;
+  const Ws2 w = carve_chunked(ws, pl, grad, dA != nullptr, dE_mode != 0, counts != nullptr, true, !e_fp8);
+  CL_TRY(check_ws(ws, ws_bytes, w.bytes));
   {
     Phase ph(CUTLOSS_PHASE_TARGETS, st);
     CL_HIP(cl::launch_zero_u64(w.err, 4, st), "zero counters");
@@ -580,7 +590,7 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
   ChunkJob j{};
   j.pl = &pl; j.A = p->A; j.E = p->E; j.e_fp8 = e_fp8;
   j.k1_epi = grad ? cl::GEMM_EPI_BCE_P : (counts ? cl::GEMM_EPI_BCE_METRICS : cl::GEMM_EPI_BCE_LOSS);
-  j.w = w.w; j.P = w.P; j.part_a = w.part_a; j.part_b = w.part_b; j.part_dA = w.part_dA;
+  j.w = w.w; j.P = w.P; j.part_a = w.part_a; j.part_b = w.part_b; j.part_dA = w.part_dA; j.Et = w.Et;
   j.k3_epi = dE_mode == 0 ? -1 : (dE_mode == 1 ? cl::GEMM_EPI_DE : cl::GEMM_EPI_SGD);
   j.uitems = w.tw.uitems; j.counts = w.tw.counts; j.S_u = w.S_u; j.dE = dE; j.lr = lr;
   CL_TRY(run_chunks(j, st));
@@ -607,9 +617,9 @@ cutloss_status ce_run_chunked(const cutloss_ce_problem* p, const float* lse_in, 
   const bool fwd = loss != nullptr;
   const ChunkPlan pl = make_chunk_plan(p->T, p->D, p->V, p->T);
   const bool grad = !fwd && (dA != nullptr || dE != nullptr);
-  const Ws2 w = carve_chunked(ws, pl, grad, !fwd && dA != nullptr, !fwd && dE != nullptr, fwd, false);
-  CL_TRY(check_ws(ws, ws_bytes, w.bytes));
   const int e_fp8 = p->e_dtype == CUTLOSS_FP8_E4M3;
+  const Ws2 w = carve_chunked(ws, pl, grad, !fwd && dA != nullptr, !fwd && dE != nullptr, fwd, false, !e_fp8);
+  CL_TRY(check_ws(ws, ws_bytes, w.bytes));
   {
     Phase ph(CUTLOSS_PHASE_TARGETS, st);
     CL_HIP(cl::launch_zero_u64(w.err, 4, st), "zero counters");
@@ -646,6 +656,7 @@ cutloss_status ce_run_chunked(const cutloss_ce_problem* p, const float* lse_in, 
   }
   j.k1_epi = cl::GEMM_EPI_CE_P;
   j.part_dA = w.part_dA;
+  j.Et = w.Et;
   // the filtered products list at most 1024 k stages per workgroup: beyond that the call
   // runs unfiltered (exact)
   if (filter_eps > 0.0f && pl.kps / 32 <= 1024 && round_up(pl.T, 32) / 32 <= 1024) {
@@ -672,7 +683,7 @@ size_t cutloss_bce_workspace_size(const cutloss_bce_problem* p, int32_t op) {
   const bool bwd = op != CUTLOSS_OP_FWD && !metrics;
   if (use_chunked(p->D, p->e_dtype == CUTLOSS_FP8_E4M3)) {
     const ChunkPlan cp = make_chunk_plan(p->T, p->D, p->V, p->nnz);
-    return carve_chunked(nullptr, cp, bwd, bwd, bwd, metrics, true).bytes;
+    return carve_chunked(nullptr, cp, bwd, bwd, bwd, metrics, true, p->e_dtype != CUTLOSS_FP8_E4M3).bytes;
   }
   const Plan pl = make_plan(p->T, p->D, p->V, p->nnz, p->e_dtype == CUTLOSS_FP8_E4M3);
   return carve(nullptr, pl, bwd, bwd, metrics).bytes;
@@ -683,7 +694,7 @@ size_t cutloss_ce_workspace_size(const cutloss_ce_problem* p, int32_t op) {
   const bool bwd = op != CUTLOSS_OP_FWD;
   if (use_chunked(p->D, p->e_dtype == CUTLOSS_FP8_E4M3)) {
     const ChunkPlan cp = make_chunk_plan(p->T, p->D, p->V, p->T);
-    return carve_chunked(nullptr, cp, bwd, bwd, bwd, !bwd, false).bytes;
+    return carve_chunked(nullptr, cp, bwd, bwd, bwd, !bwd, false, p->e_dtype != CUTLOSS_FP8_E4M3).bytes;
   }
   const Plan pl = make_plan(p->T, p->D, p->V, p->T, p->e_dtype == CUTLOSS_FP8_E4M3);
   return carve(nullptr, pl, bwd, bwd, !bwd).bytes;

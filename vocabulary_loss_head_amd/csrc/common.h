@@ -204,6 +204,10 @@ struct GemmParams {
   int32_t* flags; int64_t flag_ld; int flag_bn; int flag_gen; float filter_eps;
 };
 hipError_t launch_gemm(const GemmParams& p, hipStream_t st);
+// Et[d][v] = E[v][d] (bf16) for v < vlen, 0 for vlen <= v < mc; Et rows hold ld >= mc items.
+// mc and D multiples of 64, ld a multiple of 8.
+hipError_t launch_transpose_chunk(const uint16_t* E, int64_t vlen, int64_t mc, int64_t D, uint16_t* Et, int64_t ld,
+                                  hipStream_t st);
 int gemm_tile_m();                     // 256
 int gemm_tile_n_of(int epi, int64_t M, int64_t N, int64_t D);   // 128 or 256 for that product
 // waves along M of the logits product (row partials per item tile) for T rows, head D

@@ -37,9 +37,10 @@ constexpr int kBK = 32;
 // Two workgroup shapes: NW = 8 waves with a 4-deep ring (one workgroup per CU), and NW = 4
 // waves with 256 x 128 tiles and a 3-deep ring (72 KB of LDS, two workgroups per CU, so one
 // can run its MFMAs while the other is in its epilogue).
-template <int NW> struct Cfg {
+template <int NW, int BN> struct Cfg {
   static constexpr int THREADS = 64 * NW;
-  static constexpr int NST = NW == 4 ? 3 : 4;
+  static constexpr int NST = (NW == 4 && BN == 128) ? 3 : 4;
+  static constexpr int MINW = (NW == 4 && BN == 256) ? 1 : 2;   // waves per SIMD
 };
 constexpr int kBM = 256;
 constexpr int kGroupM = 8;
@@ -248,6 +249,7 @@ template <int NW, int BN> struct WaveGrid;
 template <> struct WaveGrid<8, 256> { static constexpr int WM = 2, WN = 4; };
 template <> struct WaveGrid<8, 128> { static constexpr int WM = 4, WN = 2; };
 template <> struct WaveGrid<4, 128> { static constexpr int WM = 2, WN = 2; };
+template <> struct WaveGrid<4, 256> { static constexpr int WM = 2, WN = 2; };
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   const bf16x2 v = __builtin_convertvector(f32x2{a, b}, bf16x2);
@@ -273,8 +275,8 @@ __device__ __forceinline__ bool map_tile(int gm, int gn, int gz, int& tm, int& t
 }
 
 template <int NW, int BN, bool AKC, bool BKC, bool AF8, bool BF8, int EPI>
-__global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
-  constexpr int kThreads = Cfg<NW>::THREADS, kNst = Cfg<NW>::NST;
+__global__ __launch_bounds__(64 * NW, (Cfg<NW, BN>::MINW)) void k_gemm(const GemmParams p) {
+  constexpr int kThreads = Cfg<NW, BN>::THREADS, kNst = Cfg<NW, BN>::NST;
   using TA = Tile<NW, kBM, AKC>;
   using TB = Tile<NW, BN, BKC>;
   constexpr int WM = WaveGrid<NW, BN>::WM, WN = WaveGrid<NW, BN>::WN;
@@ -623,15 +625,18 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
   }
 }
 
-// The three operand combinations the chunked path uses:
+// The operand combinations the chunked path uses:
 //   K1: A = E chunk (k-contiguous, bf16 or fp8), B = activations (k-contiguous)
-//   K2: A = P (k-contiguous), B = E chunk (k-major, bf16 or fp8)
+//   K2: A = P (k-contiguous), B = the transposed bf16 E chunk (k-contiguous) or the fp8
+//       E chunk itself (k-major)
 //   K3: A = P (k-major), B = activations (k-major)
 template <int NW, int BN>
 hipError_t gemm_bn(const GemmParams& p, dim3 grid, hipStream_t st) {
   const bool akc = p.a.kc, bkc = p.b.kc, af8 = p.a.fp8, bf8 = p.b.fp8;
 #define CL_G(AKC, BKC, AF8, BF8, E) k_gemm<NW, BN, AKC, BKC, AF8, BF8, E><<<grid, 64 * NW, 0, st>>>(p)
-  if (akc && bkc && !bf8) {                    // K1
+  if (akc && bkc && !af8 && !bf8 && p.epi == GEMM_EPI_ACC) {   // K2, bf16 E
+    CL_G(true, true, false, false, GEMM_EPI_ACC);
+  } else if (akc && bkc && !bf8) {             // K1
     switch (p.epi) {
 #define CL_K1(E) case E: if (af8) CL_G(true, true, true, false, E); else CL_G(true, true, false, false, E); break;
       CL_K1(GEMM_EPI_BCE_P) CL_K1(GEMM_EPI_BCE_LOSS) CL_K1(GEMM_EPI_CE_LSE) CL_K1(GEMM_EPI_CE_P)
@@ -639,9 +644,8 @@ hipError_t gemm_bn(const GemmParams& p, dim3 grid, hipStream_t st) {
 #undef CL_K1
       default: return hipErrorInvalidValue;
     }
-  } else if (akc && !bkc && !af8 && p.epi == GEMM_EPI_ACC) {    // K2
-    if (bf8) CL_G(true, false, false, true, GEMM_EPI_ACC);
-    else CL_G(true, false, false, false, GEMM_EPI_ACC);
+  } else if (akc && !bkc && !af8 && bf8 && p.epi == GEMM_EPI_ACC) {    // K2, fp8 E
+    CL_G(true, false, false, true, GEMM_EPI_ACC);
   } else if (!akc && !bkc && !af8 && !bf8) {   // K3
     if (p.epi == GEMM_EPI_DE) CL_G(false, false, false, false, GEMM_EPI_DE);
     else if (p.epi == GEMM_EPI_SGD) CL_G(false, false, false, false, GEMM_EPI_SGD);
@@ -653,7 +657,42 @@ hipError_t gemm_bn(const GemmParams& p, dim3 grid, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Et[d][v] = E[v][d] for v < vlen and 0 for vlen <= v < mc: one 64 x 64 tile per
+// workgroup, read as 128-byte row pieces of E and written as 128-byte row pieces of Et.
+__global__ __launch_bounds__(256) void k_transpose_chunk(const uint16_t* __restrict__ E, int64_t vlen, int64_t D,
+                                                         uint16_t* __restrict__ Et, int64_t ld) {
+  constexpr int S = 72;                        // LDS row stride (halfwords), keeps 16 B alignment
+  __shared__ uint16_t t[64 * S];               // t[d][v]
+  const int tid = threadIdx.x;
+  const int64_t v0 = (int64_t)blockIdx.x * 64, d0 = (int64_t)blockIdx.y * 64;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = tid / 8 + 32 * h, c = (tid % 8) * 8;
+    uint4 x = {0u, 0u, 0u, 0u};
+    if (v0 + r < vlen) x = *(const uint4*)(E + (v0 + r) * D + d0 + c);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      t[(c + 2 * j) * S + r] = (uint16_t)(w[j] & 0xffffu);
+      t[(c + 2 * j + 1) * S + r] = (uint16_t)(w[j] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int d = tid / 8 + 32 * h, c = (tid % 8) * 8;
+    *(uint4*)(Et + (d0 + d) * ld + v0 + c) = *(const uint4*)(t + d * S + c);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_transpose_chunk(const uint16_t* E, int64_t vlen, int64_t mc, int64_t D, uint16_t* Et, int64_t ld,
+                                  hipStream_t st) {
+  if (vlen <= 0 || mc % 64 != 0 || vlen > mc || D % 64 != 0 || ld < mc || ld % 8 != 0) return hipErrorInvalidValue;
+  k_transpose_chunk<<<dim3((unsigned)(mc / 64), (unsigned)(D / 64)), 256, 0, st>>>(E, vlen, D, Et, ld);
+  return hipGetLastError();
+}
 
 // Workgroup shape of a product: 4 waves (two workgroups per CU) for heads up to D = 1024,
 // where the logits epilogue and the short k loops gain most from the overlap, except the
@@ -663,7 +702,11 @@ int gemm_waves(const GemmParams& p) {
   if (p.epi == GEMM_EPI_ACC && p.M <= 128) return 8;
   return 4;
 }
+#ifdef CL_GEMM_BIG
+int tile_n_for(int nw, int64_t N) { return N <= 128 ? 128 : 256; }
+#else
 int tile_n_for(int nw, int64_t N) { return (nw == 4 || N <= 128) ? 128 : 256; }
+#endif
 
 int gemm_tile_m() { return kBM; }
 int gemm_tile_n_of(int epi, int64_t M, int64_t N, int64_t D) {
@@ -707,6 +750,9 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t st) {
   const int64_t tiles = gm * gn * gz;
   if (tiles > ((int64_t)1 << 30)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((tiles + 7) / 8 * 8));
+#ifdef CL_GEMM_BIG
+  if (nw == 4 && bn == 256) return gemm_bn<4, 256>(p, grid, st);
+#endif
   if (nw == 4) return gemm_bn<4, 128>(p, grid, st);
   return bn == 128 ? gemm_bn<8, 128>(p, grid, st) : gemm_bn<8, 256>(p, grid, st);
 }
