@@ -39,8 +39,7 @@ constexpr int kBK = 32;
 // can run its MFMAs while the other is in its epilogue).
 template <int NW, int BN> struct Cfg {
   static constexpr int THREADS = 64 * NW;
-  static constexpr int NST = (NW == 4 && BN == 128) ? 3 : 4;
-  static constexpr int MINW = (NW == 4 && BN == 256) ? 1 : 2;   // waves per SIMD
+  static constexpr int NST = NW == 4 ? 3 : 4;
 };
 constexpr int kBM = 256;
 constexpr int kGroupM = 8;
@@ -249,7 +248,6 @@ template <int NW, int BN> struct WaveGrid;
 template <> struct WaveGrid<8, 256> { static constexpr int WM = 2, WN = 4; };
 template <> struct WaveGrid<8, 128> { static constexpr int WM = 4, WN = 2; };
 template <> struct WaveGrid<4, 128> { static constexpr int WM = 2, WN = 2; };
-template <> struct WaveGrid<4, 256> { static constexpr int WM = 2, WN = 2; };
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   const bf16x2 v = __builtin_convertvector(f32x2{a, b}, bf16x2);
@@ -275,7 +273,7 @@ __device__ __forceinline__ bool map_tile(int gm, int gn, int gz, int& tm, int& t
 }
 
 template <int NW, int BN, bool AKC, bool BKC, bool AF8, bool BF8, int EPI>
-__global__ __launch_bounds__(64 * NW, (Cfg<NW, BN>::MINW)) void k_gemm(const GemmParams p) {
+__global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
   constexpr int kThreads = Cfg<NW, BN>::THREADS, kNst = Cfg<NW, BN>::NST;
   using TA = Tile<NW, kBM, AKC>;
   using TB = Tile<NW, BN, BKC>;
@@ -702,11 +700,7 @@ int gemm_waves(const GemmParams& p) {
   if (p.epi == GEMM_EPI_ACC && p.M <= 128) return 8;
   return 4;
 }
-#ifdef CL_GEMM_BIG
-int tile_n_for(int nw, int64_t N) { return N <= 128 ? 128 : 256; }
-#else
 int tile_n_for(int nw, int64_t N) { return (nw == 4 || N <= 128) ? 128 : 256; }
-#endif
 
 int gemm_tile_m() { return kBM; }
 int gemm_tile_n_of(int epi, int64_t M, int64_t N, int64_t D) {
@@ -750,9 +744,6 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t st) {
   const int64_t tiles = gm * gn * gz;
   if (tiles > ((int64_t)1 << 30)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((tiles + 7) / 8 * 8));
-#ifdef CL_GEMM_BIG
-  if (nw == 4 && bn == 256) return gemm_bn<4, 256>(p, grid, st);
-#endif
   if (nw == 4) return gemm_bn<4, 128>(p, grid, st);
   return bn == 128 ? gemm_bn<8, 128>(p, grid, st) : gemm_bn<8, 256>(p, grid, st);
 }
