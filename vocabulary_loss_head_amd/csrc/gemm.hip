@@ -43,7 +43,8 @@ template <int NW, int BN> struct Cfg {
 };
 constexpr int kBM = 256;
 constexpr int kGroupM = 8;
-constexpr int kMaxStages = 1024;      // k stages of one filtered dA / dE workgroup
+constexpr int kMaxStages = 1024;
+template <bool B> struct BoolC { static constexpr bool value = B; };      // k stages of one filtered dA / dE workgroup
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ int res_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
@@ -369,34 +370,54 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
     if constexpr (BF8) sb.store(so + TA::BYTES, tid);
   };
 
-  for (int s = 0; s < kNst - 1; ++s) {
-    if (s < nk_run) {
-      issue(s);
-      store_fp8(s);
-    }
-  }
-  for (int s = 0; s < nk_run; ++s) {
-    if constexpr (AF8 || BF8) {
-      if (s >= 1 && s + kNst - 2 < nk_run) store_fp8(s + kNst - 2);   // loaded at step s - 1
-      wait_lgkm0();
-    }
-    const int later = min(nk_run - 1 - s, kNst - 2);
-    if (later >= 2) wait_vm<2 * NPER>(); else if (later == 1) wait_vm<NPER>(); else wait_vm<0>();
-    block_sync();
-    if (s + kNst - 1 < nk_run) issue(s + kNst - 1);
+  // Software pipeline, half a stage deep: the LDS reads of one k16 half are in flight while
+  // the MFMAs of the other run, and the barrier that retires a ring slot sits between the
+  // two MFMA halves of a stage. All kNst slots are in flight after the prologue.
+  bf16x8 a0[MT], b0[NTW], a1[MT], b1[NTW];
+  auto read_half = [&](int s, int kk, bf16x8* av, bf16x8* bv) {
     const uint32_t so = (uint32_t)((s % kNst) * STAGE);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 av[MT], bv[NTW];
+    for (int mt = 0; mt < MT; ++mt) av[mt] = fa.read(so, ablk0 + mt, kk);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) av[mt] = fa.read(so, ablk0 + mt, kk);
+    for (int nt = 0; nt < NTW; ++nt) bv[nt] = fb.read(so, bblk0 + nt, kk);
+  };
+  auto mma_half = [&](const bf16x8* av, const bf16x8* bv) {
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) bv[nt] = fb.read(so, bblk0 + nt, kk);
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = mfma32(av[mt], bv[nt], acc[mt][nt]);
+      for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = mfma32(av[mt], bv[nt], acc[mt][nt]);
+  };
+  if (nk_run > 0) {
+    for (int x = 0; x < kNst; ++x) {
+      if (x < nk_run) {
+        issue(x);
+        if (x < kNst - 1) store_fp8(x);      // the last prologue stage is stored at step 0
+      }
     }
+    {
+      const int later = min(nk_run - 1, kNst - 1);   // stages after stage 0 in flight
+      if (later >= 3) wait_vm<3 * NPER>(); else if (later == 2) wait_vm<2 * NPER>();
+      else if (later == 1) wait_vm<NPER>(); else wait_vm<0>();
+    }
+    wait_lgkm0();
+    block_sync();
+    read_half(0, 0, a0, b0);
+  }
+  for (int s = 0; s < nk_run; ++s) {
+    read_half(s, 1, a1, b1);
+    mma_half(a0, b0);
+    if (s + 1 < nk_run) {
+      if constexpr (AF8 || BF8) {
+        if (s + kNst - 1 < nk_run) store_fp8(s + kNst - 1);   // loaded at step s - 1
+      }
+      const int later = min(nk_run - 2 - s, kNst - 2);        // stages after s + 1 in flight
+      if (later >= 2) wait_vm<2 * NPER>(); else if (later == 1) wait_vm<NPER>(); else wait_vm<0>();
+      wait_lgkm0();
+      block_sync();                          // stage s retired, stage s + 1 landed
+      if (s + kNst < nk_run) issue(s + kNst);
+      read_half(s + 1, 0, a0, b0);
+    }
+    mma_half(a1, b1);
   }
 
   // ---------------------------------------------------------------- epilogues
@@ -404,107 +425,114 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
                 EPI == GEMM_EPI_BCE_METRICS) {
     constexpr bool BCE_SUM = EPI == GEMM_EPI_BCE_P || EPI == GEMM_EPI_BCE_LOSS || EPI == GEMM_EPI_BCE_METRICS;
     constexpr bool WRITES_P = EPI == GEMM_EPI_BCE_P || EPI == GEMM_EPI_CE_P;
-    const int64_t split = p.part_base + (int64_t)tm * WM + wm;
-    const int64_t mw = m0 + wm * TM;          // chunk-relative first item of the wave
-    float pabs = 0.0f;                         // CE_P: largest |P| of the wave (gradient filter)
+    // Tiles inside the valid item and row ranges skip the per-element masks.
+    auto logit_tile = [&](auto tail_c) {
+      constexpr bool TAIL = decltype(tail_c)::value;
+      const int64_t split = p.part_base + (int64_t)tm * WM + wm;
+      const int64_t mw = m0 + wm * TM;          // chunk-relative first item of the wave
+      float pabs = 0.0f;                         // CE_P: largest |P| of the wave (gradient filter)
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-      const int64_t t = n0 + wn * TN + 32 * nt + l32;
-      const bool t_ok = t < p.T;
-      const bool t_st = t < p.p_rows;          // the P buffer has this row
-      float wt = 0.0f, lt = 0.0f;
-      if constexpr (WRITES_P) wt = t_ok ? p.w[t] : 0.0f;
-      if constexpr (EPI == GEMM_EPI_CE_P) lt = t_ok ? p.lse[t] * kLog2e : 0.0f;
-      // blocked P: row t, columns mw + 32 mt + 8 j + 4 h + 0..3 = 8 contiguous bytes
-      uint16_t* prow = nullptr;
-      const int64_t pbs = (int64_t)p.p_bt * 32;
-      if constexpr (WRITES_P) {
-        const int64_t ts = t_st ? t : 0;
-        prow = p.P + ((ts / p.p_bt) * p.p_nvb + (mw >> 5)) * pbs + (ts % p.p_bt) * 32 + 4 * h;
-      }
-      float relu = 0.0f, prod = 1.0f, lg = 0.0f, mx = kNegInf, sm = 0.0f, cnt = 0.0f;
-      if constexpr (EPI == GEMM_EPI_CE_LSE) {
+      for (int nt = 0; nt < NTW; ++nt) {
+        const int64_t t = n0 + wn * TN + 32 * nt + l32;
+        const bool t_ok = !TAIL || t < p.T;
+        const bool t_st = !TAIL || t < p.p_rows; // the P buffer has this row
+        float wt = 0.0f, lt = 0.0f;
+        if constexpr (WRITES_P) wt = t_ok ? p.w[t] : 0.0f;
+        if constexpr (EPI == GEMM_EPI_CE_P) lt = t_ok ? p.lse[t] * kLog2e : 0.0f;
+        // blocked P: row t, columns mw + 32 mt + 8 j + 4 h + 0..3 = 8 contiguous bytes
+        uint16_t* prow = nullptr;
+        const int64_t pbs = (int64_t)p.p_bt * 32;
+        if constexpr (WRITES_P) {
+          const int64_t ts = t_st ? t : 0;
+          prow = p.P + ((ts / p.p_bt) * p.p_nvb + (mw >> 5)) * pbs + (ts % p.p_bt) * 32 + 4 * h;
+        }
+        float relu = 0.0f, prod = 1.0f, lg = 0.0f, mx = kNegInf, sm = 0.0f, cnt = 0.0f;
+        if constexpr (EPI == GEMM_EPI_CE_LSE) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int64_t v = p.v0 + mw + 32 * mt + res_row(i, h);
-            mx = (v < p.V && t_ok) ? __builtin_fmaxf(mx, acc[mt][nt][i]) : mx;
-          }
-      }
-      const float mb = mx == kNegInf ? 0.0f : mx * kLog2e;
+            for (int i = 0; i < 16; ++i) {
+              const int64_t v = p.v0 + mw + 32 * mt + res_row(i, h);
+              mx = (!TAIL || (v < p.V && t_ok)) ? __builtin_fmaxf(mx, acc[mt][nt][i]) : mx;
+            }
+        }
+        const float mb = mx == kNegInf ? 0.0f : mx * kLog2e;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+        for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float f[4];
+          for (int j = 0; j < 4; ++j) {
+            float f[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int i = 4 * j + q;
-            const int64_t v = p.v0 + mw + 32 * mt + res_row(i, h);
-            const bool ok = v < p.V && t_ok;
-            const float x = acc[mt][nt][i];
-            f[q] = 0.0f;
-            if constexpr (EPI == GEMM_EPI_BCE_METRICS) cnt += (ok && x > 0.0f) ? 1.0f : 0.0f;
-            if constexpr (BCE_SUM) {
-              const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * kLog2e);
-              const float qv = 1.0f + e;
-              relu += ok ? __builtin_fmaxf(x, 0.0f) : 0.0f;
-              prod *= ok ? qv : 1.0f;
-              if constexpr (EPI == GEMM_EPI_BCE_P) {
-                const float r = __builtin_amdgcn_rcpf(qv);
-                const float sig = x >= 0.0f ? r : e * r;
-                f[q] = ok ? wt * sig : 0.0f;
+            for (int q = 0; q < 4; ++q) {
+              const int i = 4 * j + q;
+              const int64_t v = p.v0 + mw + 32 * mt + res_row(i, h);
+              const bool ok = !TAIL || (v < p.V && t_ok);
+              const float x = acc[mt][nt][i];
+              f[q] = 0.0f;
+              if constexpr (EPI == GEMM_EPI_BCE_METRICS) cnt += (ok && x > 0.0f) ? 1.0f : 0.0f;
+              if constexpr (BCE_SUM) {
+                const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * kLog2e);
+                const float qv = 1.0f + e;
+                relu += ok ? __builtin_fmaxf(x, 0.0f) : 0.0f;
+                prod *= ok ? qv : 1.0f;
+                if constexpr (EPI == GEMM_EPI_BCE_P) {
+                  const float r = __builtin_amdgcn_rcpf(qv);
+                  const float sig = x >= 0.0f ? r : e * r;
+                  f[q] = ok ? wt * sig : 0.0f;
+                }
+              } else if constexpr (EPI == GEMM_EPI_CE_LSE) {
+                sm += ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -mb)) : 0.0f;
+              } else {  // CE_P
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -lt));
+                f[q] = ok && wt != 0.0f ? wt * e : 0.0f;
+                pabs = __builtin_fmaxf(pabs, __builtin_fabsf(f[q]));
               }
-            } else if constexpr (EPI == GEMM_EPI_CE_LSE) {
-              sm += ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -mb)) : 0.0f;
-            } else {  // CE_P
-              const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -lt));
-              f[q] = ok && wt != 0.0f ? wt * e : 0.0f;
-              pabs = __builtin_fmaxf(pabs, __builtin_fabsf(f[q]));
+            }
+            if constexpr (WRITES_P) {
+              if (t_st) {
+                uint2 pk;
+                pk.x = pack2(f[0], f[1]);
+                pk.y = pack2(f[2], f[3]);
+                *(uint2*)(prow + mt * pbs + 8 * j) = pk;
+              }
             }
           }
-          if constexpr (WRITES_P) {
-            if (t_st) {
-              uint2 pk;
-              pk.x = pack2(f[0], f[1]);
-              pk.y = pack2(f[2], f[3]);
-              *(uint2*)(prow + mt * pbs + 8 * j) = pk;
-            }
+          if constexpr (BCE_SUM) {
+            lg += __builtin_amdgcn_logf(prod);   // log2 of a product of 16 factors in [1, 2]
+            prod = 1.0f;
           }
+          __builtin_amdgcn_sched_barrier(0);     // one 32-row slice at a time
         }
         if constexpr (BCE_SUM) {
-          lg += __builtin_amdgcn_logf(prod);   // log2 of a product of 16 factors in [1, 2]
-          prod = 1.0f;
+          float vsum = relu + lg * kLn2;
+          vsum += __shfl_xor(vsum, 32, 64);
+          if (h == 0 && t_ok) p.part_a[split * p.T + t] = vsum;
         }
-        __builtin_amdgcn_sched_barrier(0);     // one 32-row slice at a time
-      }
-      if constexpr (BCE_SUM) {
-        float vsum = relu + lg * kLn2;
-        vsum += __shfl_xor(vsum, 32, 64);
-        if (h == 0 && t_ok) p.part_a[split * p.T + t] = vsum;
-      }
-      if constexpr (EPI == GEMM_EPI_BCE_METRICS) {
-        cnt += __shfl_xor(cnt, 32, 64);
-        if (h == 0 && t_ok) p.part_b[split * p.T + t] = cnt;
-      }
-      if constexpr (EPI == GEMM_EPI_CE_LSE) {
-        const float m2 = __shfl_xor(mx, 32, 64);
-        const float s2 = __shfl_xor(sm, 32, 64);
-        const float mn = __builtin_fmaxf(mx, m2);
-        float s = 0.0f;
-        if (mn != kNegInf) s = sm * __builtin_amdgcn_exp2f((mx - mn) * kLog2e) + s2 * __builtin_amdgcn_exp2f((m2 - mn) * kLog2e);
-        if (h == 0 && t_ok) {
-          p.part_a[split * p.T + t] = mn;
-          p.part_b[split * p.T + t] = s;
+        if constexpr (EPI == GEMM_EPI_BCE_METRICS) {
+          cnt += __shfl_xor(cnt, 32, 64);
+          if (h == 0 && t_ok) p.part_b[split * p.T + t] = cnt;
+        }
+        if constexpr (EPI == GEMM_EPI_CE_LSE) {
+          const float m2 = __shfl_xor(mx, 32, 64);
+          const float s2 = __shfl_xor(sm, 32, 64);
+          const float mn = __builtin_fmaxf(mx, m2);
+          float s = 0.0f;
+          if (mn != kNegInf) s = sm * __builtin_amdgcn_exp2f((mx - mn) * kLog2e) + s2 * __builtin_amdgcn_exp2f((m2 - mn) * kLog2e);
+          if (h == 0 && t_ok) {
+            p.part_a[split * p.T + t] = mn;
+            p.part_b[split * p.T + t] = s;
+          }
         }
       }
-    }
-    if constexpr (EPI == GEMM_EPI_CE_P) {
-      // gradient filter: flag the output tile when some |P| of any wave reaches the threshold
-      if (p.flags != nullptr && __builtin_amdgcn_ballot_w64(pabs >= p.filter_eps) != 0 && lane == 0)
-        p.flags[(int64_t)tm * p.flag_ld + tn] = p.flag_gen;
-    }
+      if constexpr (EPI == GEMM_EPI_CE_P) {
+        // gradient filter: flag the output tile when some |P| of any wave reaches the threshold
+        if (p.flags != nullptr && __builtin_amdgcn_ballot_w64(pabs >= p.filter_eps) != 0 && lane == 0)
+          p.flags[(int64_t)tm * p.flag_ld + tn] = p.flag_gen;
+      }
+    };
+    // (the CE gradient epilogue keeps its masks: without them it runs out of registers)
+    if (EPI != GEMM_EPI_CE_P && p.v0 + m0 + kBM <= p.V && n0 + BN <= p.T) logit_tile(BoolC<false>{});
+    else logit_tile(BoolC<true>{});
   } else if constexpr (EPI == GEMM_EPI_ACC) {
     float* out = p.acc + (int64_t)tz * p.acc_slice;
 #pragma unroll
