@@ -363,7 +363,7 @@ __device__ __forceinline__ void grad_only(f32x16 (&acc)[MT][D / 32], const FPack
                                           uint32_t boff) {
 #pragma unroll
   for (int it = 0; it < 2 * (D / 32); ++it) {
-    const int nt = it >> 1, kk = it & 1;
+    const int nt = it % (D / 32), kk = it / (D / 32);
     const bf16x8 b = read_col_piece<D>(rb, boff, nt, kk);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt][nt] = mfma32(fi.op(mt, kk), b, acc[mt][nt]);
