@@ -305,3 +305,29 @@ def test_ce_filter_bound_limits():
     assert not z_dA.any() and not z_dE.any()
     m_dA, _ = H.ce_filter_bounds(A, E, target, 0.05)
     assert np.all(m_dA <= b_dA + 1e-15)
+
+
+def test_ce_filter_bound_brackets_brute_force_drop():
+    # drop, by brute force on the materialized softmax, every dense entry below eps and
+    # recompute both gradients: each moves by no more than the bound
+    rng = np.random.default_rng(12)
+    T, D, V = 7, 6, 50
+    A = 1.5 * rng.standard_normal((T, D))
+    E = rng.standard_normal((V, D))
+    target = rng.integers(0, V, size=T)
+    target[4] = -100
+    eps = 0.02
+    valid = target != -100
+    X = A @ E.T
+    S = np.exp(X - H.logsumexp_rows(X)[:, None]) * valid[:, None]
+    Y = np.zeros_like(S)
+    for t in np.nonzero(valid)[0]:
+        Y[t, target[t]] = 1.0
+    kept = np.where(S >= eps, S, 0.0)
+    assert 0 < np.count_nonzero(S < eps) < S.size        # some entries dropped, some kept
+    dA_full, dE_full = (S - Y) @ E, (S - Y).T @ A
+    dA_drop, dE_drop = (kept - Y) @ E, (kept - Y).T @ A
+    b_dA, b_dE = H.ce_filter_bounds(A, E, target, eps)
+    assert np.all(np.abs(dA_full - dA_drop) <= b_dA + 1e-12)
+    assert np.all(np.abs(dE_full - dE_drop) <= b_dE + 1e-12)
+    assert np.allclose(dA_full, H.ce_grads(A, E, target)[0])
