@@ -189,6 +189,16 @@ class Head:
         B.cutloss_ce_fwd(self.prob, self.loss, self.lse, self.ws)
         B.cutloss_ce_bwd_filtered(self.prob, self.lse, None, self.dA, self.dE, eps, self.ws)
 
+    def step_sgd_sr(self):
+        """The SGD step with stochastic rounding of E (a separately measured option); a new
+        seed every call."""
+        B = self.B
+        if getattr(self, "srws", None) is None:
+            self.srws = B.workspace(B.cutloss_bce_workspace_size(self.prob, B.OP_BWD_SGD_SR), self.A.device)
+            self.sr_seed = 0
+        self.sr_seed += 1
+        B.cutloss_bce_bwd_sgd_sr(self.prob, None, self.w.lr, self.sr_seed, self.dA, self.loss, self.srws)
+
     def call_name(self):
         if self.w.kind == "ce":
             return "cutloss_ce_fwd(loss, lse) + cutloss_ce_bwd(dA, dE)"
@@ -293,6 +303,9 @@ def report_all(steps, warmup):
         if w.kind == "bce":
             m_ms, _ = time_calls(h.fwd_metrics, steps, warmup)
             rec["fwd_cut_metrics_ms"] = round(m_ms, 4)
+            if h.sgd:
+                s_ms, _ = time_calls(h.step_sgd_sr, steps, warmup)
+                rec["step_sgd_stochastic_rounding_ms"] = round(s_ms, 4)
         else:
             f_ms, _ = time_calls(h.step_grad_filter, steps, warmup)
             rec["step_grad_filter_2^-12_ms"] = round(f_ms, 4)

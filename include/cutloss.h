@@ -73,7 +73,8 @@ typedef enum {
   CUTLOSS_OP_FWD = 0,
   CUTLOSS_OP_BWD = 1,
   CUTLOSS_OP_BWD_SGD = 2,
-  CUTLOSS_OP_FWD_METRICS = 3
+  CUTLOSS_OP_FWD_METRICS = 3,
+  CUTLOSS_OP_BWD_SGD_SR = 4
 } cutloss_op;
 
 /*
@@ -151,6 +152,22 @@ cutloss_status cutloss_bce_bwd(const cutloss_bce_problem* p, const float* dloss,
 cutloss_status cutloss_bce_bwd_sgd(const cutloss_bce_problem* p, const float* dloss, float lr,
                                    void* dA, float* loss_out,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * As cutloss_bce_bwd_sgd, but E' is rounded stochastically (ELMO summary, Key Contributions 1
+ * and Methodology: stochastic rounding of the BF16 / FP8 classifier weights, so that small
+ * updates are kept on average). With y = E_vd - lr dE_vd (FP8: clamped to +-448) and lo <= y
+ * <= hi its neighbours on E's storage grid, E'_vd = hi exactly when u (hi - lo) < y - lo, where
+ * u = h / 2^16 and h is the 16-bit half-word (d mod 8) (low half first) of the Philox-4x32-10
+ * output (Salmon et al., SC 2011) for counter (d / 8, v mod 2^32, v / 2^32, 0) and key
+ * (seed mod 2^32, seed / 2^32). y on the grid is kept; zero is stored as +0. The result is a
+ * deterministic function of (seed, v, d) and the update; pass a new seed per step. BF16 E
+ * assumes finite, normal-range values. Runs the chunked path for every D.
+ * Workspace: cutloss_bce_workspace_size(p, CUTLOSS_OP_BWD_SGD_SR).
+ */
+cutloss_status cutloss_bce_bwd_sgd_sr(const cutloss_bce_problem* p, const float* dloss, float lr, uint64_t seed,
+                                      void* dA, float* loss_out,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Softmax CE forward: lse[t] = logsumexp_v x_tv (every row), loss[t] = lse[t] - x_{t,y_t}

@@ -1,0 +1,122 @@
+"""GPU parity of the stochastically rounded SGD step (cutloss_bce_bwd_sgd_sr; ELMO, ai.info
+summary: stochastic rounding of the classifier weights) against the oracle's rounding with
+the same Philox uniforms.
+
+The rounding of a fixed uniform is monotone in the value rounded, so E' must lie between the
+oracle's roundings of y_ref -+ lr * tol (tol the dE tolerance, 2e-2 max|dE_ref|); most
+elements must equal the rounding of y_ref itself (fp8: all but 1%; bf16, whose grid is 16x
+finer, all but 15%)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import head_loss as H
+from oracle.stochastic import decode, sr_round, uniform16
+from workloads import make, workload
+from workloads.gen import Workload
+
+from gpu_util import canonical, check_loss, decode_inputs, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    from vocabulary_loss_head_amd import binding
+    return binding
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _run_sr(B, g, w, seed, lr, want_loss=False):
+    prob = B.bce_problem(g["A"], g["E"], g["row_ptr"], g["ids"], g["mask"], w.pad_id)
+    ws = B.workspace(B.cutloss_bce_workspace_size(prob, B.OP_BWD_SGD_SR), g["A"].device)
+    loss = torch.empty(w.T, dtype=torch.float32, device=g["A"].device) if want_loss else None
+    B.cutloss_bce_bwd_sgd_sr(prob, None, lr, seed, None, loss, ws)
+    torch.cuda.synchronize()
+    return loss
+
+
+def _codes(t: torch.Tensor, fmt):
+    if fmt == "fp8":
+        return t.cpu().numpy()
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _check_sr(E_new, E_old, items, dE_ref, lr, seed, fmt):
+    tol = 2e-2 * np.abs(dE_ref).max()
+    D = E_old.shape[1]
+    u = uniform16(np.asarray(items, dtype=np.int64)[:, None], np.arange(D)[None, :], seed)
+    y = decode(E_old, fmt) - lr * dE_ref
+    lo = sr_round(y - lr * tol, u, fmt)
+    hi = sr_round(y + lr * tol, u, fmt)
+    got = decode(E_new, fmt)
+    assert np.all((got >= lo) & (got <= hi)), "SR result outside the rounding interval"
+    exact = sr_round(y, u, fmt)
+    frac = float(np.mean(got != exact))
+    moved = float(np.mean(got != decode(E_old, fmt)))
+    print(f"[sr] {fmt}: differing from SR(E - lr dE_ref): {frac:.2e}; elements changed: {moved:.3f}")
+    # a decision flips where u (hi - lo) lies within lr |dE_gpu - dE_ref| of y - lo: the bf16
+    # grid is 16x finer than E4M3's, so flips are 16x as frequent (measured ~9% against ~0.1%)
+    assert frac < (1e-2 if fmt == "fp8" else 0.15)
+
+
+@pytest.mark.parametrize("fmt,D", [("fp8", 128), ("fp8", 768), ("bf16", 256), ("bf16", 320)])
+def test_sr_sgd_small(B, fmt, D, monkeypatch):
+    monkeypatch.setenv("CUTLOSS_MAX_CHUNK_ITEMS", "512")
+    _say(f"sr sgd {fmt} T=40 D={D} V=2000")
+    scale = 0.05 if fmt == "fp8" else 0.02
+    w = Workload("sr", "bce", 40, D, 2000, fmt, None, scale, "poisson_distinct", L=5, pad_id=-1, lr=0.01, seed=21 + D)
+    inp = make(w)
+    A64, E64 = decode_inputs(inp)
+    crow, cids, _ = canonical(inp, w.V, -1)
+    g = upload(inp)
+    seed = 0x0123456789ABCDEF + D
+    loss = _run_sr(B, g, w, seed, w.lr, want_loss=True)
+    _, dE_ref = H.bce_grads(A64, E64, crow, cids, inp["mask"])
+    check_loss(loss.cpu().numpy(), H.bce_loss(A64, E64, crow, cids, inp["mask"]), what="sr sgd loss")
+    _check_sr(_codes(g["E"], fmt), inp["E"], np.arange(w.V), dE_ref, w.lr, seed, fmt)
+
+
+def test_sr_deterministic_and_seeded(B, monkeypatch):
+    monkeypatch.setenv("CUTLOSS_MAX_CHUNK_ITEMS", "1024")
+    _say("sr determinism fp8 T=64 D=256 V=3000")
+    w = Workload("srd", "bce", 64, 256, 3000, "fp8", None, 0.05, "poisson_distinct", L=5, pad_id=-1, lr=0.01, seed=5)
+    inp = make(w)
+    outs = []
+    for seed in (7, 7, 8):
+        g = upload(inp)
+        _run_sr(B, g, w, seed, w.lr)
+        outs.append(g["E"].cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    assert not np.array_equal(outs[0], outs[2])
+
+
+def test_sr_zero_lr_keeps_weights(B):
+    _say("sr lr=0 fp8 and bf16")
+    for fmt in ("fp8", "bf16"):
+        w = Workload("sr0", "bce", 32, 128, 1500, fmt, None, 0.05, "poisson_distinct", L=5, pad_id=-1, lr=0.0, seed=6)
+        inp = make(w)
+        g = upload(inp)
+        _run_sr(B, g, w, 1, 0.0)
+        assert np.array_equal(_codes(g["E"], fmt), inp["E"])
+
+
+def test_sr_xmc_full_size_sampled(B):
+    inp = make(workload("xmc_sgd"))
+    w = inp["workload"]
+    _say(f"sr full size T={w.T} D={w.D} V={w.V}")
+    A64, E64 = decode_inputs(inp)
+    crow, cids, _ = canonical(inp, w.V, w.pad_id)
+    g = upload(inp)
+    seed = 2024
+    _run_sr(B, g, w, seed, w.lr)
+    rng = np.random.default_rng(3)
+    items = np.unique(np.concatenate([[0, 1, w.V - 1], np.unique(cids)[:32], rng.choice(w.V, 96, replace=False)]))
+    dE_ref = H.bce_items(A64, E64, crow, cids, items, inp["mask"])
+    E_new = g["E"][torch.from_numpy(items).to(g["E"].device)].cpu().numpy()
+    _check_sr(E_new, inp["E"][items], items, dE_ref, w.lr, seed, "fp8")

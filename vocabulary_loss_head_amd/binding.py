@@ -20,7 +20,7 @@ LIB_PATH = os.environ.get("CUTLOSS_LIBRARY") or os.path.join(_HERE, "libcutloss.
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 BF16, FP8_E4M3 = 0, 1
-OP_FWD, OP_BWD, OP_BWD_SGD, OP_FWD_METRICS = 0, 1, 2, 3
+OP_FWD, OP_BWD, OP_BWD_SGD, OP_FWD_METRICS, OP_BWD_SGD_SR = 0, 1, 2, 3, 4
 
 
 class CutlossError(RuntimeError):
@@ -48,7 +48,7 @@ class CeProblem(ctypes.Structure):
 
 EXPORTED = [
     "cutloss_bce_workspace_size", "cutloss_ce_workspace_size",
-    "cutloss_bce_fwd", "cutloss_bce_fwd_metrics", "cutloss_bce_bwd", "cutloss_bce_bwd_sgd",
+    "cutloss_bce_fwd", "cutloss_bce_fwd_metrics", "cutloss_bce_bwd", "cutloss_bce_bwd_sgd", "cutloss_bce_bwd_sgd_sr",
     "cutloss_ce_fwd", "cutloss_ce_bwd", "cutloss_ce_bwd_filtered",
     "cutloss_read_data_errors", "cutloss_bce_canonical_targets",
     "cutloss_profile_enable", "cutloss_profile_read",
@@ -74,6 +74,7 @@ def _load() -> ctypes.CDLL:
         "cutloss_bce_fwd_metrics": (st, [pb, P, P, P, sz, P]),
         "cutloss_bce_bwd": (st, [pb, P, P, P, P, P, sz, P]),
         "cutloss_bce_bwd_sgd": (st, [pb, P, ctypes.c_float, P, P, P, sz, P]),
+        "cutloss_bce_bwd_sgd_sr": (st, [pb, P, ctypes.c_float, ctypes.c_uint64, P, P, P, sz, P]),
         "cutloss_ce_fwd": (st, [pc, P, P, P, sz, P]),
         "cutloss_ce_bwd": (st, [pc, P, P, P, P, P, sz, P]),
         "cutloss_ce_bwd_filtered": (st, [pc, P, P, P, P, ctypes.c_float, P, sz, P]),
@@ -179,6 +180,12 @@ def cutloss_bce_bwd(problem: BceProblem, dloss, dA, dE, loss_out, ws: torch.Tens
 def cutloss_bce_bwd_sgd(problem: BceProblem, dloss, lr: float, dA, loss_out, ws: torch.Tensor, stream=None) -> None:
     _check(_lib.cutloss_bce_bwd_sgd(ctypes.byref(problem), _ptr(dloss), float(lr), _ptr(dA), _ptr(loss_out),
                                     _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def cutloss_bce_bwd_sgd_sr(problem: BceProblem, dloss, lr: float, seed: int, dA, loss_out, ws: torch.Tensor,
+                           stream=None) -> None:
+    _check(_lib.cutloss_bce_bwd_sgd_sr(ctypes.byref(problem), _ptr(dloss), float(lr), int(seed) & (2 ** 64 - 1),
+                                       _ptr(dA), _ptr(loss_out), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def cutloss_ce_fwd(problem: CeProblem, loss, lse, ws: torch.Tensor, stream=None) -> None:

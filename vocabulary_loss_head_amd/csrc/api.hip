@@ -350,7 +350,8 @@ cutloss_status check_out(const void* ptr, size_t align, const char* name, bool r
 // BCE pipeline shared by fwd / bwd / bwd_sgd.
 // want_loss: emit loss; want_dA; dE_mode: 0 none, 1 write dE, 2 SGD in place
 cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss, float* loss, void* dA, void* dE,
-                               int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st, int32_t* counts);
+                               int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st, int32_t* counts,
+                               int sr = 0, uint64_t sr_seed = 0);
 cutloss_status ce_run_chunked(const cutloss_ce_problem* p, const float* lse_in, const float* dloss, float* loss,
                               float* lse, void* dA, void* dE, void* ws, size_t ws_bytes, hipStream_t st,
                               float filter_eps);
@@ -492,6 +493,7 @@ struct ChunkJob {
   int k3_epi;            // -1: none, GEMM_EPI_DE or GEMM_EPI_SGD
   const int32_t* uitems; const int32_t* counts; const float* S_u;
   void* dE; float lr;
+  int sr; uint64_t sr_seed;   // SGD: stochastic rounding
   int32_t* flags; int64_t flag_ld; int flag_bn; float filter_eps;   // gradient filter (flags NULL: off)
 };
 
@@ -550,6 +552,7 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
       g.v0 = v0; g.V = pl.V; g.T = pl.T; g.D = pl.D;
       g.uitems = j.uitems; g.counts = j.counts; g.S_u = j.S_u;
       g.dE = j.dE; g.E_inplace = (void*)j.E; g.e_fp8 = j.e_fp8; g.lr = j.lr;
+      g.sr = j.sr; g.sr_seed = j.sr_seed;
       g.flags = j.flags; g.flag_ld = j.flag_ld; g.flag_bn = j.flag_bn; g.flag_gen = (int)(c + 1);
       CL_HIP(cl::launch_gemm(g, st), "chunk dE");
     }
@@ -558,7 +561,8 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
 }
 
 cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss, float* loss, void* dA, void* dE,
-                               int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st, int32_t* counts) {
+                               int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st, int32_t* counts,
+                               int sr, uint64_t sr_seed) {
   const ChunkPlan pl = make_chunk_plan(p->T, p->D, p->V, p->nnz);
   const bool grad = dA != nullptr || dE_mode != 0;
   const int e_fp8 = p->e_dtype == CUTLOSS_FP8_E4M3;
@@ -593,6 +597,7 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
   j.w = w.w; j.P = w.P; j.part_a = w.part_a; j.part_b = w.part_b; j.part_dA = w.part_dA; j.Et = w.Et;
   j.k3_epi = dE_mode == 0 ? -1 : (dE_mode == 1 ? cl::GEMM_EPI_DE : cl::GEMM_EPI_SGD);
   j.uitems = w.tw.uitems; j.counts = w.tw.counts; j.S_u = w.S_u; j.dE = dE; j.lr = lr;
+  j.sr = sr; j.sr_seed = sr_seed;
   CL_TRY(run_chunks(j, st));
   if (loss != nullptr || dA != nullptr) {
     Phase ph(CUTLOSS_PHASE_FINALIZE, st);
@@ -681,7 +686,7 @@ size_t cutloss_bce_workspace_size(const cutloss_bce_problem* p, int32_t op) {
   if (check_bce(p) != CUTLOSS_OK) return 0;
   const bool metrics = op == CUTLOSS_OP_FWD_METRICS;
   const bool bwd = op != CUTLOSS_OP_FWD && !metrics;
-  if (use_chunked(p->D, p->e_dtype == CUTLOSS_FP8_E4M3)) {
+  if (op == CUTLOSS_OP_BWD_SGD_SR || use_chunked(p->D, p->e_dtype == CUTLOSS_FP8_E4M3)) {
     const ChunkPlan cp = make_chunk_plan(p->T, p->D, p->V, p->nnz);
     return carve_chunked(nullptr, cp, bwd, bwd, bwd, metrics, true, p->e_dtype != CUTLOSS_FP8_E4M3).bytes;
   }
@@ -737,6 +742,18 @@ cutloss_status cutloss_bce_bwd_sgd(const cutloss_bce_problem* p, const float* dl
   CL_TRY(check_out(loss_out, 4, "loss_out", false));
   if (!(lr == lr)) return fail(CUTLOSS_ERR_INVALID_ARG, "lr is NaN");
   return bce_run(p, dloss, loss_out, dA, nullptr, 2, lr, ws, ws_bytes, (hipStream_t)stream);
+}
+
+cutloss_status cutloss_bce_bwd_sgd_sr(const cutloss_bce_problem* p, const float* dloss, float lr, uint64_t seed,
+                                      void* dA, float* loss_out, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  CL_TRY(check_bce(p));
+  CL_TRY(check_out(dloss, 4, "dloss", false));
+  CL_TRY(check_out(dA, 16, "dA", false));
+  CL_TRY(check_out(loss_out, 4, "loss_out", false));
+  if (!(lr == lr)) return fail(CUTLOSS_ERR_INVALID_ARG, "lr is NaN");
+  // the chunked products carry the rounding, for every head width
+  return bce_run_chunked(p, dloss, loss_out, dA, nullptr, 2, lr, ws, ws_bytes, (hipStream_t)stream, nullptr, 1, seed);
 }
 
 cutloss_status cutloss_ce_fwd(const cutloss_ce_problem* p, float* loss, float* lse, void* ws, size_t ws_bytes, void* stream) {

@@ -197,6 +197,7 @@ struct GemmParams {
   // DE / SGD epilogues
   const int32_t* uitems; const int32_t* counts; const float* S_u; int64_t D;
   void* dE; void* E_inplace; int e_fp8; float lr;
+  int sr; uint64_t sr_seed;  // SGD: stochastic rounding keyed by (sr_seed, v, d) when sr != 0
   // CE gradient filter: the CE_P epilogue sets flags[tm * flag_ld + tn] = flag_gen for an
   // output tile (item tile tm, row tile tn of flag_bn rows) holding some |P| >= filter_eps;
   // the dA and dE products skip the matrix work of a k stage whose P tiles are unflagged.

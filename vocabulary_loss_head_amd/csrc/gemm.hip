@@ -255,6 +255,50 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011): four 32-bit counter words, a
+// two-word key bumped by the Weyl constants between rounds, two 32x32 -> 64-bit products
+// per round.
+__device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c[0]), lo0 = 0xD2511F53u * c[0];
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c[2]), lo1 = 0xCD9E8D57u * c[2];
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
+  }
+}
+
+// Stochastic rounding of y onto a storage grid given its neighbours in magnitude,
+// lo_m <= |y| < lo_m + step (lo_m, step, |y| - lo_m exact): y goes to the upper neighbour
+// on the real line when u step < y - lo, u = h / 2^16. Zero results are +0.
+__device__ __forceinline__ float sr_pick(float y, float lo_m, float step, uint32_t h) {
+  const float m = __builtin_fabsf(y);
+  const float frac = m - lo_m;
+  if (frac == 0.0f) return y + 0.0f;
+  const float us = (float)h * (1.0f / 65536.0f) * step;
+  const bool up = y >= 0.0f ? us < frac : !(us < step - frac);   // magnitude rounds up
+  const float mag = up ? lo_m + step : lo_m;
+  return mag == 0.0f ? 0.0f : __builtin_copysignf(mag, y);
+}
+// OCP E4M3FN: saturate to +-448; spacing 2^-9 below 2^-6, else 3 mantissa bits
+__device__ __forceinline__ float sr_fp8(float y, uint32_t h) {
+  y = __builtin_amdgcn_fmed3f(y, -kFp8Max, kFp8Max);
+  const float m = __builtin_fabsf(y);
+  if (m < 0.015625f) return sr_pick(y, __builtin_floorf(m * 512.0f) * (1.0f / 512.0f), 1.0f / 512.0f, h);
+  const uint32_t b = __float_as_uint(m);
+  return sr_pick(y, __uint_as_float(b & 0xFFF00000u), __uint_as_float((b & 0x7F800000u) - (3u << 23)), h);
+}
+// bf16: 7 stored mantissa bits (finite, normal magnitudes)
+__device__ __forceinline__ float sr_bf16(float y, uint32_t h) {
+  const uint32_t b = __float_as_uint(__builtin_fabsf(y)) & 0xFFFF0000u;
+  const float lo_m = __uint_as_float(b);
+  return sr_pick(y, lo_m, __uint_as_float(b + 0x10000u) - lo_m, h);
+}
+
 // Output tile of workgroup blockIdx.x (grid padded to a multiple of 8). Returns false for
 // padding workgroups.
 __device__ __forceinline__ bool map_tile(int gm, int gn, int gz, int& tm, int& tn, int& tz) {
@@ -610,6 +654,54 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
           uint4* dst = (uint4*)((uint16_t*)p.dE + v * p.D + d0);
           dst[0] = o0;
           dst[1] = o1;
+        } else if (p.sr) {
+          // the 16 uniforms of d0 .. d0 + 15: Philox counters d / 8 (two of them), half-word d % 8
+          uint32_t hw[8];
+          {
+            const uint32_t k0 = (uint32_t)p.sr_seed, k1 = (uint32_t)(p.sr_seed >> 32);
+            uint32_t c0[4] = {(uint32_t)(d0 >> 3), (uint32_t)v, (uint32_t)((uint64_t)v >> 32), 0u};
+            uint32_t c1[4] = {(uint32_t)(d0 >> 3) + 1u, (uint32_t)v, (uint32_t)((uint64_t)v >> 32), 0u};
+            philox4x32_10(c0, k0, k1);
+            philox4x32_10(c1, k0, k1);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) { hw[q] = c0[q]; hw[4 + q] = c1[q]; }
+          }
+          auto h16 = [&](int j) -> uint32_t { return (j & 1) ? (hw[j >> 1] >> 16) : (hw[j >> 1] & 0xFFFFu); };
+          if (p.e_fp8) {
+            uint4* ep = (uint4*)((uint8_t*)p.E_inplace + v * p.D + d0);
+            const uint4 e = *ep;
+            const uint32_t w[4] = {e.x, e.y, e.z, e.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], false);
+              const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], true);
+              const float e0 = sr_fp8(__builtin_fmaf(-p.lr, g[4 * q], lo[0]), h16(4 * q));
+              const float e1 = sr_fp8(__builtin_fmaf(-p.lr, g[4 * q + 1], lo[1]), h16(4 * q + 1));
+              const float e2 = sr_fp8(__builtin_fmaf(-p.lr, g[4 * q + 2], hi[0]), h16(4 * q + 2));
+              const float e3 = sr_fp8(__builtin_fmaf(-p.lr, g[4 * q + 3], hi[1]), h16(4 * q + 3));
+              int r = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);   // exact: grid values
+              r = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, r, true);
+              o[q] = (uint32_t)r;
+            }
+            *ep = uint4{o[0], o[1], o[2], o[3]};
+          } else {
+            uint4* ep = (uint4*)((uint16_t*)p.E_inplace + v * p.D + d0);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const uint4 e = ep[q];
+              const uint32_t w[4] = {e.x, e.y, e.z, e.w};
+              uint32_t o[4];
+#pragma unroll
+              for (int b = 0; b < 4; ++b) {
+                const int j = 8 * q + 2 * b;
+                const float lo = sr_bf16(__builtin_fmaf(-p.lr, g[j], bf16_bits_to_f32(w[b] & 0xffffu)), h16(j));
+                const float hi = sr_bf16(__builtin_fmaf(-p.lr, g[j + 1], bf16_bits_to_f32(w[b] >> 16)), h16(j + 1));
+                o[b] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);   // exact
+              }
+              ep[q] = uint4{o[0], o[1], o[2], o[3]};
+            }
+          }
         } else if (p.e_fp8) {
           uint4* ep = (uint4*)((uint8_t*)p.E_inplace + v * p.D + d0);
           const uint4 e = *ep;
