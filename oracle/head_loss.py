@@ -26,6 +26,11 @@ Fused SGD (ELMO, ai.info summary, Key Contributions: classifier gradients
 fused with the SGD update so they are never stored; momentum-free SGD with FP8
 E4M3 weights): E' = fp8(E - lr dE), nearest-even, saturating.
 
+FP8 logits (ELMO, ai.info summary, Methodology: activations are cast to FP8 only for the
+matmul that produces the logits): X = fp8(A) E^T with fp8 the E4M3FN nearest-even saturating
+cast; the loss and G come from that X, dA = G E, and dE = G^T A with the unrounded A (the
+gradient products are not the logit matmul). ``A_logits`` arguments carry fp8(A).
+
 Sampled forms evaluate the same definitions for chosen rows (one pass
 x_t = E A_t each) or chosen items (x_{:,v} = A E_v each); they are exact per
 sample and let the tests check full-size problems.
@@ -72,10 +77,15 @@ def _valid_rows(T, mask):
 # BCE, full (materializes X; small shapes)
 # ----------------------------------------------------------------------------
 
-def bce_loss(A, E, crow, cids, mask=None):
+def fp8_activations(A):
+    """The E4M3FN values of A (nearest-even, saturating): the logit product's FP8 input."""
+    return decode_fp8_e4m3fn(encode_fp8_e4m3fn(A))
+
+
+def bce_loss(A, E, crow, cids, mask=None, A_logits=None):
     """Per-row BCE loss[T] by the elementwise definition."""
     T, V = A.shape[0], E.shape[0]
-    X = A @ E.T
+    X = (A if A_logits is None else A_logits) @ E.T
     Y = dense_labels(crow, cids, T, V)
     loss = bce_elementwise(X, Y).sum(axis=1)
     return np.where(_valid_rows(T, mask), loss, 0.0)
@@ -90,10 +100,10 @@ def bce_loss_dense_sparse(A, E, crow, cids, mask=None):
     return np.where(_valid_rows(T, mask), dense - sparse, 0.0)
 
 
-def bce_grads(A, E, crow, cids, mask=None, dloss=None):
+def bce_grads(A, E, crow, cids, mask=None, dloss=None, A_logits=None):
     """(dA, dE) of L = sum_t w_t loss_t."""
     T, V = A.shape[0], E.shape[0]
-    X = A @ E.T
+    X = (A if A_logits is None else A_logits) @ E.T
     Y = dense_labels(crow, cids, T, V)
     w = _weights(T, _valid_rows(T, mask), dloss)
     G = w[:, None] * (sigmoid(X) - Y)
@@ -104,11 +114,11 @@ def bce_grads(A, E, crow, cids, mask=None, dloss=None):
 # BCE, sampled (exact per sampled row / item)
 # ----------------------------------------------------------------------------
 
-def bce_rows(A, E, crow, cids, rows, mask=None, dloss=None):
+def bce_rows(A, E, crow, cids, rows, mask=None, dloss=None, A_logits=None):
     """loss[rows] and dA[rows] from x_t = E A_t for each sampled row."""
     T, V = A.shape[0], E.shape[0]
     rows = np.asarray(rows, dtype=np.int64)
-    X = A[rows] @ E.T
+    X = (A if A_logits is None else A_logits)[rows] @ E.T
     Y = np.zeros_like(X)
     for i, t in enumerate(rows):
         Y[i, cids[crow[t]:crow[t + 1]]] = 1.0
@@ -119,11 +129,11 @@ def bce_rows(A, E, crow, cids, rows, mask=None, dloss=None):
     return loss, G @ E
 
 
-def bce_items(A, E, crow, cids, items, mask=None, dloss=None):
+def bce_items(A, E, crow, cids, items, mask=None, dloss=None, A_logits=None):
     """dE[items] from x_{:,v} = A E_v for each sampled item."""
     T = A.shape[0]
     items = np.asarray(items, dtype=np.int64)
-    X = A @ E[items].T
+    X = (A if A_logits is None else A_logits) @ E[items].T
     Y = np.zeros_like(X)
     col = {int(v): j for j, v in enumerate(items)}
     for t in range(T):

@@ -331,3 +331,58 @@ def test_ce_filter_bound_brackets_brute_force_drop():
     assert np.all(np.abs(dA_full - dA_drop) <= b_dA + 1e-12)
     assert np.all(np.abs(dE_full - dE_drop) <= b_dE + 1e-12)
     assert np.allclose(dA_full, H.ce_grads(A, E, target)[0])
+
+
+# ------------------------------------------------------------------ FP8 logits (ELMO)
+
+def test_fp8_logits_reduce_to_plain_on_the_fp8_grid():
+    # activations already on the E4M3FN grid: the cast changes nothing
+    T, D, V = 6, 8, 31
+    A, E, crow, cids, mask, w = _problem(T, D, V, 21, std=0.5)
+    A8 = decode_fp8_e4m3fn(encode_fp8_e4m3fn(A))
+    assert np.array_equal(H.fp8_activations(A8), A8)
+    np.testing.assert_array_equal(H.bce_loss(A8, E, crow, cids, mask, A_logits=H.fp8_activations(A8)),
+                                  H.bce_loss(A8, E, crow, cids, mask))
+    g1 = H.bce_grads(A8, E, crow, cids, mask, w, A_logits=H.fp8_activations(A8))
+    g0 = H.bce_grads(A8, E, crow, cids, mask, w)
+    assert all(np.array_equal(a, b) for a, b in zip(g1, g0))
+
+
+def test_fp8_logits_dE_uses_the_unrounded_activations():
+    # E = 0: every logit is 0 whatever the cast, so G = w (1/2 - y) and dE_v = sum_t G_tv A_t
+    # with A itself (not fp8(A)); A off the fp8 grid tells the two apart
+    T, D, V = 5, 6, 17
+    A, _, crow, cids, mask, w = _problem(T, D, V, 22, std=0.37)
+    assert not np.array_equal(H.fp8_activations(A), A)
+    E = np.zeros((V, D))
+    dA, dE = H.bce_grads(A, E, crow, cids, mask, w, A_logits=H.fp8_activations(A))
+    assert np.all(dA == 0)
+    for v in range(V):
+        want = np.zeros(D)
+        for t in range(T):
+            if mask[t]:
+                y = 1.0 if v in set(cids[crow[t]:crow[t + 1]].tolist()) else 0.0
+                want += w[t] * (0.5 - y) * A[t]
+        np.testing.assert_allclose(dE[v], want, rtol=1e-12, atol=1e-14)
+
+
+def test_fp8_logits_match_torch_autograd_through_the_cast_input():
+    # loss and dA are those of the plain head evaluated at A8 = fp8(A) (torch autograd with A8
+    # as the leaf); dE is G^T A
+    T, D, V = 7, 16, 45
+    A, E, crow, cids, mask, w = _problem(T, D, V, 23, std=1.0)
+    A8 = H.fp8_activations(A)
+    loss_t, dA_t, _ = _torch_bce(A8, E, crow, cids, mask, w)
+    loss = H.bce_loss(A, E, crow, cids, mask, A_logits=A8)
+    dA, dE = H.bce_grads(A, E, crow, cids, mask, w, A_logits=A8)
+    np.testing.assert_allclose(loss, loss_t, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dA, dA_t, rtol=1e-10, atol=1e-12)
+    X = A8 @ E.T
+    G = (w * (mask != 0))[:, None] * (1.0 / (1.0 + np.exp(-X)) - dense_labels(crow, cids, T, V))
+    np.testing.assert_allclose(dE, G.T @ A, rtol=1e-12, atol=1e-14)
+    # sampled forms agree with the full ones
+    lr, dAr = H.bce_rows(A, E, crow, cids, [0, 3], mask, w, A_logits=A8)
+    np.testing.assert_allclose(lr, loss[[0, 3]], rtol=1e-13)
+    np.testing.assert_allclose(dAr, dA[[0, 3]], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(H.bce_items(A, E, crow, cids, [2, 44], mask, w, A_logits=A8), dE[[2, 44]],
+                               rtol=1e-12, atol=1e-15)
