@@ -189,15 +189,16 @@ class Head:
         B.cutloss_ce_fwd(self.prob, self.loss, self.lse, self.ws)
         B.cutloss_ce_bwd_filtered(self.prob, self.lse, None, self.dA, self.dE, eps, self.ws)
 
-    def step_sgd_sr(self):
-        """The SGD step with stochastic rounding of E (a separately measured option); a new
-        seed every call."""
+    def step_sgd_ex(self, stochastic=False, fp8_logits=False):
+        """The SGD step with ELMO's options (separately measured): stochastic rounding of E
+        (a new seed every call) and/or FP8 activations for the logit product."""
         B = self.B
-        if getattr(self, "srws", None) is None:
-            self.srws = B.workspace(B.cutloss_bce_workspace_size(self.prob, B.OP_BWD_SGD_SR), self.A.device)
+        if getattr(self, "exws", None) is None:
+            self.exws = B.workspace(B.cutloss_bce_workspace_size(self.prob, B.OP_BWD_SGD_EX), self.A.device)
             self.sr_seed = 0
         self.sr_seed += 1
-        B.cutloss_bce_bwd_sgd_sr(self.prob, None, self.w.lr, self.sr_seed, self.dA, self.loss, self.srws)
+        B.cutloss_bce_bwd_sgd_ex(self.prob, None, self.w.lr, self.dA, self.loss, self.exws, stochastic=stochastic,
+                                 seed=self.sr_seed, fp8_logits=fp8_logits)
 
     def call_name(self):
         if self.w.kind == "ce":
@@ -304,8 +305,12 @@ def report_all(steps, warmup):
             m_ms, _ = time_calls(h.fwd_metrics, steps, warmup)
             rec["fwd_cut_metrics_ms"] = round(m_ms, 4)
             if h.sgd:
-                s_ms, _ = time_calls(h.step_sgd_sr, steps, warmup)
+                s_ms, _ = time_calls(lambda: h.step_sgd_ex(stochastic=True), steps, warmup)
                 rec["step_sgd_stochastic_rounding_ms"] = round(s_ms, 4)
+                f_ms, _ = time_calls(lambda: h.step_sgd_ex(fp8_logits=True), steps, warmup)
+                rec["step_sgd_fp8_logits_ms"] = round(f_ms, 4)
+                b_ms, _ = time_calls(lambda: h.step_sgd_ex(stochastic=True, fp8_logits=True), steps, warmup)
+                rec["step_sgd_fp8_logits_stochastic_rounding_ms"] = round(b_ms, 4)
         else:
             f_ms, _ = time_calls(h.step_grad_filter, steps, warmup)
             rec["step_grad_filter_2^-12_ms"] = round(f_ms, 4)

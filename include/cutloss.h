@@ -74,8 +74,21 @@ typedef enum {
   CUTLOSS_OP_BWD = 1,
   CUTLOSS_OP_BWD_SGD = 2,
   CUTLOSS_OP_FWD_METRICS = 3,
-  CUTLOSS_OP_BWD_SGD_SR = 4
+  CUTLOSS_OP_BWD_SGD_EX = 4
 } cutloss_op;
+
+/* Rounding of the SGD writeback. */
+typedef enum {
+  CUTLOSS_ROUND_NEAREST_EVEN = 0,
+  CUTLOSS_ROUND_STOCHASTIC = 1
+} cutloss_rounding;
+
+/* Options of cutloss_bce_bwd_sgd_ex (NULL: nearest-even, bf16 x FP8 logits, as cutloss_bce_bwd_sgd). */
+typedef struct {
+  int32_t rounding;     /* cutloss_rounding */
+  uint64_t seed;        /* stochastic rounding key: pass a new seed every step */
+  int32_t fp8_logits;   /* 1: A is cast to FP8 E4M3FN for the logit product (FP8 E only) */
+} cutloss_sgd_options;
 
 /*
  * Multi-label BCE problem. The positives of row t are pos_ids[pos_row_ptr[t] ..
@@ -154,19 +167,25 @@ cutloss_status cutloss_bce_bwd_sgd(const cutloss_bce_problem* p, const float* dl
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * As cutloss_bce_bwd_sgd, but E' is rounded stochastically (ELMO summary, Key Contributions 1
- * and Methodology: stochastic rounding of the BF16 / FP8 classifier weights, so that small
- * updates are kept on average). With y = E_vd - lr dE_vd (FP8: clamped to +-448) and lo <= y
- * <= hi its neighbours on E's storage grid, E'_vd = hi exactly when u (hi - lo) < y - lo, where
- * u = h / 2^16 and h is the 16-bit half-word (d mod 8) (low half first) of the Philox-4x32-10
- * output (Salmon et al., SC 2011) for counter (d / 8, v mod 2^32, v / 2^32, 0) and key
- * (seed mod 2^32, seed / 2^32). y on the grid is kept; zero is stored as +0. The result is a
- * deterministic function of (seed, v, d) and the update; pass a new seed per step. BF16 E
- * assumes finite, normal-range values. Runs the chunked path for every D.
- * Workspace: cutloss_bce_workspace_size(p, CUTLOSS_OP_BWD_SGD_SR).
+ * cutloss_bce_bwd_sgd with ELMO's low-precision options (ELMO summary, Key Contributions 1
+ * and Methodology):
+ *  - rounding = CUTLOSS_ROUND_STOCHASTIC rounds E' stochastically, so that small updates are
+ *    kept on average. With y = E_vd - lr dE_vd (FP8: clamped to +-448) and lo <= y <= hi its
+ *    neighbours on E's storage grid, E'_vd = hi exactly when u (hi - lo) < y - lo, where
+ *    u = h / 2^16 and h is the 16-bit half-word (d mod 8) (low half first) of the
+ *    Philox-4x32-10 output (Salmon et al., SC 2011) for counter (d / 8, v mod 2^32, v / 2^32,
+ *    0) and key (seed mod 2^32, seed / 2^32). y on the grid is kept; zero is stored as +0. The
+ *    result is a deterministic function of (seed, v, d) and the update. BF16 E assumes
+ *    finite, normal-range values.
+ *  - fp8_logits = 1 casts A to FP8 E4M3FN (nearest-even, saturating) for the matmul that
+ *    produces the logits, which then runs on the FP8 MFMA with FP8 E; the loss and
+ *    G = w (sigmoid(X) - Y) come from those logits, dA = G E, and dE = G^T A uses A itself.
+ *    Requires FP8 E (CUTLOSS_ERR_UNSUPPORTED otherwise).
+ * Runs the chunked path for every D. Workspace: cutloss_bce_workspace_size(p,
+ * CUTLOSS_OP_BWD_SGD_EX), which covers every option.
  */
-cutloss_status cutloss_bce_bwd_sgd_sr(const cutloss_bce_problem* p, const float* dloss, float lr, uint64_t seed,
-                                      void* dA, float* loss_out,
+cutloss_status cutloss_bce_bwd_sgd_ex(const cutloss_bce_problem* p, const float* dloss, float lr,
+                                      const cutloss_sgd_options* opt, void* dA, float* loss_out,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*

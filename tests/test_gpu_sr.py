@@ -1,4 +1,4 @@
-"""GPU parity of the stochastically rounded SGD step (cutloss_bce_bwd_sgd_sr; ELMO, ai.info
+"""GPU parity of the stochastically rounded SGD step (cutloss_bce_bwd_sgd_ex with stochastic rounding; ELMO, ai.info
 summary: stochastic rounding of the classifier weights) against the oracle's rounding with
 the same Philox uniforms.
 
@@ -34,9 +34,9 @@ def _say(msg):
 
 def _run_sr(B, g, w, seed, lr, want_loss=False):
     prob = B.bce_problem(g["A"], g["E"], g["row_ptr"], g["ids"], g["mask"], w.pad_id)
-    ws = B.workspace(B.cutloss_bce_workspace_size(prob, B.OP_BWD_SGD_SR), g["A"].device)
+    ws = B.workspace(B.cutloss_bce_workspace_size(prob, B.OP_BWD_SGD_EX), g["A"].device)
     loss = torch.empty(w.T, dtype=torch.float32, device=g["A"].device) if want_loss else None
-    B.cutloss_bce_bwd_sgd_sr(prob, None, lr, seed, None, loss, ws)
+    B.cutloss_bce_bwd_sgd_ex(prob, None, lr, None, loss, ws, stochastic=True, seed=seed)
     torch.cuda.synchronize()
     return loss
 

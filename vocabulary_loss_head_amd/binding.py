@@ -20,7 +20,8 @@ LIB_PATH = os.environ.get("CUTLOSS_LIBRARY") or os.path.join(_HERE, "libcutloss.
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 BF16, FP8_E4M3 = 0, 1
-OP_FWD, OP_BWD, OP_BWD_SGD, OP_FWD_METRICS, OP_BWD_SGD_SR = 0, 1, 2, 3, 4
+OP_FWD, OP_BWD, OP_BWD_SGD, OP_FWD_METRICS, OP_BWD_SGD_EX = 0, 1, 2, 3, 4
+ROUND_NEAREST_EVEN, ROUND_STOCHASTIC = 0, 1
 
 
 class CutlossError(RuntimeError):
@@ -46,9 +47,13 @@ class CeProblem(ctypes.Structure):
     ]
 
 
+class SgdOptions(ctypes.Structure):
+    _fields_ = [("rounding", ctypes.c_int32), ("seed", ctypes.c_uint64), ("fp8_logits", ctypes.c_int32)]
+
+
 EXPORTED = [
     "cutloss_bce_workspace_size", "cutloss_ce_workspace_size",
-    "cutloss_bce_fwd", "cutloss_bce_fwd_metrics", "cutloss_bce_bwd", "cutloss_bce_bwd_sgd", "cutloss_bce_bwd_sgd_sr",
+    "cutloss_bce_fwd", "cutloss_bce_fwd_metrics", "cutloss_bce_bwd", "cutloss_bce_bwd_sgd", "cutloss_bce_bwd_sgd_ex",
     "cutloss_ce_fwd", "cutloss_ce_bwd", "cutloss_ce_bwd_filtered",
     "cutloss_read_data_errors", "cutloss_bce_canonical_targets",
     "cutloss_profile_enable", "cutloss_profile_read",
@@ -74,7 +79,7 @@ def _load() -> ctypes.CDLL:
         "cutloss_bce_fwd_metrics": (st, [pb, P, P, P, sz, P]),
         "cutloss_bce_bwd": (st, [pb, P, P, P, P, P, sz, P]),
         "cutloss_bce_bwd_sgd": (st, [pb, P, ctypes.c_float, P, P, P, sz, P]),
-        "cutloss_bce_bwd_sgd_sr": (st, [pb, P, ctypes.c_float, ctypes.c_uint64, P, P, P, sz, P]),
+        "cutloss_bce_bwd_sgd_ex": (st, [pb, P, ctypes.c_float, ctypes.POINTER(SgdOptions), P, P, P, sz, P]),
         "cutloss_ce_fwd": (st, [pc, P, P, P, sz, P]),
         "cutloss_ce_bwd": (st, [pc, P, P, P, P, P, sz, P]),
         "cutloss_ce_bwd_filtered": (st, [pc, P, P, P, P, ctypes.c_float, P, sz, P]),
@@ -182,10 +187,12 @@ def cutloss_bce_bwd_sgd(problem: BceProblem, dloss, lr: float, dA, loss_out, ws:
                                     _ptr(ws), ws.numel(), _stream(stream)))
 
 
-def cutloss_bce_bwd_sgd_sr(problem: BceProblem, dloss, lr: float, seed: int, dA, loss_out, ws: torch.Tensor,
-                           stream=None) -> None:
-    _check(_lib.cutloss_bce_bwd_sgd_sr(ctypes.byref(problem), _ptr(dloss), float(lr), int(seed) & (2 ** 64 - 1),
-                                       _ptr(dA), _ptr(loss_out), _ptr(ws), ws.numel(), _stream(stream)))
+def cutloss_bce_bwd_sgd_ex(problem: BceProblem, dloss, lr: float, dA, loss_out, ws: torch.Tensor, *,
+                           stochastic: bool = False, seed: int = 0, fp8_logits: bool = False, stream=None) -> None:
+    opt = SgdOptions(ROUND_STOCHASTIC if stochastic else ROUND_NEAREST_EVEN, int(seed) & (2 ** 64 - 1),
+                     1 if fp8_logits else 0)
+    _check(_lib.cutloss_bce_bwd_sgd_ex(ctypes.byref(problem), _ptr(dloss), float(lr), ctypes.byref(opt), _ptr(dA),
+                                       _ptr(loss_out), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def cutloss_ce_fwd(problem: CeProblem, loss, lse, ws: torch.Tensor, stream=None) -> None:

@@ -193,13 +193,14 @@ struct ChunkPlan {
   int64_t sk;         // split-K slices of the dA product
   int64_t kps;        // items per slice
   int64_t flag_bn, flag_ld;   // gradient filter flags: row tile of the logits product, row tiles
+  bool q8;            // FP8 logits: the logits product multiplies FP8 activations and FP8 E
 };
 
 constexpr int64_t kChunkPBytes = 2ll << 30;     // P buffer budget
 
-ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap) {
+ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap, bool q8 = false) {
   ChunkPlan c{};
-  c.T = T; c.D = D; c.V = V; c.cap = cap;
+  c.T = T; c.D = D; c.V = V; c.cap = cap; c.q8 = q8;
   const int64_t bm = cl::gemm_tile_m();
   c.bt = round_up(T > 0 ? T : 1, 128) <= 128 ? 128 : 256;
   c.Tp = round_up(T > 0 ? T : 1, c.bt);
@@ -214,7 +215,7 @@ ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap) {
   if (vc > round_up(V, bm)) vc = round_up(V, bm);
   c.Vc = vc;
   c.n_chunks = ceil_div(V, vc);
-  c.n_splits = ceil_div(V, bm) * cl::gemm_k1_warps_m(T, D);
+  c.n_splits = ceil_div(V, bm) * cl::gemm_k1_warps_m(T, D, q8);
   // dA product: (row tiles) x (D tiles) x slices, about 1024 workgroups
   const int64_t tiles = ceil_div(T > 0 ? T : 1, bm) * ceil_div(D, cl::gemm_tile_n_of(cl::GEMM_EPI_ACC, T, D, D));
   int64_t sk = ceil_div(1024, tiles);
@@ -243,6 +244,7 @@ struct Ws2 {
   float* red;         // staging of the split reductions
   int32_t* flags;     // gradient filter: [Vc / 256][flag_ld]
   uint16_t* Et;       // the chunk's bf16 E transposed, [D][Vc] (the dA product's k-contiguous operand)
+  uint8_t* A8;        // FP8 logits: E4M3FN copy of A [T][D]
   size_t bytes;
 };
 
@@ -287,6 +289,7 @@ Ws2 carve_chunked(void* base, const ChunkPlan& pl, bool need_P, bool need_dA, bo
   w.red = c.take<float>(std::max<size_t>(1, std::max(red_loss, red_dA)));
   w.flags = need_P ? c.take<int32_t>((size_t)(pl.Vc / 256) * pl.flag_ld) : nullptr;
   w.Et = need_dA && need_Et ? c.take<uint16_t>((size_t)pl.Vc * pl.D) : nullptr;
+  w.A8 = pl.q8 ? c.take<uint8_t>((size_t)T * pl.D) : nullptr;
   w.bytes = c.off;
   return w;
 }
@@ -351,7 +354,7 @@ cutloss_status check_out(const void* ptr, size_t align, const char* name, bool r
 // want_loss: emit loss; want_dA; dE_mode: 0 none, 1 write dE, 2 SGD in place
 cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss, float* loss, void* dA, void* dE,
                                int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st, int32_t* counts,
-                               int sr = 0, uint64_t sr_seed = 0);
+                               int sr = 0, uint64_t sr_seed = 0, bool fp8_logits = false);
 cutloss_status ce_run_chunked(const cutloss_ce_problem* p, const float* lse_in, const float* dloss, float* loss,
                               float* lse, void* dA, void* dE, void* ws, size_t ws_bytes, hipStream_t st,
                               float filter_eps);
@@ -490,6 +493,7 @@ struct ChunkJob {
   uint16_t* P; float* part_a; float* part_b;
   float* part_dA;        // NULL: no dA
   uint16_t* Et;          // bf16 E: workspace for the transposed chunk
+  const uint8_t* A8;     // FP8 logits: the activations' E4M3FN copy
   int k3_epi;            // -1: none, GEMM_EPI_DE or GEMM_EPI_SGD
   const int32_t* uitems; const int32_t* counts; const float* S_u;
   void* dE; float lr;
@@ -510,14 +514,14 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
       Phase ph(CUTLOSS_PHASE_CHUNK_LOGITS, st);
       cl::GemmParams g{};
       g.a = operand(Ec, pl.D, vlen, pl.D, 1, j.e_fp8);
-      g.b = operand(j.A, pl.D, pl.T, pl.D, 1, 0);
+      g.b = j.A8 != nullptr ? operand(j.A8, pl.D, pl.T, pl.D, 1, 1) : operand(j.A, pl.D, pl.T, pl.D, 1, 0);
       // columns t < T (tiles past T would start outside A); P rows T .. tile end are written as 0
       g.M = mc; g.N = pl.T; g.K = pl.D; g.k_per_split = pl.D;
       g.epi = j.k1_epi;
       g.v0 = v0; g.V = pl.V; g.T = pl.T; g.D = pl.D;
       g.w = j.w; g.lse = j.lse; g.P = j.P; g.p_bt = (int)pl.bt; g.p_nvb = pl.Vc / 32; g.p_rows = pl.Tp;
       g.part_a = j.part_a; g.part_b = j.part_b;
-      g.part_base = (v0 / bm) * cl::gemm_k1_warps_m(pl.T, pl.D);
+      g.part_base = (v0 / bm) * cl::gemm_k1_warps_m(pl.T, pl.D, pl.q8);
       g.flags = j.flags; g.flag_ld = j.flag_ld; g.flag_bn = j.flag_bn; g.flag_gen = (int)(c + 1);
       g.filter_eps = j.filter_eps;
       CL_HIP(cl::launch_gemm(g, st), "chunk logits");
@@ -562,8 +566,8 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
 
 cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss, float* loss, void* dA, void* dE,
                                int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st, int32_t* counts,
-                               int sr, uint64_t sr_seed) {
-  const ChunkPlan pl = make_chunk_plan(p->T, p->D, p->V, p->nnz);
+                               int sr, uint64_t sr_seed, bool fp8_logits) {
+  const ChunkPlan pl = make_chunk_plan(p->T, p->D, p->V, p->nnz, fp8_logits);
   const bool grad = dA != nullptr || dE_mode != 0;
   const int e_fp8 = p->e_dtype == CUTLOSS_FP8_E4M3;
   const Ws2 w = carve_chunked(ws, pl, grad, dA != nullptr, dE_mode != 0, counts != nullptr, true, !e_fp8);
@@ -582,8 +586,10 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
   fp.part_a = w.part_a; fp.part_dA = w.part_dA; fp.loss = loss; fp.dA = dA; fp.w_out = w.w;
   fp.pos_dot = w.pos_dot; fp.pos_sum = w.pos_sum;
   fp.part_c = w.part_b; fp.counts = counts; fp.pos_tp = counts ? w.pos_tp : nullptr;
+  fp.A8 = w.A8;
   {
     Phase ph(CUTLOSS_PHASE_ITEM_SUMS, st);
+    if (w.A8 != nullptr) CL_HIP(cl::launch_cast_fp8((const uint16_t*)p->A, p->T * p->D, w.A8, st), "fp8 activations");
     CL_HIP(cl::launch_row_weights(fp, 0, st), "row weights");
     // positive-row terms read E before any chunk's SGD step changes it
     CL_HIP(cl::launch_row_positives(fp, st), "row positives");
@@ -595,6 +601,7 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
   j.pl = &pl; j.A = p->A; j.E = p->E; j.e_fp8 = e_fp8;
   j.k1_epi = grad ? cl::GEMM_EPI_BCE_P : (counts ? cl::GEMM_EPI_BCE_METRICS : cl::GEMM_EPI_BCE_LOSS);
   j.w = w.w; j.P = w.P; j.part_a = w.part_a; j.part_b = w.part_b; j.part_dA = w.part_dA; j.Et = w.Et;
+  j.A8 = w.A8;
   j.k3_epi = dE_mode == 0 ? -1 : (dE_mode == 1 ? cl::GEMM_EPI_DE : cl::GEMM_EPI_SGD);
   j.uitems = w.tw.uitems; j.counts = w.tw.counts; j.S_u = w.S_u; j.dE = dE; j.lr = lr;
   j.sr = sr; j.sr_seed = sr_seed;
@@ -686,7 +693,16 @@ size_t cutloss_bce_workspace_size(const cutloss_bce_problem* p, int32_t op) {
   if (check_bce(p) != CUTLOSS_OK) return 0;
   const bool metrics = op == CUTLOSS_OP_FWD_METRICS;
   const bool bwd = op != CUTLOSS_OP_FWD && !metrics;
-  if (op == CUTLOSS_OP_BWD_SGD_SR || use_chunked(p->D, p->e_dtype == CUTLOSS_FP8_E4M3)) {
+  if (op == CUTLOSS_OP_BWD_SGD_EX) {   // either rounding, with or without FP8 logits
+    size_t b = 0;
+    for (const bool q8 : {false, true}) {
+      if (q8 && p->e_dtype != CUTLOSS_FP8_E4M3) continue;
+      const ChunkPlan cp = make_chunk_plan(p->T, p->D, p->V, p->nnz, q8);
+      b = std::max(b, carve_chunked(nullptr, cp, true, true, true, false, true, p->e_dtype != CUTLOSS_FP8_E4M3).bytes);
+    }
+    return b;
+  }
+  if (use_chunked(p->D, p->e_dtype == CUTLOSS_FP8_E4M3)) {
     const ChunkPlan cp = make_chunk_plan(p->T, p->D, p->V, p->nnz);
     return carve_chunked(nullptr, cp, bwd, bwd, bwd, metrics, true, p->e_dtype != CUTLOSS_FP8_E4M3).bytes;
   }
@@ -744,16 +760,24 @@ cutloss_status cutloss_bce_bwd_sgd(const cutloss_bce_problem* p, const float* dl
   return bce_run(p, dloss, loss_out, dA, nullptr, 2, lr, ws, ws_bytes, (hipStream_t)stream);
 }
 
-cutloss_status cutloss_bce_bwd_sgd_sr(const cutloss_bce_problem* p, const float* dloss, float lr, uint64_t seed,
-                                      void* dA, float* loss_out, void* ws, size_t ws_bytes, void* stream) {
+cutloss_status cutloss_bce_bwd_sgd_ex(const cutloss_bce_problem* p, const float* dloss, float lr,
+                                      const cutloss_sgd_options* opt, void* dA, float* loss_out, void* ws,
+                                      size_t ws_bytes, void* stream) {
   g_last_error.clear();
   CL_TRY(check_bce(p));
   CL_TRY(check_out(dloss, 4, "dloss", false));
   CL_TRY(check_out(dA, 16, "dA", false));
   CL_TRY(check_out(loss_out, 4, "loss_out", false));
   if (!(lr == lr)) return fail(CUTLOSS_ERR_INVALID_ARG, "lr is NaN");
-  // the chunked products carry the rounding, for every head width
-  return bce_run_chunked(p, dloss, loss_out, dA, nullptr, 2, lr, ws, ws_bytes, (hipStream_t)stream, nullptr, 1, seed);
+  const cutloss_sgd_options o = opt != nullptr ? *opt : cutloss_sgd_options{0, 0, 0};
+  if (o.rounding != CUTLOSS_ROUND_NEAREST_EVEN && o.rounding != CUTLOSS_ROUND_STOCHASTIC)
+    return fail(CUTLOSS_ERR_INVALID_ARG, "rounding must be CUTLOSS_ROUND_NEAREST_EVEN or CUTLOSS_ROUND_STOCHASTIC");
+  if (o.fp8_logits != 0 && o.fp8_logits != 1) return fail(CUTLOSS_ERR_INVALID_ARG, "fp8_logits must be 0 or 1");
+  if (o.fp8_logits && p->e_dtype != CUTLOSS_FP8_E4M3)
+    return fail(CUTLOSS_ERR_UNSUPPORTED, "FP8 logits need FP8 E");
+  // the chunked products carry both options, for every head width
+  return bce_run_chunked(p, dloss, loss_out, dA, nullptr, 2, lr, ws, ws_bytes, (hipStream_t)stream, nullptr,
+                         o.rounding == CUTLOSS_ROUND_STOCHASTIC, o.seed, o.fp8_logits != 0);
 }
 
 cutloss_status cutloss_ce_fwd(const cutloss_ce_problem* p, float* loss, float* lse, void* ws, size_t ws_bytes, void* stream) {

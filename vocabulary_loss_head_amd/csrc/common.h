@@ -158,7 +158,8 @@ struct GemmOperand {
   const void* p;
   int64_t ld, rows_valid, cols_valid;
   int kc;      // 1: [M or N][K]; 0: [K][M or N]
-  int fp8;     // OCP E4M3FN storage (widened to bf16 when staged)
+  int fp8;     // OCP E4M3FN storage (widened to bf16 when staged; with both operands FP8
+               // and k-contiguous, copied as they are and multiplied by the FP8 MFMA)
   // bt > 0: blocked bf16 storage of the chunk's gradient tile P[t][v] (t = the stored row
   // index, v = the column): element (t, v) at ((t / bt) * nvb + v / 32) * bt * 32
   // + (t % bt) * 32 + v % 32, i.e. bt x 32 blocks, contiguous, ld unused
@@ -207,12 +208,14 @@ struct GemmParams {
 hipError_t launch_gemm(const GemmParams& p, hipStream_t st);
 // Et[d][v] = E[v][d] (bf16) for v < vlen, 0 for vlen <= v < mc; Et rows hold ld >= mc items.
 // mc and D multiples of 64, ld a multiple of 8.
+// A8 = E4M3FN(A), nearest-even, saturating at +-448; n a multiple of 8
+hipError_t launch_cast_fp8(const uint16_t* A, int64_t n, uint8_t* A8, hipStream_t st);
 hipError_t launch_transpose_chunk(const uint16_t* E, int64_t vlen, int64_t mc, int64_t D, uint16_t* Et, int64_t ld,
                                   hipStream_t st);
 int gemm_tile_m();                     // 256
 int gemm_tile_n_of(int epi, int64_t M, int64_t N, int64_t D);   // 128 or 256 for that product
 // waves along M of the logits product (row partials per item tile) for T rows, head D
-int gemm_k1_warps_m(int64_t T, int64_t D);
+int gemm_k1_warps_m(int64_t T, int64_t D, bool fp8_fp8 = false);
 
 struct FinalizeParams {
   int64_t T, D, V;
@@ -234,6 +237,9 @@ struct FinalizeParams {
   // per-row positives with a positive logit (pos_tp, from k_row_positives when set), and
   // the output counts[T][4] = (TP, FP, FN, TN)
   const float* part_c; int32_t* pos_tp; int32_t* counts;
+  // FP8 logits: the activations' E4M3FN copy [T][D] that the logit product uses; the
+  // positive rows' logits are taken from it as well
+  const uint8_t* A8;
 };
 hipError_t launch_row_positives(const FinalizeParams& p, hipStream_t st);
 // kind: 0 = BCE, 1 = CE

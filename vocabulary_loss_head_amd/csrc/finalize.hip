@@ -62,7 +62,8 @@ __global__ __launch_bounds__(256) void k_finalize_rows(const FinalizeParams p, i
         float part = 0.0f;
         for (int k = 0; k < nd; ++k) {
           const int64_t d = lane + 64 * k;
-          part += bf16_bits_to_f32(A[t * D + d]) * load_e(p.E, p.e_fp8, v * D + d);
+          const float a = p.A8 != nullptr ? load_e(p.A8, 1, t * D + d) : bf16_bits_to_f32(A[t * D + d]);
+          part += a * load_e(p.E, p.e_fp8, v * D + d);
         }
         const float x = wave_sum(part);
         sum_x += x;
@@ -150,7 +151,8 @@ __global__ __launch_bounds__(256) void k_row_positives(const FinalizeParams p) {
     float part = 0.0f;
     for (int k = 0; k < nd; ++k) {
       const int64_t d = lane + 64 * k;
-      part += bf16_bits_to_f32(A[t * D + d]) * load_e(p.E, p.e_fp8, v * D + d);
+      const float a = p.A8 != nullptr ? load_e(p.A8, 1, t * D + d) : bf16_bits_to_f32(A[t * D + d]);
+      part += a * load_e(p.E, p.e_fp8, v * D + d);
     }
     const float x = wave_sum(part);
     sum_x += x;

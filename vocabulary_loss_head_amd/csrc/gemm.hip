@@ -34,6 +34,7 @@ namespace cl {
 namespace {
 
 constexpr int kBK = 32;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 // Two workgroup shapes: NW = 8 waves with a 4-deep ring (one workgroup per CU), and NW = 4
 // waves with 256 x 128 tiles and a 3-deep ring (72 KB of LDS, two workgroups per CU, so one
 // can run its MFMAs while the other is in its epilogue).
@@ -96,11 +97,13 @@ struct Tile {
 // address of element (outer0, k0) (KC) or (k0, outer0) (KR). Offsets clamp the outer
 // index into the valid range once; a stage that reaches past the valid k range (only the
 // last stages of some products) recomputes them with the k clamp as well.
-template <int NW, int R, bool KC, bool F8>
+template <int NW, int R, bool KC, bool F8, bool Q8 = false>
 struct Loader {
   using TL = Tile<NW, R, KC>;
   static constexpr int N = F8 ? TL::PIECES : TL::PER_WAVE;
-  static constexpr int ESZ = F8 ? 1 : 2;
+  static constexpr int ESZ = (F8 || Q8) ? 1 : 2;
+  static constexpr int EPP = Q8 ? 16 : 8;              // elements per 16-byte LDS piece
+  static constexpr int BK = Q8 ? 64 : kBK;             // k elements per stage
   uint32_t off[N];
 
   __device__ __forceinline__ static int byte_of(int j, int wv, int lane, int tid) {
@@ -108,7 +111,7 @@ struct Loader {
   }
   __device__ __forceinline__ static void rc(int byte, int& r, int& c) {
     r = byte / TL::ROW;
-    c = 8 * TL::phys((byte % TL::ROW) / 16, r);
+    c = EPP * TL::phys((byte % TL::ROW) / 16, r);
   }
   __device__ __forceinline__ void init(const GemmOperand& op, int64_t outer0, int wv, int lane, int tid) {
 #pragma unroll
@@ -145,7 +148,7 @@ struct Loader {
   // blocked operands are fully valid over the k range (checked by the launcher)
   __device__ __forceinline__ static bool tail(const GemmOperand& op, int64_t k0) {
     if (op.bt > 0) return false;
-    return KC ? k0 + kBK > op.cols_valid : k0 + kBK > op.rows_valid;
+    return KC ? k0 + BK > op.cols_valid : k0 + BK > op.rows_valid;
   }
   // element offset from origin(k0) with every index clamped
   __device__ __forceinline__ static int64_t clamped(const GemmOperand& op, int64_t outer0, int64_t k0, int byte) {
@@ -154,7 +157,7 @@ struct Loader {
     int64_t row, col;
     if constexpr (KC) {
       row = min(outer0 + r, op.rows_valid - 1);
-      col = min(k0 + c, op.cols_valid - 8);
+      col = min(k0 + c, op.cols_valid - EPP);
       return (row - outer0) * op.ld + (col - k0);
     } else {
       row = min(k0 + r, op.rows_valid - 1);
@@ -164,23 +167,23 @@ struct Loader {
   }
 };
 
-template <int NW, int R, bool KC>
-__device__ __forceinline__ void dma_stage(const Loader<NW, R, KC, false>& ld, const GemmOperand& op, int64_t outer0,
+template <int NW, int R, bool KC, bool Q8 = false>
+__device__ __forceinline__ void dma_stage(const Loader<NW, R, KC, false, Q8>& ld, const GemmOperand& op, int64_t outer0,
                                           int64_t k0, uint32_t lds, int wv, int lane) {
   using TL = Tile<NW, R, KC>;
-  using LD = Loader<NW, R, KC, false>;
+  using LD = Loader<NW, R, KC, false, Q8>;
   const char* org = LD::origin(op, outer0, k0);
   if (!LD::tail(op, k0)) {
 #pragma unroll
     for (int j = 0; j < TL::PER_WAVE; ++j)
-      __builtin_amdgcn_global_load_lds((const CL_GAS void*)(org + 2 * (size_t)ld.off[j]),
+      __builtin_amdgcn_global_load_lds((const CL_GAS void*)(org + LD::ESZ * (size_t)ld.off[j]),
                                        (CL_LDS void*)(uintptr_t)(lds + (wv * TL::PER_WAVE + j) * 1024), 16, 0, 0);
   } else {
 #pragma unroll
     for (int j = 0; j < TL::PER_WAVE; ++j) {
       const int kb = wv * TL::PER_WAVE + j;
       const int64_t o = LD::clamped(op, outer0, k0, kb * 1024 + 16 * lane);
-      __builtin_amdgcn_global_load_lds((const CL_GAS void*)(org + 2 * o), (CL_LDS void*)(uintptr_t)(lds + kb * 1024),
+      __builtin_amdgcn_global_load_lds((const CL_GAS void*)(org + LD::ESZ * o), (CL_LDS void*)(uintptr_t)(lds + kb * 1024),
                                        16, 0, 0);
     }
   }
@@ -245,6 +248,29 @@ struct Frag {
   }
 };
 
+// FP8 x FP8 operand fragments (v_mfma_scale_f32_32x32x64_f8f6f4, both operands E4M3): a
+// k-contiguous stage row holds 64 FP8 values in four 16-byte pieces, and lane (l32, h) takes
+// row l32 of the block, k = 32 h + 0..31: logical pieces 2h and 2h + 1 (two ds_read_b128).
+template <int NW, int R>
+struct Frag8 {
+  uint32_t p0, p1;
+  __device__ __forceinline__ void init(uint32_t blk0_off, int lane) {
+    using TL = Tile<NW, R, true>;
+    const int h = lane >> 5, r = lane & 31;
+    const int sw = (r >> 2) & 3;                 // + 32 blk leaves (r >> 2) & 3 unchanged
+    p0 = blk0_off + r * TL::ROW + 16 * ((2 * h) ^ sw);
+    p1 = blk0_off + r * TL::ROW + 16 * ((2 * h + 1) ^ sw);
+  }
+  __device__ __forceinline__ i32x8 read(uint32_t stage_off, int blk) const {
+    using TL = Tile<NW, R, true>;
+    const uint32_t o = stage_off + (uint32_t)(blk * 32 * TL::ROW);
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    const i32x4 x = *lds_ptr<i32x4>(p0 + o);
+    const i32x4 y = *lds_ptr<i32x4>(p1 + o);
+    return i32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  }
+};
+
 template <int NW, int BN> struct WaveGrid;
 template <> struct WaveGrid<8, 256> { static constexpr int WM = 2, WN = 4; };
 template <> struct WaveGrid<8, 128> { static constexpr int WM = 4, WN = 2; };
@@ -265,8 +291,9 @@ __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uin
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
     }
-    const uint32_t hi0 = __umulhi(0xD2511F53u, c[0]), lo0 = 0xD2511F53u * c[0];
-    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c[2]), lo1 = 0xCD9E8D57u * c[2];
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0], p1 = (uint64_t)0xCD9E8D57u * c[2];   // one v_mad_u64_u32 each
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
     const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
     c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
   }
@@ -275,10 +302,10 @@ __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uin
 // Stochastic rounding of y onto a storage grid given its neighbours in magnitude,
 // lo_m <= |y| < lo_m + step (lo_m, step, |y| - lo_m exact): y goes to the upper neighbour
 // on the real line when u step < y - lo, u = h / 2^16. Zero results are +0.
+// (y on the grid: frac = 0 keeps lo_m = |y| on both sides, since u step < step)
 __device__ __forceinline__ float sr_pick(float y, float lo_m, float step, uint32_t h) {
   const float m = __builtin_fabsf(y);
   const float frac = m - lo_m;
-  if (frac == 0.0f) return y + 0.0f;
   const float us = (float)h * (1.0f / 65536.0f) * step;
   const bool up = y >= 0.0f ? us < frac : !(us < step - frac);   // magnitude rounds up
   const float mag = up ? lo_m + step : lo_m;
@@ -288,9 +315,11 @@ __device__ __forceinline__ float sr_pick(float y, float lo_m, float step, uint32
 __device__ __forceinline__ float sr_fp8(float y, uint32_t h) {
   y = __builtin_amdgcn_fmed3f(y, -kFp8Max, kFp8Max);
   const float m = __builtin_fabsf(y);
-  if (m < 0.015625f) return sr_pick(y, __builtin_floorf(m * 512.0f) * (1.0f / 512.0f), 1.0f / 512.0f, h);
   const uint32_t b = __float_as_uint(m);
-  return sr_pick(y, __uint_as_float(b & 0xFFF00000u), __uint_as_float((b & 0x7F800000u) - (3u << 23)), h);
+  const bool sub = m < 0.015625f;
+  const float lo_m = sub ? __builtin_floorf(m * 512.0f) * (1.0f / 512.0f) : __uint_as_float(b & 0xFFF00000u);
+  const float step = sub ? 1.0f / 512.0f : __uint_as_float((b & 0x7F800000u) - (3u << 23));
+  return sr_pick(y, lo_m, step, h);
 }
 // bf16: 7 stored mantissa bits (finite, normal magnitudes)
 __device__ __forceinline__ float sr_bf16(float y, uint32_t h) {
@@ -317,8 +346,12 @@ __device__ __forceinline__ bool map_tile(int gm, int gn, int gz, int& tm, int& t
   return true;
 }
 
-template <int NW, int BN, bool AKC, bool BKC, bool AF8, bool BF8, int EPI>
+// Q8: both operands FP8 E4M3 and k-contiguous, copied to LDS as they are and multiplied by
+// the FP8 MFMA (64 k per stage).
+template <int NW, int BN, bool AKC, bool BKC, bool AF8, bool BF8, int EPI, bool Q8 = false>
 __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
+  static_assert(!Q8 || (AKC && BKC && !AF8 && !BF8), "fp8 x fp8 operands are k-contiguous DMA tiles");
+  constexpr int BK = Q8 ? 64 : kBK;
   constexpr int kThreads = Cfg<NW, BN>::THREADS, kNst = Cfg<NW, BN>::NST;
   using TA = Tile<NW, kBM, AKC>;
   using TB = Tile<NW, BN, BKC>;
@@ -340,11 +373,11 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
   const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * BN;
   const int64_t kz0 = (int64_t)tz * p.k_per_split;
   const int64_t klen = min(p.k_per_split, p.K - kz0);
-  const int nk = klen > 0 ? (int)(klen / kBK) : 0;
+  const int nk = klen > 0 ? (int)(klen / BK) : 0;
   const uint32_t ring0 = (uint32_t)(uintptr_t)ring;
 
-  Loader<NW, kBM, AKC, AF8> la;
-  Loader<NW, BN, BKC, BF8> lb;
+  Loader<NW, kBM, AKC, AF8, Q8> la;
+  Loader<NW, BN, BKC, BF8, Q8> lb;
   la.init(p.a, m0, wv, lane, tid);
   lb.init(p.b, n0, wv, lane, tid);
 
@@ -394,7 +427,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
       nk_run = scount;
     }
   }
-  auto stage_k = [&](int s) -> int64_t { return kz0 + (int64_t)(filt ? slist[s] : s) * kBK; };
+  auto stage_k = [&](int s) -> int64_t { return kz0 + (int64_t)(filt ? slist[s] : s) * BK; };
 
   Fp8Stage<NW, kBM, AKC> sa;
   Fp8Stage<NW, BN, BKC> sb;
@@ -405,8 +438,8 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
     const int64_t k0 = stage_k(s);
     if constexpr (AF8) sa.load(la, p.a, m0, k0, tid);
     if constexpr (BF8) sb.load(lb, p.b, n0, k0, tid);
-    if constexpr (!AF8) dma_stage<NW, kBM, AKC>(la, p.a, m0, k0, so, wv, lane);
-    if constexpr (!BF8) dma_stage<NW, BN, BKC>(lb, p.b, n0, k0, so + TA::BYTES, wv, lane);
+    if constexpr (!AF8) dma_stage<NW, kBM, AKC, Q8>(la, p.a, m0, k0, so, wv, lane);
+    if constexpr (!BF8) dma_stage<NW, BN, BKC, Q8>(lb, p.b, n0, k0, so + TA::BYTES, wv, lane);
   };
   auto store_fp8 = [&](int s) {
     const uint32_t so = ring0 + (uint32_t)((s % kNst) * STAGE);
@@ -414,6 +447,46 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
     if constexpr (BF8) sb.store(so + TA::BYTES, tid);
   };
 
+  if constexpr (Q8) {
+    // The MFMAs of stage s are issued first and run in the matrix pipe while the wave waits
+    // for stage s + 1, passes the barrier that retires stage s (its fragments are in
+    // registers) and reads stage s + 1's fragments into the same registers.
+    Frag8<NW, kBM> ga;
+    Frag8<NW, BN> gb;
+    ga.init(ring0, lane);
+    gb.init(ring0 + TA::BYTES, lane);
+    i32x8 xa[MT], xb[NTW];
+    auto read8 = [&](int s) {
+      const uint32_t so = (uint32_t)((s % kNst) * STAGE);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) xa[mt] = ga.read(so, ablk0 + mt);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) xb[nt] = gb.read(so, bblk0 + nt);
+    };
+    if (nk_run > 0) {
+      for (int x = 0; x < kNst; ++x)
+        if (x < nk_run) issue(x);
+      const int later = min(nk_run - 1, kNst - 1);
+      if (later >= 3) wait_vm<3 * NPER>(); else if (later == 2) wait_vm<2 * NPER>();
+      else if (later == 1) wait_vm<NPER>(); else wait_vm<0>();
+      block_sync();
+      read8(0);
+    }
+    for (int s = 0; s < nk_run; ++s) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa[mt], xb[nt], acc[mt][nt], 0, 0, 0, 127, 0, 127);
+      if (s + 1 < nk_run) {
+        const int later = min(nk_run - 2 - s, kNst - 2);      // stages after s + 1 in flight
+        if (later >= 2) wait_vm<2 * NPER>(); else if (later == 1) wait_vm<NPER>(); else wait_vm<0>();
+        block_sync();
+        if (s + kNst < nk_run) issue(s + kNst);
+        read8(s + 1);
+      }
+    }
+  } else {
   // Software pipeline, half a stage deep: the LDS reads of one k16 half are in flight while
   // the MFMAs of the other run, and the barrier that retires a ring slot sits between the
   // two MFMA halves of a stage. All kNst slots are in flight after the prologue.
@@ -462,6 +535,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
       read_half(s + 1, 0, a0, b0);
     }
     mma_half(a1, b1);
+  }
   }
 
   // ---------------------------------------------------------------- epilogues
@@ -752,7 +826,12 @@ template <int NW, int BN>
 hipError_t gemm_bn(const GemmParams& p, dim3 grid, hipStream_t st) {
   const bool akc = p.a.kc, bkc = p.b.kc, af8 = p.a.fp8, bf8 = p.b.fp8;
 #define CL_G(AKC, BKC, AF8, BF8, E) k_gemm<NW, BN, AKC, BKC, AF8, BF8, E><<<grid, 64 * NW, 0, st>>>(p)
-  if (akc && bkc && !af8 && !bf8 && p.epi == GEMM_EPI_ACC) {   // K2, bf16 E
+  if (akc && bkc && af8 && bf8) {              // K1 with FP8 activations and FP8 E
+    if (p.epi == GEMM_EPI_BCE_P) k_gemm<NW, BN, true, true, false, false, GEMM_EPI_BCE_P, true><<<grid, 64 * NW, 0, st>>>(p);
+    else if (p.epi == GEMM_EPI_BCE_LOSS)
+      k_gemm<NW, BN, true, true, false, false, GEMM_EPI_BCE_LOSS, true><<<grid, 64 * NW, 0, st>>>(p);
+    else return hipErrorInvalidValue;
+  } else if (akc && bkc && !af8 && !bf8 && p.epi == GEMM_EPI_ACC) {   // K2, bf16 E
     CL_G(true, true, false, false, GEMM_EPI_ACC);
   } else if (akc && bkc && !bf8) {             // K1
     switch (p.epi) {
@@ -803,7 +882,35 @@ __global__ __launch_bounds__(256) void k_transpose_chunk(const uint16_t* __restr
   }
 }
 
+// 8 activations per thread: 16 bytes in, 8 bytes out
+__global__ __launch_bounds__(256) void k_cast_fp8(const uint16_t* __restrict__ A, int64_t n8, uint8_t* __restrict__ A8) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const uint4 x = *(const uint4*)(A + 8 * i);
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t o[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const float a0 = __builtin_amdgcn_fmed3f(bf16_bits_to_f32(w[2 * q] & 0xffffu), -kFp8Max, kFp8Max);
+    const float a1 = __builtin_amdgcn_fmed3f(bf16_bits_to_f32(w[2 * q] >> 16), -kFp8Max, kFp8Max);
+    const float a2 = __builtin_amdgcn_fmed3f(bf16_bits_to_f32(w[2 * q + 1] & 0xffffu), -kFp8Max, kFp8Max);
+    const float a3 = __builtin_amdgcn_fmed3f(bf16_bits_to_f32(w[2 * q + 1] >> 16), -kFp8Max, kFp8Max);
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, r, true);
+    o[q] = (uint32_t)r;
+  }
+  *(uint2*)(A8 + 8 * i) = uint2{o[0], o[1]};
+}
+
 }  // namespace
+
+hipError_t launch_cast_fp8(const uint16_t* A, int64_t n, uint8_t* A8, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (n % 8 != 0) return hipErrorInvalidValue;
+  const int64_t n8 = n / 8;
+  k_cast_fp8<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(A, n8, A8);
+  return hipGetLastError();
+}
 
 hipError_t launch_transpose_chunk(const uint16_t* E, int64_t vlen, int64_t mc, int64_t D, uint16_t* Et, int64_t ld,
                                   hipStream_t st) {
@@ -818,6 +925,7 @@ hipError_t launch_transpose_chunk(const uint16_t* E, int64_t vlen, int64_t mc, i
 int gemm_waves(const GemmParams& p) {
   if (p.D > 1024) return 8;
   if (p.epi == GEMM_EPI_ACC && p.M <= 128) return 8;
+  if (p.a.fp8 && p.b.fp8) return 8;   // FP8 x FP8 logits: 4 waves would spill (two 8-register fragments per block)
   return 4;
 }
 int tile_n_for(int nw, int64_t N) { return (nw == 4 || N <= 128) ? 128 : 256; }
@@ -828,9 +936,10 @@ int gemm_tile_n_of(int epi, int64_t M, int64_t N, int64_t D) {
   q.epi = epi; q.M = M; q.N = N; q.D = D;
   return tile_n_for(gemm_waves(q), N);
 }
-int gemm_k1_warps_m(int64_t T, int64_t D) {
+int gemm_k1_warps_m(int64_t T, int64_t D, bool fp8_fp8) {
   GemmParams q{};
   q.D = D; q.epi = GEMM_EPI_BCE_LOSS; q.M = kBM; q.N = T;
+  q.a.fp8 = q.b.fp8 = fp8_fp8 ? 1 : 0;
   const int nw = gemm_waves(q);
   const int bn = tile_n_for(nw, T);
   return nw == 4 ? WaveGrid<4, 128>::WM : (bn == 128 ? WaveGrid<8, 128>::WM : WaveGrid<8, 256>::WM);
@@ -839,6 +948,8 @@ int gemm_k1_warps_m(int64_t T, int64_t D) {
 hipError_t launch_gemm(const GemmParams& p, hipStream_t st) {
   if (p.M <= 0 || p.N <= 0 || p.K <= 0 || p.K % kBK != 0 || p.k_per_split % kBK != 0 || p.k_per_split <= 0)
     return hipErrorInvalidValue;
+  // FP8 x FP8: 64 k per stage, no k tail, k-contiguous operands
+  if (p.a.fp8 && p.b.fp8 && (p.K % 64 != 0 || p.k_per_split % 64 != 0 || !p.a.kc || !p.b.kc)) return hipErrorInvalidValue;
   const int nw = gemm_waves(p);
   const int bn = tile_n_for(nw, p.N);
   const int64_t gm = (p.M + kBM - 1) / kBM, gn = (p.N + bn - 1) / bn, gz = (p.K + p.k_per_split - 1) / p.k_per_split;
