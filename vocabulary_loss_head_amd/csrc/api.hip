@@ -243,6 +243,7 @@ struct Ws2 {
   float* S_part;
   float* red;         // staging of the split reductions
   int32_t* flags;     // gradient filter: [Vc / 256][flag_ld]
+  int32_t* imap;      // [V] item -> unique-item index (dE / SGD epilogue)
   uint16_t* Et;       // the chunk's bf16 E transposed, [D][Vc] (the dA product's k-contiguous operand)
   uint8_t* A8;        // FP8 logits: E4M3FN copy of A [T][D]
   size_t bytes;
@@ -290,6 +291,7 @@ Ws2 carve_chunked(void* base, const ChunkPlan& pl, bool need_P, bool need_dA, bo
   w.flags = need_P ? c.take<int32_t>((size_t)(pl.Vc / 256) * pl.flag_ld) : nullptr;
   w.Et = need_dA && need_Et ? c.take<uint16_t>((size_t)pl.Vc * pl.D) : nullptr;
   w.A8 = pl.q8 ? c.take<uint8_t>((size_t)T * pl.D) : nullptr;
+  w.imap = need_Su ? c.take<int32_t>((size_t)pl.V) : nullptr;
   w.bytes = c.off;
   return w;
 }
@@ -495,7 +497,7 @@ struct ChunkJob {
   uint16_t* Et;          // bf16 E: workspace for the transposed chunk
   const uint8_t* A8;     // FP8 logits: the activations' E4M3FN copy
   int k3_epi;            // -1: none, GEMM_EPI_DE or GEMM_EPI_SGD
-  const int32_t* uitems; const int32_t* counts; const float* S_u;
+  const int32_t* uitems; const int32_t* counts; const float* S_u; const int32_t* imap;
   void* dE; float lr;
   int sr; uint64_t sr_seed;   // SGD: stochastic rounding
   int32_t* flags; int64_t flag_ld; int flag_bn; float filter_eps;   // gradient filter (flags NULL: off)
@@ -554,7 +556,7 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
       g.M = mc; g.N = pl.D; g.K = round_up(pl.T, 32); g.k_per_split = g.K;
       g.epi = j.k3_epi;
       g.v0 = v0; g.V = pl.V; g.T = pl.T; g.D = pl.D;
-      g.uitems = j.uitems; g.counts = j.counts; g.S_u = j.S_u;
+      g.uitems = j.uitems; g.counts = j.counts; g.S_u = j.S_u; g.imap = j.imap;
       g.dE = j.dE; g.E_inplace = (void*)j.E; g.e_fp8 = j.e_fp8; g.lr = j.lr;
       g.sr = j.sr; g.sr_seed = j.sr_seed;
       g.flags = j.flags; g.flag_ld = j.flag_ld; g.flag_bn = j.flag_bn; g.flag_gen = (int)(c + 1);
@@ -593,9 +595,11 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
     CL_HIP(cl::launch_row_weights(fp, 0, st), "row weights");
     // positive-row terms read E before any chunk's SGD step changes it
     CL_HIP(cl::launch_row_positives(fp, st), "row positives");
-    if (dE_mode != 0)
+    if (dE_mode != 0) {
       CL_HIP(cl::launch_item_sums(p->D, pl.cap, p->A, w.w, w.tw.csc_rows, w.tw.useg, w.tw.counts, w.S_u, w.S_part, st),
              "item sums");
+      CL_HIP(cl::launch_item_map(w.tw, p->V, pl.cap, w.imap, st), "item map");
+    }
   }
   ChunkJob j{};
   j.pl = &pl; j.A = p->A; j.E = p->E; j.e_fp8 = e_fp8;
@@ -603,7 +607,7 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
   j.w = w.w; j.P = w.P; j.part_a = w.part_a; j.part_b = w.part_b; j.part_dA = w.part_dA; j.Et = w.Et;
   j.A8 = w.A8;
   j.k3_epi = dE_mode == 0 ? -1 : (dE_mode == 1 ? cl::GEMM_EPI_DE : cl::GEMM_EPI_SGD);
-  j.uitems = w.tw.uitems; j.counts = w.tw.counts; j.S_u = w.S_u; j.dE = dE; j.lr = lr;
+  j.uitems = w.tw.uitems; j.counts = w.tw.counts; j.S_u = w.S_u; j.imap = w.imap; j.dE = dE; j.lr = lr;
   j.sr = sr; j.sr_seed = sr_seed;
   CL_TRY(run_chunks(j, st));
   if (loss != nullptr || dA != nullptr) {
@@ -648,7 +652,7 @@ cutloss_status ce_run_chunked(const cutloss_ce_problem* p, const float* lse_in, 
   ChunkJob j{};
   j.pl = &pl; j.A = p->A; j.E = p->E; j.e_fp8 = e_fp8;
   j.w = w.w; j.lse = lse_in; j.P = w.P; j.part_a = w.part_a; j.part_b = w.part_b;
-  j.uitems = w.tw.uitems; j.counts = w.tw.counts; j.S_u = w.S_u; j.dE = dE;
+  j.uitems = w.tw.uitems; j.counts = w.tw.counts; j.S_u = w.S_u; j.imap = w.imap; j.dE = dE;
   if (fwd) {
     j.k1_epi = cl::GEMM_EPI_CE_LSE;
     j.k3_epi = -1;
@@ -662,9 +666,11 @@ cutloss_status ce_run_chunked(const cutloss_ce_problem* p, const float* lse_in, 
   {
     Phase ph(CUTLOSS_PHASE_ITEM_SUMS, st);
     CL_HIP(cl::launch_row_weights(fp, 1, st), "row weights");
-    if (dE != nullptr)
+    if (dE != nullptr) {
       CL_HIP(cl::launch_item_sums(p->D, pl.cap, p->A, w.w, w.tw.csc_rows, w.tw.useg, w.tw.counts, w.S_u, w.S_part, st),
              "item sums");
+      CL_HIP(cl::launch_item_map(w.tw, p->V, pl.cap, w.imap, st), "item map");
+    }
   }
   j.k1_epi = cl::GEMM_EPI_CE_P;
   j.part_dA = w.part_dA;

@@ -111,6 +111,8 @@ hipError_t launch_targets(const TargetsWs& w, int64_t T, int64_t V, int64_t nnz,
 size_t targets_radix_blocks(int64_t nnz);
 
 hipError_t launch_zero_u64(unsigned long long* p, int n, hipStream_t st);
+// map[v] = index of v among the unique positive items, -1 for every other item v < V
+hipError_t launch_item_map(const TargetsWs& w, int64_t V, int64_t cap, int32_t* map, hipStream_t st);
 
 struct SweepParams {
   int64_t T, D, V;
@@ -197,6 +199,7 @@ struct GemmParams {
   int acc_first;            // 1: store, 0: add to the previous value
   // DE / SGD epilogues
   const int32_t* uitems; const int32_t* counts; const float* S_u; int64_t D;
+  const int32_t* imap;      // [V] item -> unique-item index (-1: none); NULL: binary search of uitems
   void* dE; void* E_inplace; int e_fp8; float lr;
   int sr; uint64_t sr_seed;  // SGD: stochastic rounding keyed by (sr_seed, v, d) when sr != 0
   // CE gradient filter: the CE_P epilogue sets flags[tm * flag_ld + tn] = flag_gen for an

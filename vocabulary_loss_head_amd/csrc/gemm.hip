@@ -672,6 +672,10 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
     block_sync();                              // every wave is done with the ring
     for (int k = tid; k < kBM; k += kThreads) {
       const int64_t v = p.v0 + m0 + k;
+      if (p.imap != nullptr) {               // one load instead of a dependent search
+        uix[k] = v < p.V ? p.imap[v] : -1;
+        continue;
+      }
       const int nu = p.counts[2];
       int lo = 0, hi = nu;
       while (lo < hi) {

@@ -14,6 +14,7 @@
 //   3. unique item list and its segment starts (for the dE sparse term);
 //   4. stable radix sort of the unique pairs by row -> canonical CSR (items
 //      ascending within a row).
+#include <algorithm>
 #include "common.h"
 
 namespace cl {
@@ -337,6 +338,24 @@ hipError_t launch_targets(const TargetsWs& w, int64_t T, int64_t V, int64_t nnz,
   const int32_t* is = inB2 ? w.valB : w.valA;
   k_copy2<<<g, 256, 0, st>>>(is, is, w.counts + 1, cap, w.cids, w.cids);
   k_row_ptr<<<grid_for(cap + 1, 256), 256, 0, st>>>(rs, w.counts + 1, cap, T, w.crow);
+  return hipGetLastError();
+}
+
+namespace {
+__global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+__global__ void k_item_map(const int32_t* __restrict__ uitems, const int32_t* __restrict__ counts, int64_t cap,
+                           int32_t* __restrict__ map) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < cap && i < counts[2]) map[uitems[i]] = (int32_t)i;
+}
+}  // namespace
+
+hipError_t launch_item_map(const TargetsWs& w, int64_t V, int64_t cap, int32_t* map, hipStream_t st) {
+  if (V <= 0) return hipSuccess;
+  k_fill_i32<<<(unsigned)std::min<int64_t>((V + 255) / 256, 4096), 256, 0, st>>>(map, V, -1);
+  if (cap > 0) k_item_map<<<grid_for(cap, 256), 256, 0, st>>>(w.uitems, w.counts, cap, map);
   return hipGetLastError();
 }
 
