@@ -689,11 +689,37 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
     constexpr int RS = TN * 4 + 16;            // fp32 row stride: 16 B pad spreads the 16-lane reads
     constexpr int MG = (WREG / (32 * RS)) < MT ? (WREG / (32 * RS)) : MT;
     constexpr int SEGS = TN / 16;
-    static_assert(MG >= 1 && MT % MG == 0 && TN % 16 == 0, "epilogue staging");
+    constexpr int SPL = 32 * MG * SEGS / 64;    // segments per lane per group
+    static_assert(MG >= 1 && MT % MG == 0 && TN % 16 == 0 && (32 * MG * SEGS) % 64 == 0, "epilogue staging");
     char* wbuf = ring + wv * WREG;
     const uint32_t wb = ring0 + (uint32_t)(wv * WREG);
+    // FP8 SGD: E bytes of the lane's segments, loaded one group ahead so that their latency
+    // overlaps the previous group's staging and update
+    constexpr bool PRE = EPI == GEMM_EPI_SGD;
+    const bool pre = PRE && p.e_fp8 && !p.sr;
+    uint4 enext[PRE ? SPL : 1];
+    auto load_e8 = [&](int g0) {
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) {
+        const int s = lane + 64 * i, row = s / SEGS, seg = s - row * SEGS;
+        const int64_t v = p.v0 + m0 + wm * TM + 32 * g0 + row;
+        const int64_t d0 = n0 + wn * TN + 16 * seg;
+        if (v < p.V && d0 < p.D) enext[i] = *(const uint4*)((const uint8_t*)p.E_inplace + v * p.D + d0);
+      }
+    };
+    if constexpr (PRE) {
+      if (pre) load_e8(0);
+    }
 #pragma unroll
     for (int g0 = 0; g0 < MT; g0 += MG) {
+      uint4 ecur[PRE ? SPL : 1];
+      if constexpr (PRE) {
+        if (pre) {
+#pragma unroll
+          for (int i = 0; i < SPL; ++i) ecur[i] = enext[i];
+          if (g0 + MG < MT) load_e8(g0 + MG);
+        }
+      }
       __syncthreads();
 #pragma unroll
       for (int mq = 0; mq < MG; ++mq)
@@ -703,7 +729,9 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
           for (int i = 0; i < 16; ++i)
             *(float*)(wbuf + (32 * mq + res_row(i, h)) * RS + 4 * (32 * nt + l32)) = acc[g0 + mq][nt][i];
       __syncthreads();
-      for (int s = lane; s < 32 * MG * SEGS; s += 64) {
+#pragma unroll
+      for (int si = 0; si < SPL; ++si) {
+        const int s = lane + 64 * si;
         const int row = s / SEGS, seg = s - row * SEGS;
         const int ml = wm * TM + 32 * g0 + row;
         const int64_t v = p.v0 + m0 + ml;
@@ -782,7 +810,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
           }
         } else if (p.e_fp8) {
           uint4* ep = (uint4*)((uint8_t*)p.E_inplace + v * p.D + d0);
-          const uint4 e = *ep;
+          const uint4 e = pre ? ecur[PRE ? si : 0] : *ep;
           const uint32_t w[4] = {e.x, e.y, e.z, e.w};
           uint32_t o[4];
 #pragma unroll
@@ -830,11 +858,15 @@ template <int NW, int BN>
 hipError_t gemm_bn(const GemmParams& p, dim3 grid, hipStream_t st) {
   const bool akc = p.a.kc, bkc = p.b.kc, af8 = p.a.fp8, bf8 = p.b.fp8;
 #define CL_G(AKC, BKC, AF8, BF8, E) k_gemm<NW, BN, AKC, BKC, AF8, BF8, E><<<grid, 64 * NW, 0, st>>>(p)
-  if (akc && bkc && af8 && bf8) {              // K1 with FP8 activations and FP8 E
-    if (p.epi == GEMM_EPI_BCE_P) k_gemm<NW, BN, true, true, false, false, GEMM_EPI_BCE_P, true><<<grid, 64 * NW, 0, st>>>(p);
-    else if (p.epi == GEMM_EPI_BCE_LOSS)
-      k_gemm<NW, BN, true, true, false, false, GEMM_EPI_BCE_LOSS, true><<<grid, 64 * NW, 0, st>>>(p);
-    else return hipErrorInvalidValue;
+  if (akc && bkc && af8 && bf8) {              // K1 with FP8 activations and FP8 E (8 waves)
+    if constexpr (NW == 8) {
+      if (p.epi == GEMM_EPI_BCE_P) k_gemm<NW, BN, true, true, false, false, GEMM_EPI_BCE_P, true><<<grid, 64 * NW, 0, st>>>(p);
+      else if (p.epi == GEMM_EPI_BCE_LOSS)
+        k_gemm<NW, BN, true, true, false, false, GEMM_EPI_BCE_LOSS, true><<<grid, 64 * NW, 0, st>>>(p);
+      else return hipErrorInvalidValue;
+    } else {
+      return hipErrorInvalidValue;
+    }
   } else if (akc && bkc && !af8 && !bf8 && p.epi == GEMM_EPI_ACC) {   // K2, bf16 E
     CL_G(true, true, false, false, GEMM_EPI_ACC);
   } else if (akc && bkc && !bf8) {             // K1
