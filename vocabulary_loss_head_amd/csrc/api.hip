@@ -194,13 +194,16 @@ struct ChunkPlan {
   int64_t kps;        // items per slice
   int64_t flag_bn, flag_ld;   // gradient filter flags: row tile of the logits product, row tiles
   bool q8;            // FP8 logits: the logits product multiplies FP8 activations and FP8 E
+  bool trans_dA;      // FP8 E, at most 128 rows: the dA product runs as dA^T = E_c^T P^T (M = D)
 };
 
 constexpr int64_t kChunkPBytes = 2ll << 30;     // P buffer budget
 
-ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap, bool q8 = false) {
+ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap, bool q8 = false, bool e_fp8 = false) {
   ChunkPlan c{};
   c.T = T; c.D = D; c.V = V; c.cap = cap; c.q8 = q8;
+  // a 256-row tile over at most 128 rows would waste half the dA product's MFMAs
+  c.trans_dA = e_fp8 && T <= 128;
   const int64_t bm = cl::gemm_tile_m();
   c.bt = round_up(T > 0 ? T : 1, 128) <= 128 ? 128 : 256;
   c.Tp = round_up(T > 0 ? T : 1, c.bt);
@@ -217,7 +220,9 @@ ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap, bool q8 
   c.n_chunks = ceil_div(V, vc);
   c.n_splits = ceil_div(V, bm) * cl::gemm_k1_warps_m(T, D, q8);
   // dA product: (row tiles) x (D tiles) x slices, about 1024 workgroups
-  const int64_t tiles = ceil_div(T > 0 ? T : 1, bm) * ceil_div(D, cl::gemm_tile_n_of(cl::GEMM_EPI_ACC, T, D, D));
+  const int64_t tiles = c.trans_dA
+      ? ceil_div(D, bm) * ceil_div(T > 0 ? T : 1, cl::gemm_tile_n_of(cl::GEMM_EPI_ACC, D, T > 0 ? T : 1, D))
+      : ceil_div(T > 0 ? T : 1, bm) * ceil_div(D, cl::gemm_tile_n_of(cl::GEMM_EPI_ACC, T, D, D));
   int64_t sk = ceil_div(1024, tiles);
   if (sk > vc / 32) sk = vc / 32;
   if (sk < 1) sk = 1;
@@ -531,20 +536,28 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
     if (j.part_dA != nullptr) {
       Phase ph(CUTLOSS_PHASE_CHUNK_DA, st);
       cl::GemmParams g{};
-      g.a = operand(j.P, 0, pl.Tp, mc, 1, 0, (int)pl.bt, pl.Vc / 32);
-      if (j.e_fp8) {
-        g.b = operand(Ec, pl.D, vlen, pl.D, 0, 1);
-      } else {
-        // k-contiguous copy of the chunk (zero past vlen): the product reads it with full-width
-        // LDS reads instead of transposing reads
-        CL_HIP(cl::launch_transpose_chunk((const uint16_t*)Ec, vlen, mc, pl.D, j.Et, pl.Vc, st), "chunk transpose");
-        g.b = operand(j.Et, pl.Vc, pl.D, mc, 1, 0);
-      }
-      g.M = pl.T; g.N = pl.D; g.K = mc; g.k_per_split = pl.kps;
       g.epi = cl::GEMM_EPI_ACC;
       g.T = pl.T; g.D = pl.D;
       g.acc = j.part_dA; g.ldacc = pl.D; g.acc_slice = pl.T * pl.D; g.acc_first = c == 0;
-      g.flags = j.flags; g.flag_ld = j.flag_ld; g.flag_bn = j.flag_bn; g.flag_gen = (int)(c + 1);
+      g.k_per_split = pl.kps; g.K = mc;
+      if (j.e_fp8 && pl.trans_dA && j.flags == nullptr) {
+        // dA^T = E_c^T P^T: M = D, N = rows, stored as [row][d]
+        g.a = operand(Ec, pl.D, vlen, pl.D, 0, 1);
+        g.b = operand(j.P, 0, pl.Tp, mc, 1, 0, (int)pl.bt, pl.Vc / 32);
+        g.M = pl.D; g.N = pl.T; g.acc_trans = 1;
+      } else {
+        g.a = operand(j.P, 0, pl.Tp, mc, 1, 0, (int)pl.bt, pl.Vc / 32);
+        if (j.e_fp8) {
+          g.b = operand(Ec, pl.D, vlen, pl.D, 0, 1);
+        } else {
+          // k-contiguous copy of the chunk (zero past vlen): the product reads it with
+          // full-width LDS reads instead of transposing reads
+          CL_HIP(cl::launch_transpose_chunk((const uint16_t*)Ec, vlen, mc, pl.D, j.Et, pl.Vc, st), "chunk transpose");
+          g.b = operand(j.Et, pl.Vc, pl.D, mc, 1, 0);
+        }
+        g.M = pl.T; g.N = pl.D;
+        g.flags = j.flags; g.flag_ld = j.flag_ld; g.flag_bn = j.flag_bn; g.flag_gen = (int)(c + 1);
+      }
       CL_HIP(cl::launch_gemm(g, st), "chunk dA");
     }
     if (j.k3_epi >= 0) {
@@ -569,7 +582,7 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
 cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss, float* loss, void* dA, void* dE,
                                int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st, int32_t* counts,
                                int sr, uint64_t sr_seed, bool fp8_logits) {
-  const ChunkPlan pl = make_chunk_plan(p->T, p->D, p->V, p->nnz, fp8_logits);
+  const ChunkPlan pl = make_chunk_plan(p->T, p->D, p->V, p->nnz, fp8_logits, p->e_dtype == CUTLOSS_FP8_E4M3);
   const bool grad = dA != nullptr || dE_mode != 0;
   const int e_fp8 = p->e_dtype == CUTLOSS_FP8_E4M3;
   const Ws2 w = carve_chunked(ws, pl, grad, dA != nullptr, dE_mode != 0, counts != nullptr, true, !e_fp8);
@@ -631,7 +644,7 @@ cutloss_status ce_run_chunked(const cutloss_ce_problem* p, const float* lse_in, 
                               float* lse, void* dA, void* dE, void* ws, size_t ws_bytes, hipStream_t st,
                               float filter_eps) {
   const bool fwd = loss != nullptr;
-  const ChunkPlan pl = make_chunk_plan(p->T, p->D, p->V, p->T);
+  const ChunkPlan pl = make_chunk_plan(p->T, p->D, p->V, p->T, false, p->e_dtype == CUTLOSS_FP8_E4M3);
   const bool grad = !fwd && (dA != nullptr || dE != nullptr);
   const int e_fp8 = p->e_dtype == CUTLOSS_FP8_E4M3;
   const Ws2 w = carve_chunked(ws, pl, grad, !fwd && dA != nullptr, !fwd && dE != nullptr, fwd, false, !e_fp8);
@@ -703,13 +716,13 @@ size_t cutloss_bce_workspace_size(const cutloss_bce_problem* p, int32_t op) {
     size_t b = 0;
     for (const bool q8 : {false, true}) {
       if (q8 && p->e_dtype != CUTLOSS_FP8_E4M3) continue;
-      const ChunkPlan cp = make_chunk_plan(p->T, p->D, p->V, p->nnz, q8);
+      const ChunkPlan cp = make_chunk_plan(p->T, p->D, p->V, p->nnz, q8, p->e_dtype == CUTLOSS_FP8_E4M3);
       b = std::max(b, carve_chunked(nullptr, cp, true, true, true, false, true, p->e_dtype != CUTLOSS_FP8_E4M3).bytes);
     }
     return b;
   }
   if (use_chunked(p->D, p->e_dtype == CUTLOSS_FP8_E4M3)) {
-    const ChunkPlan cp = make_chunk_plan(p->T, p->D, p->V, p->nnz);
+    const ChunkPlan cp = make_chunk_plan(p->T, p->D, p->V, p->nnz, false, p->e_dtype == CUTLOSS_FP8_E4M3);
     return carve_chunked(nullptr, cp, bwd, bwd, bwd, metrics, true, p->e_dtype != CUTLOSS_FP8_E4M3).bytes;
   }
   const Plan pl = make_plan(p->T, p->D, p->V, p->nnz, p->e_dtype == CUTLOSS_FP8_E4M3);
@@ -720,7 +733,7 @@ size_t cutloss_ce_workspace_size(const cutloss_ce_problem* p, int32_t op) {
   if (check_ce(p) != CUTLOSS_OK) return 0;
   const bool bwd = op != CUTLOSS_OP_FWD;
   if (use_chunked(p->D, p->e_dtype == CUTLOSS_FP8_E4M3)) {
-    const ChunkPlan cp = make_chunk_plan(p->T, p->D, p->V, p->T);
+    const ChunkPlan cp = make_chunk_plan(p->T, p->D, p->V, p->T, false, p->e_dtype == CUTLOSS_FP8_E4M3);
     return carve_chunked(nullptr, cp, bwd, bwd, bwd, !bwd, false, p->e_dtype != CUTLOSS_FP8_E4M3).bytes;
   }
   const Plan pl = make_plan(p->T, p->D, p->V, p->T, p->e_dtype == CUTLOSS_FP8_E4M3);

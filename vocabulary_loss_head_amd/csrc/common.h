@@ -196,6 +196,7 @@ struct GemmParams {
   int64_t part_base;        // split index of this chunk's first item tile
   // ACC epilogue
   float* acc; int64_t ldacc; int64_t acc_slice;   // acc + z * acc_slice
+  int acc_trans;            // 1: the product is dA^T (M = D, N = rows), stored as [row][d]
   int acc_first;            // 1: store, 0: add to the previous value
   // DE / SGD epilogues
   const int32_t* uitems; const int32_t* counts; const float* S_u; int64_t D;

@@ -653,6 +653,29 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
     else logit_tile(BoolC<true>{});
   } else if constexpr (EPI == GEMM_EPI_ACC) {
     float* out = p.acc + (int64_t)tz * p.acc_slice;
+    if (p.acc_trans) {
+      // dA^T tile: result registers 4q..4q+3 hold 4 consecutive d of row n = l32
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          const int64_t n = n0 + wn * TN + 32 * nt + l32;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t m = m0 + wm * TM + 32 * mt + 8 * q + 4 * h;
+            if (n < p.T && m < p.D) {                // D is a multiple of 64: m .. m + 3 valid
+              float4* o = (float4*)(out + n * p.ldacc + m);
+              float4 x = {acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1], acc[mt][nt][4 * q + 2], acc[mt][nt][4 * q + 3]};
+              if (!p.acc_first) {
+                const float4 y = *o;
+                x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+              }
+              *o = x;
+            }
+          }
+        }
+      return;
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -850,9 +873,11 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
 }
 
 // The operand combinations the chunked path uses:
-//   K1: A = E chunk (k-contiguous, bf16 or fp8), B = activations (k-contiguous)
+//   K1: A = E chunk (k-contiguous, bf16 or fp8), B = activations (k-contiguous); with FP8
+//       logits both FP8 and multiplied as FP8
 //   K2: A = P (k-contiguous), B = the transposed bf16 E chunk (k-contiguous) or the fp8
-//       E chunk itself (k-major)
+//       E chunk itself (k-major); for fp8 E and at most 128 rows, dA^T with A = the fp8 E
+//       chunk (k-major) and B = P (k-contiguous)
 //   K3: A = P (k-major), B = activations (k-major)
 template <int NW, int BN>
 hipError_t gemm_bn(const GemmParams& p, dim3 grid, hipStream_t st) {
@@ -879,6 +904,8 @@ hipError_t gemm_bn(const GemmParams& p, dim3 grid, hipStream_t st) {
     }
   } else if (akc && !bkc && !af8 && bf8 && p.epi == GEMM_EPI_ACC) {    // K2, fp8 E
     CL_G(true, false, false, true, GEMM_EPI_ACC);
+  } else if (!akc && bkc && af8 && !bf8 && p.epi == GEMM_EPI_ACC) {    // K2 as dA^T = E_c^T P^T, fp8 E
+    CL_G(false, true, true, false, GEMM_EPI_ACC);
   } else if (!akc && !bkc && !af8 && !bf8) {   // K3
     if (p.epi == GEMM_EPI_DE) CL_G(false, false, false, false, GEMM_EPI_DE);
     else if (p.epi == GEMM_EPI_SGD) CL_G(false, false, false, false, GEMM_EPI_SGD);
