@@ -204,24 +204,34 @@ __global__ __launch_bounds__(256) void k_item_pieces(int64_t D, const uint16_t* 
   if (a >= n) return;
   const int64_t b = min(a + kPiece, (int64_t)n);
   const int nd = (int)(D / 64);
+  constexpr int KB = 8;                         // d columns per lane in flight
   int64_t i = a;
+  int u = item_of(useg, nu, (int32_t)a);        // pairs are item-major: later items follow in order
   while (i < b) {
-    const int u = item_of(useg, nu, (int32_t)i);
     const int64_t s = useg[u], e = useg[u + 1];
     const int64_t r1 = min(e, b);
     float* dst;
     if (s >= a && e <= b) dst = S_u + (int64_t)u * D;          // complete inside this piece
     else if (s < a) dst = part + (j * 2 + 0) * D;               // began in an earlier piece
     else dst = part + (j * 2 + 1) * D;                          // continues into later pieces
-    for (int k = 0; k < nd; ++k) {
-      float acc = 0.0f;
-      for (int64_t q = i; q < r1; ++q) {
+    for (int k0 = 0; k0 < nd; k0 += KB) {
+      float acc[KB];
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) acc[kk] = 0.0f;
+      for (int64_t q = i; q < r1; ++q) {        // pair order: the sum order is fixed
         const int64_t t = csc_rows[q];
-        acc += w[t] * bf16_bits_to_f32(A[t * D + lane + 64 * k]);
+        const float wt = w[t];
+        const uint16_t* At = A + t * D + lane;
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk)
+          if (k0 + kk < nd) acc[kk] += wt * bf16_bits_to_f32(At[64 * (k0 + kk)]);
       }
-      dst[lane + 64 * k] = acc;
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk)
+        if (k0 + kk < nd) dst[lane + 64 * (k0 + kk)] = acc[kk];
     }
     i = r1;
+    ++u;
   }
 }
 
