@@ -1,0 +1,162 @@
+"""GPU edge cases of both paths (fused sweeps for D in {64, 128, 256}, chunked GEMMs
+otherwise): an empty batch, every row masked, no positives at all, a vocabulary smaller than
+one tile (V = 1 and V = 31), the widest supported head (D = 9216), and CE with every target
+ignored. Each is checked against the oracle's plain definitions (Cut BCE §I-B, the Cut Your
+Losses article's CE split) or the closed form the case reduces to."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import head_loss as H
+from oracle.targets import canonical_csr
+
+from gpu_util import bf16_to_f64, check_grad, check_loss, dev, run_bce, run_ce
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    from vocabulary_loss_head_amd import binding
+    return binding
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _bf16(x):
+    """Nearest-even bf16 bits of float32 values (the storage rounding of the inputs)."""
+    b = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
+
+
+def _dec(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _bce_inputs(T, D, V, L, seed, mask=None, std=None):
+    rng = np.random.default_rng(seed)
+    s = 1.0 / np.sqrt(D) if std is None else std
+    A = _bf16(rng.normal(0, s, (T, D)))
+    E = _bf16(rng.normal(0, s, (V, D)))
+    row_ptr = np.arange(T + 1, dtype=np.int32) * L
+    ids = rng.integers(0, V, size=T * L).astype(np.int32)
+    m = np.ones(T, dtype=np.uint8) if mask is None else mask
+    return A, E, row_ptr, ids, m
+
+
+def _upload_bce(A, E, row_ptr, ids, mask):
+    d = dev()
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(d)
+    return {"A": t(A.view(np.int16)).view(torch.bfloat16), "E": t(E.view(np.int16)).view(torch.bfloat16),
+            "row_ptr": t(row_ptr), "ids": t(ids), "mask": t(mask)}
+
+
+def _check_bce_case(B, A, E, row_ptr, ids, mask, pad_id=-1):
+    g = _upload_bce(A, E, row_ptr, ids, mask)
+    out = run_bce(B, g, pad_id)
+    A64, E64 = _dec(A), _dec(E)
+    crow, cids, _ = canonical_csr(row_ptr, ids, mask, E.shape[0], pad_id)
+    ref = H.bce_loss(A64, E64, crow, cids, mask)
+    dA_ref, dE_ref = H.bce_grads(A64, E64, crow, cids, mask)
+    check_loss(out["loss"].cpu().numpy(), ref, what="loss")
+    check_loss(out["floss"].cpu().numpy(), ref, what="fused loss")
+    check_grad(bf16_to_f64(out["dA"]), dA_ref, "dA")
+    check_grad(bf16_to_f64(out["dE"]), dE_ref, "dE")
+    return out
+
+
+@pytest.mark.parametrize("D", [128, 384])
+def test_empty_batch(B, D):
+    _say(f"empty batch D={D}")
+    d = dev()
+    V = 700
+    E = torch.from_numpy(_bf16(np.random.default_rng(1).normal(0, 0.05, (V, D))).view(np.int16)).to(d).view(torch.bfloat16)
+    A = torch.empty(1, D, dtype=torch.bfloat16, device=d)
+    rp = torch.zeros(1, dtype=torch.int32, device=d)
+    ids = torch.zeros(1, dtype=torch.int32, device=d)
+    prob = B.bce_problem(A, E, rp, ids, None, -1)
+    prob.T, prob.nnz = 0, 0
+    ws = B.workspace(B.cutloss_bce_workspace_size(prob, B.OP_BWD), d)
+    dE = torch.full((V, D), float("nan"), dtype=torch.bfloat16, device=d)
+    B.cutloss_bce_bwd(prob, None, None, dE, None, ws)
+    tgt = torch.zeros(1, dtype=torch.int64, device=d)
+    cprob = B.ce_problem(A, E, tgt, -100)
+    cprob.T = 0
+    cws = B.workspace(max(B.cutloss_ce_workspace_size(cprob, B.OP_BWD), B.cutloss_ce_workspace_size(cprob, B.OP_FWD)), d)
+    dE2 = torch.full((V, D), float("nan"), dtype=torch.bfloat16, device=d)
+    B.cutloss_ce_fwd(cprob, None, None, cws)
+    B.cutloss_ce_bwd(cprob, None, None, None, dE2, cws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dE.float()).item() == 0, "dE of an empty batch must be 0"
+    assert torch.count_nonzero(dE2.float()).item() == 0, "CE dE of an empty batch must be 0"
+
+
+@pytest.mark.parametrize("D", [64, 512])
+def test_all_rows_masked(B, D):
+    _say(f"all rows masked D={D}")
+    A, E, rp, ids, _ = _bce_inputs(40, D, 900, 4, 2)
+    out = _check_bce_case(B, A, E, rp, ids, np.zeros(40, dtype=np.uint8))
+    assert np.all(out["loss"].cpu().numpy() == 0)
+    assert torch.count_nonzero(out["dA"].float()).item() == 0
+    assert torch.count_nonzero(out["dE"].float()).item() == 0
+
+
+@pytest.mark.parametrize("D", [256, 320])
+def test_no_positives(B, D):
+    _say(f"no positives D={D}")
+    A, E, _, _, mask = _bce_inputs(50, D, 1300, 0, 3)
+    _check_bce_case(B, A, E, np.zeros(51, dtype=np.int32), np.zeros(0, dtype=np.int32), mask)
+
+
+@pytest.mark.parametrize("V,D", [(1, 64), (31, 128), (1, 448), (31, 640)])
+def test_tiny_vocabulary(B, V, D):
+    _say(f"tiny vocabulary V={V} D={D}")
+    # logits of a few units: with one item the BCE loss of a positive row is softplus(-x),
+    # and its dense - sparse evaluation cancels; |x| <~ 4 keeps that inside the tolerance
+    A, E, rp, ids, mask = _bce_inputs(37, D, V, 2, 4 + V, std=0.25)
+    mask[5] = 0
+    _check_bce_case(B, A, E, rp, ids, mask)
+    rng = np.random.default_rng(5)
+    tgt = rng.integers(0, V, size=37).astype(np.int64)
+    tgt[3] = -100
+    d = dev()
+    g = {"A": torch.from_numpy(A.view(np.int16)).to(d).view(torch.bfloat16),
+         "E": torch.from_numpy(E.view(np.int16)).to(d).view(torch.bfloat16), "target": torch.from_numpy(tgt).to(d)}
+    out = run_ce(B, g)
+    loss_ref, lse_ref = H.ce_forward(_dec(A), _dec(E), tgt)
+    dA_ref, dE_ref = H.ce_grads(_dec(A), _dec(E), tgt)
+    check_loss(out["lse"].cpu().numpy(), lse_ref, what="lse")
+    if V > 1:   # V = 1: every loss and gradient is exactly 0 (softmax of one logit is 1)
+        check_loss(out["loss"].cpu().numpy(), loss_ref, what="ce loss")
+        check_grad(bf16_to_f64(out["dA"]), dA_ref, "ce dA")
+        check_grad(bf16_to_f64(out["dE"]), dE_ref, "ce dE")
+    else:
+        assert np.all(np.abs(out["loss"].cpu().numpy()) <= 1e-6)
+        assert np.max(np.abs(bf16_to_f64(out["dA"]))) <= 1e-5 * np.max(np.abs(_dec(E)))
+
+
+def test_widest_head(B):
+    _say("widest head D=9216")
+    A, E, rp, ids, mask = _bce_inputs(9, 9216, 300, 3, 6)
+    _check_bce_case(B, A, E, rp, ids, mask)
+
+
+@pytest.mark.parametrize("D", [128, 768])
+def test_ce_every_target_ignored(B, D):
+    _say(f"ce every target ignored D={D}")
+    A, E, _, _, _ = _bce_inputs(33, D, 1100, 0, 7)
+    d = dev()
+    g = {"A": torch.from_numpy(A.view(np.int16)).to(d).view(torch.bfloat16),
+         "E": torch.from_numpy(E.view(np.int16)).to(d).view(torch.bfloat16),
+         "target": torch.full((33,), -100, dtype=torch.int64, device=d)}
+    out = run_ce(B, g)
+    _, lse_ref = H.ce_forward(_dec(A), _dec(E), np.full(33, -100))
+    check_loss(out["lse"].cpu().numpy(), lse_ref, what="lse")
+    assert np.all(out["loss"].cpu().numpy() == 0)
+    assert torch.count_nonzero(out["dA"].float()).item() == 0
+    assert torch.count_nonzero(out["dE"].float()).item() == 0

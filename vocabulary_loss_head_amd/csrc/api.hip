@@ -593,7 +593,10 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
     CL_HIP(cl::launch_targets(w.tw, p->T, p->V, p->nnz, p->pos_row_ptr, p->pos_ids, p->row_mask, p->pad_id,
                               nullptr, 0, st), "targets");
   }
-  if (p->T == 0) return CUTLOSS_OK;
+  if (p->T == 0) {   // no rows: dE = 0, E unchanged by the SGD step
+    if (dE_mode == 1) CL_HIP(cl::launch_zero_bytes(dE, (size_t)p->V * p->D * 2, st), "zero dE");
+    return CUTLOSS_OK;
+  }
   cl::FinalizeParams fp{};
   fp.T = p->T; fp.D = p->D; fp.V = p->V; fp.A = p->A; fp.E = p->E; fp.e_fp8 = e_fp8;
   fp.crow = w.tw.crow; fp.cids = w.tw.cids; fp.dloss = dloss; fp.mask = p->row_mask;
@@ -655,6 +658,7 @@ cutloss_status ce_run_chunked(const cutloss_ce_problem* p, const float* lse_in, 
     CL_HIP(cl::launch_targets(w.tw, p->T, p->V, p->T, nullptr, nullptr, nullptr, -1, p->target, p->ignore_index, st),
            "targets");
   }
+  if (p->T == 0 && !fwd && dE != nullptr) CL_HIP(cl::launch_zero_bytes(dE, (size_t)p->V * p->D * 2, st), "zero dE");
   if (p->T == 0 || (!fwd && !grad)) return CUTLOSS_OK;
   cl::FinalizeParams fp{};
   fp.T = p->T; fp.D = p->D; fp.V = p->V; fp.A = p->A; fp.E = p->E; fp.e_fp8 = e_fp8;

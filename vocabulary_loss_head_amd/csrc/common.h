@@ -111,6 +111,8 @@ hipError_t launch_targets(const TargetsWs& w, int64_t T, int64_t V, int64_t nnz,
 size_t targets_radix_blocks(int64_t nnz);
 
 hipError_t launch_zero_u64(unsigned long long* p, int n, hipStream_t st);
+// zero n bytes (n a multiple of 4) with a kernel
+hipError_t launch_zero_bytes(void* p, size_t n, hipStream_t st);
 // map[v] = index of v among the unique positive items, -1 for every other item v < V
 hipError_t launch_item_map(const TargetsWs& w, int64_t V, int64_t cap, int32_t* map, hipStream_t st);
 

@@ -352,6 +352,14 @@ __global__ void k_item_map(const int32_t* __restrict__ uitems, const int32_t* __
 }
 }  // namespace
 
+hipError_t launch_zero_bytes(void* p, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  if (n % 4 != 0) return hipErrorInvalidValue;
+  const int64_t n4 = (int64_t)(n / 4);
+  k_fill_i32<<<(unsigned)std::min<int64_t>((n4 + 255) / 256, 4096), 256, 0, st>>>((int32_t*)p, n4, 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_item_map(const TargetsWs& w, int64_t V, int64_t cap, int32_t* map, hipStream_t st) {
   if (V <= 0) return hipSuccess;
   k_fill_i32<<<(unsigned)std::min<int64_t>((V + 255) / 256, 4096), 256, 0, st>>>(map, V, -1);
