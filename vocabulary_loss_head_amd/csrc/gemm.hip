@@ -557,13 +557,11 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
         float wt = 0.0f, lt = 0.0f;
         if constexpr (WRITES_P) wt = t_ok ? p.w[t] : 0.0f;
         if constexpr (EPI == GEMM_EPI_CE_P) lt = t_ok ? p.lse[t] * kLog2e : 0.0f;
-        // blocked P: row t, columns mw + 32 mt + 8 j + 4 h + 0..3 = 8 contiguous bytes
-        uint16_t* prow = nullptr;
-        const int64_t pbs = (int64_t)p.p_bt * 32;
-        if constexpr (WRITES_P) {
-          const int64_t ts = t_st ? t : 0;
-          prow = p.P + ((ts / p.p_bt) * p.p_nvb + (mw >> 5)) * pbs + (ts % p.p_bt) * 32 + 4 * h;
-        }
+        (void)t_st;
+        // P image in LDS: item block b, tile row r, 16-byte group j of the block row (XOR
+        // swizzled by (r >> 2) & 3 so that 32 rows at once hit distinct banks), half h
+        const int pr = (int)(t - n0);
+        const uint32_t pimg = (uint32_t)(((int)((mw - m0) >> 5)) * (BN * 64) + pr * 64 + 8 * h);
         float relu = 0.0f, prod = 1.0f, lg = 0.0f, mx = kNegInf, sm = 0.0f, cnt = 0.0f;
         if constexpr (EPI == GEMM_EPI_CE_LSE) {
 #pragma unroll
@@ -607,12 +605,10 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
               }
             }
             if constexpr (WRITES_P) {
-              if (t_st) {
-                uint2 pk;
-                pk.x = pack2(f[0], f[1]);
-                pk.y = pack2(f[2], f[3]);
-                *(uint2*)(prow + mt * pbs + 8 * j) = pk;
-              }
+              uint2 pk;
+              pk.x = pack2(f[0], f[1]);
+              pk.y = pack2(f[2], f[3]);
+              *(uint2*)(ring + pimg + mt * (BN * 64) + ((j ^ ((pr >> 2) & 3)) << 4)) = pk;
             }
           }
           if constexpr (BCE_SUM) {
@@ -648,9 +644,32 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
           p.flags[(int64_t)tm * p.flag_ld + tn] = p.flag_gen;
       }
     };
+    if constexpr (WRITES_P) block_sync();       // the ring becomes the P image
     // (the CE gradient epilogue keeps its masks: without them it runs out of registers)
     if (EPI != GEMM_EPI_CE_P && p.v0 + m0 + kBM <= p.V && n0 + BN <= p.T) logit_tile(BoolC<false>{});
     else logit_tile(BoolC<true>{});
+    if constexpr (WRITES_P) {
+      // The tile's P is 8 item blocks x BN rows x 64 bytes, and each item block's rows are one
+      // contiguous run of the blocked layout (bt is a multiple of BN): copy it out in 16-byte
+      // pieces, consecutive threads on consecutive bytes of a run.
+      constexpr int IMG = 8 * BN * 64;
+      static_assert(IMG <= kNst * STAGE, "P image fits the ring");
+      block_sync();
+      const int64_t pbs = (int64_t)p.p_bt * 32;
+#pragma unroll 4
+      for (int k = tid; k < IMG / 16; k += kThreads) {
+        const int b = (16 * k) / (BN * 64);
+        const int rem = 16 * k - b * (BN * 64);
+        const int r = rem >> 6;
+        const int q = ((rem & 63) >> 4) ^ ((r >> 2) & 3);
+        const int64_t t = n0 + r;
+        if (t < p.p_rows) {
+          typedef int i32x4 __attribute__((ext_vector_type(4)));
+          const i32x4 x = *lds_ptr<i32x4>(ring0 + (uint32_t)(16 * k));
+          *(i32x4*)(p.P + ((t / p.p_bt) * p.p_nvb + ((m0 >> 5) + b)) * pbs + (t % p.p_bt) * 32 + 8 * q) = x;
+        }
+      }
+    }
   } else if constexpr (EPI == GEMM_EPI_ACC) {
     float* out = p.acc + (int64_t)tz * p.acc_slice;
     if (p.acc_trans) {
