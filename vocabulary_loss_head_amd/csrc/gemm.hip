@@ -1045,10 +1045,14 @@ hipError_t launch_transpose_chunk(const uint16_t* E, int64_t vlen, int64_t mc, i
 
 // Workgroup shape of a product: 4 waves (two workgroups per CU) for heads up to D = 1024,
 // where the logits epilogue and the short k loops gain most from the overlap, except the
-// dA product of very few rows (one row tile), which keeps 8 waves.
+// dA product of very few rows (one row tile) or over D >= 512 columns, and FP8 x FP8 logits,
+// which take 8 waves.
 int gemm_waves(const GemmParams& p) {
   if (p.D > 1024) return 8;
   if (p.epi == GEMM_EPI_ACC && p.M <= 128) return 8;
+  // dA product over a wide output (N = D >= 512): 256 x 256 tiles stream fewer operand bytes
+  // per flop than two 256 x 128 workgroups
+  if (p.epi == GEMM_EPI_ACC && p.N >= 512) return 8;
   if (p.a.fp8 && p.b.fp8) return 8;   // FP8 x FP8 logits: 4 waves would spill (two 8-register fragments per block)
   return 4;
 }
