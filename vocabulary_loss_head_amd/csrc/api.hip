@@ -10,7 +10,7 @@
 #include <string>
 #include <vector>
 
-#include "common.h"
+#include "launch.h"
 
 namespace {
 

@@ -11,7 +11,7 @@
 // item-major pairs, in row order.
 // All reductions run in a fixed order (no float atomics), so results are bitwise
 // reproducible.
-#include "common.h"
+#include "launch.h"
 
 namespace cl {
 

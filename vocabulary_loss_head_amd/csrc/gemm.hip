@@ -25,7 +25,7 @@
 // Workgroups take output tiles in an order that keeps each XCD (blockIdx % 8) on a
 // contiguous run of tiles: 8 row tiles by all column tiles, so the 32 workgroups an XCD
 // runs at once share their A and B tiles through that XCD's L2.
-#include "common.h"
+#include "launch.h"
 
 #define CL_GAS __attribute__((address_space(1)))
 

@@ -15,7 +15,7 @@
 //   4. stable radix sort of the unique pairs by row -> canonical CSR (items
 //      ascending within a row).
 #include <algorithm>
-#include "common.h"
+#include "launch.h"
 
 namespace cl {
 
