@@ -43,6 +43,22 @@ __device__ __forceinline__ bf16x8 cat_bf16(s16x4 lo, s16x4 hi) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// LDS DMA: each active lane copies 16 (or 4) bytes from global address sbase + voff to LDS
+// byte address lds + 16 * lane (4 * lane). sbase and lds are wave-uniform. Written as inline
+// asm so that the compiler's wait insertion does not track these copies: it would otherwise
+// wait for every copy in flight before each transposing LDS read (ds_read_b64_tr_b16), which
+// it cannot tell apart from the copies' destinations. Callers order every read of a
+// destination after the copy with an explicit vmcnt wait and a workgroup barrier. The
+// s_nop covers the M0-write to LDS-DMA hazard.
+__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 // 8 OCP E4M3FN bytes -> 8 bf16 (exact: every E4M3 value is a bf16 value).

@@ -36,6 +36,14 @@ namespace {
 
 constexpr int kRC = 32;          // streamed rows per chunk
 constexpr int kRing = 4;         // LDS buffers
+// LDS operand reads kept in flight ahead of their MFMAs: as many as the register budget
+// of two waves per SIMD leaves without spilling inside the chunk loop
+#ifndef CL_ROWS_READ_AHEAD
+#define CL_ROWS_READ_AHEAD 4
+#endif
+#ifndef CL_COLS_READ_AHEAD
+#define CL_COLS_READ_AHEAD 2
+#endif
 constexpr float kNegInf = -__builtin_inff();
 
 template <int D>
@@ -126,17 +134,19 @@ __device__ __forceinline__ void dma_chunk(const DmaOffsets<D>& dof, const uint16
     for (int j = 0; j <= G::LPWP; ++j) {
       if (j == G::LPWP && nb == G::LPWP) break;
       const int kb = DmaOffsets<D>::block(j, wv);
-      __builtin_amdgcn_global_load_lds((const CL_GAS void*)(cbase + 2 * (uint32_t)dof.off[j]),
-                                       (CL_LDS void*)(uintptr_t)(buf + kb * 1024), 16, 0, 0);
+      lds_dma16(cbase, 2 * (uint32_t)dof.off[j], buf + kb * 1024);
     }
   } else {
+    // the offsets of a short chunk are computed here from an opaque copy of the lane id,
+    // so that none of their terms is hoisted out of the chunk loop into live registers
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int j = 0; j <= G::LPWP; ++j) {
       if (j == G::LPWP && nb == G::LPWP) break;
       const int kb = DmaOffsets<D>::block(j, wv);
-      const int32_t o = DmaOffsets<D>::at(kb, lane, lim);
-      __builtin_amdgcn_global_load_lds((const CL_GAS void*)(cbase + 2 * (uint32_t)o),
-                                       (CL_LDS void*)(uintptr_t)(buf + kb * 1024), 16, 0, 0);
+      const int32_t o = DmaOffsets<D>::at(kb, ln, lim);
+      lds_dma16(cbase, 2 * (uint32_t)o, buf + kb * 1024);
     }
   }
 }
@@ -146,7 +156,7 @@ __device__ __forceinline__ void dma_chunk(const DmaOffsets<D>& dof, const uint16
 __device__ __forceinline__ void dma_vec(const float* v, int64_t row0, int64_t n, uint32_t buf, int lane) {
   int64_t r = row0 + pi_row(lane & 31);
   r = r < n ? r : n - 1;
-  if (lane < 32) __builtin_amdgcn_global_load_lds((const CL_GAS void*)(v + r), (CL_LDS void*)(uintptr_t)buf, 4, 0, 0);
+  if (lane < 32) lds_dma4(v, 4 * (uint32_t)r, buf);
 }
 
 template <int D, bool FP8>
@@ -329,16 +339,30 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // y = logits of the chunk in buffer `boff` for the MT stationary tiles.
-template <int D, int MT>
+template <int D, int MT, int RA>
 __device__ __forceinline__ void chunk_logits(const bf16x8 (&sf)[MT][D / 16], f32x16 (&y)[MT], const ReadBase<D>& rb,
                                              uint32_t boff) {
+  constexpr int KS = D / 16;
+  constexpr int PF = KS < RA ? KS : RA;
+  bf16x8 ra[PF];
+#pragma unroll
+  for (int j = 0; j < PF; ++j) ra[j] = read_row_piece<D>(rb, boff, j);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) y[mt] = f32x16{};
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const bf16x8 ra = read_row_piece<D>(rb, boff, ks);
+  for (int ks = 0; ks < KS; ++ks) {
+    const bf16x8 a = ra[ks % PF];
+    if (ks + PF < KS) ra[ks % PF] = read_row_piece<D>(rb, boff, ks + PF);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) y[mt] = mfma32(ra, sf[mt][ks], y[mt]);
+    for (int mt = 0; mt < MT; ++mt) y[mt] = mfma32(a, sf[mt][ks], y[mt]);
+  }
+  // keep PF reads in flight: the first PF reads, then each step's MFMAs followed by the
+  // read that refills the slot they consumed
+  __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
+    if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
 }
 
@@ -358,24 +382,30 @@ __device__ __forceinline__ void epilogue(const f32x16 (&y)[MT], Epi<MT, RM>& ep,
   ep.end();
 }
 
-template <int D, int MT>
+template <int D, int MT, int RA>
 __device__ __forceinline__ void grad_only(f32x16 (&acc)[MT][D / 32], const FPack<MT>& fi, const ReadBase<D>& rb,
                                           uint32_t boff) {
+  constexpr int NI = 2 * (D / 32);
+  constexpr int PF = NI < RA ? NI : RA;
+  bf16x8 rbuf[PF];
 #pragma unroll
-  for (int it = 0; it < 2 * (D / 32); ++it) {
+  for (int j = 0; j < PF; ++j) rbuf[j] = read_col_piece<D>(rb, boff, j % (D / 32), j / (D / 32));
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
     const int nt = it % (D / 32), kk = it / (D / 32);
-    const bf16x8 b = read_col_piece<D>(rb, boff, nt, kk);
+    const bf16x8 b = rbuf[it % PF];
+    if (it + PF < NI) rbuf[it % PF] = read_col_piece<D>(rb, boff, (it + PF) % (D / 32), (it + PF) / (D / 32));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt][nt] = mfma32(fi.op(mt, kk), b, acc[mt][nt]);
   }
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
+    if (it + PF < NI) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
 }
 
-// ------------------------------------------------------------------------------------
-// The chunk loop shared by both sweeps. issue(c, boff) enqueues the DMA of chunk c into
-// the buffer at ring offset boff (NPER0 instructions on wave 0, NPER on the others);
-// prep(c, boff) points the epilogue at the chunk's per-row inputs. Three chunks are in
-// flight beyond the current one.
-// ------------------------------------------------------------------------------------
 // CE gradient filter (Cut Your Losses article, the note on the softmax tail below numerical
 // precision): true when some |P| of the wave's chunk tile is at least the bf16 pattern
 // `bits`; wave-uniform.
@@ -394,7 +424,13 @@ __device__ __forceinline__ bool wave_any_at_least(const FPack<MT>& f, uint32_t b
   return __builtin_amdgcn_ballot_w64(m >= bits) != 0;
 }
 
-template <int D, int MT, int RM, int NPER0, int NPER, class Issue, class Prep>
+// ------------------------------------------------------------------------------------
+// The chunk loop shared by both sweeps. issue(c, boff) enqueues the DMA of chunk c into
+// the buffer at ring offset boff (NPER0 instructions on wave 0, NPER on the others);
+// prep(c, boff) points the epilogue at the chunk's per-row inputs. Three chunks are in
+// flight beyond the current one.
+// ------------------------------------------------------------------------------------
+template <int D, int MT, int RM, int NPER0, int NPER, int RA, class Issue, class Prep>
 __device__ __forceinline__ void sweep_loop(int nch, int64_t rows_left0, const bf16x8 (&sf)[MT][D / 16],
                                            f32x16 (&acc)[MT][D / 32], Epi<MT, RM>& ep, const ReadBase<D>& rb,
                                            int h, int wv, uint32_t filter_bits, Issue issue, Prep prep) {
@@ -403,6 +439,9 @@ __device__ __forceinline__ void sweep_loop(int nch, int64_t rows_left0, const bf
   constexpr int AHEAD = 3;
   static_assert(2 * NPER0 < 16 && kRing == 4, "vmcnt / ring");
   if (nch <= 0) return;
+  // the stationary operand's loads complete here: the compiler does not count the LDS
+  // copies, so no wait of its own may remain pending inside the loop
+  wait_vm<0>();
 #pragma unroll
   for (int k = 0; k < AHEAD; ++k)
     if (k < nch) issue(k, (uint32_t)(k * G::BUF));
@@ -420,7 +459,7 @@ __device__ __forceinline__ void sweep_loop(int nch, int64_t rows_left0, const bf
     block_sync();
     if (c + AHEAD < nch) issue(c + AHEAD, (uint32_t)(((c + AHEAD) & (kRing - 1)) * G::BUF));
     prep(c, boff);
-    chunk_logits<D, MT>(sf, y, rb, boff);
+    chunk_logits<D, MT, RA>(sf, y, rb, boff);
     const int64_t left = rows_left0 - (int64_t)c * kRC;
     if (left < kRC) {
       mask_tail<MT>(y, (int)left, h);
@@ -431,7 +470,7 @@ __device__ __forceinline__ void sweep_loop(int nch, int64_t rows_left0, const bf
     if constexpr (HAS_F) {
       bool keep = true;
       if constexpr (RM == 4 || RM == 6) keep = filter_bits == 0 || wave_any_at_least(f, filter_bits);
-      if (keep) grad_only<D, MT>(acc, f, rb, boff);
+      if (keep) grad_only<D, MT, RA>(acc, f, rb, boff);
     }
   }
 }
@@ -502,7 +541,7 @@ __global__ __launch_bounds__(256, Tiling<D>::WPE) void k_rows2(const SweepParams
     dma_chunk<D>(dof, E, r_begin + (int64_t)c * kRC, r_end, ring0 + boff, wv, lane);
   };
   auto prep = [&](int, uint32_t) {};
-  sweep_loop<D, MT, RM, G::LPWP + 1, G::LPWP>(nch, r_end - r_begin, sf, acc, ep, rb, h, wv, p.filter_bits, issue, prep);
+  sweep_loop<D, MT, RM, G::LPWP + 1, G::LPWP, CL_ROWS_READ_AHEAD>(nch, r_end - r_begin, sf, acc, ep, rb, h, wv, p.filter_bits, issue, prep);
 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -593,7 +632,7 @@ __global__ __launch_bounds__(256, Tiling<D>::WPE) void k_cols2(const SweepParams
     if constexpr (KIND == 1) dma_vec(p.lse, r0, p.T, vb + kRC * 4, lane);
   };
   auto prep = [&](int, uint32_t boff) { ep.vb = vec0 + (boff / G::BUF) * (NV * kRC * 4); };
-  sweep_loop<D, MT, RM, G::LPWP + 1 + NV, G::LPWP + NV>(nch, p.T, sf, acc, ep, rb, h, wv, p.filter_bits, issue, prep);
+  sweep_loop<D, MT, RM, G::LPWP + 1 + NV, G::LPWP + NV, CL_COLS_READ_AHEAD>(nch, p.T, sf, acc, ep, rb, h, wv, p.filter_bits, issue, prep);
 
   // sparse positive term: index of each item of the block in the sorted unique-item list
   for (int k = tid; k < SB; k += 256) {
