@@ -168,7 +168,10 @@ struct Loader {
   }
 };
 
-template <int NW, int R, bool KC, bool Q8 = false>
+// ASM: issue the copies as inline asm (lds_dma16), for kernels whose every global load is an
+// LDS copy; kernels that also stage an operand through registers keep the builtin, so that
+// the compiler's waits for those registers count the copies issued after them.
+template <int NW, int R, bool KC, bool Q8 = false, bool ASM = false>
 __device__ __forceinline__ void dma_stage(const Loader<NW, R, KC, false, Q8>& ld, const GemmOperand& op, int64_t outer0,
                                           int64_t k0, uint32_t lds, int wv, int lane) {
   using TL = Tile<NW, R, KC>;
@@ -176,16 +179,20 @@ __device__ __forceinline__ void dma_stage(const Loader<NW, R, KC, false, Q8>& ld
   const char* org = LD::origin(op, outer0, k0);
   if (!LD::tail(op, k0)) {
 #pragma unroll
-    for (int j = 0; j < TL::PER_WAVE; ++j)
-      __builtin_amdgcn_global_load_lds((const CL_GAS void*)(org + LD::ESZ * (size_t)ld.off[j]),
-                                       (CL_LDS void*)(uintptr_t)(lds + (wv * TL::PER_WAVE + j) * 1024), 16, 0, 0);
+    for (int j = 0; j < TL::PER_WAVE; ++j) {
+      const uint32_t dst = lds + (wv * TL::PER_WAVE + j) * 1024;
+      if constexpr (ASM) lds_dma16(org, (uint32_t)(LD::ESZ * ld.off[j]), dst);
+      else __builtin_amdgcn_global_load_lds((const CL_GAS void*)(org + LD::ESZ * (size_t)ld.off[j]),
+                                            (CL_LDS void*)(uintptr_t)dst, 16, 0, 0);
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < TL::PER_WAVE; ++j) {
       const int kb = wv * TL::PER_WAVE + j;
       const int64_t o = LD::clamped(op, outer0, k0, kb * 1024 + 16 * lane);
-      __builtin_amdgcn_global_load_lds((const CL_GAS void*)(org + LD::ESZ * o), (CL_LDS void*)(uintptr_t)(lds + kb * 1024),
-                                       16, 0, 0);
+      if constexpr (ASM) lds_dma16(org, (uint32_t)(LD::ESZ * o), lds + kb * 1024);
+      else __builtin_amdgcn_global_load_lds((const CL_GAS void*)(org + LD::ESZ * o), (CL_LDS void*)(uintptr_t)(lds + kb * 1024),
+                                            16, 0, 0);
     }
   }
 }
@@ -463,6 +470,10 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
   RegStage16<NW, BN, BKC> rb;
   // fp8 register loads are issued before the stage's DMAs, so waiting for them at the
   // next step does not wait for those DMAs.
+  constexpr bool ALL_DMA = !AF8 && !BF8 && !ARG && !BRG;
+  // with every copy invisible to the compiler's waits, none of its own loads may be left
+  // pending inside the main loop
+  if constexpr (ALL_DMA) wait_vm<0>();
   auto issue = [&](int s) {
     const uint32_t so = ring0 + (uint32_t)((s % kNst) * STAGE);
     const int64_t k0 = stage_k(s);
@@ -470,8 +481,8 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
     if constexpr (BF8) sb.load(lb, p.b, n0, k0, tid);
     if constexpr (ARG) ra.load(la, p.a, m0, k0, tid);
     if constexpr (BRG) rb.load(lb, p.b, n0, k0, tid);
-    if constexpr (!AF8 && !ARG) dma_stage<NW, kBM, AKC, Q8>(la, p.a, m0, k0, so, wv, lane);
-    if constexpr (!BF8 && !BRG) dma_stage<NW, BN, BKC, Q8>(lb, p.b, n0, k0, so + TA::BYTES, wv, lane);
+    if constexpr (!AF8 && !ARG) dma_stage<NW, kBM, AKC, Q8, ALL_DMA>(la, p.a, m0, k0, so, wv, lane);
+    if constexpr (!BF8 && !BRG) dma_stage<NW, BN, BKC, Q8, ALL_DMA>(lb, p.b, n0, k0, so + TA::BYTES, wv, lane);
   };
   auto store_fp8 = [&](int s) {
     const uint32_t so = ring0 + (uint32_t)((s % kNst) * STAGE);
