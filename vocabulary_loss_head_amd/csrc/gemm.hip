@@ -168,6 +168,14 @@ struct Loader {
   }
 };
 
+// Tail stages compute their clamped offsets from an opaque copy of the thread index, so
+// that none of those terms is hoisted out of the main loop into registers held for the
+// whole loop (they pushed the register-staged products into spilling).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // ASM: issue the copies as inline asm (lds_dma16), for kernels whose every global load is an
 // LDS copy; kernels that also stage an operand through registers keep the builtin, so that
 // the compiler's waits for those registers count the copies issued after them.
@@ -186,10 +194,11 @@ __device__ __forceinline__ void dma_stage(const Loader<NW, R, KC, false, Q8>& ld
                                             (CL_LDS void*)(uintptr_t)dst, 16, 0, 0);
     }
   } else {
+    const int ln = opaque(lane);
 #pragma unroll
     for (int j = 0; j < TL::PER_WAVE; ++j) {
       const int kb = wv * TL::PER_WAVE + j;
-      const int64_t o = LD::clamped(op, outer0, k0, kb * 1024 + 16 * lane);
+      const int64_t o = LD::clamped(op, outer0, k0, kb * 1024 + 16 * ln);
       if constexpr (ASM) lds_dma16(org, (uint32_t)(LD::ESZ * o), lds + kb * 1024);
       else __builtin_amdgcn_global_load_lds((const CL_GAS void*)(org + LD::ESZ * o), (CL_LDS void*)(uintptr_t)(lds + kb * 1024),
                                             16, 0, 0);
@@ -208,9 +217,10 @@ struct Fp8Stage {
 #pragma unroll
       for (int i = 0; i < TL::PIECES; ++i) q[i] = *(const uint2*)(org + ld.off[i]);
     } else {
+      const int t = opaque(tid);
 #pragma unroll
       for (int i = 0; i < TL::PIECES; ++i)
-        q[i] = *(const uint2*)(org + LD::clamped(op, outer0, k0, 16 * (tid + 64 * NW * i)));
+        q[i] = *(const uint2*)(org + LD::clamped(op, outer0, k0, 16 * (t + 64 * NW * i)));
     }
   }
   __device__ __forceinline__ void store(uint32_t lds, int tid) const {
@@ -235,9 +245,10 @@ struct RegStage16 {
 #pragma unroll
       for (int i = 0; i < TL::PIECES; ++i) q[i] = *(const v4i*)(org + 2 * (size_t)ld.off[i]);
     } else {
+      const int t = opaque(tid);
 #pragma unroll
       for (int i = 0; i < TL::PIECES; ++i)
-        q[i] = *(const v4i*)(org + 2 * LD::clamped(op, outer0, k0, 16 * (tid + 64 * NW * i)));
+        q[i] = *(const v4i*)(org + 2 * LD::clamped(op, outer0, k0, 16 * (t + 64 * NW * i)));
     }
   }
   __device__ __forceinline__ void store(uint32_t lds, int tid) const {

@@ -1,18 +1,21 @@
 // Logit-tile sweeps for bf16 streamed operands and D in {64, 128, 256} (gfx950).
 //
-// Same computation as the register-staged sweeps in sweep.hip (derivation from Cut
-// Binary Cross Entropy §III-A..C and the Cut Your Losses article there), arranged for
-// measured CDNA4 limits:
-//  * each wave holds MT 32-row tiles of the stationary matrix (64 rows for D = 256), so
-//    every LDS read of a streamed chunk feeds MT MFMAs in the logit product and in the
-//    gradient product: half the LDS traffic per MFMA of a one-tile wave;
-//  * gradient modes overlap VALU and matrix work inside each wave: the sigmoid/exp
-//    epilogue of chunk c is issued in one basic block with the gradient MFMAs of chunk
-//    c-1 (shaped by sched_group_barrier), so the epilogue hides under matrix work;
+// The computation follows Cut Binary Cross Entropy §III-A..C (dense softplus term, sigmoid
+// gradient recomputed per tile) and the Cut Your Losses article (online logsumexp, softmax
+// gradient), arranged for measured CDNA4 limits:
+//  * each wave holds MT 32-row tiles of the stationary matrix in VGPRs (MT = 2 for
+//    D <= 128, 1 for D = 256, where the 128 gradient accumulators and 64 stationary
+//    registers of a tile fill the 256 VGPRs of two waves per SIMD), so every LDS read of a
+//    streamed chunk feeds MT MFMAs in the logit product and in the gradient product;
+//  * the logit and gradient products keep several LDS operand reads in flight ahead of
+//    their MFMAs; the sigmoid/exp epilogue of one wave runs while the other wave of the
+//    SIMD issues matrix work;
 //  * streamed 32-row chunks go HBM/L2 -> LDS by global_load_lds_dwordx4 (no staging
-//    registers, no ds_write) into a 4-buffer ring inside one LDS array. Each step waits
-//    for its own DMA with an explicit vmcnt, one s_barrier publishes the chunk to the
-//    workgroup and retires the oldest buffer, and the next DMA is issued right after;
+//    registers, no ds_write) into a 4-buffer ring inside one LDS array. The copies are
+//    issued as inline asm (lds_dma16): the compiler would otherwise wait for all copies in
+//    flight before every transposing read. Each step waits for its own copies with an
+//    explicit vmcnt, one s_barrier publishes the chunk to the workgroup and retires the
+//    oldest buffer, and the next copies are issued right after;
 //  * rows past the end of a range are fetched as copies of the last valid row (never
 //    out of bounds) and their logits are set to -inf, which makes every epilogue
 //    (softplus, sigmoid, exp) contribute exactly zero; only the last chunk of a range
