@@ -109,8 +109,9 @@ struct Plan {
 // chip about twice; a multiple of 8 so each split maps to one XCD.
 Plan make_plan(int64_t T, int64_t D, int64_t V, int64_t cap, int e_fp8) {
   Plan pl{T, D, V, cap, 1, 0};
-  const int64_t rpb = cl::sweep2_rows_supported(D, e_fp8) ? cl::sweep2_rows_per_block(D) : 128;
-  const int64_t target = 1024;
+  const bool sw = cl::sweep2_rows_supported(D, e_fp8);
+  const int64_t rpb = sw ? cl::sweep2_rows_per_block(D) : 128;
+  const int64_t target = 4096 / (sw ? cl::sweep2_waves_per_block(D) : 4);   // about 4096 waves
   const int64_t nsb = (T + rpb - 1) / rpb;
   int64_t ns = nsb > 0 ? (target + nsb - 1) / nsb : 1;
   const int64_t max_ns = (V + 31) / 32;

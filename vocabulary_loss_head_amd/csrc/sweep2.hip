@@ -49,6 +49,14 @@ constexpr int kRing = 4;         // LDS buffers
 #endif
 constexpr float kNegInf = -__builtin_inff();
 
+// For each D: MT stationary 32-row tiles per wave, NW waves per workgroup and WPE
+// workgroups per CU (two waves per SIMD in every case). With NW = 8 the two waves of a
+// SIMD belong to one workgroup and run out of phase (see sweep_loop).
+template <int D> struct Tiling;
+template <> struct Tiling<64> { static constexpr int MT = 2, NW = 4, WPE = 2; };
+template <> struct Tiling<128> { static constexpr int MT = 2, NW = 4, WPE = 1; };
+template <> struct Tiling<256> { static constexpr int MT = 1, NW = 8, WPE = 1; };
+
 template <int D>
 struct Geo {
   static constexpr int NCH = D / 8;             // 16-byte pieces per row
@@ -56,21 +64,10 @@ struct Geo {
   static constexpr int ROWP = ROW + 16;         // LDS row stride
   static constexpr int KBP = (kRC * ROWP + 1023) / 1024;   // DMA blocks per chunk (4 n + 1)
   static constexpr int BUF = KBP * 1024;        // LDS bytes per ring buffer
-  static constexpr int LPWP = KBP / 4;          // blocks of every wave; wave 0 also takes the last
-  static_assert(KBP % 4 == 1, "padded chunk layout");
+  static constexpr int LPWP = KBP / Tiling<D>::NW;   // blocks of every wave; wave 0 also takes the last
+  static_assert(KBP % Tiling<D>::NW == 1, "padded chunk layout");
 };
 
-// tiles per wave and waves per SIMD for each D
-template <int D> struct Tiling;
-template <> struct Tiling<64> { static constexpr int MT = 2, WPE = 2; };
-template <> struct Tiling<128> { static constexpr int MT = 2, WPE = 1; };
-#ifndef CL_T256_WPE
-#define CL_T256_WPE 2
-#endif
-#ifndef CL_T256_MT
-#define CL_T256_MT 1
-#endif
-template <> struct Tiling<256> { static constexpr int MT = CL_T256_MT, WPE = CL_T256_WPE; };
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 template <class T>
@@ -430,18 +427,32 @@ __device__ __forceinline__ bool wave_any_at_least(const FPack<MT>& f, uint32_t b
 // ------------------------------------------------------------------------------------
 // The chunk loop shared by both sweeps. issue(c, boff) enqueues the DMA of chunk c into
 // the buffer at ring offset boff (NPER0 instructions on wave 0, NPER on the others);
-// prep(c, boff) points the epilogue at the chunk's per-row inputs. Three chunks are in
-// flight beyond the current one.
+// prep(c, boff) points the epilogue at the chunk's per-row inputs.
+// Per chunk a wave computes the logit tile (matrix work), its epilogue (VALU work) and the
+// gradient product (matrix work). With 8-wave workgroups the second half of the waves
+// lags by a chunk phase: in the period of chunk c it runs the epilogue and gradient
+// product of chunk c - 1 and then the logits of chunk c, whose tile it keeps for the next
+// period. The two waves that share a SIMD (wv and wv + 4) thus offer VALU work while the
+// other issues MFMAs. The lagging waves still read chunk c - 1 during period c, so only
+// two chunks are in flight beyond the current one; otherwise three.
 // ------------------------------------------------------------------------------------
+template <int D, int MT, int RM, bool TAIL>
+__device__ __forceinline__ void epilogue_and_mask(f32x16 (&y)[MT], Epi<MT, RM>& ep, FPack<MT>& f, int64_t left, int h) {
+  if (TAIL) mask_tail<MT>(y, (int)left, h);
+  epilogue<MT, RM, TAIL>(y, ep, f, h);
+}
+
 template <int D, int MT, int RM, int NPER0, int NPER, int RA, class Issue, class Prep>
 __device__ __forceinline__ void sweep_loop(int nch, int64_t rows_left0, const bf16x8 (&sf)[MT][D / 16],
                                            f32x16 (&acc)[MT][D / 32], Epi<MT, RM>& ep, const ReadBase<D>& rb,
                                            int h, int wv, uint32_t filter_bits, Issue issue, Prep prep) {
   using G = Geo<D>;
   constexpr bool HAS_F = EpiHasF<RM>::value;
-  constexpr int AHEAD = 3;
+  constexpr bool SHIFT = Tiling<D>::NW == 8;
+  constexpr int AHEAD = SHIFT ? 2 : 3;
   static_assert(2 * NPER0 < 16 && kRing == 4, "vmcnt / ring");
   if (nch <= 0) return;
+  const bool lag = SHIFT && wv >= 4;       // wave-uniform
   // the stationary operand's loads complete here: the compiler does not count the LDS
   // copies, so no wait of its own may remain pending inside the loop
   wait_vm<0>();
@@ -450,10 +461,21 @@ __device__ __forceinline__ void sweep_loop(int nch, int64_t rows_left0, const bf
     if (k < nch) issue(k, (uint32_t)(k * G::BUF));
   FPack<MT> f;
   f32x16 y[MT];
-  for (int c = 0; c < nch; ++c) {
-    const uint32_t boff = (uint32_t)((c & (kRing - 1)) * G::BUF);
-    // chunk c in LDS: own DMAs of later chunks (up to AHEAD - 1) may stay in flight
-    const int later = min(nch - 1 - c, AHEAD - 1);
+  // epilogue and gradient product of chunk k (buffer at ring offset bk), y holding its logits
+  auto finish = [&](int k, uint32_t bk) {
+    const int64_t left = rows_left0 - (int64_t)k * kRC;
+    if (left < kRC) epilogue_and_mask<D, MT, RM, true>(y, ep, f, left, h);
+    else epilogue_and_mask<D, MT, RM, false>(y, ep, f, left, h);
+    if constexpr (HAS_F) {
+      bool keep = true;
+      if constexpr (RM == 4 || RM == 6) keep = filter_bits == 0 || wave_any_at_least(f, filter_bits);
+      if (keep) grad_only<D, MT, RA>(acc, f, rb, bk);
+    }
+  };
+  // top of the period of chunk c: own copies of chunk c done, chunk c published, copies
+  // of chunk c + AHEAD issued
+  auto period = [&](int c) {
+    const int later = min(nch - 1 - c, AHEAD - 1);   // own later chunks left in flight
     if (wv == 0) {
       if (later >= 2) wait_vm<2 * NPER0>(); else if (later == 1) wait_vm<NPER0>(); else wait_vm<0>();
     } else {
@@ -461,20 +483,31 @@ __device__ __forceinline__ void sweep_loop(int nch, int64_t rows_left0, const bf
     }
     block_sync();
     if (c + AHEAD < nch) issue(c + AHEAD, (uint32_t)(((c + AHEAD) & (kRing - 1)) * G::BUF));
-    prep(c, boff);
+  };
+  if (!lag) {
+    for (int c = 0; c < nch; ++c) {
+      const uint32_t boff = (uint32_t)((c & (kRing - 1)) * G::BUF);
+      period(c);
+      prep(c, boff);
+      chunk_logits<D, MT, RA>(sf, y, rb, boff);
+      finish(c, boff);
+    }
+    return;
+  }
+  period(0);
+  chunk_logits<D, MT, RA>(sf, y, rb, 0);
+  for (int c = 1; c < nch; ++c) {
+    const uint32_t boff = (uint32_t)((c & (kRing - 1)) * G::BUF);
+    const uint32_t bprev = (uint32_t)(((c - 1) & (kRing - 1)) * G::BUF);
+    period(c);
+    prep(c - 1, bprev);
+    finish(c - 1, bprev);
     chunk_logits<D, MT, RA>(sf, y, rb, boff);
-    const int64_t left = rows_left0 - (int64_t)c * kRC;
-    if (left < kRC) {
-      mask_tail<MT>(y, (int)left, h);
-      epilogue<MT, RM, true>(y, ep, f, h);
-    } else {
-      epilogue<MT, RM, false>(y, ep, f, h);
-    }
-    if constexpr (HAS_F) {
-      bool keep = true;
-      if constexpr (RM == 4 || RM == 6) keep = filter_bits == 0 || wave_any_at_least(f, filter_bits);
-      if (keep) grad_only<D, MT, RA>(acc, f, rb, boff);
-    }
+  }
+  {
+    const uint32_t blast = (uint32_t)(((nch - 1) & (kRing - 1)) * G::BUF);
+    prep(nch - 1, blast);
+    finish(nch - 1, blast);
   }
 }
 
@@ -492,13 +525,13 @@ template <> struct RowsRM<4> { static constexpr int RM = 4; };
 template <> struct RowsRM<5> { static constexpr int RM = 7; };
 
 template <int D, int MODE>
-__global__ __launch_bounds__(256, Tiling<D>::WPE) void k_rows2(const SweepParams p) {
+__global__ __launch_bounds__(64 * Tiling<D>::NW, Tiling<D>::WPE) void k_rows2(const SweepParams p) {
   using G = Geo<D>;
   constexpr int MT = Tiling<D>::MT;
   constexpr int RM = RowsRM<MODE>::RM;
   constexpr bool HAS_F = EpiHasF<RM>::value;
   constexpr int KS = D / 16, NT = D / 32;
-  constexpr int SB = 128 * MT;                  // stationary rows per workgroup
+  constexpr int SB = 32 * MT * Tiling<D>::NW;   // stationary rows per workgroup
   __shared__ __attribute__((aligned(1024))) char ring[kRing * G::BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
@@ -591,13 +624,13 @@ __global__ __launch_bounds__(256, Tiling<D>::WPE) void k_rows2(const SweepParams
 // E <- round(E - lr dE) in place.
 // ------------------------------------------------------------------------------------
 template <int D, int KIND, int EPI, bool SFP8>
-__global__ __launch_bounds__(256, Tiling<D>::WPE) void k_cols2(const SweepParams p) {
+__global__ __launch_bounds__(64 * Tiling<D>::NW, Tiling<D>::WPE) void k_cols2(const SweepParams p) {
   using G = Geo<D>;
   constexpr int MT = Tiling<D>::MT;
   constexpr int RM = KIND == 0 ? 5 : 6;
   constexpr int NT = D / 32, KS = D / 16;
   constexpr int NV = KIND == 1 ? 2 : 1;     // per-row vectors streamed with A: w (and lse)
-  constexpr int SB = 128 * MT;
+  constexpr int SB = 32 * MT * Tiling<D>::NW;
   __shared__ __attribute__((aligned(1024))) char ring[kRing * G::BUF];
   __shared__ __attribute__((aligned(256))) float vecs[kRing][NV][kRC];
   __shared__ int uix[SB];
@@ -638,7 +671,7 @@ __global__ __launch_bounds__(256, Tiling<D>::WPE) void k_cols2(const SweepParams
   sweep_loop<D, MT, RM, G::LPWP + 1 + NV, G::LPWP + NV, CL_COLS_READ_AHEAD>(nch, p.T, sf, acc, ep, rb, h, wv, p.filter_bits, issue, prep);
 
   // sparse positive term: index of each item of the block in the sorted unique-item list
-  for (int k = tid; k < SB; k += 256) {
+  for (int k = tid; k < SB; k += 64 * Tiling<D>::NW) {
     const int64_t v = v_blk + k;
     const int nu = p.counts[2];
     int lo = 0, hi = nu;
@@ -680,8 +713,9 @@ __global__ __launch_bounds__(256, Tiling<D>::WPE) void k_cols2(const SweepParams
 
 template <int D>
 hipError_t rows2_d(const SweepParams& p, int mode, hipStream_t st) {
-  const int nsb = (int)((p.T + 128 * Tiling<D>::MT - 1) / (128 * Tiling<D>::MT));
-  const dim3 grid((unsigned)(nsb * p.n_splits)), block(256);
+  constexpr int SB = 32 * Tiling<D>::MT * Tiling<D>::NW;
+  const int nsb = (int)((p.T + SB - 1) / SB);
+  const dim3 grid((unsigned)(nsb * p.n_splits)), block(64 * Tiling<D>::NW);
   switch (mode) {
     case 0: k_rows2<D, 0><<<grid, block, 0, st>>>(p); break;
     case 1: k_rows2<D, 1><<<grid, block, 0, st>>>(p); break;
@@ -696,8 +730,8 @@ hipError_t rows2_d(const SweepParams& p, int mode, hipStream_t st) {
 
 template <int D>
 hipError_t cols2_d(const SweepParams& p, int kind, int epi, hipStream_t st) {
-  const int64_t sb = 128 * Tiling<D>::MT;
-  const dim3 grid((unsigned)((p.V + sb - 1) / sb)), block(256);
+  const int64_t sb = 32 * Tiling<D>::MT * Tiling<D>::NW;
+  const dim3 grid((unsigned)((p.V + sb - 1) / sb)), block(64 * Tiling<D>::NW);
   const int key = kind * 4 + epi * 2 + (p.e_fp8 ? 1 : 0);
   switch (key) {
     case 0: k_cols2<D, 0, 0, false><<<grid, block, 0, st>>>(p); break;
@@ -717,10 +751,19 @@ bool sweep2_rows_supported(int64_t D, int e_fp8) { return !e_fp8 && (D == 64 || 
 bool sweep2_cols_supported(int64_t D) { return D == 64 || D == 128 || D == 256; }
 int sweep2_rows_per_block(int64_t D) {
   switch (D) {
-    case 64: return 128 * Tiling<64>::MT;
-    case 128: return 128 * Tiling<128>::MT;
-    case 256: return 128 * Tiling<256>::MT;
+    case 64: return 32 * Tiling<64>::MT * Tiling<64>::NW;
+    case 128: return 32 * Tiling<128>::MT * Tiling<128>::NW;
+    case 256: return 32 * Tiling<256>::MT * Tiling<256>::NW;
     default: return 128;
+  }
+}
+
+int sweep2_waves_per_block(int64_t D) {
+  switch (D) {
+    case 64: return Tiling<64>::NW;
+    case 128: return Tiling<128>::NW;
+    case 256: return Tiling<256>::NW;
+    default: return 4;
   }
 }
 
