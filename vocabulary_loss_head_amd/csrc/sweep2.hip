@@ -44,6 +44,9 @@ constexpr int kRing = 4;         // LDS buffers
 #ifndef CL_ROWS_READ_AHEAD
 #define CL_ROWS_READ_AHEAD 4
 #endif
+#ifndef CL_COLS_LOGITS_READ_AHEAD
+#define CL_COLS_LOGITS_READ_AHEAD 4
+#endif
 #ifndef CL_COLS_READ_AHEAD
 #define CL_COLS_READ_AHEAD 2
 #endif
@@ -442,7 +445,7 @@ __device__ __forceinline__ void epilogue_and_mask(f32x16 (&y)[MT], Epi<MT, RM>& 
   epilogue<MT, RM, TAIL>(y, ep, f, h);
 }
 
-template <int D, int MT, int RM, int NPER0, int NPER, int RA, class Issue, class Prep>
+template <int D, int MT, int RM, int NPER0, int NPER, int RAL, int RAG, class Issue, class Prep>
 __device__ __forceinline__ void sweep_loop(int nch, int64_t rows_left0, const bf16x8 (&sf)[MT][D / 16],
                                            f32x16 (&acc)[MT][D / 32], Epi<MT, RM>& ep, const ReadBase<D>& rb,
                                            int h, int wv, uint32_t filter_bits, Issue issue, Prep prep) {
@@ -469,7 +472,7 @@ __device__ __forceinline__ void sweep_loop(int nch, int64_t rows_left0, const bf
     if constexpr (HAS_F) {
       bool keep = true;
       if constexpr (RM == 4 || RM == 6) keep = filter_bits == 0 || wave_any_at_least(f, filter_bits);
-      if (keep) grad_only<D, MT, RA>(acc, f, rb, bk);
+      if (keep) grad_only<D, MT, RAG>(acc, f, rb, bk);
     }
   };
   // top of the period of chunk c: own copies of chunk c done, chunk c published, copies
@@ -489,20 +492,20 @@ __device__ __forceinline__ void sweep_loop(int nch, int64_t rows_left0, const bf
       const uint32_t boff = (uint32_t)((c & (kRing - 1)) * G::BUF);
       period(c);
       prep(c, boff);
-      chunk_logits<D, MT, RA>(sf, y, rb, boff);
+      chunk_logits<D, MT, RAL>(sf, y, rb, boff);
       finish(c, boff);
     }
     return;
   }
   period(0);
-  chunk_logits<D, MT, RA>(sf, y, rb, 0);
+  chunk_logits<D, MT, RAL>(sf, y, rb, 0);
   for (int c = 1; c < nch; ++c) {
     const uint32_t boff = (uint32_t)((c & (kRing - 1)) * G::BUF);
     const uint32_t bprev = (uint32_t)(((c - 1) & (kRing - 1)) * G::BUF);
     period(c);
     prep(c - 1, bprev);
     finish(c - 1, bprev);
-    chunk_logits<D, MT, RA>(sf, y, rb, boff);
+    chunk_logits<D, MT, RAL>(sf, y, rb, boff);
   }
   {
     const uint32_t blast = (uint32_t)(((nch - 1) & (kRing - 1)) * G::BUF);
@@ -577,7 +580,7 @@ __global__ __launch_bounds__(64 * Tiling<D>::NW, Tiling<D>::WPE) void k_rows2(co
     dma_chunk<D>(dof, E, r_begin + (int64_t)c * kRC, r_end, ring0 + boff, wv, lane);
   };
   auto prep = [&](int, uint32_t) {};
-  sweep_loop<D, MT, RM, G::LPWP + 1, G::LPWP, CL_ROWS_READ_AHEAD>(nch, r_end - r_begin, sf, acc, ep, rb, h, wv, p.filter_bits, issue, prep);
+  sweep_loop<D, MT, RM, G::LPWP + 1, G::LPWP, CL_ROWS_READ_AHEAD, CL_ROWS_READ_AHEAD>(nch, r_end - r_begin, sf, acc, ep, rb, h, wv, p.filter_bits, issue, prep);
 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -668,7 +671,7 @@ __global__ __launch_bounds__(64 * Tiling<D>::NW, Tiling<D>::WPE) void k_cols2(co
     if constexpr (KIND == 1) dma_vec(p.lse, r0, p.T, vb + kRC * 4, lane);
   };
   auto prep = [&](int, uint32_t boff) { ep.vb = vec0 + (boff / G::BUF) * (NV * kRC * 4); };
-  sweep_loop<D, MT, RM, G::LPWP + 1 + NV, G::LPWP + NV, CL_COLS_READ_AHEAD>(nch, p.T, sf, acc, ep, rb, h, wv, p.filter_bits, issue, prep);
+  sweep_loop<D, MT, RM, G::LPWP + 1 + NV, G::LPWP + NV, CL_COLS_LOGITS_READ_AHEAD, CL_COLS_READ_AHEAD>(nch, p.T, sf, acc, ep, rb, h, wv, p.filter_bits, issue, prep);
 
   // sparse positive term: index of each item of the block in the sorted unique-item list
   for (int k = tid; k < SB; k += 64 * Tiling<D>::NW) {
