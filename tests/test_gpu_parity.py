@@ -64,7 +64,10 @@ def test_tiny_bce_full(B):
     _bce_full_check(B, inp, pad_id=0, dloss=inp["dloss"])
 
 
-@pytest.mark.parametrize("T,D,V", [(1, 64, 33), (33, 128, 1001), (130, 256, 4097), (257, 64, 2000), (129, 512, 777)])
+# T = 333 at D = 256 gives two 256-row workgroups of the rows sweep, the second one ragged
+# in both its leading and its lagging half of waves
+@pytest.mark.parametrize("T,D,V", [(1, 64, 33), (33, 128, 1001), (130, 256, 4097), (333, 256, 2531), (257, 64, 2000),
+                                   (129, 512, 777)])
 def test_bce_ragged_with_pads_and_repeats(B, T, D, V):
     _say(f"ragged T={T} D={D} V={V}")
     w = Workload("ragged", "bce", T, D, V, "bf16", None, None, "uniform_any", L=12, pad_id=0, mask_frac=0.2,
@@ -135,7 +138,7 @@ def test_determinism(B):
                            b[k].view(torch.int16) if b[k].dtype == torch.bfloat16 else b[k]), k
 
 
-@pytest.mark.parametrize("T,D,V", [(70, 128, 3001), (200, 256, 5000), (33, 64, 100)])
+@pytest.mark.parametrize("T,D,V", [(70, 128, 3001), (200, 256, 5000), (300, 256, 2049), (33, 64, 100)])
 def test_ce_small(B, T, D, V):
     _say(f"ce T={T} D={D} V={V}")
     w = Workload("ce", "ce", T, D, V, "bf16", None, None, "ce_uniform", L=1, pad_id=-1, ignore_frac=0.1, seed=12 + T)
