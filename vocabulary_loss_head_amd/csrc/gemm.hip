@@ -97,18 +97,17 @@ struct Tile {
 // address of element (outer0, k0) (KC) or (k0, outer0) (KR). Offsets clamp the outer
 // index into the valid range once; a stage that reaches past the valid k range (only the
 // last stages of some products) recomputes them with the k clamp as well.
-// RG: a bf16 operand staged through registers (global load, then ds_write) instead of DMA
-template <int NW, int R, bool KC, bool F8, bool Q8 = false, bool RG = false>
+template <int NW, int R, bool KC, bool F8, bool Q8 = false>
 struct Loader {
   using TL = Tile<NW, R, KC>;
-  static constexpr int N = (F8 || RG) ? TL::PIECES : TL::PER_WAVE;
+  static constexpr int N = F8 ? TL::PIECES : TL::PER_WAVE;
   static constexpr int ESZ = (F8 || Q8) ? 1 : 2;
   static constexpr int EPP = Q8 ? 16 : 8;              // elements per 16-byte LDS piece
   static constexpr int BK = Q8 ? 64 : kBK;             // k elements per stage
   uint32_t off[N];
 
   __device__ __forceinline__ static int byte_of(int j, int wv, int lane, int tid) {
-    return (F8 || RG) ? 16 * (tid + 64 * NW * j) : (wv * TL::PER_WAVE + j) * 1024 + 16 * lane;
+    return F8 ? 16 * (tid + 64 * NW * j) : (wv * TL::PER_WAVE + j) * 1024 + 16 * lane;
   }
   __device__ __forceinline__ static void rc(int byte, int& r, int& c) {
     r = byte / TL::ROW;
@@ -170,7 +169,7 @@ struct Loader {
 
 // Tail stages compute their clamped offsets from an opaque copy of the thread index, so
 // that none of those terms is hoisted out of the main loop into registers held for the
-// whole loop (they pushed the register-staged products into spilling).
+// whole loop (they pushed register-heavy products into spilling).
 __device__ __forceinline__ int opaque(int x) {
   asm volatile("" : "+v"(x));
   return x;
@@ -227,33 +226,6 @@ struct Fp8Stage {
 #pragma unroll
     for (int i = 0; i < TL::PIECES; ++i)
       *(CL_LDS bf16x8*)(uintptr_t)(lds + 16 * (tid + 64 * NW * i)) = fp8x8_to_bf16x8(q[i]);
-  }
-};
-
-// A bf16 stage tile staged through registers: each thread loads 16-byte pieces (the LDS
-// positions 16 (tid + 64 NW i)) and writes them to LDS one step later. Faster than the DMA for
-// the dE product, whose two operands are k-major.
-template <int NW, int R, bool KC>
-struct RegStage16 {
-  using TL = Tile<NW, R, KC>;
-  using LD = Loader<NW, R, KC, false, false, true>;
-  typedef int v4i __attribute__((ext_vector_type(4)));
-  v4i q[TL::PIECES];
-  __device__ __forceinline__ void load(const LD& ld, const GemmOperand& op, int64_t outer0, int64_t k0, int tid) {
-    const char* org = LD::origin(op, outer0, k0);
-    if (!LD::tail(op, k0)) {
-#pragma unroll
-      for (int i = 0; i < TL::PIECES; ++i) q[i] = *(const v4i*)(org + 2 * (size_t)ld.off[i]);
-    } else {
-      const int t = opaque(tid);
-#pragma unroll
-      for (int i = 0; i < TL::PIECES; ++i)
-        q[i] = *(const v4i*)(org + 2 * LD::clamped(op, outer0, k0, 16 * (t + 64 * NW * i)));
-    }
-  }
-  __device__ __forceinline__ void store(uint32_t lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < TL::PIECES; ++i) *(CL_LDS v4i*)(uintptr_t)(lds + 16 * (tid + 64 * NW * i)) = q[i];
   }
 };
 
@@ -393,7 +365,7 @@ __device__ __forceinline__ bool map_tile(int gm, int gn, int gz, int& tm, int& t
 
 // Q8: both operands FP8 E4M3 and k-contiguous, copied to LDS as they are and multiplied by
 // the FP8 MFMA (64 k per stage).
-template <int NW, int BN, bool AKC, bool BKC, bool AF8, bool BF8, int EPI, bool Q8 = false, bool RG = false>
+template <int NW, int BN, bool AKC, bool BKC, bool AF8, bool BF8, int EPI, bool Q8 = false>
 __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
   static_assert(!Q8 || (AKC && BKC && !AF8 && !BF8), "fp8 x fp8 operands are k-contiguous DMA tiles");
   constexpr int BK = Q8 ? 64 : kBK;
@@ -404,8 +376,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
   constexpr int TM = kBM / WM, TN = BN / WN;
   constexpr int MT = TM / 32, NTW = TN / 32;
   constexpr int STAGE = TA::BYTES + TB::BYTES;
-  constexpr bool ARG = RG && !AF8 && !Q8, BRG = RG && !BF8 && !Q8;   // register-staged bf16 operands
-  constexpr int NPER = ((AF8 || ARG) ? TA::PIECES : TA::PER_WAVE) + ((BF8 || BRG) ? TB::PIECES : TB::PER_WAVE);
+  constexpr int NPER = (AF8 ? TA::PIECES : TA::PER_WAVE) + (BF8 ? TB::PIECES : TB::PER_WAVE);
   __shared__ __attribute__((aligned(1024))) char ring[kNst * STAGE];
 
   int tm, tn, tz;
@@ -422,8 +393,8 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
   const int nk = klen > 0 ? (int)(klen / BK) : 0;
   const uint32_t ring0 = (uint32_t)(uintptr_t)ring;
 
-  Loader<NW, kBM, AKC, AF8, Q8, ARG> la;
-  Loader<NW, BN, BKC, BF8, Q8, BRG> lb;
+  Loader<NW, kBM, AKC, AF8, Q8> la;
+  Loader<NW, BN, BKC, BF8, Q8> lb;
   la.init(p.a, m0, wv, lane, tid);
   lb.init(p.b, n0, wv, lane, tid);
 
@@ -477,11 +448,9 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
 
   Fp8Stage<NW, kBM, AKC> sa;
   Fp8Stage<NW, BN, BKC> sb;
-  RegStage16<NW, kBM, AKC> ra;
-  RegStage16<NW, BN, BKC> rb;
   // fp8 register loads are issued before the stage's DMAs, so waiting for them at the
   // next step does not wait for those DMAs.
-  constexpr bool ALL_DMA = !AF8 && !BF8 && !ARG && !BRG;
+  constexpr bool ALL_DMA = !AF8 && !BF8;
   // with every copy invisible to the compiler's waits, none of its own loads may be left
   // pending inside the main loop
   if constexpr (ALL_DMA) wait_vm<0>();
@@ -490,17 +459,13 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
     const int64_t k0 = stage_k(s);
     if constexpr (AF8) sa.load(la, p.a, m0, k0, tid);
     if constexpr (BF8) sb.load(lb, p.b, n0, k0, tid);
-    if constexpr (ARG) ra.load(la, p.a, m0, k0, tid);
-    if constexpr (BRG) rb.load(lb, p.b, n0, k0, tid);
-    if constexpr (!AF8 && !ARG) dma_stage<NW, kBM, AKC, Q8, ALL_DMA>(la, p.a, m0, k0, so, wv, lane);
-    if constexpr (!BF8 && !BRG) dma_stage<NW, BN, BKC, Q8, ALL_DMA>(lb, p.b, n0, k0, so + TA::BYTES, wv, lane);
+    if constexpr (!AF8) dma_stage<NW, kBM, AKC, Q8, ALL_DMA>(la, p.a, m0, k0, so, wv, lane);
+    if constexpr (!BF8) dma_stage<NW, BN, BKC, Q8, ALL_DMA>(lb, p.b, n0, k0, so + TA::BYTES, wv, lane);
   };
   auto store_fp8 = [&](int s) {
     const uint32_t so = ring0 + (uint32_t)((s % kNst) * STAGE);
     if constexpr (AF8) sa.store(so, tid);
     if constexpr (BF8) sb.store(so + TA::BYTES, tid);
-    if constexpr (ARG) ra.store(so, tid);
-    if constexpr (BRG) rb.store(so + TA::BYTES, tid);
   };
 
   if constexpr (Q8) {
@@ -580,7 +545,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
     read_half(s, 1, a1, b1);
     mma_half(a0, b0);
     if (s + 1 < nk_run) {
-      if constexpr (AF8 || BF8 || ARG || BRG) {
+      if constexpr (AF8 || BF8) {
         if (s + kNst - 1 < nk_run) store_fp8(s + kNst - 1);   // loaded at step s - 1
       }
       const int later = min(nk_run - 2 - s, kNst - 2);        // stages after s + 1 in flight
@@ -982,14 +947,10 @@ hipError_t gemm_bn(const GemmParams& p, dim3 grid, hipStream_t st) {
   } else if (!akc && bkc && af8 && !bf8 && p.epi == GEMM_EPI_ACC) {    // K2 as dA^T = E_c^T P^T, fp8 E
     CL_G(false, true, true, false, GEMM_EPI_ACC);
   } else if (!akc && !bkc && !af8 && !bf8) {   // K3: both operands k-major
-    // long k (many rows): stage the operands through registers; short k: DMA
-    const bool rg = p.k_per_split >= 1024;
     if (p.epi == GEMM_EPI_DE) {
-      if (rg) k_gemm<NW, BN, false, false, false, false, GEMM_EPI_DE, false, true><<<grid, 64 * NW, 0, st>>>(p);
-      else CL_G(false, false, false, false, GEMM_EPI_DE);
+      CL_G(false, false, false, false, GEMM_EPI_DE);
     } else if (p.epi == GEMM_EPI_SGD) {
-      if (rg) k_gemm<NW, BN, false, false, false, false, GEMM_EPI_SGD, false, true><<<grid, 64 * NW, 0, st>>>(p);
-      else CL_G(false, false, false, false, GEMM_EPI_SGD);
+      CL_G(false, false, false, false, GEMM_EPI_SGD);
     } else {
       return hipErrorInvalidValue;
     }
