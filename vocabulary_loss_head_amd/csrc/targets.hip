@@ -111,41 +111,48 @@ __global__ void k_row_compact_ce(int64_t T, const int64_t* __restrict__ target, 
 
 // Single-workgroup exclusive scan: out[i] = sum in[0..i), out[n] = total.
 // If n_dev != NULL the length is min(n, *n_dev) and entries past it read as 0.
+// Tiles of 4096 entries, 4 per thread: each wave scans its 64 thread sums with shuffles,
+// the 16 wave totals meet in LDS, and a running carry links the tiles (two barriers per
+// tile). Integer sums, so the result does not depend on the order.
 __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ in, int64_t n, const int32_t* n_dev,
                                                int32_t* __restrict__ out, int32_t* total_out) {
-  __shared__ int32_t s[1024];
-  __shared__ int32_t carry;
-  const int tid = threadIdx.x;
+  __shared__ int32_t wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int64_t m = n;
   if (n_dev != nullptr) m = min((int64_t)*n_dev, n);
-  if (tid == 0) carry = 0;
-  __syncthreads();
+  int32_t carry = 0;                      // the same value in every thread
   for (int64_t base = 0; base < n; base += 4096) {
     int v[4];
-    int64_t i0 = base + (int64_t)tid * 4;
+    const int64_t i0 = base + (int64_t)tid * 4;
     int local = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       v[j] = (i0 + j < m) ? in[i0 + j] : 0;
       local += v[j];
     }
-    s[tid] = local;
-    __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {
-      int t = tid >= o ? s[tid - o] : 0;
-      __syncthreads();
-      s[tid] += t;
-      __syncthreads();
+    int x = local;                        // inclusive scan over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
     }
-    int run = s[tid] - local + carry;
+    if (lane == 63) wsum[wv] = x;
+    __syncthreads();
+    int wpre = 0, tot = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int t = wsum[k];
+      wpre += k < wv ? t : 0;
+      tot += t;
+    }
+    int run = carry + wpre + x - local;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (i0 + j < n) out[i0 + j] = run;
       run += v[j];
     }
-    __syncthreads();
-    if (tid == 1023) carry += s[1023];
-    __syncthreads();
+    carry += tot;
+    __syncthreads();                      // wsum is rewritten by the next tile
   }
   if (tid == 0) {
     out[n] = carry;
