@@ -158,9 +158,11 @@ def test_ce_small(B, T, D, V):
     assert out["n_err"] == 1
 
 
-def test_sgd_fp8_small(B):
-    _say("sgd fp8 T=40 D=128 V=2000")
-    w = Workload("sgd", "bce", 40, 128, 2000, "fp8", None, 0.05, "poisson_distinct", L=5, pad_id=-1, lr=0.01, seed=13)
+@pytest.mark.parametrize("D", [128, 256])
+def test_sgd_fp8_small(B, D):
+    _say(f"sgd fp8 T=40 D={D} V=2000")
+    w = Workload("sgd", "bce", 40, D, 2000, "fp8", None, 0.05, "poisson_distinct", L=5, pad_id=-1, lr=0.01,
+                 seed=13 if D == 128 else 14)
     inp = make(w)
     A64, E64 = decode_inputs(inp)
     crow, cids, _ = canonical(inp, w.V, -1)
