@@ -21,6 +21,19 @@ __device__ __forceinline__ float load_e(const void* E, int e_fp8, int64_t idx) {
   return e_fp8 ? fp8_to_f32(((const uint8_t*)E)[idx]) : bf16_bits_to_f32(((const uint16_t*)E)[idx]);
 }
 
+// four consecutive elements idx .. idx + 3 of E (idx a multiple of 4)
+__device__ __forceinline__ f32x4 load_e4(const void* E, int e_fp8, int64_t idx) {
+  if (e_fp8) {
+    const uint32_t q = *(const uint32_t*)((const uint8_t*)E + idx);
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)q, false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)q, true);
+    return f32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+  const uint2 q = *(const uint2*)((const uint16_t*)E + idx);
+  return f32x4{__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xffff0000u), __uint_as_float(q.y << 16),
+               __uint_as_float(q.y & 0xffff0000u)};
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
   return v;
@@ -116,20 +129,23 @@ __global__ __launch_bounds__(256) void k_finalize_rows(const FinalizeParams p, i
   }
 
   if (want_dA) {
+    // lane owns 4 consecutive d per 256-wide slab: 16-byte partial loads, 8-byte stores; each
+    // element is summed over the splits and the positives in the same order as before
     const float w = row_weight(p, kind, t);
     uint16_t* dA = (uint16_t*)p.dA;
-    for (int k = 0; k < nd; ++k) {
-      const int64_t d = lane + 64 * k;
-      float g = 0.0f;
+    for (int64_t d = 4 * lane; d < D; d += 256) {
+      f32x4 g = {0.0f, 0.0f, 0.0f, 0.0f};
       if (valid) {
-        float acc = 0.0f;
-        for (int j = 0; j < p.n_splits_dA; ++j) acc += p.part_dA[((int64_t)j * p.T + t) * D + d];
-        float corr = 0.0f;                       // sum of E_p over the row's positives
-        if (p.pos_sum != nullptr) corr = p.pos_sum[t * D + d];
-        else for (int32_t e = pb; e < pe; ++e) corr += load_e(p.E, p.e_fp8, (int64_t)p.cids[e] * D + d);
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < p.n_splits_dA; ++j) acc += *(const f32x4*)(p.part_dA + ((int64_t)j * p.T + t) * D + d);
+        f32x4 corr = {0.0f, 0.0f, 0.0f, 0.0f};   // sum of E_p over the row's positives
+        if (p.pos_sum != nullptr) corr = *(const f32x4*)(p.pos_sum + t * D + d);
+        else for (int32_t e = pb; e < pe; ++e) corr += load_e4(p.E, p.e_fp8, (int64_t)p.cids[e] * D + d);
         g = p.dA_weighted ? acc - w * corr : w * (acc - corr);
       }
-      dA[t * D + d] = (uint16_t)f32_to_bf16_bits(g);
+      const uint32_t lo = f32_to_bf16_bits(g[0]) | (f32_to_bf16_bits(g[1]) << 16);
+      const uint32_t hi = f32_to_bf16_bits(g[2]) | (f32_to_bf16_bits(g[3]) << 16);
+      *(uint2*)(dA + t * D + d) = uint2{lo, hi};
     }
   }
 }
