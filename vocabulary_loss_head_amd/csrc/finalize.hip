@@ -34,6 +34,11 @@ __device__ __forceinline__ f32x4 load_e4(const void* E, int e_fp8, int64_t idx) 
                __uint_as_float(q.y & 0xffff0000u)};
 }
 
+// A_t[d .. d + 3] (bf16, or the FP8 copy of A when the logits run in FP8)
+__device__ __forceinline__ f32x4 load_a4(const FinalizeParams& p, int64_t idx) {
+  return p.A8 != nullptr ? load_e4(p.A8, 1, idx) : load_e4(p.A, 0, idx);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
   return v;
@@ -50,15 +55,27 @@ __device__ __forceinline__ float row_weight(const FinalizeParams& p, int kind, i
   return p.dloss ? p.dloss[t] : 1.0f;
 }
 
-// One wave per row; lanes over d (d = lane + 64 k).
+// This lane's share of the positive logit A_t . E_v: lane owns d = 4 lane + 256 k + 0..3.
+__device__ __forceinline__ float pos_dot_part(const FinalizeParams& p, int64_t t, int64_t v, int lane) {
+  float part = 0.0f;
+  for (int64_t d = 4 * lane; d < p.D; d += 256) {
+    const f32x4 a = load_a4(p, t * p.D + d);
+    const f32x4 e = load_e4(p.E, p.e_fp8, v * p.D + d);
+    part += a[0] * e[0];
+    part += a[1] * e[1];
+    part += a[2] * e[2];
+    part += a[3] * e[3];
+  }
+  return part;
+}
+
+// One wave per row; lanes over d.
 __global__ __launch_bounds__(256) void k_finalize_rows(const FinalizeParams p, int kind, int want_loss, int want_dA) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= p.T) return;
   const int64_t D = p.D;
-  const int nd = (int)(D / 64);
   const bool valid = row_valid(p, kind, t);
-  const uint16_t* A = (const uint16_t*)p.A;
   const int32_t pb = p.crow[t], pe = p.crow[t + 1];
 
   if (want_loss) {
@@ -71,14 +88,7 @@ __global__ __launch_bounds__(256) void k_finalize_rows(const FinalizeParams p, i
       if (p.pos_tp != nullptr) tp = p.pos_tp[t];
     } else {
       for (int32_t e = pb; e < pe; ++e) {
-        const int64_t v = p.cids[e];
-        float part = 0.0f;
-        for (int k = 0; k < nd; ++k) {
-          const int64_t d = lane + 64 * k;
-          const float a = p.A8 != nullptr ? load_e(p.A8, 1, t * D + d) : bf16_bits_to_f32(A[t * D + d]);
-          part += a * load_e(p.E, p.e_fp8, v * D + d);
-        }
-        const float x = wave_sum(part);
+        const float x = wave_sum(pos_dot_part(p, t, (int64_t)p.cids[e], lane));
         sum_x += x;
         tp += x > 0.0f ? 1 : 0;
       }
@@ -157,31 +167,21 @@ __global__ __launch_bounds__(256) void k_row_positives(const FinalizeParams p) {
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= p.T) return;
   const int64_t D = p.D;
-  const int nd = (int)(D / 64);
-  const uint16_t* A = (const uint16_t*)p.A;
   const int32_t pb = p.crow[t], pe = p.crow[t + 1];
   float sum_x = 0.0f;
   int tp = 0;
   for (int32_t e = pb; e < pe; ++e) {
-    const int64_t v = p.cids[e];
-    float part = 0.0f;
-    for (int k = 0; k < nd; ++k) {
-      const int64_t d = lane + 64 * k;
-      const float a = p.A8 != nullptr ? load_e(p.A8, 1, t * D + d) : bf16_bits_to_f32(A[t * D + d]);
-      part += a * load_e(p.E, p.e_fp8, v * D + d);
-    }
-    const float x = wave_sum(part);
+    const float x = wave_sum(pos_dot_part(p, t, (int64_t)p.cids[e], lane));
     sum_x += x;
     tp += x > 0.0f ? 1 : 0;
   }
   if (lane == 0) p.pos_dot[t] = sum_x;
   if (lane == 0 && p.pos_tp != nullptr) p.pos_tp[t] = tp;
   if (p.pos_sum == nullptr) return;          // no dA requested
-  for (int k = 0; k < nd; ++k) {
-    const int64_t d = lane + 64 * k;
-    float corr = 0.0f;
-    for (int32_t e = pb; e < pe; ++e) corr += load_e(p.E, p.e_fp8, (int64_t)p.cids[e] * D + d);
-    p.pos_sum[t * D + d] = corr;
+  for (int64_t d = 4 * lane; d < D; d += 256) {
+    f32x4 corr = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int32_t e = pb; e < pe; ++e) corr += load_e4(p.E, p.e_fp8, (int64_t)p.cids[e] * D + d);
+    *(f32x4*)(p.pos_sum + t * D + d) = corr;
   }
 }
 
