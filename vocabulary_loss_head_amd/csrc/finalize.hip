@@ -219,8 +219,8 @@ __global__ __launch_bounds__(256) void k_item_pieces(int64_t D, const uint16_t* 
   const int64_t a = j * kPiece;
   if (a >= n) return;
   const int64_t b = min(a + kPiece, (int64_t)n);
-  const int nd = (int)(D / 64);
-  constexpr int KB = 8;                         // d columns per lane in flight
+  const int ns = (int)((D + 255) / 256);        // 256-wide d slabs; lane owns 4 d of each
+  constexpr int KB = 2;                         // slabs per lane in flight
   int64_t i = a;
   int u = item_of(useg, nu, (int32_t)a);        // pairs are item-major: later items follow in order
   while (i < b) {
@@ -230,21 +230,24 @@ __global__ __launch_bounds__(256) void k_item_pieces(int64_t D, const uint16_t* 
     if (s >= a && e <= b) dst = S_u + (int64_t)u * D;          // complete inside this piece
     else if (s < a) dst = part + (j * 2 + 0) * D;               // began in an earlier piece
     else dst = part + (j * 2 + 1) * D;                          // continues into later pieces
-    for (int k0 = 0; k0 < nd; k0 += KB) {
-      float acc[KB];
+    for (int k0 = 0; k0 < ns; k0 += KB) {
+      f32x4 acc[KB];
 #pragma unroll
-      for (int kk = 0; kk < KB; ++kk) acc[kk] = 0.0f;
+      for (int kk = 0; kk < KB; ++kk) acc[kk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       for (int64_t q = i; q < r1; ++q) {        // pair order: the sum order is fixed
         const int64_t t = csc_rows[q];
         const float wt = w[t];
-        const uint16_t* At = A + t * D + lane;
 #pragma unroll
-        for (int kk = 0; kk < KB; ++kk)
-          if (k0 + kk < nd) acc[kk] += wt * bf16_bits_to_f32(At[64 * (k0 + kk)]);
+        for (int kk = 0; kk < KB; ++kk) {
+          const int64_t d = 4 * lane + 256 * (k0 + kk);
+          if (d < D) acc[kk] += wt * load_e4(A, 0, t * D + d);
+        }
       }
 #pragma unroll
-      for (int kk = 0; kk < KB; ++kk)
-        if (k0 + kk < nd) dst[lane + 64 * (k0 + kk)] = acc[kk];
+      for (int kk = 0; kk < KB; ++kk) {
+        const int64_t d = 4 * lane + 256 * (k0 + kk);
+        if (d < D) *(f32x4*)(dst + d) = acc[kk];
+      }
     }
     i = r1;
     ++u;
