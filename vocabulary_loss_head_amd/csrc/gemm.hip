@@ -454,6 +454,36 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
   // with every copy invisible to the compiler's waits, none of its own loads may be left
   // pending inside the main loop
   if constexpr (ALL_DMA) wait_vm<0>();
+
+  // dE/SGD epilogue geometry: each wave stages MG row tiles at a time through its share of
+  // the ring as fp32 rows of stride RS; a lane then owns SPL segments of 16 adjacent d
+  constexpr int WREG = kNst * STAGE / NW;    // LDS bytes per wave
+  constexpr int RS = TN * 4 + 16;            // fp32 row stride: 16 B pad spreads the 16-lane reads
+  constexpr int MG = (WREG / (32 * RS)) < MT ? (WREG / (32 * RS)) : MT;
+  constexpr int SEGS = TN / 16;
+  constexpr int SPL = 32 * MG * SEGS / 64;    // segments per lane per group
+  constexpr int NG = MT / MG > 0 ? MT / MG : 1;
+  // FP8 SGD (round to nearest): the E bytes of all the lane's segments are loaded here, before
+  // the first stage's copies, so their HBM latency overlaps the pipeline's start and the
+  // epilogue never waits for E
+  constexpr bool PRE = EPI == GEMM_EPI_SGD;
+  const bool pre = PRE && p.e_fp8 && !p.sr;
+  uint4 epre[PRE ? SPL * NG : 1];
+  if constexpr (PRE) {
+    if (pre) {
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) {
+          const int sg = lane + 64 * i, row = sg / SEGS, seg = sg - row * SEGS;
+          const int64_t v = p.v0 + m0 + wm * TM + 32 * (gi * MG) + row;
+          const int64_t d0 = n0 + wn * TN + 16 * seg;
+          epre[gi * SPL + i] = (v < p.V && d0 < p.D)
+                                   ? *(const uint4*)((const uint8_t*)p.E_inplace + v * p.D + d0)
+                                   : uint4{0u, 0u, 0u, 0u};
+        }
+    }
+  }
   auto issue = [&](int s) {
     const uint32_t so = ring0 + (uint32_t)((s % kNst) * STAGE);
     const int64_t k0 = stage_k(s);
@@ -748,41 +778,11 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
       }
       uix[k] = (lo < nu && (int64_t)p.uitems[lo] == v) ? lo : -1;
     }
-    constexpr int WREG = kNst * STAGE / NW;    // LDS bytes per wave
-    constexpr int RS = TN * 4 + 16;            // fp32 row stride: 16 B pad spreads the 16-lane reads
-    constexpr int MG = (WREG / (32 * RS)) < MT ? (WREG / (32 * RS)) : MT;
-    constexpr int SEGS = TN / 16;
-    constexpr int SPL = 32 * MG * SEGS / 64;    // segments per lane per group
     static_assert(MG >= 1 && MT % MG == 0 && TN % 16 == 0 && (32 * MG * SEGS) % 64 == 0, "epilogue staging");
     char* wbuf = ring + wv * WREG;
     const uint32_t wb = ring0 + (uint32_t)(wv * WREG);
-    // FP8 SGD: E bytes of the lane's segments, loaded one group ahead so that their latency
-    // overlaps the previous group's staging and update
-    constexpr bool PRE = EPI == GEMM_EPI_SGD;
-    const bool pre = PRE && p.e_fp8 && !p.sr;
-    uint4 enext[PRE ? SPL : 1];
-    auto load_e8 = [&](int g0) {
-#pragma unroll
-      for (int i = 0; i < SPL; ++i) {
-        const int s = lane + 64 * i, row = s / SEGS, seg = s - row * SEGS;
-        const int64_t v = p.v0 + m0 + wm * TM + 32 * g0 + row;
-        const int64_t d0 = n0 + wn * TN + 16 * seg;
-        if (v < p.V && d0 < p.D) enext[i] = *(const uint4*)((const uint8_t*)p.E_inplace + v * p.D + d0);
-      }
-    };
-    if constexpr (PRE) {
-      if (pre) load_e8(0);
-    }
 #pragma unroll
     for (int g0 = 0; g0 < MT; g0 += MG) {
-      uint4 ecur[PRE ? SPL : 1];
-      if constexpr (PRE) {
-        if (pre) {
-#pragma unroll
-          for (int i = 0; i < SPL; ++i) ecur[i] = enext[i];
-          if (g0 + MG < MT) load_e8(g0 + MG);
-        }
-      }
       __syncthreads();
 #pragma unroll
       for (int mq = 0; mq < MG; ++mq)
@@ -873,7 +873,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
           }
         } else if (p.e_fp8) {
           uint4* ep = (uint4*)((uint8_t*)p.E_inplace + v * p.D + d0);
-          const uint4 e = pre ? ecur[PRE ? si : 0] : *ep;
+          const uint4 e = pre ? epre[PRE ? (g0 / MG) * SPL + si : 0] : *ep;
           const uint32_t w[4] = {e.x, e.y, e.z, e.w};
           uint32_t o[4];
 #pragma unroll
