@@ -707,17 +707,23 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
       static_assert(IMG <= kNst * STAGE, "P image fits the ring");
       block_sync();
       const int64_t pbs = (int64_t)p.p_bt * 32;
+      // all BN rows of the tile lie in one row block of the layout (bt is a multiple of BN and
+      // n0 of BN): its block index and first row offset are per-workgroup constants, so the
+      // copy loop does no 64-bit division
+      const int64_t tblk = n0 / p.p_bt;
+      const int64_t toff = n0 - tblk * p.p_bt;
+      uint16_t* const pblk = p.P + (tblk * p.p_nvb + (m0 >> 5)) * pbs + toff * 32;
+      const int64_t rows_here = p.p_rows - n0;
 #pragma unroll 4
       for (int k = tid; k < IMG / 16; k += kThreads) {
         const int b = (16 * k) / (BN * 64);
         const int rem = 16 * k - b * (BN * 64);
         const int r = rem >> 6;
         const int q = ((rem & 63) >> 4) ^ ((r >> 2) & 3);
-        const int64_t t = n0 + r;
-        if (t < p.p_rows) {
+        if (r < rows_here) {
           typedef int i32x4 __attribute__((ext_vector_type(4)));
           const i32x4 x = *lds_ptr<i32x4>(ring0 + (uint32_t)(16 * k));
-          *(i32x4*)(p.P + ((t / p.p_bt) * p.p_nvb + ((m0 >> 5) + b)) * pbs + (t % p.p_bt) * 32 + 8 * q) = x;
+          *(i32x4*)(pblk + (int64_t)b * pbs + r * 32 + 8 * q) = x;
         }
       }
     }
