@@ -49,7 +49,10 @@ __device__ __forceinline__ bf16x8 cat_bf16(s16x4 lo, s16x4 hi) {
 // wait for every copy in flight before each transposing LDS read (ds_read_b64_tr_b16), which
 // it cannot tell apart from the copies' destinations. Callers order every read of a
 // destination after the copy with an explicit vmcnt wait and a workgroup barrier. The
-// s_nop covers the M0-write to LDS-DMA hazard.
+// s_nop covers the M0-write to LDS-DMA hazard. M0 is a reserved register (the compiler warns
+// about the clobber); in the kernels that use these copies nothing else reads M0 (no
+// builtin LDS copies, no relative register addressing, no messages), which the generated
+// code shows, so no value of the compiler's own is overwritten.
 __device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
