@@ -76,19 +76,22 @@ def test_bce_ragged_with_pads_and_repeats(B, T, D, V):
     _bce_full_check(B, inp, pad_id=0, dloss=inp["dloss"])
 
 
-def test_bce_high_scale_stress(B):
-    # Cut BCE §IV-A mini-benchmark distribution: A, E ~ N(0, I), D = 128, L = 8 uniform
-    # targets in [0, V) (pads and repeats included): saturated sigmoids, large softplus.
-    _say("stress N(0,1) T=96 D=128 V=5000")
-    w = Workload("stress", "bce", 96, 128, 5000, "bf16", 1.0, 1.0, "uniform_any", L=8, pad_id=0, seed=7)
+@pytest.mark.parametrize("T,D", [(96, 128), (300, 256)])
+def test_bce_high_scale_stress(B, T, D):
+    # Cut BCE §IV-A mini-benchmark distribution: A, E ~ N(0, I), L = 8 uniform targets in
+    # [0, V) (pads and repeats included): saturated sigmoids, large softplus.
+    _say(f"stress N(0,1) T={T} D={D} V=5000")
+    w = Workload("stress", "bce", T, D, 5000, "bf16", 1.0, 1.0, "uniform_any", L=8, pad_id=0, seed=7 + D)
     inp = make(w)
     _bce_full_check(B, inp, pad_id=0)
 
 
-def test_bce_closed_forms(B):
+@pytest.mark.parametrize("T,D", [(70, 128), (270, 256)])
+def test_bce_closed_forms(B, T, D):
     # A = 0: loss = V ln 2, dA_t = 0.5 sum_v E_v - sum_p E_p, dE = 0
     # E = 0: loss = V ln 2, dA = 0, dE_v = sum_t w_t (0.5 - y_tv) A_t
-    w = Workload("cf", "bce", 70, 128, 3000, "bf16", None, None, "uniform_any", L=6, pad_id=0, mask_frac=0.1, seed=8)
+    w = Workload("cf", "bce", T, D, 3000, "bf16", None, None, "uniform_any", L=6, pad_id=0, mask_frac=0.1,
+                 seed=8 if D == 128 else 9)
     inp = make(w)
     for zero in ("A", "E"):
         _say(f"closed form {zero}=0")
