@@ -121,15 +121,22 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ in, i
   int64_t m = n;
   if (n_dev != nullptr) m = min((int64_t)*n_dev, n);
   int32_t carry = 0;                      // the same value in every thread
+  // the next tile's entries are loaded while the current one is scanned
+  int vn[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) vn[j] = ((int64_t)tid * 4 + j < m) ? in[(int64_t)tid * 4 + j] : 0;
   for (int64_t base = 0; base < n; base += 4096) {
     int v[4];
     const int64_t i0 = base + (int64_t)tid * 4;
     int local = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v[j] = (i0 + j < m) ? in[i0 + j] : 0;
+      v[j] = vn[j];
       local += v[j];
     }
+    const int64_t i1 = i0 + 4096;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vn[j] = (i1 + j < m) ? in[i1 + j] : 0;
     int x = local;                        // inclusive scan over the wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
