@@ -267,10 +267,20 @@ __global__ __launch_bounds__(256) void k_item_fixup(int64_t D, const int32_t* __
   const int64_t s = useg[u], e = useg[u + 1];
   if (!(e > b && s >= a)) return;
   const int64_t j1 = (e - 1) / kPiece;
-  for (int64_t d = threadIdx.x; d < D; d += 256) {
-    float acc = part[(j * 2 + 1) * D + d];
-    for (int64_t jj = j + 1; jj <= j1; ++jj) acc += part[(jj * 2 + 0) * D + d];
-    S_u[(int64_t)u * D + d] = acc;
+  // 4 consecutive d per thread; the pieces j + 1 .. j1 go round-robin to four partial sums
+  // (long chains: a popular item spans many pieces), combined in a fixed order
+  for (int64_t d = 4 * (int64_t)threadIdx.x; d < D; d += 1024) {
+    f32x4 a0 = *(const f32x4*)(part + (j * 2 + 1) * D + d);
+    f32x4 a1 = {0.0f, 0.0f, 0.0f, 0.0f}, a2 = a1, a3 = a1;
+    int64_t jj = j + 1;
+    for (; jj + 3 <= j1; jj += 4) {
+      a0 += *(const f32x4*)(part + (jj * 2 + 0) * D + d);
+      a1 += *(const f32x4*)(part + ((jj + 1) * 2 + 0) * D + d);
+      a2 += *(const f32x4*)(part + ((jj + 2) * 2 + 0) * D + d);
+      a3 += *(const f32x4*)(part + ((jj + 3) * 2 + 0) * D + d);
+    }
+    for (; jj <= j1; ++jj) a0 += *(const f32x4*)(part + (jj * 2 + 0) * D + d);
+    *(f32x4*)(S_u + (int64_t)u * D + d) = (a0 + a1) + (a2 + a3);
   }
 }
 
