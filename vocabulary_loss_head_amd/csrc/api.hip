@@ -252,6 +252,7 @@ struct Ws2 {
   int32_t* imap;      // [V] item -> unique-item index (dE / SGD epilogue)
   uint16_t* Et;       // the chunk's bf16 E transposed, [D][Vc] (the dA product's k-contiguous operand)
   uint8_t* A8;        // FP8 logits: E4M3FN copy of A [T][D]
+  uint16_t* Aw;       // BCE dE product: the rows of A weighted by w, bf16 [T][D]
   size_t bytes;
 };
 
@@ -298,6 +299,7 @@ Ws2 carve_chunked(void* base, const ChunkPlan& pl, bool need_P, bool need_dA, bo
   w.Et = need_dA && need_Et ? c.take<uint16_t>((size_t)pl.Vc * pl.D) : nullptr;
   w.A8 = pl.q8 ? c.take<uint8_t>((size_t)T * pl.D) : nullptr;
   w.imap = need_Su ? c.take<int32_t>((size_t)pl.V) : nullptr;
+  w.Aw = need_Su ? c.take<uint16_t>((size_t)T * pl.D) : nullptr;
   w.bytes = c.off;
   return w;
 }
@@ -502,6 +504,7 @@ struct ChunkJob {
   float* part_dA;        // NULL: no dA
   uint16_t* Et;          // bf16 E: workspace for the transposed chunk
   const uint8_t* A8;     // FP8 logits: the activations' E4M3FN copy
+  const void* A_dE;      // the dE product's activations operand (NULL: A)
   int k3_epi;            // -1: none, GEMM_EPI_DE or GEMM_EPI_SGD
   const int32_t* uitems; const int32_t* counts; const float* S_u; const int32_t* imap;
   void* dE; float lr;
@@ -565,7 +568,7 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
       Phase ph(CUTLOSS_PHASE_CHUNK_DE, st);
       cl::GemmParams g{};
       g.a = operand(j.P, 0, pl.Tp, mc, 0, 0, (int)pl.bt, pl.Vc / 32);
-      g.b = operand(j.A, pl.D, pl.T, pl.D, 0, 0);
+      g.b = operand(j.A_dE != nullptr ? j.A_dE : j.A, pl.D, pl.T, pl.D, 0, 0);
       // k = t over the rows the logits product wrote (T rounded up to the k stage)
       g.M = mc; g.N = pl.D; g.K = round_up(pl.T, 32); g.k_per_split = g.K;
       g.epi = j.k3_epi;
@@ -601,7 +604,8 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
   cl::FinalizeParams fp{};
   fp.T = p->T; fp.D = p->D; fp.V = p->V; fp.A = p->A; fp.E = p->E; fp.e_fp8 = e_fp8;
   fp.crow = w.tw.crow; fp.cids = w.tw.cids; fp.dloss = dloss; fp.mask = p->row_mask;
-  fp.n_splits = (int)pl.n_splits; fp.n_splits_dA = (int)pl.sk; fp.dA_weighted = 1;
+  // the gradient tile holds the unweighted sigmoid: w scales dA here and A in the dE product
+  fp.n_splits = (int)pl.n_splits; fp.n_splits_dA = (int)pl.sk; fp.dA_weighted = 0;
   fp.part_a = w.part_a; fp.part_dA = w.part_dA; fp.loss = loss; fp.dA = dA; fp.w_out = w.w;
   fp.pos_dot = w.pos_dot; fp.pos_sum = w.pos_sum;
   fp.part_c = w.part_b; fp.counts = counts; fp.pos_tp = counts ? w.pos_tp : nullptr;
@@ -616,10 +620,12 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
       CL_HIP(cl::launch_item_sums(p->D, pl.cap, p->A, w.w, w.tw.csc_rows, w.tw.useg, w.tw.counts, w.S_u, w.S_part, st),
              "item sums");
       CL_HIP(cl::launch_item_map(w.tw, p->V, pl.cap, w.imap, st), "item map");
+      CL_HIP(cl::launch_scale_rows(p->A, w.w, p->T, p->D, w.Aw, st), "weighted activations");
     }
   }
   ChunkJob j{};
   j.pl = &pl; j.A = p->A; j.E = p->E; j.e_fp8 = e_fp8;
+  j.A_dE = dE_mode != 0 ? w.Aw : nullptr;
   j.k1_epi = grad ? cl::GEMM_EPI_BCE_P : (counts ? cl::GEMM_EPI_BCE_METRICS : cl::GEMM_EPI_BCE_LOSS);
   j.w = w.w; j.P = w.P; j.part_a = w.part_a; j.part_b = w.part_b; j.part_dA = w.part_dA; j.Et = w.Et;
   j.A8 = w.A8;

@@ -185,6 +185,17 @@ __global__ __launch_bounds__(256) void k_row_positives(const FinalizeParams p) {
   }
 }
 
+__global__ __launch_bounds__(256) void k_scale_rows(const uint16_t* __restrict__ A, const float* __restrict__ w,
+                                                    int64_t n4, int64_t D, uint16_t* __restrict__ Aw) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 4 elements (one row: D % 4 == 0)
+  if (i >= n4) return;
+  const float wt = w[(4 * i) / D];
+  const f32x4 a = load_e4(A, 0, 4 * i);
+  const uint32_t lo = f32_to_bf16_bits(wt * a[0]) | (f32_to_bf16_bits(wt * a[1]) << 16);
+  const uint32_t hi = f32_to_bf16_bits(wt * a[2]) | (f32_to_bf16_bits(wt * a[3]) << 16);
+  *(uint2*)(Aw + 4 * i) = uint2{lo, hi};
+}
+
 __global__ void k_row_weights(const FinalizeParams p, int kind) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t < p.T) p.w_out[t] = row_weight(p, kind, t);
@@ -355,6 +366,13 @@ hipError_t launch_finalize_rows(const FinalizeParams& p, int kind, int want_loss
 hipError_t launch_row_positives(const FinalizeParams& p, hipStream_t st) {
   if (p.T == 0) return hipSuccess;
   k_row_positives<<<(unsigned)((p.T + 3) / 4), 256, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_rows(const void* A, const float* w, int64_t T, int64_t D, uint16_t* Aw, hipStream_t st) {
+  const int64_t n4 = T * D / 4;
+  if (n4 == 0) return hipSuccess;
+  k_scale_rows<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>((const uint16_t*)A, w, n4, D, Aw);
   return hipGetLastError();
 }
 

@@ -606,7 +606,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
         const bool t_ok = !TAIL || t < p.T;
         const bool t_st = !TAIL || t < p.p_rows; // the P buffer has this row
         float wt = 0.0f, lt = 0.0f;
-        if constexpr (WRITES_P) wt = t_ok ? p.w[t] : 0.0f;
+        if constexpr (EPI == GEMM_EPI_CE_P) wt = t_ok ? p.w[t] : 0.0f;
         if constexpr (EPI == GEMM_EPI_CE_P) lt = t_ok ? p.lse[t] * kLog2e : 0.0f;
         (void)t_st;
         // P image in LDS: item block b, tile row r, 16-byte group j of the block row (XOR
@@ -642,10 +642,10 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
                 const float qv = 1.0f + e;
                 relu += ok ? __builtin_fmaxf(x, 0.0f) : 0.0f;
                 prod *= ok ? qv : 1.0f;
-                if constexpr (EPI == GEMM_EPI_BCE_P) {
+                if constexpr (EPI == GEMM_EPI_BCE_P) {   // unweighted: w enters through dA and A_w
                   const float r = __builtin_amdgcn_rcpf(qv);
                   const float sig = x >= 0.0f ? r : e * r;
-                  f[q] = ok ? wt * sig : 0.0f;
+                  f[q] = ok ? sig : 0.0f;
                 }
               } else if constexpr (EPI == GEMM_EPI_CE_LSE) {
                 sm += ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -mb)) : 0.0f;

@@ -85,7 +85,7 @@ struct FinalizeParams {
   const int64_t* ce_target; int64_t ignore_index;  // CE
   int n_splits;             // loss / lse partials
   int n_splits_dA;          // dA partials
-  int dA_weighted;          // 1: dA partials already carry w_t (chunked path)
+  int dA_weighted;          // 1: dA partials already carry w_t (chunked CE path)
   const float* part_a; const float* part_b; const float* part_dA;
   float* loss; float* lse; void* dA;
   const float* lse_in;      // CE backward: lse from the forward
@@ -110,6 +110,9 @@ hipError_t launch_finalize_rows(const FinalizeParams& p, int kind, int want_loss
 size_t reduce_splits_tmp_floats(int64_t S, int64_t N, int mode);
 hipError_t launch_reduce_splits(float* pa, float* pb, int64_t S, int64_t N, float* tmp, int mode, hipStream_t st);
 hipError_t launch_row_weights(const FinalizeParams& p, int kind, hipStream_t st);
+// Aw[t][d] = bf16(w[t] * A[t][d]): the activations weighted per row (the BCE dE product's
+// operand, so that the gradient tile can hold the unweighted sigmoid)
+hipError_t launch_scale_rows(const void* A, const float* w, int64_t T, int64_t D, uint16_t* Aw, hipStream_t st);
 // Sparse dE term S_u (one row per unique positive item); `part` holds
 // 2 * item_sum_parts(nnz_cap) * D floats of piece partials.
 size_t item_sum_parts(int64_t nnz_cap);
