@@ -190,7 +190,7 @@ struct ChunkPlan {
   int64_t bt;         // P row-block height: 128 for T <= 128, else 256 (blocks of bt x 32)
   int64_t Vc;         // items per chunk (multiple of the item tile)
   int64_t n_chunks;
-  int64_t n_splits;   // loss / lse partials: item tiles x waves along the item dimension
+  int64_t n_splits;   // loss / lse partials: one per item tile
   int64_t sk;         // split-K slices of the dA product
   int64_t kps;        // items per slice
   int64_t flag_bn, flag_ld;   // gradient filter flags: row tile of the logits product, row tiles
@@ -219,7 +219,7 @@ ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap, bool q8 
   if (vc > round_up(V, bm)) vc = round_up(V, bm);
   c.Vc = vc;
   c.n_chunks = ceil_div(V, vc);
-  c.n_splits = ceil_div(V, bm) * cl::gemm_k1_warps_m(T, D, q8);
+  c.n_splits = ceil_div(V, bm);   // one loss partial per item tile (its wave rows combined)
   // dA product: (row tiles) x (D tiles) x slices, about 1024 workgroups
   const int64_t tiles = c.trans_dA
       ? ceil_div(D, bm) * ceil_div(T > 0 ? T : 1, cl::gemm_tile_n_of(cl::GEMM_EPI_ACC, D, T > 0 ? T : 1, D))
@@ -532,7 +532,7 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
       g.v0 = v0; g.V = pl.V; g.T = pl.T; g.D = pl.D;
       g.w = j.w; g.lse = j.lse; g.P = j.P; g.p_bt = (int)pl.bt; g.p_nvb = pl.Vc / 32; g.p_rows = pl.Tp;
       g.part_a = j.part_a; g.part_b = j.part_b;
-      g.part_base = (v0 / bm) * cl::gemm_k1_warps_m(pl.T, pl.D, pl.q8);
+      g.part_base = v0 / bm;
       g.flags = j.flags; g.flag_ld = j.flag_ld; g.flag_bn = j.flag_bn; g.flag_gen = (int)(c + 1);
       g.filter_eps = j.filter_eps;
       CL_HIP(cl::launch_gemm(g, st), "chunk logits");

@@ -594,10 +594,15 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
                 EPI == GEMM_EPI_BCE_METRICS) {
     constexpr bool BCE_SUM = EPI == GEMM_EPI_BCE_P || EPI == GEMM_EPI_BCE_LOSS || EPI == GEMM_EPI_BCE_METRICS;
     constexpr bool WRITES_P = EPI == GEMM_EPI_BCE_P || EPI == GEMM_EPI_CE_P;
+    // row partials of the WM wave rows, combined in wave-row order into one partial per item
+    // tile (half or a quarter of the split-reduction traffic)
+    constexpr bool PARTS = BCE_SUM || EPI == GEMM_EPI_CE_LSE;
+    constexpr bool TWO = EPI == GEMM_EPI_BCE_METRICS || EPI == GEMM_EPI_CE_LSE;
+    __shared__ float comb_a[PARTS ? WM : 1][PARTS ? BN : 1];
+    __shared__ float comb_b[TWO ? WM : 1][TWO ? BN : 1];
     // Tiles inside the valid item and row ranges skip the per-element masks.
     auto logit_tile = [&](auto tail_c) {
       constexpr bool TAIL = decltype(tail_c)::value;
-      const int64_t split = p.part_base + (int64_t)tm * WM + wm;
       const int64_t mw = m0 + wm * TM;          // chunk-relative first item of the wave
       float pabs = 0.0f;                         // CE_P: largest |P| of the wave (gradient filter)
 #pragma unroll
@@ -668,14 +673,15 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
           }
           __builtin_amdgcn_sched_barrier(0);     // one 32-row slice at a time
         }
+        const int rr = wn * TN + 32 * nt + l32;   // row of the tile
         if constexpr (BCE_SUM) {
           float vsum = relu + lg * kLn2;
           vsum += __shfl_xor(vsum, 32, 64);
-          if (h == 0 && t_ok) p.part_a[split * p.T + t] = vsum;
+          if (h == 0) comb_a[wm][rr] = vsum;
         }
         if constexpr (EPI == GEMM_EPI_BCE_METRICS) {
           cnt += __shfl_xor(cnt, 32, 64);
-          if (h == 0 && t_ok) p.part_b[split * p.T + t] = cnt;
+          if (h == 0) comb_b[wm][rr] = cnt;
         }
         if constexpr (EPI == GEMM_EPI_CE_LSE) {
           const float m2 = __shfl_xor(mx, 32, 64);
@@ -683,9 +689,9 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
           const float mn = __builtin_fmaxf(mx, m2);
           float s = 0.0f;
           if (mn != kNegInf) s = sm * __builtin_amdgcn_exp2f((mx - mn) * kLog2e) + s2 * __builtin_amdgcn_exp2f((m2 - mn) * kLog2e);
-          if (h == 0 && t_ok) {
-            p.part_a[split * p.T + t] = mn;
-            p.part_b[split * p.T + t] = s;
+          if (h == 0) {
+            comb_a[wm][rr] = mn;
+            comb_b[wm][rr] = s;
           }
         }
       }
@@ -699,6 +705,38 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
     // (the CE gradient epilogue keeps its masks: without them it runs out of registers)
     if (EPI != GEMM_EPI_CE_P && p.v0 + m0 + kBM <= p.V && n0 + BN <= p.T) logit_tile(BoolC<false>{});
     else logit_tile(BoolC<true>{});
+    if constexpr (PARTS) {
+      __syncthreads();
+      const int64_t split = p.part_base + (int64_t)tm;
+      for (int r = tid; r < BN; r += kThreads) {
+        const int64_t t = n0 + r;
+        if (t >= p.T) continue;
+        if constexpr (EPI == GEMM_EPI_CE_LSE) {
+          float mn = kNegInf;
+#pragma unroll
+          for (int q = 0; q < WM; ++q) mn = __builtin_fmaxf(mn, comb_a[q][r]);
+          float sum = 0.0f;
+          if (mn != kNegInf) {
+#pragma unroll
+            for (int q = 0; q < WM; ++q)
+              if (comb_a[q][r] != kNegInf) sum += comb_b[q][r] * __builtin_amdgcn_exp2f((comb_a[q][r] - mn) * kLog2e);
+          }
+          p.part_a[split * p.T + t] = mn;
+          p.part_b[split * p.T + t] = sum;
+        } else {
+          float va = 0.0f;
+#pragma unroll
+          for (int q = 0; q < WM; ++q) va += comb_a[q][r];
+          p.part_a[split * p.T + t] = va;
+          if constexpr (EPI == GEMM_EPI_BCE_METRICS) {
+            float vb = 0.0f;
+#pragma unroll
+            for (int q = 0; q < WM; ++q) vb += comb_b[q][r];
+            p.part_b[split * p.T + t] = vb;
+          }
+        }
+      }
+    }
     if constexpr (WRITES_P) {
       // The tile's P is 8 item blocks x BN rows x 64 bytes, and each item block's rows are one
       // contiguous run of the blocked layout (bt is a multiple of BN): copy it out in 16-byte
@@ -1052,14 +1090,6 @@ int gemm_tile_n_of(int epi, int64_t M, int64_t N, int64_t D) {
   GemmParams q{};
   q.epi = epi; q.M = M; q.N = N; q.D = D;
   return tile_n_for(gemm_waves(q), N);
-}
-int gemm_k1_warps_m(int64_t T, int64_t D, bool fp8_fp8) {
-  GemmParams q{};
-  q.D = D; q.epi = GEMM_EPI_BCE_LOSS; q.M = kBM; q.N = T;
-  q.a.fp8 = q.b.fp8 = fp8_fp8 ? 1 : 0;
-  const int nw = gemm_waves(q);
-  const int bn = tile_n_for(nw, T);
-  return nw == 4 ? WaveGrid<4, 128>::WM : (bn == 128 ? WaveGrid<8, 128>::WM : WaveGrid<8, 256>::WM);
 }
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t st) {

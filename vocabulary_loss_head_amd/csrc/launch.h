@@ -74,8 +74,6 @@ hipError_t launch_transpose_chunk(const uint16_t* E, int64_t vlen, int64_t mc, i
                                   hipStream_t st);
 int gemm_tile_m();                     // 256
 int gemm_tile_n_of(int epi, int64_t M, int64_t N, int64_t D);   // 128 or 256 for that product
-// waves along M of the logits product (row partials per item tile) for T rows, head D
-int gemm_k1_warps_m(int64_t T, int64_t D, bool fp8_fp8 = false);
 
 struct FinalizeParams {
   int64_t T, D, V;
