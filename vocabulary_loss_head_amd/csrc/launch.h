@@ -26,7 +26,7 @@ struct GemmOperand {
 };
 
 enum {
-  GEMM_EPI_BCE_P = 0,     // logits (M = chunk items, N = rows): P = w sigmoid(x), softplus partials
+  GEMM_EPI_BCE_P = 0,     // logits (M = chunk items, N = rows): P = sigmoid(x) (unweighted), softplus partials
   GEMM_EPI_BCE_LOSS = 1,  // softplus partials only
   GEMM_EPI_CE_LSE = 2,    // running (max, sum) partials
   GEMM_EPI_CE_P = 3,      // P = w exp(x - lse)
