@@ -264,7 +264,7 @@ def record(name, steps, warmup, with_cpu):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.e_dtype == "bf16" else "bf16 A x fp8 E (widened to bf16)",
-        "data": "synthetic (seeded; A,E ~ N(0, std) rounded to the storage format; see DESIGN.md input recipe)",
+        "data": "synthetic (seeded; A,E ~ N(0, std) rounded to the storage format)",
         "config": {"workload": f"{name}: {'softmax CE' if w.kind == 'ce' else 'multi-label BCE'} head "
                                f"T={T} D={D} V={V}", "T": T, "D": D, "V": V, "call": h.call_name()},
         "rows_per_s": round(T / (ms * 1e-3), 1),
@@ -334,8 +334,8 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the vocabulary-parallel design is described in DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the vocabulary-parallel form is designed but not built)", file=sys.stderr)
         sys.exit(2)
     if args.all:
         report_all(args.steps, args.warmup)

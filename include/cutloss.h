@@ -58,7 +58,7 @@ extern "C" {
 typedef enum {
   CUTLOSS_OK = 0,
   CUTLOSS_ERR_INVALID_ARG = 1,  /* a NULL/misaligned pointer or a bad size */
-  CUTLOSS_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement (e.g. D % 64 != 0) */
+  CUTLOSS_ERR_UNSUPPORTED = 2,  /* a valid request the library does not implement (e.g. D % 64 != 0) */
   CUTLOSS_ERR_WORKSPACE = 3,    /* workspace smaller than the size query returned */
   CUTLOSS_ERR_HIP = 4           /* a HIP launch/runtime error; text in cutloss_last_error() */
 } cutloss_status;
