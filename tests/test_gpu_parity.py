@@ -103,13 +103,16 @@ def test_bce_closed_forms(B, T, D):
         np.testing.assert_allclose(out["loss"].cpu().numpy()[valid], w.V * math.log(2.0), rtol=1e-5)
 
 
-def test_canonical_targets_bit_exact(B):
-    _say("canonical targets")
-    w = Workload("canon", "bce", 300, 64, 5000, "bf16", None, None, "uniform_any", L=20, pad_id=0, mask_frac=0.3, seed=9)
+# 6,000 IDs: the radix passes form their own block offsets; 150,000 IDs (147 sort blocks of
+# 1,024): the histograms are scanned by a kernel of their own
+@pytest.mark.parametrize("T,V,L", [(300, 5000, 20), (3000, 200_000, 50)])
+def test_canonical_targets_bit_exact(B, T, V, L):
+    _say(f"canonical targets T={T} V={V} L={L}")
+    w = Workload("canon", "bce", T, 64, V, "bf16", None, None, "uniform_any", L=L, pad_id=0, mask_frac=0.3, seed=9)
     inp = make(w)
     # plant out-of-range IDs and an empty row
     ids = inp["ids"].copy()
-    ids[::37] = 5000 + np.arange(len(ids[::37]))
+    ids[::37] = V + np.arange(len(ids[::37]))
     ids[5::41] = -3
     inp["ids"] = ids
     g = upload(inp)

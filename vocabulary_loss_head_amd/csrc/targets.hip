@@ -20,6 +20,7 @@
 namespace cl {
 
 constexpr int RS_TILE = 1024;
+constexpr int kRsOwnOffsetsMaxBlocks = 128;
 
 size_t targets_radix_blocks(int64_t nnz) { return nnz <= 0 ? 1 : (size_t)((nnz + RS_TILE - 1) / RS_TILE); }
 
@@ -185,16 +186,48 @@ __global__ __launch_bounds__(256) void k_rs_hist(const int32_t* __restrict__ kin
   hist[(int64_t)tid * nblk + b] = h[tid];
 }
 
+// First output slot of block b's keys with digit tid: the exclusive prefix of the block
+// histograms taken in digit-major order (every block's count of smaller digits, then the
+// count of digit tid in blocks before b). Each thread reads one digit's nblk counts; tmp is
+// 256 ints of LDS.
+__device__ __forceinline__ int32_t rs_block_offset(const int32_t* __restrict__ hist, int nblk, int64_t b, int tid,
+                                                   int32_t* tmp) {
+  const int32_t* row = hist + (int64_t)tid * nblk;
+  int32_t tot = 0, pre = 0;
+#pragma unroll 8
+  for (int k = 0; k < nblk; ++k) {
+    const int32_t c = row[k];
+    tot += c;
+    pre += k < b ? c : 0;
+  }
+  tmp[tid] = tot;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {          // inclusive scan of the digit totals
+    const int32_t add = tid >= o ? tmp[tid - o] : 0;
+    __syncthreads();
+    tmp[tid] += add;
+    __syncthreads();
+  }
+  return tmp[tid] - tot + pre;
+}
+
+// hscan: the scanned histograms, or null to derive block b's offsets from hist itself
 __global__ __launch_bounds__(256) void k_rs_scatter(const int32_t* __restrict__ kin, const int32_t* __restrict__ vin,
                                                     int32_t* __restrict__ kout, int32_t* __restrict__ vout,
                                                     const int32_t* n_dev, int shift,
-                                                    const int32_t* __restrict__ hscan, int nblk) {
+                                                    const int32_t* __restrict__ hscan,
+                                                    const int32_t* __restrict__ hist, int nblk) {
   __shared__ int32_t run[256];
   __shared__ int32_t wcnt[4][256];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t b = blockIdx.x;
   const int64_t n = *n_dev;
-  run[tid] = hscan[(int64_t)tid * nblk + b];
+  if (hscan != nullptr) {
+    run[tid] = hscan[(int64_t)tid * nblk + b];
+  } else {
+    const int32_t o = rs_block_offset(hist, nblk, b, tid, run);
+    run[tid] = o;                                 // own slot, after the scan's last barrier
+  }
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) wcnt[k][tid] = 0;
@@ -309,8 +342,11 @@ static bool radix_sort(const TargetsWs& w, int32_t* kA, int32_t* vA, int32_t* kB
     int32_t* ko = inB ? kA : kB;
     int32_t* vo = inB ? vA : vB;
     k_rs_hist<<<nblk, 256, 0, st>>>(ki, n_dev, shift, w.hist, nblk);
-    k_scan<<<1, 1024, 0, st>>>(w.hist, (int64_t)256 * nblk, nullptr, w.hscan, nullptr);
-    k_rs_scatter<<<nblk, 256, 0, st>>>(ki, vi, ko, vo, n_dev, shift, w.hscan, nblk);
+    // up to 128 blocks each scatter block reads the whole histogram table (128 KB) and forms
+    // its own offsets; larger sorts scan the table once in a kernel of its own
+    const bool own = nblk <= kRsOwnOffsetsMaxBlocks;
+    if (!own) k_scan<<<1, 1024, 0, st>>>(w.hist, (int64_t)256 * nblk, nullptr, w.hscan, nullptr);
+    k_rs_scatter<<<nblk, 256, 0, st>>>(ki, vi, ko, vo, n_dev, shift, own ? nullptr : w.hscan, w.hist, nblk);
     inB = !inB;
   }
   return inB;
