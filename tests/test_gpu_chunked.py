@@ -56,7 +56,9 @@ def _bce_check(B, inp, pad_id, dloss=None):
     return out
 
 
-@pytest.mark.parametrize("T,D,V", [(70, 320, 3001), (129, 512, 1001), (33, 768, 700), (300, 384, 2100)])
+# D = 1088 (above 1024, at most 128 rows): 8-wave logits workgroups whose four wave rows merge
+# their loss partials per item tile
+@pytest.mark.parametrize("T,D,V", [(70, 320, 3001), (129, 512, 1001), (33, 768, 700), (300, 384, 2100), (40, 1088, 900)])
 def test_bce_chunked_ragged(B, T, D, V):
     _say(f"chunked bce T={T} D={D} V={V}")
     w = Workload("chunk", "bce", T, D, V, "bf16", None, None, "uniform_any", L=10, pad_id=0, mask_frac=0.15,
