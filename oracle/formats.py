@@ -7,8 +7,8 @@
   value 448, smallest subnormal 2^-9.
 
 Encoding (used by the oracle for the SGD writeback) rounds to nearest with
-ties to even, saturates finite overflow to +-448 and keeps the sign of zero,
-as IEEE rounding does.
+ties to even and keeps the sign of zero, as IEEE rounding does; FP8 saturates
+finite overflow to +-448, bfloat16 is encoded for finite values within its range.
 """
 from __future__ import annotations
 
@@ -62,3 +62,28 @@ def encode_fp8_e4m3fn(x) -> np.ndarray:
     code = code | (neg.astype(np.int64) << 7)
     code = np.where(np.isnan(x), 0x7F, code)
     return code.astype(np.uint8)
+
+
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def encode_bf16(x) -> np.ndarray:
+    """float64 -> bf16 bit pattern: nearest, ties to even, sign of zero kept (finite values
+    of magnitude up to the largest bf16; subnormals on the 2^-133 grid)."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(~np.isfinite(x)) or np.any(np.abs(x) > BF16_MAX):
+        raise ValueError("encode_bf16 takes finite values within the bf16 range")
+    neg = np.signbit(x)
+    a = np.abs(x)
+    # quantum of the binade that holds a: 8 significant bits, so 2^(e-7) for a in
+    # [2^e, 2^(e+1)), e >= -126; 2^-133 below the smallest normal
+    with np.errstate(divide="ignore"):
+        _, ex = np.frexp(a)                       # a = f * 2^ex, f in [0.5, 1)
+    e = np.maximum(ex - 1, -126)
+    q = np.exp2((e - 7).astype(np.float64))
+    r = np.rint(a / q) * q                        # np.rint: round half to even
+    if np.any(r > BF16_MAX):
+        raise ValueError("value rounds past the largest bf16")
+    # every bf16 value is a float32 value: its upper 16 bits are the pattern
+    bits = (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    return bits | (neg.astype(np.uint16) << np.uint16(15))

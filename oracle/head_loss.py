@@ -24,7 +24,8 @@ target == ignore_index contribute 0. Gradient: G = w (softmax(X) - onehot(y)).
 
 Fused SGD (ELMO, ai.info summary, Key Contributions: classifier gradients
 fused with the SGD update so they are never stored; momentum-free SGD with FP8
-E4M3 weights): E' = fp8(E - lr dE), nearest-even, saturating.
+E4M3 weights): E' = fp8(E - lr dE), nearest-even, saturating; for bfloat16 weights
+E' = bf16(E - lr dE), nearest-even.
 
 FP8 logits (ELMO, ai.info summary, Methodology: activations are cast to FP8 only for the
 matmul that produces the logits): X = fp8(A) E^T with fp8 the E4M3FN nearest-even saturating
@@ -39,7 +40,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import decode_fp8_e4m3fn, encode_fp8_e4m3fn
+from .formats import decode_bf16, decode_fp8_e4m3fn, encode_bf16, encode_fp8_e4m3fn
 from .targets import dense_labels
 
 
@@ -245,6 +246,11 @@ def ce_filter_bounds(A, E, target, eps, ignore_index=-100, dloss=None):
 def sgd_fp8(E_codes, dE, lr):
     """E' = fp8(E - lr dE) for FP8 E4M3FN codes; dE in float64."""
     return encode_fp8_e4m3fn(decode_fp8_e4m3fn(E_codes) - lr * np.asarray(dE, dtype=np.float64))
+
+
+def sgd_bf16(E_bits, dE, lr):
+    """E' = bf16(E - lr dE) (nearest-even) for bfloat16 bit patterns; dE in float64."""
+    return encode_bf16(decode_bf16(E_bits) - lr * np.asarray(dE, dtype=np.float64))
 
 
 def logits_bytes_fp32(T: int, V: int) -> int:

@@ -93,3 +93,36 @@ def test_generator_fp8_encoder_matches_nearest_even_table():
     idx = np.where(cand.sum(1) > 1, np.argmax(cand & even, axis=1), np.argmin(d, axis=1))
     ref = idx.astype(np.uint8) | ((np.signbit(x) & (idx != 0)).astype(np.uint8) << 7)
     assert np.array_equal(_fp8_bytes(x), ref)
+
+
+def _bf16_nearest_even_by_search(x):
+    """Brute force: the nearest finite bf16 value by a search of the sorted grid of every
+    non-negative finite pattern, ties to the even pattern, sign applied afterwards."""
+    bits = np.arange(0x7F80, dtype=np.uint32).astype(np.uint16)      # +0 .. largest finite
+    vals = decode_bf16(bits)
+    a = np.abs(x)
+    hi = np.searchsorted(vals, a, side="left").clip(0, len(vals) - 1)
+    lo = (hi - 1).clip(0, None)
+    dlo, dhi = np.abs(a - vals[lo]), np.abs(vals[hi] - a)
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    return bits[pick] | (np.signbit(x).astype(np.uint16) << np.uint16(15))
+
+
+def test_bf16_encode_matches_nearest_even_search_and_torch():
+    from oracle.formats import encode_bf16
+    rng = np.random.default_rng(5)
+    grid = decode_bf16(np.arange(0x7F80, dtype=np.uint32).astype(np.uint16))
+    mids = (grid[:-1] + grid[1:]) / 2                        # exact ties
+    x = np.concatenate([grid[::7], mids[::5], np.nextafter(mids[::5], 0.0), np.nextafter(mids[::5], np.inf),
+                        rng.normal(0, 1, 100000) * np.exp2(rng.integers(-130, 120, 100000)),
+                        rng.normal(0, 0.05, 100000)])
+    x = np.concatenate([x, -x[::3]])
+    assert np.array_equal(encode_bf16(x), _bf16_nearest_even_by_search(x))
+    # float32-exact inputs: one correct rounding, as torch's float32 -> bfloat16 cast
+    x32 = x.astype(np.float32)
+    x32 = x32[np.isfinite(x32)].astype(np.float64)
+    ref = torch.from_numpy(x32.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(encode_bf16(x32), ref)
+    assert encode_bf16(np.array([-0.0, 0.0])).tolist() == [0x8000, 0x0000]
+    with pytest.raises(ValueError):
+        encode_bf16(np.array([np.inf]))

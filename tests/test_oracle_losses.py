@@ -279,6 +279,26 @@ def test_sgd_fp8_matches_torch_rounding():
     assert np.array_equal(ours, ref)
 
 
+def test_sgd_bf16_matches_torch_rounding():
+    from oracle.formats import decode_bf16
+    rng = np.random.default_rng(16)
+    # E on the bf16 grid near N(0, 1/16), lr a power of two, dE on a 2^-12 grid: E - lr dE is
+    # exact in float32, so torch's float32 -> bfloat16 cast rounds once, like the oracle
+    E32 = torch.from_numpy(rng.normal(0, 0.0625, (64, 48)).astype(np.float32)).to(torch.bfloat16)
+    E_bits = E32.view(torch.int16).numpy().view(np.uint16)
+    dE = np.round(rng.normal(0, 2.0, (64, 48)) * 4096) / 4096
+    lr = 2.0 ** -7
+    ours = H.sgd_bf16(E_bits, dE, lr)
+    pre = decode_bf16(E_bits) - lr * dE
+    assert np.array_equal(pre.astype(np.float32).astype(np.float64), pre)
+    ref = torch.from_numpy(pre.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    # lr = 0 keeps every pattern; a step of one ulp moves to the neighbouring pattern
+    assert np.array_equal(H.sgd_bf16(E_bits, dE, 0.0), E_bits | 0)
+    one = np.array([0x3F80], dtype=np.uint16)                  # 1.0, next pattern up is 1 + 2^-7
+    assert H.sgd_bf16(one, np.array([-(2.0 ** -7)]), 1.0).tolist() == [0x3F81]
+
+
 def test_ce_filter_bound_limits():
     # eps above every probability: the bound covers dropping the whole dense part, i.e. the
     # gap between the full gradient and the target-only gradient; eps = 0 bounds nothing

@@ -3,6 +3,7 @@ library routine, closed forms and identities, independent of the oracle's own co
 from __future__ import annotations
 
 import numpy as np
+import pytest
 from sklearn.metrics import confusion_matrix
 
 from oracle.metrics import cut_metrics, cut_metrics_rows
@@ -89,3 +90,79 @@ def test_sampled_rows_bracket_the_exact_counts():
     Az = np.zeros_like(A)
     _, tl, th, pl, ph = cut_metrics_rows(Az, E, crow, cids, [0], None)
     assert tl[0] == 0 and pl[0] == 0 and ph[0] == 0       # band 0 at A = 0: x = 0 is not > 0
+
+
+# ---------------------------------------------------------------- the decision band itself
+
+def _fp32_dots(p):
+    """float32 sums of the exact float32 products p[..., D] in several orders: sequential,
+    reversed, a pairwise tree, blocks of 16 and 32 summed in float32 and then across blocks
+    (the k step of the bf16 matrix instructions), and a fixed random permutation."""
+    p = np.asarray(p, dtype=np.float32)
+    D = p.shape[-1]
+
+    def seq(q):
+        s = np.zeros(q.shape[:-1], dtype=np.float32)
+        for k in range(q.shape[-1]):
+            s = (s + q[..., k]).astype(np.float32)
+        return s
+
+    def tree(q):
+        while q.shape[-1] > 1:
+            if q.shape[-1] % 2:
+                q = np.concatenate([q, np.zeros(q.shape[:-1] + (1,), np.float32)], axis=-1)
+            q = (q[..., 0::2] + q[..., 1::2]).astype(np.float32)
+        return q[..., 0]
+
+    def blocks(q, b):
+        parts = [seq(q[..., i:i + b]) for i in range(0, q.shape[-1], b)]
+        return seq(np.stack(parts, axis=-1))
+
+    perm = np.random.default_rng(0).permutation(D)
+    return [seq(p), seq(p[..., ::-1]), tree(p), blocks(p, 16), blocks(p, 32), seq(p[..., perm])]
+
+
+@pytest.mark.parametrize("D,std", [(64, None), (256, None), (768, None), (256, 1.0)])
+def test_decision_band_covers_fp32_evaluations(D, std):
+    """Every float32 evaluation order of a logit of bf16 operands lies within the band of
+    the exact value (products of two bf16 values are exact in float32)."""
+    import torch
+    from oracle.formats import decode_bf16
+    from oracle.metrics import decision_band
+    rng = np.random.default_rng(D)
+    s = std if std is not None else 1.0 / np.sqrt(D)
+
+    def bf16(x):
+        return decode_bf16(torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+                           .view(np.uint16))
+    A = bf16(rng.normal(0, s, (24, D)))
+    E = bf16(rng.normal(0, s, (200, D)))
+    exact = A @ E.T                                          # float64: error far below the band
+    band = decision_band(A, E, D)
+    prods = (A[:, None, :] * E[None, :, :]).astype(np.float32)
+    assert np.array_equal(prods.astype(np.float64), A[:, None, :] * E[None, :, :])
+    worst = 0.0
+    for got in _fp32_dots(prods):
+        err = np.abs(got.astype(np.float64) - exact)
+        assert np.all(err <= band)
+        worst = max(worst, float((err / band).max()))
+    assert worst > 0.0
+
+
+@pytest.mark.parametrize("D", [16, 64, 256, 1024])
+def test_decision_band_is_within_a_small_factor_of_a_reachable_error(D):
+    """A sequential float32 sum that loses every small term: a = (1, d, d, ...), e = 1 with
+    d the largest bf16 value below half an ulp of 1. The float32 sum stays 1, an error of
+    (D - 1) d, about half the band: a band without its factor D would not cover it, and
+    one more than 4x wider than needed fails the second check."""
+    from oracle.metrics import decision_band
+    d = (1.0 - 2.0 ** -8) * 2.0 ** -24                     # 8 significant bits: a bf16 value
+    a = np.full(D, d)
+    a[0] = 1.0
+    e = np.ones(D)
+    got = _fp32_dots(a[None, None, :] * e)[0][0, 0]
+    assert got == np.float32(1.0)
+    err = abs(float(got) - (1.0 + (D - 1) * d))
+    band = float(decision_band(a[None, :], e[None, :], D)[0, 0])
+    assert err <= band
+    assert err >= band / 4
