@@ -41,9 +41,10 @@
  *  - Paths: heads with D in {64, 128, 256} and bf16 E run fused logit-tile sweeps that
  *    never write a logit; every other head (any D that is a multiple of 64, or FP8 E)
  *    runs a chunked path that keeps one vocabulary chunk's bf16 gradient tile
- *    (T x Vc, at most 2 GiB by default) in the workspace. The environment variable
- *    CUTLOSS_MAX_CHUNK_ITEMS caps Vc (read when a call or size query plans the work,
- *    so set it before both).
+ *    (T x Vc) in the workspace: Vc is at most ceil(V / 8) items rounded up to 256, so the
+ *    tile holds at most about an eighth of the T x V logits, and the tile is at most
+ *    2 GiB. The environment variable CUTLOSS_MAX_CHUNK_ITEMS caps Vc further (read when a
+ *    call or size query plans the work, so set it before both).
  */
 #ifndef CUTLOSS_H
 #define CUTLOSS_H
@@ -119,7 +120,9 @@ typedef struct {
 
 /*
  * Workspace size in bytes for `op` on problem `p` (0 if the problem is invalid).
- * It grows with T, D, nnz and the vocabulary tile count, never with T*V.
+ * On the fused-sweep path it grows with T, D, nnz and the vocabulary tile count, never
+ * with T*V; the chunked path adds one chunk's gradient tile (at most T * ceil(V/8) bf16
+ * values, at most 2 GiB) and the chunk's transposed E.
  */
 size_t cutloss_bce_workspace_size(const cutloss_bce_problem* p, int32_t op);
 size_t cutloss_ce_workspace_size(const cutloss_ce_problem* p, int32_t op);

@@ -85,3 +85,22 @@ def test_workspace_size_does_not_grow_with_T_times_V(B):
     assert B.cutloss_bce_workspace_size(_bce(B, D=100), B.OP_FWD) == 0
     # far below the materialized logits (4 T V bytes)
     assert a < 4 * 4096 * 1_000_000 / 50
+
+
+def test_chunked_workspace_holds_a_fraction_of_the_logits(B):
+    # the chunked path keeps one vocabulary chunk's bf16 gradient tile, at most an eighth of
+    # the T x V logits whatever T is: the 3M-item FP8 head (T = 128) and the LM head (CE)
+    # stay far below even a bf16 T x V tensor (2 T V bytes)
+    T, D, V = 128, 768, 3_000_000
+    p = B.BceProblem(T, D, V, 0x10000, 0x20000, B.FP8_E4M3, 0x30000, 0x40000, 641, None, -1)
+    for op in (B.OP_BWD, B.OP_BWD_SGD, B.OP_BWD_SGD_EX):
+        ws = B.cutloss_bce_workspace_size(p, op)
+        assert 0 < ws < 2 * T * V / 3, (op, ws)
+    T, D, V = 8192, 2304, 256_000
+    c = B.CeProblem(T, D, V, 0x10000, 0x20000, B.BF16, 0x30000, -100)
+    ws = B.cutloss_ce_workspace_size(c, B.OP_BWD)
+    assert 0 < ws < 2 * T * V / 3, ws
+    # eight times the vocabulary: the tile reaches its fixed 2 GiB budget, and the workspace
+    # falls further behind the logits
+    big = B.cutloss_ce_workspace_size(B.CeProblem(T, D, 8 * V, 0x10000, 0x20000, B.BF16, 0x30000, -100), B.OP_BWD)
+    assert ws < big < 2 * T * (8 * V) / 8

@@ -142,3 +142,48 @@ def test_ce_chunked(B, T, D, V):
     check_grad(bf16_to_f64(out["dA"]), dA, "dA")
     check_grad(bf16_to_f64(out["dE"]), dE, "dE")
     assert out["n_err"] == 1
+
+
+def test_chunked_determinism_reused_workspace(B):
+    """Two calls on one reused workspace give identical bits on the chunked path: split-K dA
+    partials, their fixed-order reduction, the loss partials and the dE product (BCE at
+    D = 512 over six 512-item chunks), and the CE path with and without the gradient filter."""
+    _say("chunked determinism, reused workspace")
+    w = Workload("det_chunk", "bce", 300, 512, 2900, "bf16", None, None, "zipf", L=8, pad_id=0, mask_frac=0.1,
+                 seed=23)
+    g = upload(make(w))
+    dev = g["A"].device
+    prob = B.bce_problem(g["A"], g["E"], g["row_ptr"], g["ids"], g["mask"], 0)
+    ws = B.workspace(B.cutloss_bce_workspace_size(prob, B.OP_BWD), dev)
+    outs = []
+    for _ in range(2):
+        loss = torch.empty(w.T, dtype=torch.float32, device=dev)
+        dA = torch.empty(w.T, w.D, dtype=torch.bfloat16, device=dev)
+        dE = torch.empty(w.V, w.D, dtype=torch.bfloat16, device=dev)
+        B.cutloss_bce_bwd(prob, None, dA, dE, loss, ws)
+        outs.append((loss, dA.view(torch.int16), dE.view(torch.int16)))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+    wc = Workload("det_ce", "ce", 257, 384, 2100, "bf16", 1.0, 1.0, "ce_uniform", L=1, pad_id=-1, ignore_frac=0.1,
+                  seed=24)
+    gc = upload(make(wc))
+    pc = B.ce_problem(gc["A"], gc["E"], gc["target"], -100)
+    wsc = B.workspace(max(B.cutloss_ce_workspace_size(pc, B.OP_BWD), B.cutloss_ce_workspace_size(pc, B.OP_FWD)), dev)
+    for eps in (None, 2.0 ** -12):
+        res = []
+        for _ in range(2):
+            loss = torch.empty(wc.T, dtype=torch.float32, device=dev)
+            lse = torch.empty(wc.T, dtype=torch.float32, device=dev)
+            B.cutloss_ce_fwd(pc, loss, lse, wsc)
+            dA = torch.empty(wc.T, wc.D, dtype=torch.bfloat16, device=dev)
+            dE = torch.empty(wc.V, wc.D, dtype=torch.bfloat16, device=dev)
+            if eps is None:
+                B.cutloss_ce_bwd(pc, lse, None, dA, dE, wsc)
+            else:
+                B.cutloss_ce_bwd_filtered(pc, lse, None, dA, dE, eps, wsc)
+            res.append((loss, lse, dA.view(torch.int16), dE.view(torch.int16)))
+        torch.cuda.synchronize()
+        for a, b in zip(*res):
+            assert torch.equal(a, b), f"CE eps={eps}"

@@ -35,13 +35,14 @@ def _say(msg):
     print(f"[case] {msg}", flush=True)
 
 
-def _grads(B, g, eps=None):
+def _grads(B, g, eps=None, ws=None):
     A, E = g["A"], g["E"]
     T, D = A.shape
     V = E.shape[0]
     prob = B.ce_problem(A, E, g["target"], -100)
-    ws = B.workspace(max(B.cutloss_ce_workspace_size(prob, B.OP_BWD), B.cutloss_ce_workspace_size(prob, B.OP_FWD)),
-                     A.device)
+    if ws is None:
+        ws = B.workspace(max(B.cutloss_ce_workspace_size(prob, B.OP_BWD), B.cutloss_ce_workspace_size(prob, B.OP_FWD)),
+                         A.device)
     loss = torch.empty(T, dtype=torch.float32, device=A.device)
     lse = torch.empty(T, dtype=torch.float32, device=A.device)
     B.cutloss_ce_fwd(prob, loss, lse, ws)
@@ -138,3 +139,26 @@ def test_filter_skips_cold_item_tiles(B, D, monkeypatch):
     cold = np.mean(e1[768:] != e0[768:])
     print(f"[filter] cold dE rows changed: {cold:.3f}, hot: {np.mean(e1[:512] != e0[:512]):.3f}")
     assert cold > 0.5, "no cold item tile was skipped"
+
+
+@pytest.mark.parametrize("D", [128, 384])
+def test_filter_reused_workspace_matches_fresh(B, D, monkeypatch):
+    # a hot case (large logits: many flagged tiles) and then a cold one (near-uniform softmax:
+    # no dense tile reaches eps) through one workspace: the second result equals the result of
+    # a fresh workspace bit for bit, so nothing of the first call's tile decisions survives
+    monkeypatch.setenv("CUTLOSS_MAX_CHUNK_ITEMS", "512")
+    eps = 2.0 ** -12
+    _say(f"filter workspace reuse hot -> cold, D={D}")
+    hot = upload(_case(96, D, 2600, 1.0, 1000 + D))
+    cold = upload(_case(96, D, 2600, 0.05, 1100 + D))
+    prob = B.ce_problem(hot["A"], hot["E"], hot["target"], -100)
+    ws = B.workspace(max(B.cutloss_ce_workspace_size(prob, B.OP_BWD), B.cutloss_ce_workspace_size(prob, B.OP_FWD)),
+                     hot["A"].device)
+    ws.fill_(0x5A)                      # whatever a caller's buffer held before
+    _grads(B, hot, eps=eps, ws=ws)
+    a_reused, e_reused = _grads(B, cold, eps=eps, ws=ws)
+    a_fresh, e_fresh = _grads(B, cold, eps=eps)
+    assert np.array_equal(a_reused, a_fresh) and np.array_equal(e_reused, e_fresh)
+    a_hot2, e_hot2 = _grads(B, hot, eps=eps, ws=ws)
+    a_hot, e_hot = _grads(B, hot, eps=eps)
+    assert np.array_equal(a_hot2, a_hot) and np.array_equal(e_hot2, e_hot)

@@ -187,19 +187,54 @@ def test_sgd_fp8_small(B, D):
     _check_sgd(g["E"].cpu().numpy(), inp["E"], dE_ref, w.lr)
 
 
-def _check_sgd(E_new, E_old, dE_ref, lr):
-    """E' must be fp8(E - lr (dE_ref + delta)) for some |delta| <= 2e-2 max|dE_ref| per element."""
-    from oracle.formats import decode_fp8_e4m3fn
+def _check_sgd(E_new, E_old, dE_ref, lr, fmt="fp8", max_frac=1e-2):
+    """E' must be round(E - lr (dE_ref + delta)) for some |delta| <= 2e-2 max|dE_ref| per
+    element (round: nearest-even onto E's grid, FP8 E4M3FN or bf16); fewer than max_frac of
+    the elements may differ from round(E - lr dE_ref) itself."""
+    from oracle.formats import decode_bf16, decode_fp8_e4m3fn
+    sgd, dec = (H.sgd_fp8, decode_fp8_e4m3fn) if fmt == "fp8" else (H.sgd_bf16, decode_bf16)
     tol = 2e-2 * np.abs(dE_ref).max()
-    lo = H.sgd_fp8(E_old, dE_ref + tol, lr)
-    hi = H.sgd_fp8(E_old, dE_ref - tol, lr)
-    got = decode_fp8_e4m3fn(E_new)
-    vlo, vhi = decode_fp8_e4m3fn(lo), decode_fp8_e4m3fn(hi)
+    lo = sgd(E_old, dE_ref + tol, lr)
+    hi = sgd(E_old, dE_ref - tol, lr)
+    got = dec(E_new)
+    vlo, vhi = dec(lo), dec(hi)
     assert np.all((got >= vlo) & (got <= vhi)), "SGD result outside the rounding interval"
-    exact = decode_fp8_e4m3fn(H.sgd_fp8(E_old, dE_ref, lr))
+    exact = dec(sgd(E_old, dE_ref, lr))
     frac = float(np.mean(got != exact))
-    print(f"[sgd] fraction differing from fp8(E - lr dE_ref): {frac:.2e}")
-    assert frac < 1e-2
+    print(f"[sgd] fraction differing from {fmt}(E - lr dE_ref): {frac:.2e}")
+    assert frac < max_frac
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_sgd_bf16_fused_sweeps(B, D):
+    """bf16 E at D in {64, 128, 256}: the cols sweep applies E <- bf16(E - lr dE) in place
+    in its epilogue (dE never stored); the rows sweep of the same call reads E first."""
+    _say(f"sgd bf16 T=150 D={D} V=3000 (fused sweeps)")
+    w = Workload("sgd_bf16", "bce", 150, D, 3000, "bf16", None, None, "poisson_distinct", L=5, pad_id=-1, lr=0.01,
+                 mask_frac=0.1, seed=15 if D == 128 else 16)
+    inp = make(w)
+    A64, E64 = decode_inputs(inp)
+    crow, cids, _ = canonical(inp, w.V, -1)
+    g = upload(inp)
+    dev = g["A"].device
+    prob = B.bce_problem(g["A"], g["E"], g["row_ptr"], g["ids"], g["mask"], -1)
+    ws = B.workspace(B.cutloss_bce_workspace_size(prob, B.OP_BWD_SGD), dev)
+    dE = torch.empty(w.V, w.D, dtype=torch.bfloat16, device=dev)
+    B.cutloss_bce_bwd(prob, None, None, dE, None, ws)
+    loss = torch.empty(w.T, dtype=torch.float32, device=dev)
+    dA = torch.empty(w.T, w.D, dtype=torch.bfloat16, device=dev)
+    B.cutloss_bce_bwd_sgd(prob, None, w.lr, dA, loss, ws)
+    torch.cuda.synchronize()
+    dA_ref, dE_ref = H.bce_grads(A64, E64, crow, cids, inp["mask"])
+    check_grad(bf16_to_f64(dE), dE_ref, "dE (bf16 E, unfused)")
+    check_grad(bf16_to_f64(dA), dA_ref, "dA (fused SGD call, old E)")
+    check_loss(loss.cpu().numpy(), H.bce_loss(A64, E64, crow, cids, inp["mask"]), what="sgd fused loss")
+    E_new = g["E"].view(torch.int16).cpu().numpy().view(np.uint16)
+    # bf16's grid is 32x finer than E4M3's: a larger share of the steps sits near a rounding
+    # boundary within the gradient tolerance
+    _check_sgd(E_new, inp["E"], dE_ref, w.lr, fmt="bf16", max_frac=0.15)
+    # masked rows and rows with no positive still move E through the dense term only
+    assert not np.array_equal(E_new, inp["E"])
 
 
 # ----------------------------------------------------------------------------- full size

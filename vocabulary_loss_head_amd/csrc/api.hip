@@ -178,7 +178,7 @@ Ws carve(void* base, const Plan& pl, bool need_dA, bool need_Su, bool two_partia
 // Chunked path (wide heads, FP8 E): see gemm.hip.
 // ---------------------------------------------------------------------------------
 bool use_chunked(int64_t D, int e_fp8) {
-  return !(cl::sweep2_rows_supported(D, e_fp8) && cl::sweep2_cols_supported(D));
+  return !(cl::sweep2_rows_supported(D, e_fp8) && cl::sweep2_cols_supported(D, e_fp8));
 }
 
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -199,6 +199,10 @@ struct ChunkPlan {
 };
 
 constexpr int64_t kChunkPBytes = 2ll << 30;     // P buffer budget
+// at least this many vocabulary chunks whatever T is, so that the gradient tile of a chunk
+// holds at most an eighth of the T x V logits (ELMO's 8-way label chunking of the logit
+// buffer, ai.info summary, Main Findings)
+constexpr int64_t kMinChunks = 8;
 
 ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap, bool q8 = false, bool e_fp8 = false) {
   ChunkPlan c{};
@@ -209,6 +213,7 @@ ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap, bool q8 
   c.bt = round_up(T > 0 ? T : 1, 128) <= 128 ? 128 : 256;
   c.Tp = round_up(T > 0 ? T : 1, c.bt);
   int64_t vc = kChunkPBytes / (c.Tp * 2) / bm * bm;
+  vc = std::min(vc, round_up(ceil_div(V, kMinChunks), bm));
   // CUTLOSS_MAX_CHUNK_ITEMS caps the chunk (rounded down to the item tile): a tuning knob,
   // and the way tests exercise several chunks on small problems
   if (const char* env = std::getenv("CUTLOSS_MAX_CHUNK_ITEMS")) {
@@ -703,6 +708,9 @@ cutloss_status ce_run_chunked(const cutloss_ce_problem* p, const float* lse_in, 
   // runs unfiltered (exact)
   if (filter_eps > 0.0f && pl.kps / 32 <= 1024 && round_up(pl.T, 32) / 32 <= 1024) {
     j.flags = w.flags; j.flag_ld = pl.flag_ld; j.flag_bn = (int)pl.flag_bn; j.filter_eps = filter_eps;
+    // chunk c flags its tiles with c + 1: flags left in a reused workspace by an earlier call
+    // would match, so the region starts at 0 in every call
+    CL_HIP(cl::launch_zero_bytes(w.flags, (size_t)(pl.Vc / 256) * pl.flag_ld * sizeof(int32_t), st), "zero flags");
   }
   j.k3_epi = dE != nullptr ? cl::GEMM_EPI_DE : -1;
   CL_TRY(run_chunks(j, st));

@@ -167,7 +167,7 @@ struct SweepParams {
 hipError_t launch_sweep2_rows(const SweepParams& p, int mode, hipStream_t st);
 hipError_t launch_sweep2_cols(const SweepParams& p, int kind, int epi, hipStream_t st);
 bool sweep2_rows_supported(int64_t D, int e_fp8);
-bool sweep2_cols_supported(int64_t D);
+bool sweep2_cols_supported(int64_t D, int e_fp8);
 int sweep2_rows_per_block(int64_t D);   // stationary rows per workgroup of the LDS-DMA rows sweep
 int sweep2_waves_per_block(int64_t D);  // waves per workgroup of the LDS-DMA sweeps
 

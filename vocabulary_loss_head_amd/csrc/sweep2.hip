@@ -622,11 +622,11 @@ __global__ __launch_bounds__(64 * Tiling<D>::NW, Tiling<D>::WPE) void k_rows2(co
 }
 
 // ------------------------------------------------------------------------------------
-// cols sweep: 128*MT stationary E rows per workgroup, A streamed with the row weights
-// (and the CE logsumexp). KIND 0 BCE, 1 CE. EPI 0 writes dE (bf16), EPI 1 applies
-// E <- round(E - lr dE) in place.
+// cols sweep: 128*MT stationary E rows per workgroup (bf16 E), A streamed with the row
+// weights (and the CE logsumexp). KIND 0 BCE, 1 CE. EPI 0 writes dE (bf16), EPI 1 applies
+// E <- bf16(E - lr dE) in place (nearest-even).
 // ------------------------------------------------------------------------------------
-template <int D, int KIND, int EPI, bool SFP8>
+template <int D, int KIND, int EPI>
 __global__ __launch_bounds__(64 * Tiling<D>::NW, Tiling<D>::WPE) void k_cols2(const SweepParams p) {
   using G = Geo<D>;
   constexpr int MT = Tiling<D>::MT;
@@ -652,7 +652,7 @@ __global__ __launch_bounds__(64 * Tiling<D>::NW, Tiling<D>::WPE) void k_cols2(co
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int64_t srow = s_wave + 32 * mt + l32;
-    load_stationary<D, SFP8>(sf[mt], p.E, srow, srow < p.V, h);
+    load_stationary<D, false>(sf[mt], p.E, srow, srow < p.V, h);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x16{};
   }
@@ -702,9 +702,6 @@ __global__ __launch_bounds__(64 * Tiling<D>::NW, Tiling<D>::WPE) void k_cols2(co
         if (u >= 0) gv -= p.S_u[(int64_t)u * D + d];
         if constexpr (EPI == 0) {
           ((uint16_t*)p.dE)[v * D + d] = (uint16_t)f32_to_bf16_bits(gv);
-        } else if constexpr (SFP8) {
-          uint8_t* e8 = (uint8_t*)p.E_inplace + v * D + d;
-          *e8 = (uint8_t)f32_to_fp8_sat(fp8_to_f32(*e8) - p.lr * gv);
         } else {
           uint16_t* e16 = (uint16_t*)p.E_inplace + v * D + d;
           *e16 = (uint16_t)f32_to_bf16_bits(bf16_bits_to_f32(*e16) - p.lr * gv);
@@ -735,14 +732,11 @@ template <int D>
 hipError_t cols2_d(const SweepParams& p, int kind, int epi, hipStream_t st) {
   const int64_t sb = 32 * Tiling<D>::MT * Tiling<D>::NW;
   const dim3 grid((unsigned)((p.V + sb - 1) / sb)), block(64 * Tiling<D>::NW);
-  const int key = kind * 4 + epi * 2 + (p.e_fp8 ? 1 : 0);
-  switch (key) {
-    case 0: k_cols2<D, 0, 0, false><<<grid, block, 0, st>>>(p); break;
-    case 1: k_cols2<D, 0, 0, true><<<grid, block, 0, st>>>(p); break;
-    case 2: k_cols2<D, 0, 1, false><<<grid, block, 0, st>>>(p); break;
-    case 3: k_cols2<D, 0, 1, true><<<grid, block, 0, st>>>(p); break;
-    case 4: k_cols2<D, 1, 0, false><<<grid, block, 0, st>>>(p); break;
-    case 5: k_cols2<D, 1, 0, true><<<grid, block, 0, st>>>(p); break;
+  if (p.e_fp8) return hipErrorInvalidValue;     // FP8 E runs the chunked path
+  switch (kind * 2 + epi) {
+    case 0: k_cols2<D, 0, 0><<<grid, block, 0, st>>>(p); break;
+    case 1: k_cols2<D, 0, 1><<<grid, block, 0, st>>>(p); break;
+    case 2: k_cols2<D, 1, 0><<<grid, block, 0, st>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -751,7 +745,7 @@ hipError_t cols2_d(const SweepParams& p, int kind, int epi, hipStream_t st) {
 }  // namespace
 
 bool sweep2_rows_supported(int64_t D, int e_fp8) { return !e_fp8 && (D == 64 || D == 128 || D == 256); }
-bool sweep2_cols_supported(int64_t D) { return D == 64 || D == 128 || D == 256; }
+bool sweep2_cols_supported(int64_t D, int e_fp8) { return !e_fp8 && (D == 64 || D == 128 || D == 256); }
 int sweep2_rows_per_block(int64_t D) {
   switch (D) {
     case 64: return 32 * Tiling<64>::MT * Tiling<64>::NW;
