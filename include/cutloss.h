@@ -159,6 +159,24 @@ cutloss_status cutloss_bce_bwd(const cutloss_bce_problem* p, const float* dloss,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * cutloss_bce_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation). Same arguments, outputs
+ * and kernels, without a workspace argument: the scratch space is a fixed array inside the
+ * library, 64 MiB per GPU (CUTLOSS_STATIC_SCRATCH_BYTES), created with the library's code
+ * on each GPU it runs on and held until the process ends. Nothing is allocated by the call.
+ * A problem whose cutloss_bce_workspace_size(p, CUTLOSS_OP_BWD) exceeds that size returns
+ * CUTLOSS_ERR_WORKSPACE before anything is launched. The array belongs to the device that
+ * is current when the call is made, and `stream` must belong to that device. Every call on
+ * one GPU shares the array, which keeps the last call's contents (each call sets up what it
+ * reads): calls that overlap on one GPU (on different streams, or from several host threads
+ * without ordering) race and give undefined results. Data errors are counted but cannot be
+ * read back (cutloss_read_data_errors needs a caller workspace).
+ */
+#define CUTLOSS_STATIC_SCRATCH_BYTES (64ull << 20)
+cutloss_status cutloss_bce_bwd_noalloc(const cutloss_bce_problem* p, const float* dloss,
+                                       void* dA, void* dE, float* loss_out, void* stream);
+
+/*
  * BCE backward fused with SGD on E: E <- round(E - lr * dE), dE never stored
  * (ELMO summary, Key Contributions 2: gradient fusion; Methodology: momentum-free
  * SGD, FP8 E4M3 weights). Rounding to E's dtype is nearest-even; FP8 saturates at

@@ -53,7 +53,8 @@ class SgdOptions(ctypes.Structure):
 
 EXPORTED = [
     "cutloss_bce_workspace_size", "cutloss_ce_workspace_size",
-    "cutloss_bce_fwd", "cutloss_bce_fwd_metrics", "cutloss_bce_bwd", "cutloss_bce_bwd_sgd", "cutloss_bce_bwd_sgd_ex",
+    "cutloss_bce_fwd", "cutloss_bce_fwd_metrics", "cutloss_bce_bwd", "cutloss_bce_bwd_noalloc", "cutloss_bce_bwd_sgd",
+    "cutloss_bce_bwd_sgd_ex",
     "cutloss_ce_fwd", "cutloss_ce_bwd", "cutloss_ce_bwd_filtered",
     "cutloss_read_data_errors", "cutloss_bce_canonical_targets",
     "cutloss_profile_enable", "cutloss_profile_read",
@@ -78,6 +79,7 @@ def _load() -> ctypes.CDLL:
         "cutloss_bce_fwd": (st, [pb, P, P, sz, P]),
         "cutloss_bce_fwd_metrics": (st, [pb, P, P, P, sz, P]),
         "cutloss_bce_bwd": (st, [pb, P, P, P, P, P, sz, P]),
+        "cutloss_bce_bwd_noalloc": (st, [pb, P, P, P, P, P]),
         "cutloss_bce_bwd_sgd": (st, [pb, P, ctypes.c_float, P, P, P, sz, P]),
         "cutloss_bce_bwd_sgd_ex": (st, [pb, P, ctypes.c_float, ctypes.POINTER(SgdOptions), P, P, P, sz, P]),
         "cutloss_ce_fwd": (st, [pc, P, P, P, sz, P]),
@@ -180,6 +182,15 @@ def cutloss_bce_fwd_metrics(problem: BceProblem, loss, counts, ws: torch.Tensor,
 def cutloss_bce_bwd(problem: BceProblem, dloss, dA, dE, loss_out, ws: torch.Tensor, stream=None) -> None:
     _check(_lib.cutloss_bce_bwd(ctypes.byref(problem), _ptr(dloss), _ptr(dA), _ptr(dE), _ptr(loss_out),
                                 _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def cutloss_bce_bwd_noalloc(problem: BceProblem, dloss, dA, dE, loss_out, stream=None) -> None:
+    """cutloss_bce_bwd with the library's fixed scratch array instead of a workspace."""
+    _check(_lib.cutloss_bce_bwd_noalloc(ctypes.byref(problem), _ptr(dloss), _ptr(dA), _ptr(dE), _ptr(loss_out),
+                                        _stream(stream)))
+
+
+STATIC_SCRATCH_BYTES = 64 << 20
 
 
 def cutloss_bce_bwd_sgd(problem: BceProblem, dloss, lr: float, dA, loss_out, ws: torch.Tensor, stream=None) -> None:

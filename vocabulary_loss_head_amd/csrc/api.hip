@@ -723,6 +723,33 @@ cutloss_status ce_run_chunked(const cutloss_ce_problem* p, const float* lse_in, 
   return CUTLOSS_OK;
 }
 
+// ---- allocation-free variant of cutloss_bce_bwd: the workspace is a fixed device array of
+// the library (one copy per GPU, held until the process ends)
+constexpr size_t kStaticScratchBytes = 64ull << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`, looked up on the first call on
+// that device. In host code the array's name stands for a host-side shadow, never for the
+// device memory, so only this address is passed to kernels.
+cutloss_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  CL_HIP(hipGetDevice(&dev), "current device");
+  if (dev < 0 || dev >= kMaxDevices) return fail(CUTLOSS_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    CL_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "scratch array address");
+    if (ptr == nullptr) return fail(CUTLOSS_ERR_HIP, "scratch array address is NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return CUTLOSS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -785,6 +812,23 @@ cutloss_status cutloss_bce_bwd(const cutloss_bce_problem* p, const float* dloss,
   CL_TRY(check_out(dE, 16, "dE", false));
   CL_TRY(check_out(loss_out, 4, "loss_out", false));
   return bce_run(p, dloss, loss_out, dA, dE, dE ? 1 : 0, 0.0f, ws, ws_bytes, (hipStream_t)stream);
+}
+
+cutloss_status cutloss_bce_bwd_noalloc(const cutloss_bce_problem* p, const float* dloss, void* dA, void* dE,
+                                       float* loss_out, void* stream) {
+  g_last_error.clear();
+  CL_TRY(check_bce(p));
+  CL_TRY(check_out(dloss, 4, "dloss", false));
+  CL_TRY(check_out(dA, 16, "dA", false));
+  CL_TRY(check_out(dE, 16, "dE", false));
+  CL_TRY(check_out(loss_out, 4, "loss_out", false));
+  const size_t need = cutloss_bce_workspace_size(p, CUTLOSS_OP_BWD);
+  if (need > kStaticScratchBytes)
+    return fail(CUTLOSS_ERR_WORKSPACE, "problem needs %zu bytes of scratch; the allocation-free call has %zu",
+                need, kStaticScratchBytes);
+  void* ws = nullptr;
+  CL_TRY(scratch_of_current_device(&ws));
+  return bce_run(p, dloss, loss_out, dA, dE, dE ? 1 : 0, 0.0f, ws, kStaticScratchBytes, (hipStream_t)stream);
 }
 
 cutloss_status cutloss_bce_bwd_sgd(const cutloss_bce_problem* p, const float* dloss, float lr, void* dA, float* loss_out,
