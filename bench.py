@@ -4,15 +4,21 @@ Default: one step = one cutloss_bce_bwd call with the loss emitted by the same p
 (fused forward+backward) on the sequential-recommendation head T = 4096 (B=16, N=256),
 D = 256, V = 876,939 (Zipf(1.1) positives, L = 8, 10% padding rows), inputs resident in
 HBM. It prints ONE JSON line: value = counted TFLOP/s with 8*T*V*D FLOPs per step (2TVD
-forward, 6TVD recompute-backward), a `roofline` object for the dominant kernel (HIP
-events recorded by the library around its launches, on the launch stream) and a
-`cpu_baseline` object that times the fp64 CPU oracle on a bounded sample of the same
-workload.
+forward, 6TVD recompute-backward) over `--steps` back-to-back steps timed with nothing else
+recorded; a `roofline` object for the dominant kernel, whose launch duration comes from a
+separate pass of the same length with the library's HIP events recorded around each kernel
+phase on the launch stream; and a `cpu_baseline` object that times the fp64 CPU oracle on a
+bounded sample of the same workload.
 
 --workload NAME times another configuration the same way (its fused step: BCE
 cutloss_bce_bwd with loss; softmax CE cutloss_ce_fwd + cutloss_ce_bwd; the FP8 XMC head
-cutloss_bce_bwd_sgd with loss). --all prints one JSON line per configuration with the
-forward-only and fused-step timings (a report, not the benchmark contract line).
+cutloss_bce_bwd_sgd with loss). --all prints one report line per configuration (not the
+benchmark contract line): median, p10 and p90 of 500 (or, for the two heaviest heads, 100)
+back-to-back forward calls and fused steps (the Cut BCE mini-benchmark's steady-state
+protocol, §IV-A), counted rates over all rows and over valid rows, fractions of the bf16
+MFMA peak (and of the HBM peak for the FP8 head), peak HBM use against the materialized
+logits, per-phase times, the separately measured options, and the oracle's CPU time with
+the full-size time extrapolated. --all --only --workload NAME reports one configuration.
 
 roofline.traffic is the HBM byte count per launch of the dominant kernel measured with
 rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, each scaled by the factor a plain copy of
@@ -78,6 +84,7 @@ def copy_calibration(nbytes: int, reps: int = 5) -> None:
 
 
 def _cpu_threads() -> int:
+    """Threads the oracle's BLAS actually runs with."""
     try:
         from threadpoolctl import threadpool_info
         n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
@@ -85,40 +92,81 @@ def _cpu_threads() -> int:
             return int(max(n))
     except Exception:
         pass
-    return os.cpu_count() or 1
+    return 1
 
 
-def cpu_baseline(inp, rows_n=512, items_n=4096):
-    """Time the oracle (unchanged) on a bounded sample: loss+dA for `rows_n` rows and, for
-    the multi-label heads, dE for `items_n` items. The rate is counted FLOPs of that
-    sampled share of a step per second (a row carries 2VD forward + 2VD dA, an item 2TD
-    recompute + 2TD dE)."""
+def cpu_baseline(inp, rows_n=512, items_n=4096, full=False):
+    """Time the oracle (unchanged) on a bounded sample of the same inputs: loss+dA for
+    `rows_n` rows (one x_t = E A_t pass each) and dE for `items_n` items (x_v = A E_v each;
+    for softmax CE after the logsumexp of every row, whose time is counted with the rows).
+    The rate is the metric's counted FLOPs of that share of a step (a row carries 2VD
+    forward + 2VD dA, an item 2TD recompute + 2TD dE) per second; the full-size time
+    t_row * T + t_item * V is extrapolated from the two per-sample times. full=True runs
+    the whole oracle instead (small heads)."""
     from oracle import head_loss as H
     from oracle.formats import decode_bf16, decode_fp8_e4m3fn
     from oracle.targets import canonical_csr
     w = inp["workload"]
     A64 = decode_bf16(inp["A"])
     E64 = decode_bf16(inp["E"]) if inp["E"].dtype == np.uint16 else decode_fp8_e4m3fn(inp["E"])
+    rec = {"unit": "TFLOP/s", "cores": _cpu_threads(), "host_cpu_count": os.cpu_count(), "kind": "oracle"}
+    if full:
+        t0 = time.perf_counter()
+        if w.kind == "bce":
+            crow, cids, _ = canonical_csr(inp["row_ptr"], inp["ids"], inp["mask"], w.V, w.pad_id)
+            H.bce_loss(A64, E64, crow, cids, inp["mask"])
+            H.bce_grads(A64, E64, crow, cids, inp["mask"])
+        else:
+            H.ce_forward(A64, E64, inp["target"])
+            H.ce_grads(A64, E64, inp["target"])
+        dt = time.perf_counter() - t0
+        rec.update({"value": 8.0 * w.T * w.V * w.D / dt / 1e12, "seconds": round(dt, 4),
+                    "full_size_seconds": round(dt, 4),
+                    "sample": f"fp64 oracle, whole fwd+bwd (logits materialized) of T={w.T}, D={w.D}, V={w.V}"})
+        return rec
     rng = np.random.default_rng(0)
     rows_n = min(rows_n, w.T)
-    items_n = min(items_n, w.V) if w.kind == "bce" else 0
+    items_n = min(items_n, w.V)
     rows = np.sort(rng.choice(w.T, rows_n, replace=False))
-    t0 = time.perf_counter()
+    items = np.sort(rng.choice(w.V, items_n, replace=False))
     if w.kind == "bce":
         crow, cids, _ = canonical_csr(inp["row_ptr"], inp["ids"], inp["mask"], w.V, w.pad_id)
+        t0 = time.perf_counter()
         H.bce_rows(A64, E64, crow, cids, rows, inp["mask"])
-        items = np.sort(rng.choice(w.V, items_n, replace=False))
+        t1 = time.perf_counter()
         H.bce_items(A64, E64, crow, cids, items, inp["mask"])
+        t2 = time.perf_counter()
+        t_row, t_item = (t1 - t0) / rows_n, (t2 - t1) / items_n
     else:
+        t0 = time.perf_counter()
         H.ce_rows(A64, E64, inp["target"], rows)
-    dt = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        # dE of an item needs the logsumexp of every row: the oracle's own values, stored by
+        # tests/golden/make_llm_ce_lse.py for the LM head (its time is the rows' forward
+        # pass, already in t_row), else computed here and counted with the rows
+        lse_all = None
+        gold = os.path.join(ROOT, "tests", "golden", f"{w.name}_lse.npy")
+        if os.path.exists(gold):
+            lse_all = np.load(gold)
+            if lse_all.shape != (w.T,):
+                lse_all = None
+        t_lse = 0.0
+        if lse_all is None:
+            lse_all = H.ce_lse(A64, E64, np.arange(w.T))
+            t_lse = time.perf_counter() - t1
+        t2 = time.perf_counter()
+        H.ce_items(A64, E64, inp["target"], items, lse_all)
+        t3 = time.perf_counter()
+        t_row, t_item = (t1 - t0) / rows_n + t_lse / w.T, (t3 - t2) / items_n
+        t2 = t3
+    dt = t2 - t0
     flops = rows_n * 4.0 * w.V * w.D + items_n * 4.0 * w.T * w.D
-    what = f"loss+dA for {rows_n} rows (one x_t = E A_t pass each)"
-    if items_n:
-        what += f" and dE for {items_n} items (x_v = A E_v each)"
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _cpu_threads(), "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"fp64 oracle: {what} of the same T={w.T}, D={w.D}, V={w.V} inputs"}
+    rec.update({"value": flops / dt / 1e12, "seconds": round(dt, 3),
+                "extrapolated_full_size_seconds": round(t_row * w.T + t_item * w.V, 1),
+                "sample": f"fp64 oracle: loss+dA for {rows_n} rows (one x_t = E A_t pass each) and dE for "
+                          f"{items_n} items (x_v = A E_v each) of the same T={w.T}, D={w.D}, V={w.V} inputs; "
+                          f"full size extrapolated as t_row*T + t_item*V"})
+    return rec
 
 
 class Head:
@@ -209,6 +257,10 @@ class Head:
 
 
 def time_calls(fn, steps, warmup, profile=False):
+    """Mean ms per call of `steps` back-to-back calls after `warmup` untimed ones, bracketed
+    by device synchronizations. With profile=True the library's per-phase HIP events are
+    recorded (a separate pass from the timed contract line) and returned as
+    {phase: (ms per step, launches per step)}."""
     import torch
     from vocabulary_loss_head_amd import binding as B
     for _ in range(warmup):
@@ -227,31 +279,60 @@ def time_calls(fn, steps, warmup, profile=False):
     phases = {}
     if profile:
         B.cutloss_profile_enable(False)
-        # {phase: (ms per step, launches per step)}
         phases = {k: (v[0] / steps, v[1] / steps) for k, v in B.cutloss_profile_read().items() if v[1]}
     return ev0.elapsed_time(ev1) / steps, phases
+
+
+def time_per_call(fn, n, warmup):
+    """Per-call device times of n back-to-back calls (a HIP event on the calling stream
+    between consecutive calls), after `warmup` untimed calls: median, p10, p90, mean (ms)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    evs[0].record()
+    for i in range(n):
+        fn()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    t = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(n)])
+    return {"median": round(float(np.median(t)), 4), "p10": round(float(np.percentile(t, 10)), 4),
+            "p90": round(float(np.percentile(t, 90)), 4), "mean": round(float(t.mean()), 4), "calls": n}
 
 
 def e_bytes(w):
     return w.V * w.D * (1 if w.e_dtype == "fp8" else 2)
 
 
-def record(name, steps, warmup, with_cpu):
+def _load(name):
     import torch
     from workloads import make, workload
-    w = workload(name)
-    inp = make(w)
+    inp = make(workload(name))
     h = Head(inp)
     torch.cuda.synchronize()
+    return inp, h
+
+
+def _dominant_sweep(phases):
+    # dominant kernel phase of the fused sweeps (D <= 256): one launch per step each;
+    # each sweep executes 4TVD per launch (logit recompute + dA or dE)
+    return max(("rows_sweep", "cols_sweep"), key=lambda k: phases.get(k, (0.0, 0))[0])
+
+
+def record(name, steps, warmup, with_cpu):
+    """The contract line: `steps` fused steps timed with nothing else recorded, then a
+    separate pass of the same length with the library's phase events for the roofline."""
+    import torch
+    inp, h = _load(name)
+    w = h.w
     torch.cuda.reset_peak_memory_stats()
-    ms, phases = time_calls(h.step, steps, warmup, profile=True)
+    ms, _ = time_calls(h.step, steps, warmup, profile=False)
     peak = torch.cuda.max_memory_allocated()
+    _, phases = time_calls(h.step, steps, 1, profile=True)
     T, D, V = w.T, w.D, w.V
     tflops = 8.0 * T * V * D / (ms * 1e-3) / 1e12
     n_valid = int(inp["mask"].sum()) if "mask" in inp else int((inp["target"] != -100).sum())
-    # dominant kernel phase of the fused sweeps (D <= 256): one launch per step each;
-    # the rows sweep executes 4TVD per launch (logit recompute + dA)
-    dom = max(("rows_sweep", "cols_sweep"), key=lambda k: phases.get(k, (0.0, 0))[0])
     rec = {
         "metric": METRIC if name == "seqrec_bce" else f"{name}: fused fwd+bwd TFLOP/s (8TVD counted)",
         "value": round(tflops, 2),
@@ -277,46 +358,91 @@ def record(name, steps, warmup, with_cpu):
         "logits_fp32_bytes": 4 * T * V,
     }
     if name == "seqrec_bce":
-        dom_flops = 4.0 * T * V * D
-        achieved = dom_flops / (phases[dom][0] / phases[dom][1] * 1e-3) / 1e12
+        dom = _dominant_sweep(phases)
+        achieved = 4.0 * T * V * D / (phases[dom][0] / phases[dom][1] * 1e-3) / 1e12
         kname = f"k_{dom.split('_')[0]}2"
         rec["roofline"] = {"kernel": f"{kname} (fused {dom.replace('_', ' ')})", "bound": "mfma",
                            "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(kname)}
     if w.lr > 0:
-        # fused SGD step: E is read and written once at the least
         rec["e_traffic_GBps"] = round(2 * e_bytes(w) / (ms * 1e-3) / 1e9, 1)
     if with_cpu:
         rec["cpu_baseline"] = cpu_baseline(inp)
     return rec, h
 
 
-def report_all(steps, warmup):
+# calls per timed configuration, after the Cut BCE mini-benchmark's 500 steady-state
+# iterations (§IV-A); the two heaviest heads take 100
+CALLS = {"tiny_bce": 500, "seqrec_bce": 500, "seqrec_bce_large": 100, "llm_ce": 100, "xmc_sgd": 500}
+
+
+def config_record(name, calls=None, with_cpu=True):
+    """One report line per configuration: forward and fused-step call statistics, counted
+    rates over all rows and over valid rows, fractions of peak, peak HBM use against the
+    materialized logits, per-phase times from a separate profiled pass, the separately
+    measured options, and the oracle's CPU time."""
     import torch
-    for name in ALL:
-        rec, h = record(name, steps, warmup, with_cpu=False)
-        fwd_ms, fwd_phases = time_calls(h.fwd, steps, warmup)
-        w = h.w
-        rec["fwd_ms"] = round(fwd_ms, 4)
-        rec["fwd_tflops"] = round(2.0 * w.T * w.V * w.D / (fwd_ms * 1e-3) / 1e12, 2)
-        rec["fwd_pct_bf16_peak"] = round(100.0 * rec["fwd_tflops"] / PEAK_BF16_TFLOPS, 2)
-        rec["fwd_e_read_GBps"] = round(e_bytes(w) / (fwd_ms * 1e-3) / 1e9, 1)
-        if w.kind == "bce":
-            m_ms, _ = time_calls(h.fwd_metrics, steps, warmup)
-            rec["fwd_cut_metrics_ms"] = round(m_ms, 4)
-            if h.sgd:
-                s_ms, _ = time_calls(lambda: h.step_sgd_ex(stochastic=True), steps, warmup)
-                rec["step_sgd_stochastic_rounding_ms"] = round(s_ms, 4)
-                f_ms, _ = time_calls(lambda: h.step_sgd_ex(fp8_logits=True), steps, warmup)
-                rec["step_sgd_fp8_logits_ms"] = round(f_ms, 4)
-                b_ms, _ = time_calls(lambda: h.step_sgd_ex(stochastic=True, fp8_logits=True), steps, warmup)
-                rec["step_sgd_fp8_logits_stochastic_rounding_ms"] = round(b_ms, 4)
-        else:
-            f_ms, _ = time_calls(h.step_grad_filter, steps, warmup)
-            rec["step_grad_filter_2^-12_ms"] = round(f_ms, 4)
-        print(json.dumps(rec), flush=True)
-        del h
-        torch.cuda.empty_cache()
+    inp, h = _load(name)
+    w = h.w
+    T, D, V = w.T, w.D, w.V
+    n = calls or CALLS[name]
+    n_valid = int(inp["mask"].sum()) if "mask" in inp else int((inp["target"] != -100).sum())
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    step = time_per_call(h.step, n, 10)
+    peak = torch.cuda.max_memory_allocated()
+    fwd = time_per_call(h.fwd, n, 10)
+    _, phases = time_calls(h.step, min(n, 50), 2, profile=True)
+    sm, fm = step["median"] * 1e-3, fwd["median"] * 1e-3
+    rec = {
+        "workload": name, "kind": w.kind, "T": T, "D": D, "V": V, "e_dtype": w.e_dtype, "valid_rows": n_valid,
+        "call": h.call_name(),
+        "step_ms": step, "fwd_ms": fwd,
+        "rows_per_s": round(T / sm, 1),
+        "step_tflops_counted_8TVD": round(8.0 * T * V * D / sm / 1e12, 2),
+        "step_tflops_valid_rows": round(8.0 * n_valid * V * D / sm / 1e12, 2),
+        "fwd_tflops_counted_2TVD": round(2.0 * T * V * D / fm / 1e12, 2),
+        "fwd_tflops_valid_rows": round(2.0 * n_valid * V * D / fm / 1e12, 2),
+        "step_pct_bf16_peak": round(100.0 * 8.0 * T * V * D / sm / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "fwd_pct_bf16_peak": round(100.0 * 2.0 * T * V * D / fm / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "input_bytes_resident": int(base),
+        "peak_hbm_bytes": int(peak),
+        "workspace_bytes": h.ws_bytes,
+        "logits_fp32_bytes": 4 * T * V,
+        "phase_ms_per_step": {k: round(v[0], 4) for k, v in phases.items()},
+        "phase_launches_per_step": {k: round(v[1], 2) for k, v in phases.items()},
+    }
+    if w.e_dtype == "fp8":
+        # E streaming dominates at T = 128: the forward reads E once; the SGD step reads it
+        # at least once and writes it once (two sweeps over E read it twice)
+        eb = e_bytes(w)
+        rec["fwd_e_read_GBps"] = round(eb / fm / 1e9, 1)
+        rec["fwd_pct_hbm_peak"] = round(100.0 * eb / fm / 1e9 / PEAK_HBM_GBS, 2)
+        rec["step_e_GBps_single_pass_count"] = round(2 * eb / sm / 1e9, 1)
+        rec["step_e_GBps_two_sweep_count"] = round(3 * eb / sm / 1e9, 1)
+        rec["step_pct_hbm_peak_two_sweep_count"] = round(100.0 * 3 * eb / sm / 1e9 / PEAK_HBM_GBS, 2)
+    opts = {}
+    m = max(20, n // 5)
+    if w.kind == "bce":
+        opts["fwd_cut_metrics_ms"] = time_per_call(h.fwd_metrics, m, 3)
+        if h.sgd:
+            opts["step_sgd_stochastic_rounding_ms"] = time_per_call(lambda: h.step_sgd_ex(stochastic=True), m, 3)
+            opts["step_sgd_fp8_logits_ms"] = time_per_call(lambda: h.step_sgd_ex(fp8_logits=True), m, 3)
+            opts["step_sgd_fp8_logits_stochastic_rounding_ms"] = time_per_call(
+                lambda: h.step_sgd_ex(stochastic=True, fp8_logits=True), m, 3)
+    else:
+        opts["step_grad_filter_2^-12_ms"] = time_per_call(h.step_grad_filter, m, 3)
+    rec["options"] = opts
+    del h
+    torch.cuda.empty_cache()
+    if with_cpu:
+        rec["cpu_baseline"] = cpu_baseline(inp, full=(name == "tiny_bce"))
+    return rec
+
+
+def report_all(names, with_cpu):
+    for name in names:
+        print(json.dumps(config_record(name, with_cpu=with_cpu)), flush=True)
 
 
 def main():
@@ -326,6 +452,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="seqrec_bce", choices=ALL)
     ap.add_argument("--all", action="store_true", help="one report line per configuration")
+    ap.add_argument("--only", action="store_true", help="with --all: only the --workload configuration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
@@ -338,7 +465,8 @@ def main():
               "(the vocabulary-parallel form is designed but not built)", file=sys.stderr)
         sys.exit(2)
     if args.all:
-        report_all(args.steps, args.warmup)
+        report_all(ALL if args.workload == "seqrec_bce" and not args.only else [args.workload],
+                   with_cpu=not args.no_cpu_baseline)
         return
     rec, _ = record(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu_baseline)
     print(json.dumps(rec), flush=True)
