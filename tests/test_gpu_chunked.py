@@ -95,7 +95,9 @@ def _sgd_case(B, T, D, V, seed):
     g = upload(inp)
     dev = g["A"].device
     prob = B.bce_problem(g["A"], g["E"], g["row_ptr"], g["ids"], g["mask"], -1)
-    ws = B.workspace(B.cutloss_bce_workspace_size(prob, B.OP_BWD_SGD), dev)
+    # one workspace for the unfused backward and the SGD step: large enough for both
+    ws = B.workspace(max(B.cutloss_bce_workspace_size(prob, B.OP_BWD), B.cutloss_bce_workspace_size(prob, B.OP_BWD_SGD)),
+                     dev)
     dE = torch.empty(w.V, w.D, dtype=torch.bfloat16, device=dev)
     dA = torch.empty(w.T, w.D, dtype=torch.bfloat16, device=dev)
     B.cutloss_bce_bwd(prob, None, dA, dE, None, ws)

@@ -174,7 +174,9 @@ def test_sgd_fp8_small(B, D):
     crow, cids, _ = canonical(inp, w.V, -1)
     g = upload(inp)
     prob = B.bce_problem(g["A"], g["E"], g["row_ptr"], g["ids"], g["mask"], -1)
-    ws = B.workspace(B.cutloss_bce_workspace_size(prob, B.OP_BWD_SGD), g["A"].device)
+    # one workspace for the unfused backward and the SGD step: large enough for both
+    ws = B.workspace(max(B.cutloss_bce_workspace_size(prob, B.OP_BWD), B.cutloss_bce_workspace_size(prob, B.OP_BWD_SGD)),
+                     g["A"].device)
     # unfused dE on the same fp8 E first
     dE = torch.empty(w.V, w.D, dtype=torch.bfloat16, device=g["A"].device)
     B.cutloss_bce_bwd(prob, None, None, dE, None, ws)
@@ -218,7 +220,9 @@ def test_sgd_bf16_fused_sweeps(B, D):
     g = upload(inp)
     dev = g["A"].device
     prob = B.bce_problem(g["A"], g["E"], g["row_ptr"], g["ids"], g["mask"], -1)
-    ws = B.workspace(B.cutloss_bce_workspace_size(prob, B.OP_BWD_SGD), dev)
+    # one workspace for the unfused backward and the SGD step: large enough for both
+    ws = B.workspace(max(B.cutloss_bce_workspace_size(prob, B.OP_BWD), B.cutloss_bce_workspace_size(prob, B.OP_BWD_SGD)),
+                     dev)
     dE = torch.empty(w.V, w.D, dtype=torch.bfloat16, device=dev)
     B.cutloss_bce_bwd(prob, None, None, dE, None, ws)
     loss = torch.empty(w.T, dtype=torch.float32, device=dev)
