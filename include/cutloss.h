@@ -260,6 +260,22 @@ cutloss_status cutloss_bce_canonical_targets(const cutloss_bce_problem* p,
                                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Test hook: the sparse correction's positive logits as the loss computes them
+ * (Cut Binary Cross Entropy, Section I-B, fused direct BCE formulation: the loss is the
+ * dense softplus sum minus the sum of the logits of a row's positives).
+ * Canonicalizes the positive sets as cutloss_bce_canonical_targets does, then writes
+ * sum_x[t] = sum over the canonical positives p of row t of x_tp = A_t . E_p (fp32, summed
+ * in ascending item order; 0 for masked rows and rows without positives) and, if x_pos is
+ * not NULL, x_pos[e] = x_tp for every canonical pair e in the order of the canonical CSR
+ * (rows ascending, items ascending within a row; at most nnz entries). sum_x holds T floats,
+ * x_pos nnz floats, both device memory owned by the caller. The workspace holds only the
+ * canonical targets: cutloss_bce_workspace_size(p, op) of any op suffices. Asynchronous on
+ * `stream`; data errors are counted as by the other entry points.
+ */
+cutloss_status cutloss_bce_positive_logits(const cutloss_bce_problem* p, float* sum_x, float* x_pos,
+                                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Profiling hook. While enabled (process-wide), every entry point records a HIP event
  * pair on the caller's stream around each of its kernel phases:
  *   0 target canonicalization, 1 rows sweep (loss/LSE partials, dA partials),

@@ -101,6 +101,22 @@ def bce_loss_dense_sparse(A, E, crow, cids, mask=None):
     return np.where(_valid_rows(T, mask), dense - sparse, 0.0)
 
 
+def positive_logits(A, E, crow, cids):
+    """The sparse correction's terms (Cut BCE §I-B): x_tp = A_t . E_p for every canonical
+    pair, one indexed dot product each (X is not formed), and their per-row sums.
+
+    Returns (x_pos [nnz'] in the order of cids, sum_x [T]); rows without positives sum to 0."""
+    T = A.shape[0]
+    crow = np.asarray(crow, dtype=np.int64)
+    cids = np.asarray(cids, dtype=np.int64)
+    rows = np.repeat(np.arange(T), np.diff(crow))
+    x_pos = np.einsum("ij,ij->i", A[rows], E[cids]) if len(cids) else np.zeros(0)
+    sum_x = np.zeros(T, dtype=np.float64)
+    for t in range(T):
+        sum_x[t] = x_pos[crow[t]:crow[t + 1]].sum()
+    return x_pos, sum_x
+
+
 def bce_grads(A, E, crow, cids, mask=None, dloss=None, A_logits=None):
     """(dA, dE) of L = sum_t w_t loss_t."""
     T, V = A.shape[0], E.shape[0]

@@ -97,6 +97,29 @@ def _torch_bce(A, E, crow, cids, mask, w):
     return per.detach().numpy(), At.grad.numpy(), Et.grad.numpy()
 
 
+def test_positive_logits_by_brute_force_and_torch_bce():
+    # Cut BCE §I-B: the sparse correction's terms x_tp = A_t . E_p, pinned two ways: a
+    # scalar loop over (t, p, d) on the canonical pairs, and the split of torch's library
+    # BCE loss, sum_v softplus(x_tv) - loss_t = sum_p x_tp for every valid row
+    T, D, V = 7, 5, 29
+    A, E, crow, cids, mask, w = _problem(T, D, V, 11, std=0.9, L=6)
+    x_pos, sum_x = H.positive_logits(A, E, crow, cids)
+    assert x_pos.shape == (len(cids),) and sum_x.shape == (T,)
+    for t in range(T):
+        acc_row = 0.0
+        for e in range(crow[t], crow[t + 1]):
+            acc = 0.0
+            for d in range(D):
+                acc += A[t, d] * E[cids[e], d]
+            assert x_pos[e] == pytest.approx(acc, rel=1e-13, abs=1e-15)
+            acc_row += acc
+        assert sum_x[t] == pytest.approx(acc_row, rel=1e-13, abs=1e-15)
+    assert np.all(sum_x[mask == 0] == 0)      # masked rows keep no canonical positives
+    loss_t, _, _ = _torch_bce(A, E, crow, cids, np.ones(T, np.uint8), np.ones(T))
+    dense = torch.nn.functional.softplus(torch.tensor(A @ E.T)).sum(1).numpy()
+    np.testing.assert_allclose(dense - loss_t, sum_x, rtol=1e-10, atol=1e-12)
+
+
 @pytest.mark.parametrize("seed,std", [(3, None), (4, 1.0), (5, 3.0)])
 def test_bce_matches_torch_library_and_autograd(seed, std):
     T, D, V = 8, 16, 77

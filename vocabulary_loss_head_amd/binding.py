@@ -56,7 +56,7 @@ EXPORTED = [
     "cutloss_bce_fwd", "cutloss_bce_fwd_metrics", "cutloss_bce_bwd", "cutloss_bce_bwd_noalloc", "cutloss_bce_bwd_sgd",
     "cutloss_bce_bwd_sgd_ex",
     "cutloss_ce_fwd", "cutloss_ce_bwd", "cutloss_ce_bwd_filtered",
-    "cutloss_read_data_errors", "cutloss_bce_canonical_targets",
+    "cutloss_read_data_errors", "cutloss_bce_canonical_targets", "cutloss_bce_positive_logits",
     "cutloss_profile_enable", "cutloss_profile_read",
     "cutloss_status_string", "cutloss_last_error", "cutloss_version",
 ]
@@ -87,6 +87,7 @@ def _load() -> ctypes.CDLL:
         "cutloss_ce_bwd_filtered": (st, [pc, P, P, P, P, ctypes.c_float, P, sz, P]),
         "cutloss_read_data_errors": (st, [P, P, ctypes.POINTER(ctypes.c_int64)]),
         "cutloss_bce_canonical_targets": (st, [pb, P, P, P, P, ctypes.POINTER(ctypes.c_int64), P, sz, P]),
+        "cutloss_bce_positive_logits": (st, [pb, P, P, P, sz, P]),
         "cutloss_profile_enable": (st, [ctypes.c_int32]),
         "cutloss_profile_read": (st, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]),
         "cutloss_status_string": (ctypes.c_char_p, [st]),
@@ -232,6 +233,11 @@ def cutloss_bce_canonical_targets(problem: BceProblem, crow, cids, items, rows, 
     _check(_lib.cutloss_bce_canonical_targets(ctypes.byref(problem), _ptr(crow), _ptr(cids), _ptr(items), _ptr(rows),
                                               ctypes.byref(n), _ptr(ws), ws.numel(), _stream(stream)))
     return int(n.value)
+
+
+def cutloss_bce_positive_logits(problem: BceProblem, sum_x, x_pos, ws: torch.Tensor, stream=None) -> None:
+    _check(_lib.cutloss_bce_positive_logits(ctypes.byref(problem), _ptr(sum_x), _ptr(x_pos), _ptr(ws), ws.numel(),
+                                            _stream(stream)))
 
 
 def cutloss_profile_enable(enable: bool) -> None:

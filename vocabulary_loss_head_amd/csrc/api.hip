@@ -931,6 +931,28 @@ cutloss_status cutloss_bce_canonical_targets(const cutloss_bce_problem* p, int32
   return CUTLOSS_OK;
 }
 
+cutloss_status cutloss_bce_positive_logits(const cutloss_bce_problem* p, float* sum_x, float* x_pos,
+                                           void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  CL_TRY(check_bce(p));
+  if (sum_x == nullptr) return fail(CUTLOSS_ERR_INVALID_ARG, "NULL output");
+  hipStream_t st = (hipStream_t)stream;
+  Plan pl = make_plan(p->T, p->D, p->V, p->nnz, p->e_dtype == CUTLOSS_FP8_E4M3);
+  pl.n_splits = 0;   // the canonical targets only: a prefix of every operation's workspace
+  const Ws w = carve(ws, pl, false, false, false);
+  CL_TRY(check_ws(ws, ws_bytes, w.bytes));
+  if (p->T == 0) return CUTLOSS_OK;
+  CL_HIP(cl::launch_zero_u64(w.err, 4, st), "zero counters");
+  CL_HIP(cl::launch_targets(w.tw, p->T, p->V, p->nnz, p->pos_row_ptr, p->pos_ids, p->row_mask, p->pad_id, nullptr, 0, st), "targets");
+  cl::FinalizeParams fp{};
+  fp.T = p->T; fp.D = p->D; fp.V = p->V;
+  fp.A = p->A; fp.E = p->E; fp.e_fp8 = p->e_dtype == CUTLOSS_FP8_E4M3;
+  fp.crow = w.tw.crow; fp.cids = w.tw.cids;
+  fp.pos_dot = sum_x; fp.pos_x = x_pos;
+  CL_HIP(cl::launch_row_positives(fp, st), "row positives");
+  return CUTLOSS_OK;
+}
+
 cutloss_status cutloss_profile_enable(int32_t enable) {
   std::lock_guard<std::mutex> g(g_prof_mu);
   g_prof_on = enable != 0;

@@ -172,6 +172,7 @@ __global__ __launch_bounds__(256) void k_row_positives(const FinalizeParams p) {
   int tp = 0;
   for (int32_t e = pb; e < pe; ++e) {
     const float x = wave_sum(pos_dot_part(p, t, (int64_t)p.cids[e], lane));
+    if (p.pos_x != nullptr && lane == 0) p.pos_x[e] = x;
     sum_x += x;
     tp += x > 0.0f ? 1 : 0;
   }

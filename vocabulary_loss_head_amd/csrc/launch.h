@@ -91,6 +91,7 @@ struct FinalizeParams {
   // positive-row terms computed before E changes (chunked path): if set, finalize reads
   // them instead of E: pos_dot[t] = sum_p A_t . E_p, pos_sum[t][d] = sum_p E_p[d]
   float* pos_dot; float* pos_sum;
+  float* pos_x;             // k_row_positives only, if set: x_tp per canonical positive (cids order)
   // Cut Metrics: per-split counts of logits > 0 (floats, exact below 2^24) in part_c, the
   // per-row positives with a positive logit (pos_tp, from k_row_positives when set), and
   // the output counts[T][4] = (TP, FP, FN, TN)
