@@ -117,7 +117,9 @@ def test_no_positives(B, D):
 def test_tiny_vocabulary(B, V, D):
     _say(f"tiny vocabulary V={V} D={D}")
     # logits of a few units: with one item the BCE loss of a positive row is softplus(-x),
-    # and its dense - sparse evaluation cancels; |x| <~ 4 keeps that inside the tolerance
+    # and its dense - sparse evaluation cancels; std 0.25 keeps dense / loss below the
+    # ~1e3 at which the fp32 difference leaves the relative tolerance (measured by
+    # test_dense_minus_sparse_cancellation_limit)
     A, E, rp, ids, mask = _bce_inputs(37, D, V, 2, 4 + V, std=0.25)
     mask[5] = 0
     _check_bce_case(B, A, E, rp, ids, mask)
@@ -160,3 +162,46 @@ def test_ce_every_target_ignored(B, D):
     assert np.all(out["loss"].cpu().numpy() == 0)
     assert torch.count_nonzero(out["dA"].float()).item() == 0
     assert torch.count_nonzero(out["dE"].float()).item() == 0
+
+
+@pytest.mark.parametrize("D", [64, 512])
+def test_dense_minus_sparse_cancellation_limit(B, D):
+    """Where the dense - sparse evaluation of the loss (Cut Binary Cross Entropy, §I-B) stops
+    meeting the relative tolerance. In fp32, dense_t - sum_p x_tp keeps an absolute error of
+    a few ulps of dense_t, so a row whose confident positives carry nearly all of dense_t
+    loses relative accuracy in proportion to dense_t / loss_t. With E = I the logits are A
+    exactly: A_tv = +s_t on 8 positives and -s_t elsewhere, so loss_t = V softplus(-s_t) and
+    dense_t = 8 s_t + loss_t, for s_t from 1 to 14 over the rows (dense / loss from 4 to
+    2e6). Every row stays within 2^-18 dense_t of the fp64 value (64 ulps; the kernels sum
+    V softplus terms and subtract the positives' sum); rows with dense / loss <= 1000 stay
+    within the 1e-3 relative tolerance (measured: 0.2 to 7 ulps of dense_t on both paths,
+    relative error 1.5e-4 at dense / loss = 1.7e3, 7e-4 at 1e4, 4e-2 at 4e5)."""
+    T, V = 64, D
+    s = np.round(np.linspace(1.0, 14.0, T) * 4) / 4            # multiples of 1/4: bf16-exact
+    pos = [sorted({(7 * t + 13 * j) % V for j in range(8)}) for t in range(T)]
+    A = np.empty((T, D), dtype=np.float32)
+    for t in range(T):
+        A[t] = -s[t]
+        A[t, pos[t]] = s[t]
+    E = np.eye(V, D, dtype=np.float32)
+    Ab, Eb = _bf16(A), _bf16(E)
+    row_ptr = np.zeros(T + 1, dtype=np.int32)
+    row_ptr[1:] = np.cumsum([len(p) for p in pos])
+    ids = np.array([v for p in pos for v in p], dtype=np.int32)
+    mask = np.ones(T, dtype=np.uint8)
+    _say(f"cancellation limit D={D}")
+    out = run_bce(B, _upload_bce(Ab, Eb, row_ptr, ids, mask), -1)
+    A64, E64 = _dec(Ab), _dec(Eb)
+    crow, cids, _ = canonical_csr(row_ptr, ids, mask, V, -1)
+    ref = H.bce_loss(A64, E64, crow, cids, mask)
+    dense = H.softplus(A64 @ E64.T).sum(axis=1)
+    for name in ("loss", "floss"):
+        got = out[name].cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref)
+        ratio = dense / ref
+        for t in (0, 8, 16, 24, 32, 40, 48, 56, 63):
+            _say(f"{name} s={s[t]:.2f} dense/loss={ratio[t]:.3g} rel err={err[t] / ref[t]:.3g} "
+                 f"err/ulp(dense)={err[t] / (2.0 ** -24 * dense[t]):.2f}")
+        assert np.all(err <= 2.0 ** -18 * dense), f"{name}: error beyond 64 ulps of the dense sum"
+        ok = ratio <= 1000
+        assert np.all(err[ok] <= 1e-3 * ref[ok]), f"{name}: relative tolerance missed at dense/loss <= 1000"
