@@ -15,19 +15,19 @@
 // (no recompute), and at D >= 512 each GEMM stays compute-bound with P in HBM.
 //
 // Kernel: 8 waves, 256 x (256 | 128) output tile, K stages of 32 in a 4-deep LDS ring.
-// bf16 operands arrive by global_load_lds_dwordx4 (lane-linear 1 KB blocks) from a
-// wave-uniform tile origin plus per-lane offsets fixed at kernel start; FP8 operands go
-// through registers and are widened to bf16 exactly on the way to LDS. An operand tile
-// is either k-contiguous ([rows][32 k], read with ds_read_b128) or k-major
-// ([32 k][cols], read transposed with ds_read_b64_tr_b16); both read patterns give lane
-// (l, h) the k values 16 kk + 8 h + 0..7, so any pair of modes composes.
+// Every operand arrives by global_load_lds_dwordx4 (lane-linear 1 KB blocks) from a
+// wave-uniform tile origin plus per-lane offsets fixed at kernel start. FP8 operands are
+// copied as raw bytes and widened to bf16 (exactly) after the fragment read. An operand
+// tile is either k-contiguous ([rows][32 k], read with ds_read_b128, or ds_read_b64 for
+// FP8) or k-major ([32 k][cols], read transposed with ds_read_b64_tr_b16, or
+// ds_read_b64_tr_b8 for FP8); every read pattern gives lane (l, h) the k values
+// 16 kk + 8 h + 0..7, so any pair of modes composes.
 //
 // Workgroups take output tiles in an order that keeps each XCD (blockIdx % 8) on a
 // contiguous run of tiles: 8 row tiles by all column tiles, so the 32 workgroups an XCD
 // runs at once share their A and B tiles through that XCD's L2.
 #include "launch.h"
 
-#define CL_GAS __attribute__((address_space(1)))
 
 namespace cl {
 
@@ -67,6 +67,17 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0xF70 | (N & 15) | ((N >> 4) << 14));
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Wait until at most `later` stages of NPER copies each are in flight (L: the most there
+// can be; more is waited down to L).
+template <int NPER, int L>
+__device__ __forceinline__ void wait_later(int later) {
+  if constexpr (L <= 0) {
+    wait_vm<0>();
+  } else {
+    if (later >= L) wait_vm<L * NPER>();
+    else wait_later<NPER, L - 1>(later);
+  }
+}
 
 __device__ __forceinline__ void block_sync() {
   asm volatile("" ::: "memory");
@@ -76,19 +87,28 @@ __device__ __forceinline__ void block_sync() {
   asm volatile("" ::: "memory");
 }
 
-// One stage of one operand: R rows (KC) or R columns (KR) by 32 k, bf16 in LDS.
-template <int NW, int R, bool KC>
+// One stage of one operand: R rows (KC) or R columns (KR) by 32 k, in LDS as bf16 (ESZ 2)
+// or as the raw bytes of an FP8 operand (ESZ 1).
+template <int NW, int R, bool KC, int ESZ = 2>
 struct Tile {
-  static constexpr int BYTES = 64 * R;
+  static constexpr int BYTES = 32 * ESZ * R;
   static constexpr int KB = BYTES / 1024;
   static constexpr int PER_WAVE = KB / NW;            // DMA blocks per wave
-  static constexpr int ROW = KC ? 64 : 2 * R;         // bytes per LDS row
+  static constexpr int ROW = KC ? 32 * ESZ : ESZ * R; // bytes per LDS row
   static constexpr int NCH = ROW / 16;
-  static constexpr int PIECES = BYTES / 16 / (64 * NW);  // staged pieces per thread
-  static_assert(PER_WAVE >= 1 && PIECES >= 1, "tile");
-  __device__ __forceinline__ static int phys(int lp, int r) {   // an involution in lp
-    if constexpr (KC) return lp ^ ((r >> 2) & 3);
-    else return lp ^ (swz_kr(r) & (NCH - 1));
+  static_assert(PER_WAVE >= 1 && KB % NW == 0, "tile");
+  // 16-byte piece lp of row r goes to piece phys(lp, r) of that row (an involution in lp).
+  // FP8 k-contiguous rows are 32 bytes: rows r and r + 8 swap their two pieces, so a
+  // fragment read (32 rows, one 8-byte half each) spreads over twice the banks. FP8 k-major
+  // rows: the 8 rows one transposed read touches take 8 different pieces (16 over the wave).
+  __device__ __forceinline__ static int phys(int lp, int r) {
+    if constexpr (ESZ == 1) {
+      if constexpr (KC) return lp ^ ((r >> 3) & 1);
+      else return lp ^ (r & 15 & (NCH - 1));
+    } else {
+      if constexpr (KC) return lp ^ ((r >> 2) & 3);
+      else return lp ^ (swz_kr(r) & (NCH - 1));
+    }
   }
 };
 
@@ -99,15 +119,17 @@ struct Tile {
 // last stages of some products) recomputes them with the k clamp as well.
 template <int NW, int R, bool KC, bool F8, bool Q8 = false>
 struct Loader {
-  using TL = Tile<NW, R, KC>;
-  static constexpr int N = F8 ? TL::PIECES : TL::PER_WAVE;
+  // F8: an FP8 operand copied as raw bytes (32 k per stage); Q8: FP8 x FP8 tiles (64 k per
+  // stage, the bf16 tile's byte geometry)
+  using TL = Tile<NW, R, KC, F8 ? 1 : 2>;
+  static constexpr int N = TL::PER_WAVE;
   static constexpr int ESZ = (F8 || Q8) ? 1 : 2;
-  static constexpr int EPP = Q8 ? 16 : 8;              // elements per 16-byte LDS piece
+  static constexpr int EPP = (F8 || Q8) ? 16 : 8;      // elements per 16-byte LDS piece
   static constexpr int BK = Q8 ? 64 : kBK;             // k elements per stage
   uint32_t off[N];
 
-  __device__ __forceinline__ static int byte_of(int j, int wv, int lane, int tid) {
-    return F8 ? 16 * (tid + 64 * NW * j) : (wv * TL::PER_WAVE + j) * 1024 + 16 * lane;
+  __device__ __forceinline__ static int byte_of(int j, int wv, int lane, int /*tid*/) {
+    return (wv * TL::PER_WAVE + j) * 1024 + 16 * lane;
   }
   __device__ __forceinline__ static void rc(int byte, int& r, int& c) {
     r = byte / TL::ROW;
@@ -133,7 +155,7 @@ struct Loader {
         const int64_t row = min(outer0 + r, op.rows_valid - 1) - outer0;
         off[j] = (uint32_t)(row * op.ld + c);
       } else {
-        const int64_t col = min(outer0 + c, op.cols_valid - 8) - outer0;
+        const int64_t col = min(outer0 + c, op.cols_valid - EPP) - outer0;
         off[j] = (uint32_t)(r * op.ld + col);
       }
     }
@@ -150,19 +172,26 @@ struct Loader {
     if (op.bt > 0) return false;
     return KC ? k0 + BK > op.cols_valid : k0 + BK > op.rows_valid;
   }
-  // element offset from origin(k0) with every index clamped
-  __device__ __forceinline__ static int64_t clamped(const GemmOperand& op, int64_t outer0, int64_t k0, int byte) {
+  // A k index at or below every clamped k index of the stage at k0: tail stages take their
+  // origin there, so that each lane's offset (a 32-bit unsigned register for the LDS copy)
+  // is non-negative even when the whole stage lies past the valid k range.
+  __device__ __forceinline__ static int64_t tail_k(const GemmOperand& op, int64_t k0) {
+    return KC ? min(k0, (int64_t)op.cols_valid - EPP) : min(k0, (int64_t)op.rows_valid - 1);
+  }
+  // element offset from origin(kb) of the stage at k0 with every index clamped (kb <= k0,
+  // kb at or below every clamped k index)
+  __device__ __forceinline__ static int64_t clamped(const GemmOperand& op, int64_t outer0, int64_t k0, int64_t kb, int byte) {
     int r, c;
     rc(byte, r, c);
     int64_t row, col;
     if constexpr (KC) {
       row = min(outer0 + r, op.rows_valid - 1);
       col = min(k0 + c, op.cols_valid - EPP);
-      return (row - outer0) * op.ld + (col - k0);
+      return (row - outer0) * op.ld + (col - kb);
     } else {
       row = min(k0 + r, op.rows_valid - 1);
-      col = min(outer0 + c, op.cols_valid - 8);
-      return (row - k0) * op.ld + (col - outer0);
+      col = min(outer0 + c, op.cols_valid - EPP);
+      return (row - kb) * op.ld + (col - outer0);
     }
   }
 };
@@ -175,69 +204,58 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
-// ASM: issue the copies as inline asm (lds_dma16), for kernels whose every global load is an
-// LDS copy; kernels that also stage an operand through registers keep the builtin, so that
-// the compiler's waits for those registers count the copies issued after them.
-template <int NW, int R, bool KC, bool Q8 = false, bool ASM = false>
-__device__ __forceinline__ void dma_stage(const Loader<NW, R, KC, false, Q8>& ld, const GemmOperand& op, int64_t outer0,
+// The copies are issued as inline asm (lds_dma16): every global load of a kernel's main loop
+// is an LDS copy, and the loop's own waits count them.
+template <int NW, int R, bool KC, bool F8, bool Q8>
+__device__ __forceinline__ void dma_stage(const Loader<NW, R, KC, F8, Q8>& ld, const GemmOperand& op, int64_t outer0,
                                           int64_t k0, uint32_t lds, int wv, int lane) {
-  using TL = Tile<NW, R, KC>;
-  using LD = Loader<NW, R, KC, false, Q8>;
+  using LD = Loader<NW, R, KC, F8, Q8>;
+  using TL = typename LD::TL;
   const char* org = LD::origin(op, outer0, k0);
   if (!LD::tail(op, k0)) {
 #pragma unroll
     for (int j = 0; j < TL::PER_WAVE; ++j) {
       const uint32_t dst = lds + (wv * TL::PER_WAVE + j) * 1024;
-      if constexpr (ASM) lds_dma16(org, (uint32_t)(LD::ESZ * ld.off[j]), dst);
-      else __builtin_amdgcn_global_load_lds((const CL_GAS void*)(org + LD::ESZ * (size_t)ld.off[j]),
-                                            (CL_LDS void*)(uintptr_t)dst, 16, 0, 0);
+      lds_dma16(org, (uint32_t)(LD::ESZ * ld.off[j]), dst);
     }
   } else {
     const int ln = opaque(lane);
+    const int64_t kt = LD::tail_k(op, k0);
+    const char* orgt = LD::origin(op, outer0, kt);
 #pragma unroll
     for (int j = 0; j < TL::PER_WAVE; ++j) {
-      const int kb = wv * TL::PER_WAVE + j;
-      const int64_t o = LD::clamped(op, outer0, k0, kb * 1024 + 16 * ln);
-      if constexpr (ASM) lds_dma16(org, (uint32_t)(LD::ESZ * o), lds + kb * 1024);
-      else __builtin_amdgcn_global_load_lds((const CL_GAS void*)(org + LD::ESZ * o), (CL_LDS void*)(uintptr_t)(lds + kb * 1024),
-                                            16, 0, 0);
+      const int blk = wv * TL::PER_WAVE + j;
+      const int64_t o = LD::clamped(op, outer0, k0, kt, blk * 1024 + 16 * ln);
+      lds_dma16(orgt, (uint32_t)(LD::ESZ * o), lds + blk * 1024);
     }
   }
 }
 
-template <int NW, int R, bool KC>
-struct Fp8Stage {
-  using TL = Tile<NW, R, KC>;
-  using LD = Loader<NW, R, KC, true>;
-  uint2 q[TL::PIECES];
-  __device__ __forceinline__ void load(const LD& ld, const GemmOperand& op, int64_t outer0, int64_t k0, int tid) {
-    const char* org = LD::origin(op, outer0, k0);
-    if (!LD::tail(op, k0)) {
-#pragma unroll
-      for (int i = 0; i < TL::PIECES; ++i) q[i] = *(const uint2*)(org + ld.off[i]);
-    } else {
-      const int t = opaque(tid);
-#pragma unroll
-      for (int i = 0; i < TL::PIECES; ++i)
-        q[i] = *(const uint2*)(org + LD::clamped(op, outer0, k0, 16 * (t + 64 * NW * i)));
-    }
-  }
-  __device__ __forceinline__ void store(uint32_t lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < TL::PIECES; ++i)
-      *(CL_LDS bf16x8*)(uintptr_t)(lds + 16 * (tid + 64 * NW * i)) = fp8x8_to_bf16x8(q[i]);
-  }
-};
-
 // MFMA operand fragments of a stage tile: lane (l32, h) gets index l32 of the 32-wide
 // block `blk` and k = 16 kk + 8 h + 0..7.
-template <int NW, int R, bool KC>
+// F8: the tile holds raw FP8 bytes, read 8 per lane and widened to bf16 (exact). A
+// k-contiguous row read is one ds_read_b64; a k-major tile is read with ds_read_b64_tr_b8:
+// in each 16-lane group g, lane i receives byte i mod 8 of the 8-byte reads of lanes
+// floor(i/8) + 2j, j = 0..7, so lane s of the group reads row k0 + 8 (g >> 1) + (s >> 1),
+// columns 16 (g & 1) + 8 (s & 1) + 0..7, and lane i gets column 16 (g & 1) + i of those
+// 8 rows in k order.
+template <int NW, int R, bool KC, bool F8 = false>
 struct Frag {
   uint32_t base0, base1;   // KC: row-read base; KR: transposed-read bases (k rows +0..3, +4..7)
   __device__ __forceinline__ void init(uint32_t blk0_off, int lane) {
-    using TL = Tile<NW, R, KC>;
+    using TL = Tile<NW, R, KC, F8 ? 1 : 2>;
     const int h = lane >> 5, l32 = lane & 31;
-    if constexpr (KC) {
+    if constexpr (F8) {
+      if constexpr (KC) {
+        const int r = l32;                       // + 32 blk leaves (r >> 3) & 1 unchanged
+        base0 = blk0_off + r * TL::ROW + 16 * ((r >> 3) & 1) + 8 * h;
+      } else {
+        const int g = (lane >> 4) & 3, sl = lane & 15;
+        const int kr = 8 * (g >> 1) + (sl >> 1);   // + 16 kk leaves kr & 15 unchanged
+        base0 = blk0_off + kr * TL::ROW + 16 * ((g & 1) ^ (kr & 15 & (TL::NCH - 1))) + 8 * (sl & 1);
+      }
+      base1 = 0;
+    } else if constexpr (KC) {
       const int r = l32;                         // + 32 blk: does not change (r >> 2) & 3
       const int sw = (r >> 2) & 3;
       base0 = blk0_off + r * TL::ROW + 16 * ((sw & 2) | (h ^ (sw & 1)));
@@ -253,8 +271,19 @@ struct Frag {
   }
   // blk: 32-wide block index within the tile's R; kk: 16-k half of the stage
   __device__ __forceinline__ bf16x8 read(uint32_t stage_off, int blk, int kk) const {
-    using TL = Tile<NW, R, KC>;
-    if constexpr (KC) {
+    using TL = Tile<NW, R, KC, F8 ? 1 : 2>;
+    if constexpr (F8) {
+      if constexpr (KC) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 q = *lds_ptr<u32x2>(((base0 ^ (uint32_t)(16 * kk)) + (uint32_t)(blk * 32 * TL::ROW)) + stage_off);
+        return fp8x8_to_bf16x8(uint2{q[0], q[1]});
+      } else {
+        typedef int i32x2 __attribute__((ext_vector_type(2)));
+        const uint32_t o = (base0 ^ (uint32_t)(32 * blk)) + stage_off + (uint32_t)(kk * 16 * TL::ROW);
+        const i32x2 q = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CL_LDS i32x2*)(uintptr_t)o);
+        return fp8x8_to_bf16x8(uint2{(uint32_t)q[0], (uint32_t)q[1]});
+      }
+    } else if constexpr (KC) {
       return *lds_ptr<bf16x8>(((base0 ^ (uint32_t)(32 * kk)) + (uint32_t)(blk * 32 * TL::ROW)) + stage_off);
     } else {
       const uint32_t o = stage_off + (uint32_t)(kk * 16 * TL::ROW);
@@ -369,15 +398,22 @@ template <int NW, int BN, bool AKC, bool BKC, bool AF8, bool BF8, int EPI, bool 
 __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
   static_assert(!Q8 || (AKC && BKC && !AF8 && !BF8), "fp8 x fp8 operands are k-contiguous DMA tiles");
   constexpr int BK = Q8 ? 64 : kBK;
-  constexpr int kThreads = Cfg<NW, BN>::THREADS, kNst = Cfg<NW, BN>::NST;
-  using TA = Tile<NW, kBM, AKC>;
-  using TB = Tile<NW, BN, BKC>;
+  constexpr int kThreads = Cfg<NW, BN>::THREADS;
+  using TA = Tile<NW, kBM, AKC, AF8 ? 1 : 2>;
+  using TB = Tile<NW, BN, BKC, BF8 ? 1 : 2>;
   constexpr int WM = WaveGrid<NW, BN>::WM, WN = WaveGrid<NW, BN>::WN;
   constexpr int TM = kBM / WM, TN = BN / WN;
   constexpr int MT = TM / 32, NTW = TN / 32;
   constexpr int STAGE = TA::BYTES + TB::BYTES;
-  constexpr int NPER = (AF8 ? TA::PIECES : TA::PER_WAVE) + (BF8 ? TB::PIECES : TB::PER_WAVE);
-  __shared__ __attribute__((aligned(1024))) char ring[kNst * STAGE];
+  constexpr int NPER = TA::PER_WAVE + TB::PER_WAVE;   // LDS copies per wave and stage
+  // The ring keeps the size of the bf16 tiles' ring when an operand is FP8 (the epilogues
+  // stage the P image and the dE tile through it). FP8 stages are smaller, but a deeper ring
+  // in the same bytes measured no faster on the 3M-item head: its products are bound by
+  // HBM bandwidth once the copies run ahead.
+  constexpr int kNst = Cfg<NW, BN>::NST;
+  constexpr int RING = kNst * (Tile<NW, kBM, AKC>::BYTES + Tile<NW, BN, BKC>::BYTES);
+  static_assert(kNst * STAGE <= RING && (kNst - 1) * NPER < 64, "ring");
+  __shared__ __attribute__((aligned(1024))) char ring[RING];
 
   int tm, tn, tz;
   if (!map_tile((int)((p.M + kBM - 1) / kBM), (int)((p.N + BN - 1) / BN),
@@ -398,8 +434,8 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
   la.init(p.a, m0, wv, lane, tid);
   lb.init(p.b, n0, wv, lane, tid);
 
-  Frag<NW, kBM, AKC> fa;
-  Frag<NW, BN, BKC> fb;
+  Frag<NW, kBM, AKC, AF8> fa;
+  Frag<NW, BN, BKC, BF8> fb;
   fa.init(ring0, lane);
   fb.init(ring0 + TA::BYTES, lane);
   const int ablk0 = (wm * TM) / 32, bblk0 = (wn * TN) / 32;
@@ -446,18 +482,14 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
   }
   auto stage_k = [&](int s) -> int64_t { return kz0 + (int64_t)(filt ? slist[s] : s) * BK; };
 
-  Fp8Stage<NW, kBM, AKC> sa;
-  Fp8Stage<NW, BN, BKC> sb;
-  // fp8 register loads are issued before the stage's DMAs, so waiting for them at the
-  // next step does not wait for those DMAs.
-  constexpr bool ALL_DMA = !AF8 && !BF8;
-  // with every copy invisible to the compiler's waits, none of its own loads may be left
-  // pending inside the main loop
-  if constexpr (ALL_DMA) wait_vm<0>();
+  // Every operand tile arrives by LDS copy, issued as inline asm so that the compiler's
+  // waits do not count the copies; none of its own loads may then be left pending inside
+  // the main loop.
+  wait_vm<0>();
 
   // dE/SGD epilogue geometry: each wave stages MG row tiles at a time through its share of
   // the ring as fp32 rows of stride RS; a lane then owns SPL segments of 16 adjacent d
-  constexpr int WREG = kNst * STAGE / NW;    // LDS bytes per wave
+  constexpr int WREG = RING / NW;            // LDS bytes per wave
   constexpr int RS = TN * 4 + 16;            // fp32 row stride: 16 B pad spreads the 16-lane reads
   constexpr int MG = (WREG / (32 * RS)) < MT ? (WREG / (32 * RS)) : MT;
   constexpr int SEGS = TN / 16;
@@ -487,15 +519,8 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
   auto issue = [&](int s) {
     const uint32_t so = ring0 + (uint32_t)((s % kNst) * STAGE);
     const int64_t k0 = stage_k(s);
-    if constexpr (AF8) sa.load(la, p.a, m0, k0, tid);
-    if constexpr (BF8) sb.load(lb, p.b, n0, k0, tid);
-    if constexpr (!AF8) dma_stage<NW, kBM, AKC, Q8, ALL_DMA>(la, p.a, m0, k0, so, wv, lane);
-    if constexpr (!BF8) dma_stage<NW, BN, BKC, Q8, ALL_DMA>(lb, p.b, n0, k0, so + TA::BYTES, wv, lane);
-  };
-  auto store_fp8 = [&](int s) {
-    const uint32_t so = ring0 + (uint32_t)((s % kNst) * STAGE);
-    if constexpr (AF8) sa.store(so, tid);
-    if constexpr (BF8) sb.store(so + TA::BYTES, tid);
+    dma_stage<NW, kBM, AKC, AF8, Q8>(la, p.a, m0, k0, so, wv, lane);
+    dma_stage<NW, BN, BKC, BF8, Q8>(lb, p.b, n0, k0, so + TA::BYTES, wv, lane);
   };
 
   if constexpr (Q8) {
@@ -556,17 +581,9 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
       for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = mfma32(av[mt], bv[nt], acc[mt][nt]);
   };
   if (nk_run > 0) {
-    for (int x = 0; x < kNst; ++x) {
-      if (x < nk_run) {
-        issue(x);
-        if (x < kNst - 1) store_fp8(x);      // the last prologue stage is stored at step 0
-      }
-    }
-    {
-      const int later = min(nk_run - 1, kNst - 1);   // stages after stage 0 in flight
-      if (later >= 3) wait_vm<3 * NPER>(); else if (later == 2) wait_vm<2 * NPER>();
-      else if (later == 1) wait_vm<NPER>(); else wait_vm<0>();
-    }
+    for (int x = 0; x < kNst; ++x)
+      if (x < nk_run) issue(x);
+    wait_later<NPER, kNst - 1>(min(nk_run - 1, kNst - 1));   // stages after stage 0 in flight
     wait_lgkm0();
     block_sync();
     read_half(0, 0, a0, b0);
@@ -575,11 +592,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
     read_half(s, 1, a1, b1);
     mma_half(a0, b0);
     if (s + 1 < nk_run) {
-      if constexpr (AF8 || BF8) {
-        if (s + kNst - 1 < nk_run) store_fp8(s + kNst - 1);   // loaded at step s - 1
-      }
-      const int later = min(nk_run - 2 - s, kNst - 2);        // stages after s + 1 in flight
-      if (later >= 2) wait_vm<2 * NPER>(); else if (later == 1) wait_vm<NPER>(); else wait_vm<0>();
+      wait_later<NPER, kNst - 2>(min(nk_run - 2 - s, kNst - 2));   // stages after s + 1 in flight
       wait_lgkm0();
       block_sync();                          // stage s retired, stage s + 1 landed
       if (s + kNst < nk_run) issue(s + kNst);
@@ -742,7 +755,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
       // contiguous run of the blocked layout (bt is a multiple of BN): copy it out in 16-byte
       // pieces, consecutive threads on consecutive bytes of a run.
       constexpr int IMG = 8 * BN * 64;
-      static_assert(IMG <= kNst * STAGE, "P image fits the ring");
+      static_assert(IMG <= RING, "P image fits the ring");
       block_sync();
       const int64_t pbs = (int64_t)p.p_bt * 32;
       // all BN rows of the tile lie in one row block of the layout (bt is a multiple of BN and
@@ -987,7 +1000,10 @@ hipError_t gemm_bn(const GemmParams& p, dim3 grid, hipStream_t st) {
       default: return hipErrorInvalidValue;
     }
   } else if (akc && !bkc && !af8 && bf8 && p.epi == GEMM_EPI_ACC) {    // K2, fp8 E
-    CL_G(true, false, false, true, GEMM_EPI_ACC);
+    // the raw FP8 tile of BN columns must split into whole 1 KB copies per wave (the
+    // planner never pairs an FP8 B tile of 128 columns with 8 waves)
+    if constexpr (BN * 32 / 1024 >= NW && (BN * 32 / 1024) % NW == 0) CL_G(true, false, false, true, GEMM_EPI_ACC);
+    else return hipErrorInvalidValue;
   } else if (!akc && bkc && af8 && !bf8 && p.epi == GEMM_EPI_ACC) {    // K2 as dA^T = E_c^T P^T, fp8 E
     CL_G(false, true, true, false, GEMM_EPI_ACC);
   } else if (!akc && !bkc && !af8 && !bf8) {   // K3: both operands k-major
