@@ -43,8 +43,9 @@
  *    runs a chunked path that keeps one vocabulary chunk's bf16 gradient tile
  *    (T x Vc) in the workspace: Vc is at most ceil(V / 8) items rounded up to 256, so the
  *    tile holds at most about an eighth of the T x V logits, and the tile is at most
- *    2 GiB. The environment variable CUTLOSS_MAX_CHUNK_ITEMS caps Vc further (read when a
- *    call or size query plans the work, so set it before both).
+ *    2 GiB. A forward stores no tile and runs the vocabulary as one chunk. The environment
+ *    variable CUTLOSS_MAX_CHUNK_ITEMS caps Vc further (read when a call or size query plans
+ *    the work, so set it before both).
  */
 #ifndef CUTLOSS_H
 #define CUTLOSS_H
@@ -121,8 +122,8 @@ typedef struct {
 /*
  * Workspace size in bytes for `op` on problem `p` (0 if the problem is invalid).
  * On the fused-sweep path it grows with T, D, nnz and the vocabulary tile count, never
- * with T*V; the chunked path adds one chunk's gradient tile (at most T * ceil(V/8) bf16
- * values, at most 2 GiB) and the chunk's transposed E.
+ * with T*V; the chunked path's backward adds one chunk's gradient tile (at most
+ * T * ceil(V/8) bf16 values, at most 2 GiB) and the chunk's transposed E.
  */
 size_t cutloss_bce_workspace_size(const cutloss_bce_problem* p, int32_t op);
 size_t cutloss_ce_workspace_size(const cutloss_ce_problem* p, int32_t op);

@@ -204,7 +204,8 @@ constexpr int64_t kChunkPBytes = 2ll << 30;     // P buffer budget
 // buffer, ai.info summary, Main Findings)
 constexpr int64_t kMinChunks = 8;
 
-ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap, bool q8 = false, bool e_fp8 = false) {
+ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap, bool q8 = false, bool e_fp8 = false,
+                          bool no_tile = false) {
   ChunkPlan c{};
   c.T = T; c.D = D; c.V = V; c.cap = cap; c.q8 = q8;
   // a 256-row tile over at most 128 rows would waste half the dA product's MFMAs
@@ -214,6 +215,8 @@ ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap, bool q8 
   c.Tp = round_up(T > 0 ? T : 1, c.bt);
   int64_t vc = kChunkPBytes / (c.Tp * 2) / bm * bm;
   vc = std::min(vc, round_up(ceil_div(V, kMinChunks), bm));
+  // a call that stores no gradient tile (a forward) runs the whole vocabulary as one chunk
+  if (no_tile) vc = round_up(V > 0 ? V : 1, bm);
   // CUTLOSS_MAX_CHUNK_ITEMS caps the chunk (rounded down to the item tile): a tuning knob,
   // and the way tests exercise several chunks on small problems
   if (const char* env = std::getenv("CUTLOSS_MAX_CHUNK_ITEMS")) {
@@ -591,8 +594,8 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
 cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss, float* loss, void* dA, void* dE,
                                int dE_mode, float lr, void* ws, size_t ws_bytes, hipStream_t st, int32_t* counts,
                                int sr, uint64_t sr_seed, bool fp8_logits) {
-  const ChunkPlan pl = make_chunk_plan(p->T, p->D, p->V, p->nnz, fp8_logits, p->e_dtype == CUTLOSS_FP8_E4M3);
   const bool grad = dA != nullptr || dE_mode != 0;
+  const ChunkPlan pl = make_chunk_plan(p->T, p->D, p->V, p->nnz, fp8_logits, p->e_dtype == CUTLOSS_FP8_E4M3, !grad);
   const int e_fp8 = p->e_dtype == CUTLOSS_FP8_E4M3;
   const Ws2 w = carve_chunked(ws, pl, grad, dA != nullptr, dE_mode != 0, counts != nullptr, true, !e_fp8);
   CL_TRY(check_ws(ws, ws_bytes, w.bytes));
@@ -659,8 +662,8 @@ cutloss_status ce_run_chunked(const cutloss_ce_problem* p, const float* lse_in, 
                               float* lse, void* dA, void* dE, void* ws, size_t ws_bytes, hipStream_t st,
                               float filter_eps) {
   const bool fwd = loss != nullptr;
-  const ChunkPlan pl = make_chunk_plan(p->T, p->D, p->V, p->T, false, p->e_dtype == CUTLOSS_FP8_E4M3);
   const bool grad = !fwd && (dA != nullptr || dE != nullptr);
+  const ChunkPlan pl = make_chunk_plan(p->T, p->D, p->V, p->T, false, p->e_dtype == CUTLOSS_FP8_E4M3, !grad);
   const int e_fp8 = p->e_dtype == CUTLOSS_FP8_E4M3;
   const Ws2 w = carve_chunked(ws, pl, grad, !fwd && dA != nullptr, !fwd && dE != nullptr, fwd, false, !e_fp8);
   CL_TRY(check_ws(ws, ws_bytes, w.bytes));
@@ -768,7 +771,7 @@ size_t cutloss_bce_workspace_size(const cutloss_bce_problem* p, int32_t op) {
     return b;
   }
   if (use_chunked(p->D, p->e_dtype == CUTLOSS_FP8_E4M3)) {
-    const ChunkPlan cp = make_chunk_plan(p->T, p->D, p->V, p->nnz, false, p->e_dtype == CUTLOSS_FP8_E4M3);
+    const ChunkPlan cp = make_chunk_plan(p->T, p->D, p->V, p->nnz, false, p->e_dtype == CUTLOSS_FP8_E4M3, !bwd);
     return carve_chunked(nullptr, cp, bwd, bwd, bwd, metrics, true, p->e_dtype != CUTLOSS_FP8_E4M3).bytes;
   }
   const Plan pl = make_plan(p->T, p->D, p->V, p->nnz, p->e_dtype == CUTLOSS_FP8_E4M3);
@@ -779,7 +782,7 @@ size_t cutloss_ce_workspace_size(const cutloss_ce_problem* p, int32_t op) {
   if (check_ce(p) != CUTLOSS_OK) return 0;
   const bool bwd = op != CUTLOSS_OP_FWD;
   if (use_chunked(p->D, p->e_dtype == CUTLOSS_FP8_E4M3)) {
-    const ChunkPlan cp = make_chunk_plan(p->T, p->D, p->V, p->T, false, p->e_dtype == CUTLOSS_FP8_E4M3);
+    const ChunkPlan cp = make_chunk_plan(p->T, p->D, p->V, p->T, false, p->e_dtype == CUTLOSS_FP8_E4M3, !bwd);
     return carve_chunked(nullptr, cp, bwd, bwd, bwd, !bwd, false, p->e_dtype != CUTLOSS_FP8_E4M3).bytes;
   }
   const Plan pl = make_plan(p->T, p->D, p->V, p->T, p->e_dtype == CUTLOSS_FP8_E4M3);
