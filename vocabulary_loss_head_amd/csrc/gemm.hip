@@ -495,11 +495,11 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
   constexpr int SEGS = TN / 16;
   constexpr int SPL = 32 * MG * SEGS / 64;    // segments per lane per group
   constexpr int NG = MT / MG > 0 ? MT / MG : 1;
-  // FP8 SGD (round to nearest): the E bytes of all the lane's segments are loaded here, before
+  // FP8 SGD (either rounding): the E bytes of all the lane's segments are loaded here, before
   // the first stage's copies, so their HBM latency overlaps the pipeline's start and the
   // epilogue never waits for E
   constexpr bool PRE = EPI == GEMM_EPI_SGD;
-  const bool pre = PRE && p.e_fp8 && !p.sr;
+  const bool pre = PRE && p.e_fp8;
   uint4 epre[PRE ? SPL * NG : 1];
   if constexpr (PRE) {
     if (pre) {
@@ -895,7 +895,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm(const GemmParams p) {
           auto h16 = [&](int j) -> uint32_t { return (j & 1) ? (hw[j >> 1] >> 16) : (hw[j >> 1] & 0xFFFFu); };
           if (p.e_fp8) {
             uint4* ep = (uint4*)((uint8_t*)p.E_inplace + v * p.D + d0);
-            const uint4 e = *ep;
+            const uint4 e = pre ? epre[PRE ? (g0 / MG) * SPL + si : 0] : *ep;
             const uint32_t w[4] = {e.x, e.y, e.z, e.w};
             uint32_t o[4];
 #pragma unroll
