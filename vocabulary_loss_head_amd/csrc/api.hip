@@ -228,11 +228,16 @@ ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap, bool q8 
   c.Vc = vc;
   c.n_chunks = ceil_div(V, vc);
   c.n_splits = ceil_div(V, bm);   // one loss partial per item tile (its wave rows combined)
-  // dA product: (row tiles) x (D tiles) x slices, about 1024 workgroups
+  // dA product: (row tiles) x (D tiles) x split-K slices. Every slice's partial [T][D] is
+  // read and rewritten once per chunk, so fewer, longer slices move fewer bytes; heads up to
+  // D = 1024 take about 512 workgroups, wider (compute-bound) ones about 1024. The
+  // transposed product (3 tiles at D = 768) rounds down, so that its one-per-CU workgroups
+  // fill whole waves (510 on 256 CUs; 1026 left a fifth wave of 2).
   const int64_t tiles = c.trans_dA
       ? ceil_div(D, bm) * ceil_div(T > 0 ? T : 1, cl::gemm_tile_n_of(cl::GEMM_EPI_ACC, D, T > 0 ? T : 1, D))
       : ceil_div(T > 0 ? T : 1, bm) * ceil_div(D, cl::gemm_tile_n_of(cl::GEMM_EPI_ACC, T, D, D));
-  int64_t sk = ceil_div(1024, tiles);
+  const int64_t blocks = D <= 1024 ? 512 : 1024;
+  int64_t sk = c.trans_dA ? blocks / tiles : ceil_div(blocks, tiles);
   if (sk > vc / 32) sk = vc / 32;
   if (sk < 1) sk = 1;
   c.kps = round_up(ceil_div(vc, sk), 32);
