@@ -1123,6 +1123,9 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t st) {
   if ((gm - 1) * kBM >= a_outer || (gn - 1) * bn >= b_outer || p.a.rows_valid < 1 || p.b.rows_valid < 1 ||
       p.a.cols_valid < 8 || p.b.cols_valid < 8)
     return hipErrorInvalidValue;
+  // a 16-byte piece of an FP8 operand holds 16 elements: at least one whole piece per row
+  // (the loaders clamp columns to cols_valid - 16)
+  if ((p.a.fp8 && p.a.cols_valid < 16) || (p.b.fp8 && p.b.cols_valid < 16)) return hipErrorInvalidValue;
   // blocked operands (bf16 only): bt a multiple of 32 (a k stage of 32 stored rows stays in
   // one row block), the whole k range valid, and every column of a tile stored
   for (const GemmOperand* op : {&p.a, &p.b}) {
