@@ -385,7 +385,7 @@ def config_record(name, calls=None, with_cpu=True):
     inp, h = _load(name)
     w = h.w
     T, D, V = w.T, w.D, w.V
-    n = calls or CALLS[name]
+    n = calls or CALLS.get(name, 500)
     n_valid = int(inp["mask"].sum()) if "mask" in inp else int((inp["target"] != -100).sum())
     torch.cuda.reset_peak_memory_stats()
     base = torch.cuda.memory_allocated()
@@ -450,7 +450,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="seqrec_bce", choices=ALL)
+    ap.add_argument("--workload", default="seqrec_bce", choices=ALL + ["cutbce_minibench"])
     ap.add_argument("--all", action="store_true", help="one report line per configuration")
     ap.add_argument("--only", action="store_true", help="with --all: only the --workload configuration")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -4,9 +4,10 @@
 // gradient recomputed per tile) and the Cut Your Losses article (online logsumexp, softmax
 // gradient), arranged for measured CDNA4 limits:
 //  * each wave holds MT 32-row tiles of the stationary matrix in VGPRs (MT = 2 for
-//    D <= 128, 1 for D = 256, where the 128 gradient accumulators and 64 stationary
-//    registers of a tile fill the 256 VGPRs of two waves per SIMD), so every LDS read of a
-//    streamed chunk feeds MT MFMAs in the logit product and in the gradient product;
+//    D = 64; 1 for D = 128 and 256, where the 128 gradient accumulators and 64 stationary
+//    registers of a D = 256 tile fill the 256 VGPRs of two waves per SIMD), so every LDS
+//    read of a streamed chunk feeds MT MFMAs in the logit product and in the gradient
+//    product;
 //  * the logit and gradient products keep several LDS operand reads in flight ahead of
 //    their MFMAs; the sigmoid/exp epilogue of one wave runs while the other wave of the
 //    SIMD issues matrix work;
@@ -53,11 +54,14 @@ constexpr int kRing = 4;         // LDS buffers
 constexpr float kNegInf = -__builtin_inff();
 
 // For each D: MT stationary 32-row tiles per wave, NW waves per workgroup and WPE
-// workgroups per CU (two waves per SIMD in every case). With NW = 8 the two waves of a
+// workgroups per CU (two waves per SIMD in every case). At D = 128, MT = 2 would need one
+// wave per SIMD (the accumulators of two tiles exceed 256 registers); the epilogue then
+// has no second wave to run beside, and the sweeps take 24% longer than with MT = 1 and
+// two waves per SIMD (T = 16384, V = 100000). With NW = 8 the two waves of a
 // SIMD belong to one workgroup and run out of phase (see sweep_loop).
 template <int D> struct Tiling;
 template <> struct Tiling<64> { static constexpr int MT = 2, NW = 4, WPE = 2; };
-template <> struct Tiling<128> { static constexpr int MT = 2, NW = 4, WPE = 1; };
+template <> struct Tiling<128> { static constexpr int MT = 1, NW = 8, WPE = 1; };
 template <> struct Tiling<256> { static constexpr int MT = 1, NW = 8, WPE = 1; };
 
 template <int D>

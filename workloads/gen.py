@@ -81,6 +81,11 @@ WORKLOADS = {
     # extreme multi-label head, fp8 weights, fused SGD
     "xmc_sgd": Workload("xmc_sgd", "bce", 128, 768, 3000000, "fp8", None, 0.05,
                         "poisson_distinct", L=5, pad_id=-1, lr=0.01, seed=5),
+    # the Cut BCE mini-benchmark shape (§IV-A): B = N = 128, V = 100k, D = 128, L = 8,
+    # A, E ~ N(0, I), targets uniform in [0, V); a point of comparison with the page's
+    # timing, not one of the five configurations
+    "cutbce_minibench": Workload("cutbce_minibench", "bce", 16384, 128, 100000, "bf16", 1.0, 1.0,
+                                 "uniform_any", L=8, pad_id=-1, seed=6),
 }
 
 
