@@ -112,32 +112,51 @@ __global__ void k_row_compact_ce(int64_t T, const int64_t* __restrict__ target, 
 
 // Single-workgroup exclusive scan: out[i] = sum in[0..i), out[n] = total.
 // If n_dev != NULL the length is min(n, *n_dev) and entries past it read as 0.
-// Tiles of 4096 entries, 4 per thread: each wave scans its 64 thread sums with shuffles,
-// the 16 wave totals meet in LDS, and a running carry links the tiles (two barriers per
-// tile). Integer sums, so the result does not depend on the order.
+// Tiles of 16384 entries, 16 consecutive ones per thread (four 16-byte loads and stores
+// where the buffers allow): each thread sums its entries, each wave scans its 64 thread
+// sums with shuffles, the 16 wave totals meet in LDS, and a running carry links the tiles
+// (two barriers per tile). The next tile is loaded while the current one is scanned, so
+// a tile costs about one memory latency. Integer sums, so the result does not depend on
+// the order.
+constexpr int kScanPer = 16;
+constexpr int64_t kScanTile = 1024 * kScanPer;
+
+__device__ __forceinline__ void scan_load(const int32_t* __restrict__ in, int64_t i0, int64_t m, bool vec,
+                                          int (&v)[kScanPer]) {
+  if (vec && i0 + kScanPer <= m) {
+    const int4* p = (const int4*)(in + i0);
+#pragma unroll
+    for (int q = 0; q < kScanPer / 4; ++q) {
+      const int4 x = p[q];
+      v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) v[j] = (i0 + j < m) ? in[i0 + j] : 0;
+  }
+}
+
 __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ in, int64_t n, const int32_t* n_dev,
                                                int32_t* __restrict__ out, int32_t* total_out) {
   __shared__ int32_t wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int64_t m = n;
   if (n_dev != nullptr) m = min((int64_t)*n_dev, n);
+  // 16-byte accesses need 16-byte aligned buffers (entry offsets are multiples of 16)
+  const bool vin = ((uintptr_t)in & 15) == 0, vout = ((uintptr_t)out & 15) == 0;
   int32_t carry = 0;                      // the same value in every thread
-  // the next tile's entries are loaded while the current one is scanned
-  int vn[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) vn[j] = ((int64_t)tid * 4 + j < m) ? in[(int64_t)tid * 4 + j] : 0;
-  for (int64_t base = 0; base < n; base += 4096) {
-    int v[4];
-    const int64_t i0 = base + (int64_t)tid * 4;
+  int vn[kScanPer];
+  scan_load(in, (int64_t)tid * kScanPer, m, vin, vn);
+  for (int64_t base = 0; base < n; base += kScanTile) {
+    const int64_t i0 = base + (int64_t)tid * kScanPer;
+    int v[kScanPer];
     int local = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kScanPer; ++j) {
       v[j] = vn[j];
       local += v[j];
     }
-    const int64_t i1 = i0 + 4096;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) vn[j] = (i1 + j < m) ? in[i1 + j] : 0;
+    if (base + kScanTile < n) scan_load(in, i0 + kScanTile, m, vin, vn);
     int x = local;                        // inclusive scan over the wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -154,10 +173,20 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ in, i
       tot += t;
     }
     int run = carry + wpre + x - local;
+    int r[kScanPer];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (i0 + j < n) out[i0 + j] = run;
+    for (int j = 0; j < kScanPer; ++j) {
+      r[j] = run;
       run += v[j];
+    }
+    if (vout && i0 + kScanPer <= n) {
+      int4* q = (int4*)(out + i0);
+#pragma unroll
+      for (int k = 0; k < kScanPer / 4; ++k) q[k] = make_int4(r[4 * k], r[4 * k + 1], r[4 * k + 2], r[4 * k + 3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kScanPer; ++j)
+        if (i0 + j < n) out[i0 + j] = r[j];
     }
     carry += tot;
     __syncthreads();                      // wsum is rewritten by the next tile
