@@ -65,14 +65,22 @@ __device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint3
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 // 8 OCP E4M3FN bytes -> 8 bf16 (exact: every E4M3 value is a bf16 value).
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint2 q) {
-  f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, false);
-  f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, true);
-  f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, false);
-  f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, true);
-  bf16x8 r = {(__bf16)a[0], (__bf16)a[1], (__bf16)b[0], (__bf16)b[1],
-              (__bf16)c[0], (__bf16)c[1], (__bf16)d[0], (__bf16)d[1]};
+// Two E4M3FN values (bytes 0-1, or 2-3 with HI, of w) to a bf16 pair in one instruction,
+// exactly (every E4M3FN value is a bf16 value; scale 1). Inline asm: the compiler's builtin
+// for this instruction treats its result as 16 bits wide and drops the second element.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  uint32_t r;
+  if constexpr (HI) asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0 op_sel:[1,0,0]" : "=v"(r) : "v"(w));
+  else asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0" : "=v"(r) : "v"(w));
   return r;
+}
+
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint2 q) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 r = {fp8x2_to_bf16x2<false>(q.x), fp8x2_to_bf16x2<true>(q.x), fp8x2_to_bf16x2<false>(q.y),
+                   fp8x2_to_bf16x2<true>(q.y)};
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 __device__ __forceinline__ float fp8_to_f32(uint32_t byte) {
