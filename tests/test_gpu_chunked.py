@@ -125,6 +125,14 @@ def test_sgd_fp8_chunked_ragged(B):
     _sgd_case(B, 130, 192, 1537, 32)
 
 
+@pytest.mark.parametrize("T,D,V", [(1, 128, 33), (128, 1024, 700), (97, 896, 1000)])
+def test_sgd_fp8_whole_rows(B, T, D, V):
+    """The nearest-even FP8 SGD of heads of at most 128 rows updates whole E rows: one row,
+    a 32-item block that ends a row past the vocabulary, eight and seven 128-column slices."""
+    _say(f"fp8 SGD whole rows T={T} D={D} V={V}")
+    _sgd_case(B, T, D, V, 40 + T)
+
+
 @pytest.mark.parametrize("T,D,V", [(70, 384, 3001), (33, 2304, 700), (257, 512, 1300)])
 def test_ce_chunked(B, T, D, V):
     _say(f"chunked ce T={T} D={D} V={V}")

@@ -266,6 +266,7 @@ struct Ws2 {
   uint16_t* Et;       // the chunk's bf16 E transposed, [D][Vc] (the dA product's k-contiguous operand)
   uint8_t* A8;        // FP8 logits: E4M3FN copy of A [T][D]
   uint16_t* Aw;       // BCE dE product: the rows of A weighted by w, bf16 [T][D]
+  uint16_t* AwT;      // the same transposed, [D][128] bf16 (FP8 SGD of heads of at most 128 rows)
   size_t bytes;
 };
 
@@ -313,6 +314,7 @@ Ws2 carve_chunked(void* base, const ChunkPlan& pl, bool need_P, bool need_dA, bo
   w.A8 = pl.q8 ? c.take<uint8_t>((size_t)T * pl.D) : nullptr;
   w.imap = need_Su ? c.take<int32_t>((size_t)pl.V) : nullptr;
   w.Aw = need_Su ? c.take<uint16_t>((size_t)T * pl.D) : nullptr;
+  w.AwT = need_Su && cl::sgd_rows_supported(pl.Tp, pl.D) ? c.take<uint16_t>((size_t)pl.D * pl.Tp) : nullptr;
   w.bytes = c.off;
   return w;
 }
@@ -518,6 +520,7 @@ struct ChunkJob {
   uint16_t* Et;          // bf16 E: workspace for the transposed chunk
   const uint8_t* A8;     // FP8 logits: the activations' E4M3FN copy
   const void* A_dE;      // the dE product's activations operand (NULL: A)
+  const uint16_t* AwT;   // non-NULL: the SGD product runs as whole-row updates (sgd_rows.hip)
   int k3_epi;            // -1: none, GEMM_EPI_DE or GEMM_EPI_SGD
   const int32_t* uitems; const int32_t* counts; const float* S_u; const int32_t* imap;
   void* dE; float lr;
@@ -577,7 +580,13 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
       }
       CL_HIP(cl::launch_gemm(g, st), "chunk dA");
     }
-    if (j.k3_epi >= 0) {
+    if (j.k3_epi == cl::GEMM_EPI_SGD && j.AwT != nullptr) {
+      Phase ph(CUTLOSS_PHASE_CHUNK_DE, st);
+      cl::SgdRowsParams s{};
+      s.V = pl.V; s.v0 = v0; s.nblk = ceil_div(vlen, 32); s.D = (int)pl.D;
+      s.P = j.P; s.AwT = j.AwT; s.S_u = j.S_u; s.imap = j.imap; s.E = (uint8_t*)j.E; s.lr = j.lr;
+      CL_HIP(cl::launch_sgd_rows(s, st), "chunk SGD rows");
+    } else if (j.k3_epi >= 0) {
       Phase ph(CUTLOSS_PHASE_CHUNK_DE, st);
       cl::GemmParams g{};
       g.a = operand(j.P, 0, pl.Tp, mc, 0, 0, (int)pl.bt, pl.Vc / 32);
@@ -604,6 +613,8 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
   const int e_fp8 = p->e_dtype == CUTLOSS_FP8_E4M3;
   const Ws2 w = carve_chunked(ws, pl, grad, dA != nullptr, dE_mode != 0, counts != nullptr, true, !e_fp8);
   CL_TRY(check_ws(ws, ws_bytes, w.bytes));
+  // FP8 SGD with nearest-even rounding over at most 128 rows: whole-row updates
+  const bool sgd_rows = dE_mode == 2 && e_fp8 && sr == 0 && w.AwT != nullptr;
   {
     Phase ph(CUTLOSS_PHASE_TARGETS, st);
     CL_HIP(cl::launch_zero_u64(w.err, 4, st), "zero counters");
@@ -633,12 +644,16 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
       CL_HIP(cl::launch_item_sums(p->D, pl.cap, p->A, w.w, w.tw.csc_rows, w.tw.useg, w.tw.counts, w.S_u, w.S_part, st),
              "item sums");
       CL_HIP(cl::launch_item_map(w.tw, p->V, pl.cap, w.imap, st), "item map");
-      CL_HIP(cl::launch_scale_rows(p->A, w.w, p->T, p->D, w.Aw, st), "weighted activations");
+      if (sgd_rows)
+        CL_HIP(cl::launch_weighted_transpose(p->A, w.w, p->T, p->D, w.AwT, st), "weighted activations");
+      else
+        CL_HIP(cl::launch_scale_rows(p->A, w.w, p->T, p->D, w.Aw, st), "weighted activations");
     }
   }
   ChunkJob j{};
   j.pl = &pl; j.A = p->A; j.E = p->E; j.e_fp8 = e_fp8;
   j.A_dE = dE_mode != 0 ? w.Aw : nullptr;
+  j.AwT = sgd_rows ? w.AwT : nullptr;
   j.k1_epi = grad ? cl::GEMM_EPI_BCE_P : (counts ? cl::GEMM_EPI_BCE_METRICS : cl::GEMM_EPI_BCE_LOSS);
   j.w = w.w; j.P = w.P; j.part_a = w.part_a; j.part_b = w.part_b; j.part_dA = w.part_dA; j.Et = w.Et;
   j.A8 = w.A8;

@@ -75,6 +75,27 @@ hipError_t launch_transpose_chunk(const uint16_t* E, int64_t vlen, int64_t mc, i
 int gemm_tile_m();                     // 256
 int gemm_tile_n_of(int epi, int64_t M, int64_t N, int64_t D);   // 128 or 256 for that product
 
+// ----------------------------------------------------------------------------------
+// FP8 SGD product for heads of at most 128 rows (sgd_rows.hip): E <- E4M3(E - lr (P^T A_w
+// - S)) with nearest-even rounding, whole E rows of 32 items per workgroup.
+// ----------------------------------------------------------------------------------
+struct SgdRowsParams {
+  int64_t V;             // items; rows at or past V are neither read for real nor written
+  int64_t v0;            // first item of the chunk
+  int64_t nblk;          // 32-item blocks of the chunk (the grid)
+  int D;                 // a multiple of 128, at most 1024
+  const uint16_t* P;     // the chunk's gradient tile in blocks of 128 rows x 32 items (bt = 128)
+  const uint16_t* AwT;   // [D][128] bf16: bf16(w_t A[t][d]) for t < T, 0 past T
+  const float* S_u;      // [unique items][D] positive-row sums
+  const int32_t* imap;   // [V] item -> unique-item index, -1 for none
+  uint8_t* E;            // [V][D] E4M3FN, updated in place
+  float lr;
+};
+bool sgd_rows_supported(int64_t Tp, int64_t D);   // Tp: rows of the gradient tile (128)
+hipError_t launch_weighted_transpose(const void* A, const float* w, int64_t T, int64_t D, uint16_t* AwT,
+                                     hipStream_t st);
+hipError_t launch_sgd_rows(const SgdRowsParams& p, hipStream_t st);
+
 struct FinalizeParams {
   int64_t T, D, V;
   const void* A; const void* E; int e_fp8;
