@@ -521,6 +521,7 @@ struct ChunkJob {
   const uint8_t* A8;     // FP8 logits: the activations' E4M3FN copy
   const void* A_dE;      // the dE product's activations operand (NULL: A)
   const uint16_t* AwT;   // non-NULL: the SGD product runs as whole-row updates (sgd_rows.hip)
+  bool rows_logits;      // the BCE logits product streams 32-item blocks (logits_rows.hip)
   int k3_epi;            // -1: none, GEMM_EPI_DE or GEMM_EPI_SGD
   const int32_t* uitems; const int32_t* counts; const float* S_u; const int32_t* imap;
   void* dE; float lr;
@@ -537,7 +538,15 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
     const int64_t vlen = std::min(pl.Vc, pl.V - v0);
     const int64_t mc = round_up(vlen, bm);
     const void* Ec = (const char*)j.E + v0 * pl.D * esz;
-    {
+    if (j.rows_logits) {
+      Phase ph(CUTLOSS_PHASE_CHUNK_LOGITS, st);
+      cl::LogitsRowsParams r{};
+      r.V = pl.V; r.T = pl.T; r.v0 = v0; r.nblk = mc / 32; r.nslots = mc / bm; r.part_base = v0 / bm;
+      r.D = (int)pl.D; r.E = (const uint8_t*)Ec - v0 * pl.D; r.A = (const uint16_t*)j.A;
+      r.P = j.k1_epi == cl::GEMM_EPI_BCE_P ? j.P : nullptr; r.part_a = j.part_a;
+      r.part_b = j.k1_epi == cl::GEMM_EPI_BCE_METRICS ? j.part_b : nullptr;
+      CL_HIP(cl::launch_logits_rows(r, st), "chunk logits rows");
+    } else {
       Phase ph(CUTLOSS_PHASE_CHUNK_LOGITS, st);
       cl::GemmParams g{};
       g.a = operand(Ec, pl.D, vlen, pl.D, 1, j.e_fp8);
@@ -655,6 +664,9 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
   j.A_dE = dE_mode != 0 ? w.Aw : nullptr;
   j.AwT = sgd_rows ? w.AwT : nullptr;
   j.k1_epi = grad ? cl::GEMM_EPI_BCE_P : (counts ? cl::GEMM_EPI_BCE_METRICS : cl::GEMM_EPI_BCE_LOSS);
+  // FP8 E over at most 128 rows (BCE loss, with P or with the metrics' counts): the
+  // streaming logits product
+  j.rows_logits = e_fp8 && !pl.q8 && cl::logits_rows_supported(pl.Tp, p->D);
   j.w = w.w; j.P = w.P; j.part_a = w.part_a; j.part_b = w.part_b; j.part_dA = w.part_dA; j.Et = w.Et;
   j.A8 = w.A8;
   j.k3_epi = dE_mode == 0 ? -1 : (dE_mode == 1 ? cl::GEMM_EPI_DE : cl::GEMM_EPI_SGD);

@@ -92,6 +92,26 @@ struct SgdRowsParams {
   float lr;
 };
 bool sgd_rows_supported(int64_t Tp, int64_t D);   // Tp: rows of the gradient tile (128)
+
+// ----------------------------------------------------------------------------------
+// BCE logits product for FP8 E and heads of at most 128 rows (logits_rows.hip): loss
+// partials and (P != NULL) the unweighted sigmoid tile, streaming 32-item blocks of E.
+// ----------------------------------------------------------------------------------
+struct LogitsRowsParams {
+  int64_t V, T;          // items, rows (1 .. 128)
+  int64_t v0;            // first item of the chunk
+  int64_t nblk;          // 32-item blocks of the chunk's P region: 8 * nslots
+  int64_t nslots;        // the chunk's loss slots: its 256-item tiles
+  int64_t part_base;     // the chunk's first slot (v0 / 256)
+  int D;                 // a multiple of 128, at most 768
+  const uint8_t* E;      // [V][D] E4M3FN
+  const uint16_t* A;     // [T][D] bf16
+  uint16_t* P;           // the chunk's gradient tile in 128 x 32 blocks, or NULL
+  float* part_a;         // [slots][T] softplus partials
+  float* part_b;         // [slots][T] counts of positive logits (Cut Metrics forward), or NULL
+};
+bool logits_rows_supported(int64_t Tp, int64_t D);
+hipError_t launch_logits_rows(const LogitsRowsParams& p, hipStream_t st);
 hipError_t launch_weighted_transpose(const void* A, const float* w, int64_t T, int64_t D, uint16_t* AwT,
                                      hipStream_t st);
 hipError_t launch_sgd_rows(const SgdRowsParams& p, hipStream_t st);

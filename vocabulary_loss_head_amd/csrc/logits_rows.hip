@@ -1,0 +1,234 @@
+// Logits product of the chunked path for FP8 E and heads of at most 128 rows (the XMC head:
+// T = 128, D = 768, V = 3M): per vocabulary chunk, every row's BCE softplus partial and, for a
+// backward, the unweighted sigmoid tile P in its blocked layout, or, for the Cut Metrics
+// forward, the row's count of positive logits (Cut Binary Cross Entropy §III-A/B: the dense
+// softplus term, the gradient recomputed per tile; §III-D: the metrics' dense counts; ELMO,
+// ai.info summary: FP8 E4M3 label weights, widened here exactly to bf16 for the MFMA).
+//
+// With so few rows the product is a stream over E (2D flops per logit, D bytes of E per item),
+// so it is shaped like one:
+//  * a workgroup has eight waves: wave w holds rows 32 (w % 4) .. + 32 of A over one half of D
+//    in registers as the MFMA's B operand (D/8 VGPRs: 96 at D = 768), one workgroup per CU;
+//  * persistent workgroups walk the chunk's 32-item blocks. A block's E rows (32 x D bytes)
+//    are copied into LDS with global_load_lds two blocks ahead, into three buffers, at a
+//    row stride of D + 16 bytes, so that the fragment reads of the 32 items spread over the
+//    banks and every read is a per-lane base plus an immediate;
+//  * a wave widens each 8-byte fragment of its half (four instructions for 8 values) and
+//    issues D/32 MFMAs per block; the two halves of a row quarter then exchange partial
+//    logits through LDS, so that each finishes 16 of the 32 items;
+//  * each lane sums its row's softplus terms in registers across blocks (the log taken once
+//    per block); sigma goes through an LDS image of the block's P (128 rows x 32 items) and
+//    out as one contiguous 8 KB run in 16-byte pieces;
+//  * workgroup g of a chunk writes loss slot part_base + g and the chunk's slots past the
+//    workgroups are zeroed, so the finalization sums the slots as it does for the GEMM's
+//    per-tile partials.
+#include "launch.h"
+
+#include <algorithm>
+
+namespace cl {
+
+namespace {
+
+constexpr int kLItems = 32;                    // items per block
+constexpr int kLRows = 128;                    // rows of a P block (T at most)
+constexpr int kLPRow = 2 * kLItems + 16;       // LDS stride of a P-image row (bytes)
+constexpr int kLPImg = kLRows * kLPRow;
+constexpr int kLMaxWorkgroups = 256;           // one per CU
+constexpr float kLNegInf = -__builtin_inff();
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0xF70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// MODE 0: loss partials; 1: loss partials and P; 2: loss partials and positive-logit counts
+template <int D, int MODE>
+__global__ __launch_bounds__(512, 1) void k_logits_rows(const LogitsRowsParams p) {
+  constexpr bool WP = MODE == 1, CNT = MODE == 2;
+  constexpr int DH = D / 2;                    // columns of a wave's half
+  constexpr int KH = DH / 16;                  // its MFMA k steps
+  constexpr int ER = D + 16;                   // LDS stride of an E row
+  constexpr int NC = (kLItems * ER + 1023) / 1024;   // 1 KB copies of a block's image
+  constexpr int EB = NC * 1024;
+  constexpr int C0 = NC / 8;                   // copies per block of waves NC % 8 .. 7 (others + 1)
+  constexpr int NBUF = 3;                      // E buffers: two blocks in flight beyond the current
+  constexpr int OFF_P = NBUF * EB;             // the P image
+  constexpr int OFF_X = OFF_P + (WP ? kLPImg : 0);   // partial-logit exchange, [8 waves][8][64]
+  constexpr int OFF_F = OFF_X + 8 * 8 * 64 * 4;      // loss (and count) exchange, [2][128]
+  __shared__ __attribute__((aligned(1024))) char lds[OFF_F + 8 * kLRows];
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tq = wv & 3, dh = wv >> 2;
+  const int64_t g = blockIdx.x, ng = gridDim.x;
+  const uint32_t l0 = lds_u32(lds);
+  const int t = 32 * tq + l32;                 // this lane's row
+  const bool t_ok = t < p.T;
+  const int ncp = wv < NC % 8 ? C0 + 1 : C0;   // this wave's copies per block
+
+  // the chunk's loss (and count) slots past the workgroups' own
+  for (int64_t sl = ng + g; sl < p.nslots; sl += ng)
+    for (int r = tid; r < p.T; r += 512) {
+      p.part_a[(p.part_base + sl) * p.T + r] = 0.0f;
+      if constexpr (CNT) p.part_b[(p.part_base + sl) * p.T + r] = 0.0f;
+    }
+
+  // the held B operand: row t of A, columns DH dh + 16 ks + 8 h .. + 8 (zero past T)
+  bf16x8 ast[KH];
+#pragma unroll
+  for (int ks = 0; ks < KH; ++ks)
+    ast[ks] = t_ok ? *(const bf16x8*)(p.A + (int64_t)t * D + DH * dh + 16 * ks + 8 * h) : bf16x8{};
+
+  // copies of block bb into buffer q, copy kb = wv + 8 x: image byte o holds item o / ER,
+  // byte o % ER of its row (the pad bytes and the bytes past the image fetch the block's
+  // first byte). Rows past V (the chunk's last blocks run to its 256-item rounding) fetch
+  // row V - 1, from a base row clamped the same way, so every offset is non-negative.
+  auto issue = [&](int64_t bb, int q) {
+    const int64_t vb = p.v0 + bb * kLItems;
+    const int64_t rb = vb < p.V ? vb : p.V - 1;
+#pragma unroll
+    for (int x = 0; x < (NC + 7) / 8; ++x) {
+      const int kb = wv + 8 * x;
+      if (kb >= NC) break;
+      const int o = kb * 1024 + 16 * lane;
+      const int r = o / ER, c = o - r * ER;
+      uint32_t src = 0u;
+      if (r < kLItems && c < D) {
+        int64_t v = vb + r;
+        v = v < p.V ? v : p.V - 1;
+        src = (uint32_t)((v - rb) * D + c);
+      }
+      lds_dma16(p.E + rb * D, src, l0 + (uint32_t)(q * EB + kb * 1024));
+    }
+  };
+  // wait until block k's copies are in: n later blocks' copies (ncp each) may stay in flight
+  auto wait_for = [&](int n) {
+    if (n == 2) {
+      if (ncp == C0 + 1) wait_vm<2 * (C0 + 1)>(); else wait_vm<2 * C0>();
+    } else if (n == 1) {
+      if (ncp == C0 + 1) wait_vm<C0 + 1>(); else wait_vm<C0>();
+    } else {
+      wait_vm<0>();
+    }
+  };
+  // the held operand's loads complete here: no wait of the compiler's own for them may
+  // remain inside the loop, where it would also wait for later blocks' copies
+  wait_vm<0>();
+  int64_t b = g;
+  issue(b, 0);
+  if (b + ng < p.nblk) issue(b + ng, 1);
+  float relu = 0.0f, lg = 0.0f, cnt = 0.0f;
+  int q = 0;
+  for (; b < p.nblk; b += ng) {
+    const bool m2 = b + 2 * ng < p.nblk;         // uniform over the workgroup
+    if (m2) issue(b + 2 * ng, q == 0 ? 2 : q - 1);
+    wait_for(m2 ? 2 : (b + ng < p.nblk ? 1 : 0));
+    __syncthreads();                             // block b's copies are visible
+
+    // A operand: item l32, columns DH dh + 16 ks + 8 h .. + 8
+    const uint32_t eb = l0 + (uint32_t)(q * EB + l32 * ER + DH * dh + 8 * h);
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KH; ++ks) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 raw = *(const CL_LDS u32x2*)(uintptr_t)(eb + (uint32_t)(16 * ks));
+      acc = mfma32(fp8x8_to_bf16x8(uint2{raw[0], raw[1]}), ast[ks], acc);
+    }
+    // result register i holds item 8 (i >> 2) + 4 h + (i & 3): half dh keeps items
+    // 16 dh .. 16 dh + 15 (registers 8 dh .. 8 dh + 7) and hands the others to its partner
+    float* const xb = (float*)(lds + OFF_X);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xb[(wv * 8 + j) * 64 + lane] = acc[8 * (1 - dh) + j];
+    __syncthreads();
+    float x8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x8[j] = acc[8 * dh + j] + xb[((wv ^ 4) * 8 + j) * 64 + lane];
+
+    // register j: item 16 dh + 8 (j >> 2) + 4 h + (j & 3), row t; items past V become -inf,
+    // which adds 0 to both sums and gives sigma 0
+    const int64_t vb = p.v0 + b * kLItems;
+    float prod = 1.0f;
+    float f[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int it = 16 * dh + 8 * (j >> 2) + 4 * h + (j & 3);
+      const float x = vb + it < p.V ? x8[j] : kLNegInf;
+      const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * kLog2e);   // e^-|x| in [0, 1]
+      const float qv = 1.0f + e;
+      relu += __builtin_fmaxf(x, 0.0f);
+      prod *= qv;
+      if constexpr (CNT) cnt += x > 0.0f ? 1.0f : 0.0f;   // exact in fp32 below 2^24
+      if constexpr (WP) {                        // unweighted: w enters through dA and A_w
+        const float r = __builtin_amdgcn_rcpf(qv);
+        f[j] = x >= 0.0f ? r : e * r;
+      }
+    }
+    lg += __builtin_amdgcn_logf(prod);           // log2 of a product of 8 factors in [1, 2]
+    if constexpr (WP) {
+      char* const pimg = lds + OFF_P;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        uint2 pk;
+        pk.x = t_ok ? f32_to_bf16_bits(f[4 * jj]) | (f32_to_bf16_bits(f[4 * jj + 1]) << 16) : 0u;
+        pk.y = t_ok ? f32_to_bf16_bits(f[4 * jj + 2]) | (f32_to_bf16_bits(f[4 * jj + 3]) << 16) : 0u;
+        *(uint2*)(pimg + t * kLPRow + 2 * (16 * dh + 8 * jj + 4 * h)) = pk;
+      }
+      __syncthreads();
+      // the block's P: 128 rows x 64 bytes, contiguous in the blocked layout; thread tid
+      // copies 16-byte piece tid (row tid / 4, quarter tid % 4)
+      uint16_t* const pb = p.P + b * (kLRows * kLItems);
+      const int r = tid >> 2, qq = tid & 3;
+      *(uint4*)(pb + r * kLItems + 8 * qq) = *(const uint4*)(pimg + r * kLPRow + 16 * qq);
+    }
+    __syncthreads();                             // buffer q, the exchange and the P image are free
+    q = q == NBUF - 1 ? 0 : q + 1;
+  }
+  // a row's partial: the two halves of each wave, then the two column halves, in that order
+  float vs = relu + lg * kLn2;
+  vs += __shfl_xor(vs, 32, 64);
+  float* const fb = (float*)(lds + OFF_F);
+  if constexpr (CNT) cnt += __shfl_xor(cnt, 32, 64);
+  if (dh == 1 && h == 0) {
+    fb[t] = vs;
+    if constexpr (CNT) fb[kLRows + t] = cnt;
+  }
+  __syncthreads();
+  if (dh == 0 && h == 0 && t_ok) {
+    p.part_a[(p.part_base + g) * p.T + t] = vs + fb[t];
+    if constexpr (CNT) p.part_b[(p.part_base + g) * p.T + t] = cnt + fb[kLRows + t];
+  }
+}
+
+template <int D>
+hipError_t launch_d(const LogitsRowsParams& p, unsigned grid, hipStream_t st) {
+  if (p.P != nullptr) k_logits_rows<D, 1><<<grid, 512, 0, st>>>(p);
+  else if (p.part_b != nullptr) k_logits_rows<D, 2><<<grid, 512, 0, st>>>(p);
+  else k_logits_rows<D, 0><<<grid, 512, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool logits_rows_supported(int64_t Tp, int64_t D) { return Tp == kLRows && D % 128 == 0 && D >= 128 && D <= 768; }
+
+hipError_t launch_logits_rows(const LogitsRowsParams& p, hipStream_t st) {
+  if (!logits_rows_supported(kLRows, p.D) || p.T < 1 || p.T > kLRows || p.nslots < 1 || p.nblk != 8 * p.nslots ||
+      p.V <= 0 || p.v0 < 0 || p.v0 >= p.V || p.E == nullptr || p.A == nullptr || p.part_a == nullptr ||
+      (p.P != nullptr && p.part_b != nullptr))
+    return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)std::min<int64_t>(kLMaxWorkgroups, p.nslots);
+  switch (p.D) {
+    case 128: return launch_d<128>(p, grid, st);
+    case 256: return launch_d<256>(p, grid, st);
+    case 384: return launch_d<384>(p, grid, st);
+    case 512: return launch_d<512>(p, grid, st);
+    case 640: return launch_d<640>(p, grid, st);
+    case 768: return launch_d<768>(p, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace cl
