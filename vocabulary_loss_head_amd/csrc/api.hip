@@ -192,6 +192,7 @@ struct ChunkPlan {
   int64_t n_chunks;
   int64_t n_splits;   // loss / lse partials: one per item tile
   int64_t sk;         // split-K slices of the dA product
+  int64_t sk_rows;    // dA partials of the whole-row FP8 SGD product when it also forms dA (0: n/a)
   int64_t kps;        // items per slice
   int64_t flag_bn, flag_ld;   // gradient filter flags: row tile of the logits product, row tiles
   bool q8;            // FP8 logits: the logits product multiplies FP8 activations and FP8 E
@@ -242,6 +243,7 @@ ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap, bool q8 
   if (sk < 1) sk = 1;
   c.kps = round_up(ceil_div(vc, sk), 32);
   c.sk = ceil_div(vc, c.kps);
+  c.sk_rows = e_fp8 && cl::sgd_rows_supported(c.Tp, D) ? cl::sgd_rows_dA_splits(ceil_div(std::min(vc, V), 32), D) : 0;
   c.flag_bn = cl::gemm_tile_n_of(cl::GEMM_EPI_CE_P, vc, T > 0 ? T : 1, D);
   c.flag_ld = ceil_div(T > 0 ? T : 1, c.flag_bn);
   return c;
@@ -300,14 +302,15 @@ Ws2 carve_chunked(void* base, const ChunkPlan& pl, bool need_P, bool need_dA, bo
   w.part_a = c.take<float>((size_t)pl.n_splits * T);
   w.part_b = two_partials ? c.take<float>((size_t)pl.n_splits * T) : nullptr;
   w.P = need_P ? c.take<uint16_t>((size_t)pl.Vc * pl.Tp) : nullptr;
-  w.part_dA = need_dA ? c.take<float>((size_t)pl.sk * T * pl.D) : nullptr;
+  const int64_t n_dA = std::max(pl.sk, pl.sk_rows);
+  w.part_dA = need_dA ? c.take<float>((size_t)n_dA * T * pl.D) : nullptr;
   w.pos_dot = need_pos ? c.take<float>(T) : nullptr;
   w.pos_sum = need_pos && need_dA ? c.take<float>((size_t)T * pl.D) : nullptr;
   w.pos_tp = need_pos ? c.take<int32_t>(T) : nullptr;
   w.S_u = need_Su ? c.take<float>((size_t)cap * pl.D) : nullptr;
   w.S_part = need_Su ? c.take<float>(2 * cl::item_sum_parts(cap) * pl.D) : nullptr;
   const size_t red_loss = cl::reduce_splits_tmp_floats(pl.n_splits, T, two_partials ? 1 : 0);
-  const size_t red_dA = need_dA ? cl::reduce_splits_tmp_floats(pl.sk, T * pl.D, 0) : 0;
+  const size_t red_dA = need_dA ? cl::reduce_splits_tmp_floats(n_dA, T * pl.D, 0) : 0;
   w.red = c.take<float>(std::max<size_t>(1, std::max(red_loss, red_dA)));
   w.flags = need_P ? c.take<int32_t>((size_t)(pl.Vc / 256) * pl.flag_ld) : nullptr;
   w.Et = need_dA && need_Et ? c.take<uint16_t>((size_t)pl.Vc * pl.D) : nullptr;
@@ -521,6 +524,7 @@ struct ChunkJob {
   const uint8_t* A8;     // FP8 logits: the activations' E4M3FN copy
   const void* A_dE;      // the dE product's activations operand (NULL: A)
   const uint16_t* AwT;   // non-NULL: the SGD product runs as whole-row updates (sgd_rows.hip)
+  bool rows_dA;          // with AwT: that product also forms the dA partials (no separate dA product)
   bool rows_logits;      // the BCE logits product streams 32-item blocks (logits_rows.hip)
   int k3_epi;            // -1: none, GEMM_EPI_DE or GEMM_EPI_SGD
   const int32_t* uitems; const int32_t* counts; const float* S_u; const int32_t* imap;
@@ -562,7 +566,7 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
       g.filter_eps = j.filter_eps;
       CL_HIP(cl::launch_gemm(g, st), "chunk logits");
     }
-    if (j.part_dA != nullptr) {
+    if (j.part_dA != nullptr && !j.rows_dA) {
       Phase ph(CUTLOSS_PHASE_CHUNK_DA, st);
       cl::GemmParams g{};
       g.epi = cl::GEMM_EPI_ACC;
@@ -594,6 +598,9 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
       cl::SgdRowsParams s{};
       s.V = pl.V; s.v0 = v0; s.nblk = ceil_div(vlen, 32); s.D = (int)pl.D;
       s.P = j.P; s.AwT = j.AwT; s.S_u = j.S_u; s.imap = j.imap; s.E = (uint8_t*)j.E; s.lr = j.lr;
+      if (j.rows_dA) {
+        s.T = pl.T; s.dA_part = j.part_dA; s.dA_splits = pl.sk_rows; s.dA_first = c == 0;
+      }
       CL_HIP(cl::launch_sgd_rows(s, st), "chunk SGD rows");
     } else if (j.k3_epi >= 0) {
       Phase ph(CUTLOSS_PHASE_CHUNK_DE, st);
@@ -622,8 +629,11 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
   const int e_fp8 = p->e_dtype == CUTLOSS_FP8_E4M3;
   const Ws2 w = carve_chunked(ws, pl, grad, dA != nullptr, dE_mode != 0, counts != nullptr, true, !e_fp8);
   CL_TRY(check_ws(ws, ws_bytes, w.bytes));
-  // FP8 SGD with nearest-even rounding over at most 128 rows: whole-row updates
+  // FP8 SGD with nearest-even rounding over at most 128 rows: whole-row updates, which also
+  // form the dA partials from the E they read before updating it
   const bool sgd_rows = dE_mode == 2 && e_fp8 && sr == 0 && w.AwT != nullptr;
+  const bool rows_dA = sgd_rows && dA != nullptr && pl.sk_rows > 0;
+  const int64_t n_dA = rows_dA ? pl.sk_rows : pl.sk;
   {
     Phase ph(CUTLOSS_PHASE_TARGETS, st);
     CL_HIP(cl::launch_zero_u64(w.err, 4, st), "zero counters");
@@ -638,7 +648,7 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
   fp.T = p->T; fp.D = p->D; fp.V = p->V; fp.A = p->A; fp.E = p->E; fp.e_fp8 = e_fp8;
   fp.crow = w.tw.crow; fp.cids = w.tw.cids; fp.dloss = dloss; fp.mask = p->row_mask;
   // the gradient tile holds the unweighted sigmoid: w scales dA here and A in the dE product
-  fp.n_splits = (int)pl.n_splits; fp.n_splits_dA = (int)pl.sk; fp.dA_weighted = 0;
+  fp.n_splits = (int)pl.n_splits; fp.n_splits_dA = (int)n_dA; fp.dA_weighted = 0;
   fp.part_a = w.part_a; fp.part_dA = w.part_dA; fp.loss = loss; fp.dA = dA; fp.w_out = w.w;
   fp.pos_dot = w.pos_dot; fp.pos_sum = w.pos_sum;
   fp.part_c = w.part_b; fp.counts = counts; fp.pos_tp = counts ? w.pos_tp : nullptr;
@@ -663,6 +673,7 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
   j.pl = &pl; j.A = p->A; j.E = p->E; j.e_fp8 = e_fp8;
   j.A_dE = dE_mode != 0 ? w.Aw : nullptr;
   j.AwT = sgd_rows ? w.AwT : nullptr;
+  j.rows_dA = rows_dA;
   j.k1_epi = grad ? cl::GEMM_EPI_BCE_P : (counts ? cl::GEMM_EPI_BCE_METRICS : cl::GEMM_EPI_BCE_LOSS);
   // FP8 E over at most 128 rows (BCE loss, with P or with the metrics' counts): the
   // streaming logits product
@@ -682,7 +693,7 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
       fp.n_splits = 1;
     }
     if (dA != nullptr) {
-      CL_HIP(cl::launch_reduce_splits(w.part_dA, nullptr, pl.sk, p->T * p->D, w.red, 0, st), "dA partials");
+      CL_HIP(cl::launch_reduce_splits(w.part_dA, nullptr, n_dA, p->T * p->D, w.red, 0, st), "dA partials");
       fp.n_splits_dA = 1;
     }
     CL_HIP(cl::launch_finalize_rows(fp, 0, loss != nullptr, dA != nullptr, st), "finalize rows");

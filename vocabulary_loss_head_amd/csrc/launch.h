@@ -90,8 +90,17 @@ struct SgdRowsParams {
   const int32_t* imap;   // [V] item -> unique-item index, -1 for none
   uint8_t* E;            // [V][D] E4M3FN, updated in place
   float lr;
+  // dA (optional): dA_part[r][t][d] (r < dA_splits, t < T) += sum over the items that block
+  // row r of the chunk covers of P[t][v] E[v][d], E read before its update; dA_first: the
+  // chunk starts the sums (its partials are stored, not added to). NULL: no dA.
+  int64_t T;
+  float* dA_part;
+  int64_t dA_splits;
+  int dA_first;
 };
 bool sgd_rows_supported(int64_t Tp, int64_t D);   // Tp: rows of the gradient tile (128)
+// the dA partials of a head whose first chunk has nblk 32-item blocks: one per block row
+int64_t sgd_rows_dA_splits(int64_t nblk, int64_t D);
 
 // ----------------------------------------------------------------------------------
 // BCE logits product for FP8 E and heads of at most 128 rows (logits_rows.hip): loss

@@ -16,7 +16,15 @@
 //    block waits only for its own copies (an explicit vmcnt);
 //  * the block is read transposed as the A operand (rows = items, k = t): 8 MFMAs a wave;
 //  * the 32 x 128 result passes through LDS so that each of the 256 threads updates one
-//    contiguous 16-byte piece of a row.
+//    contiguous 16-byte piece of a row;
+//  * with dA requested, the same two LDS images also give the slice's share of the row
+//    gradient, sum over the chunk's items of P[t][v] E[v][d] with E before its update (the
+//    backward's G E, Cut Binary Cross Entropy §III-B): the block is read row-wise as the A
+//    operand (rows t, k = items) and the E slice transposed (ds_read_b64_tr_b8, k = items) as
+//    the B operand, each wave accumulating a 64 x 64 tile in registers over all of its
+//    blocks. The workgroup's 128 x 128 tile is one split partial of dA; the partial carries
+//    over from one chunk to the next (loaded at the start, stored at the end), so that the
+//    separate dA product and its second pass over E and P are not needed.
 #include "launch.h"
 
 #include <algorithm>
@@ -30,7 +38,9 @@ constexpr int kSgdRows = 128;                      // rows (k) of a gradient-til
 constexpr int kSgdCols = 128;                      // columns of a workgroup's slice (4 waves x 32)
 constexpr int kPRow = 2 * kSgdItems + 16;          // LDS stride of a block row (bytes)
 constexpr int kPImg = 12 * 1024;                   // LDS image of a block: 10 KB used, 3 copies a wave
-constexpr int kEImg = kSgdItems * kSgdCols;        // the items' slices of E: 32 x 128 bytes
+// the items' slices of E: 32 rows of 128 bytes, the 16-byte piece c of row v stored at piece
+// c ^ (v & 7) of the row, so that the transposed reads (8 rows, one piece) meet 8 bank groups
+constexpr int kEImg = kSgdItems * kSgdCols;
 constexpr int kMapImg = 4 * 256;                   // unique-item indices: one 256-byte slot a wave
 constexpr int kStageRow = 4 * kSgdCols + 16;       // fp32 result row (+16 bytes)
 constexpr int kOffE = 2 * kPImg;
@@ -52,6 +62,14 @@ __device__ __forceinline__ s16x4 read_tr16(uint32_t lds) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((CL_LDS s16x4*)(uintptr_t)lds);
 }
 
+// 8 bytes of a transposed 8 x 16 byte block: within a 16-lane group, lane i receives byte
+// i % 8 of the 8-byte rows that lanes i / 8, i / 8 + 2, ..., i / 8 + 14 address
+__device__ __forceinline__ uint2 read_tr8(uint32_t lds) {
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CL_LDS i32x2*)(uintptr_t)lds);
+  return uint2{(uint32_t)r[0], (uint32_t)r[1]};
+}
+
 // A_w^T[d][t] = bf16(w_t A[t][d]) for t < T and 0 for T <= t < 128: the same rounding of
 // the same product as the row-major weighted activations of the general path.
 __global__ __launch_bounds__(256) void k_weighted_t(const uint16_t* __restrict__ A, const float* __restrict__ w,
@@ -66,7 +84,7 @@ __global__ __launch_bounds__(256) void k_weighted_t(const uint16_t* __restrict__
 
 // Workgroup g sweeps slice g % ns (ns = D / 128) over the blocks g / ns, g / ns + R, ...
 // (R = gridDim.x / ns); every wave of it runs the same blocks, so the barriers match.
-__global__ __launch_bounds__(256) void k_sgd_rows(const SgdRowsParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_sgd_rows(const SgdRowsParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[kLds];
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -85,6 +103,26 @@ __global__ __launch_bounds__(256) void k_sgd_rows(const SgdRowsParams p) {
 #pragma unroll
     for (int ks = 0; ks < kSgdRows / 16; ++ks) bst[ks] = *(const bf16x8*)(at + 16 * ks);
   }
+  // dA tile of the wave: rows 64 th .. 64 th + 63, columns c0 + 64 dh .. + 63; register i of
+  // tile (mt, nt) holds row 64 th + 32 mt + 8 (i >> 2) + 4 h + (i & 3), column
+  // c0 + 64 dh + 32 nt + l32 of split partial r
+  const int th = wv & 1, dh = wv >> 1;
+  const bool want_dA = p.dA_part != nullptr;
+  float* const part = want_dA ? p.dA_part + (int64_t)(blockIdx.x / ns) * p.T * D : nullptr;
+  f32x16 dacc[2][2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      dacc[mt][nt] = f32x16{};
+      if (want_dA && !p.dA_first) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int64_t t = 64 * th + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (t < p.T) dacc[mt][nt][i] = part[t * D + c0 + 64 * dh + 32 * nt + l32];
+        }
+      }
+    }
   // copies of block jb into buffer q, kCopies per wave: image byte o of the P block holds
   // row o / kPRow, byte o % kPRow (pad bytes fetch byte 0); wave wv copies the 128-byte
   // slices of items 8 wv .. 8 wv + 7 and (in its own slot) the 32 items' indices. Rows
@@ -101,9 +139,10 @@ __global__ __launch_bounds__(256) void k_sgd_rows(const SgdRowsParams p) {
     }
     const int64_t vb = p.v0 + jb * kSgdItems;
     {
+      // LDS piece lane & 7 of row 8 wv + (lane >> 3) holds the row's piece (lane & 7) ^ (lane >> 3)
       int64_t v = vb + 8 * wv + (lane >> 3);
       v = v < p.V ? v : p.V - 1;
-      lds_dma16(p.E + vb * D, (uint32_t)((v - vb) * D + c0 + 16 * (lane & 7)),
+      lds_dma16(p.E + vb * D, (uint32_t)((v - vb) * D + c0 + 16 * ((lane & 7) ^ (lane >> 3))),
                 l0 + (uint32_t)(kOffE + q * kEImg + wv * 1024));
     }
     {
@@ -121,6 +160,12 @@ __global__ __launch_bounds__(256) void k_sgd_rows(const SgdRowsParams p) {
   // (m = 0..3) of k step ks, from the 16-lane group's row and item offsets
   const uint32_t ta0 = (uint32_t)((8 * h + (s >> 2)) * kPRow + 2 * (4 * (s & 3) + 16 * ((lane >> 4) & 1)));
   const int it = tid >> 3, pc = tid & 7;         // the update's item and 16-column piece
+  // dA operands: the block's rows 64 th + 32 mt + l32 at items 16 ks + 8 h (16 bytes), and
+  // the E slice read transposed: in 16-lane group gq, lane s addresses item row
+  // 16 ks + 8 h + (s >> 1), bytes 8 (s & 1) of piece 4 dh + 2 nt + (gq & 1) (swizzled)
+  const uint32_t pa0 = (uint32_t)((64 * th + l32) * kPRow + 2 * 8 * h);
+  const uint32_t eb0 = (uint32_t)((8 * h + (s >> 1)) * kSgdCols + 8 * (s & 1));
+  const int epc = 4 * dh + ((lane >> 4) & 1);
   int q = 0;
   for (; j < p.nblk; j += rstep) {
     const bool more = j + rstep < p.nblk;        // uniform over the workgroup
@@ -135,6 +180,24 @@ __global__ __launch_bounds__(256) void k_sgd_rows(const SgdRowsParams p) {
       const bf16x8 a = cat_bf16(read_tr16(ta + (uint32_t)(16 * ks * kPRow)),
                                 read_tr16(ta + (uint32_t)((16 * ks + 4) * kPRow)));
       acc = mfma32(a, bst[ks], acc);
+    }
+    if (want_dA) {
+      const uint32_t pb = l0 + (uint32_t)(q * kPImg) + pa0;
+      const uint32_t eb = l0 + (uint32_t)(kOffE + q * kEImg) + eb0;
+#pragma unroll
+      for (int ks = 0; ks < kSgdItems / 16; ++ks) {
+        bf16x8 pa[2], eb8[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          pa[mt] = *(const CL_LDS bf16x8*)(uintptr_t)(pb + (uint32_t)(32 * mt * kPRow + 32 * ks));
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          eb8[nt] = fp8x8_to_bf16x8(read_tr8(eb + (uint32_t)(16 * ks * kSgdCols + 16 * ((epc + 2 * nt) ^ (s >> 1)))));
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) dacc[mt][nt] = mfma32(pa[mt], eb8[nt], dacc[mt][nt]);
+      }
     }
     // result register i of a lane: item 8 (i >> 2) + 4 h + (i & 3), column 32 wv + l32
     char* const stage = lds + kOffStage;
@@ -160,7 +223,7 @@ __global__ __launch_bounds__(256) void k_sgd_rows(const SgdRowsParams p) {
     }
     const int64_t v = p.v0 + j * kSgdItems + it;
     if (v < p.V) {
-      const uint4 e = *(const uint4*)(lds + kOffE + q * kEImg + it * kSgdCols + 16 * pc);
+      const uint4 e = *(const uint4*)(lds + kOffE + q * kEImg + it * kSgdCols + 16 * (pc ^ (it & 7)));
       const uint32_t w4[4] = {e.x, e.y, e.z, e.w};
       uint32_t o[4];
 #pragma unroll
@@ -182,11 +245,26 @@ __global__ __launch_bounds__(256) void k_sgd_rows(const SgdRowsParams p) {
     __syncthreads();                             // buffer q and the stage are free again
     q ^= 1;
   }
+  if (want_dA) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int64_t t = 64 * th + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (t < p.T) part[t * D + c0 + 64 * dh + 32 * nt + l32] = dacc[mt][nt][i];
+        }
+  }
 }
 
 }  // namespace
 
 bool sgd_rows_supported(int64_t Tp, int64_t D) { return Tp == kSgdRows && D % 128 == 0 && D >= 128 && D <= 1024; }
+
+int64_t sgd_rows_dA_splits(int64_t nblk, int64_t D) {
+  return std::max<int64_t>(1, std::min<int64_t>(nblk, 768 / std::max<int64_t>(1, D / kSgdCols)));
+}
 
 hipError_t launch_weighted_transpose(const void* A, const float* w, int64_t T, int64_t D, uint16_t* AwT,
                                      hipStream_t st) {
@@ -204,7 +282,13 @@ hipError_t launch_sgd_rows(const SgdRowsParams& p, hipStream_t st) {
   if (p.v0 + (p.nblk - 1) * kSgdItems >= p.V) return hipErrorInvalidValue;
   // about three workgroups per CU (51 KB of LDS each), every slice with the same block rows
   const int64_t ns = p.D / kSgdCols;
-  const int64_t rows = std::max<int64_t>(1, std::min<int64_t>(p.nblk, 768 / ns));
+  int64_t rows = std::max<int64_t>(1, std::min<int64_t>(p.nblk, 768 / ns));
+  if (p.dA_part != nullptr) {
+    // one dA partial per block row: the first chunk writes every one of them
+    if (p.T < 1 || p.T > kSgdRows || p.dA_splits < 1 || p.dA_splits > 768 / ns) return hipErrorInvalidValue;
+    if (p.dA_first && p.nblk < p.dA_splits) return hipErrorInvalidValue;
+    rows = std::min<int64_t>(p.nblk, p.dA_splits);
+  }
   k_sgd_rows<<<(unsigned)(ns * rows), 256, 0, st>>>(p);
   return hipGetLastError();
 }
