@@ -161,12 +161,73 @@ __global__ __launch_bounds__(256) void k_finalize_rows(const FinalizeParams p, i
 }
 
 // pos_dot[t] = sum_p A_t . E_p and pos_sum[t][d] = sum_p E_p[d], one wave per row, in
-// positive order (the same order finalize uses when it reads E directly).
+// positive order (the same order finalize uses when it reads E directly). For D <= 256 NS
+// the row of A stays in registers and the E rows of four positives are loaded together;
+// every sum still runs over d slabs and positives in order.
+constexpr int kPosBatch = 4;
+
+template <int NS>
+__device__ __forceinline__ void row_positives_held(const FinalizeParams& p, int64_t t, int lane) {
+  const int64_t D = p.D;
+  const int32_t pb = p.crow[t], pe = p.crow[t + 1];
+  f32x4 a[NS], corr[NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    const int64_t d = 4 * lane + 256 * k;
+    a[k] = d < D ? load_a4(p, t * D + d) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    corr[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  float sum_x = 0.0f;
+  int tp = 0;
+  for (int32_t e0 = pb; e0 < pe; e0 += kPosBatch) {
+    f32x4 ev[kPosBatch][NS];
+#pragma unroll
+    for (int b = 0; b < kPosBatch; ++b) {
+      const int64_t v = p.cids[min(e0 + b, pe - 1)];
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const int64_t d = 4 * lane + 256 * k;
+        ev[b][k] = d < D ? load_e4(p.E, p.e_fp8, v * D + d) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kPosBatch; ++b) {
+      if (e0 + b >= pe) break;
+      float part = 0.0f;
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        if (4 * lane + 256 * k < D) {
+          part += a[k][0] * ev[b][k][0];
+          part += a[k][1] * ev[b][k][1];
+          part += a[k][2] * ev[b][k][2];
+          part += a[k][3] * ev[b][k][3];
+          corr[k] += ev[b][k];
+        }
+      }
+      const float x = wave_sum(part);
+      if (p.pos_x != nullptr && lane == 0) p.pos_x[e0 + b] = x;
+      sum_x += x;
+      tp += x > 0.0f ? 1 : 0;
+    }
+  }
+  if (lane == 0) p.pos_dot[t] = sum_x;
+  if (lane == 0 && p.pos_tp != nullptr) p.pos_tp[t] = tp;
+  if (p.pos_sum == nullptr) return;          // no dA requested
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    const int64_t d = 4 * lane + 256 * k;
+    if (d < D) *(f32x4*)(p.pos_sum + t * D + d) = corr[k];
+  }
+}
+
 __global__ __launch_bounds__(256) void k_row_positives(const FinalizeParams p) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= p.T) return;
   const int64_t D = p.D;
+  if (D <= 256) return row_positives_held<1>(p, t, lane);
+  if (D <= 512) return row_positives_held<2>(p, t, lane);
+  if (D <= 1024) return row_positives_held<4>(p, t, lane);
   const int32_t pb = p.crow[t], pe = p.crow[t + 1];
   float sum_x = 0.0f;
   int tp = 0;
@@ -208,19 +269,34 @@ __global__ void k_row_weights(const FinalizeParams p, int kind) {
 // there; an item crossing piece boundaries leaves its run at the end of its first
 // piece in part[j][1], its runs covering or starting later pieces in part[j][0], and
 // k_item_fixup adds them in piece order. Every sum runs in a fixed order.
-constexpr int kPiece = 32;
+constexpr int kPiece = 16;
+constexpr int kPieceBatch = 8;     // pairs whose rows of A are loaded together
+constexpr int kPieceSlabs = 4;     // 256-wide d slabs per pass over the piece (D <= 1024: one)
 
-// index of the unique item that holds pair i (useg ascending, useg[0] = 0)
-__device__ __forceinline__ int item_of(const int32_t* useg, int nu, int32_t i) {
-  int lo = 0, hi = nu;          // first index with useg[idx] > i, minus one
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (useg[mid] <= i) lo = mid + 1;
-    else hi = mid;
-  }
-  return lo - 1;
+__device__ __forceinline__ int lane_i32(int32_t v, int i) { return __builtin_amdgcn_readlane(v, i); }
+__device__ __forceinline__ float lane_f32(float v, int i) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), i));
 }
 
+// index of the unique item that holds pair i: the last u < nu with useg[u] <= i (useg
+// ascending, useg[0] = 0 <= i < useg[nu]), narrowed 64 ways a step by the wave's lanes
+__device__ __forceinline__ int item_of_wave(const int32_t* useg, int nu, int32_t i, int lane) {
+  int lo = 0, hi = nu;
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int idx = lo + lane * step;
+    const unsigned long long m = __ballot(idx < hi && useg[idx] <= i);   // a prefix of lanes, lane 0 set
+    const int L = 63 - __clzll(m);
+    const int nlo = lo + L * step;
+    hi = min(hi, nlo + step);
+    lo = nlo;
+  }
+  return lo;
+}
+
+// The piece's pairs sit one a lane (row t and weight w_t of pair a + i in lane i) and the
+// ends of its items likewise, so that the rows of A of kPieceBatch pairs are requested
+// together; the sum of each item still runs over its pairs in order.
 __global__ __launch_bounds__(256) void k_item_pieces(int64_t D, const uint16_t* __restrict__ A, const float* __restrict__ w,
                                                      const int32_t* __restrict__ csc_rows, const int32_t* __restrict__ useg,
                                                      const int32_t* __restrict__ counts, float* __restrict__ S_u,
@@ -231,38 +307,63 @@ __global__ __launch_bounds__(256) void k_item_pieces(int64_t D, const uint16_t* 
   const int64_t a = j * kPiece;
   if (a >= n) return;
   const int64_t b = min(a + kPiece, (int64_t)n);
-  const int ns = (int)((D + 255) / 256);        // 256-wide d slabs; lane owns 4 d of each
-  constexpr int KB = 2;                         // slabs per lane in flight
-  int64_t i = a;
-  int u = item_of(useg, nu, (int32_t)a);        // pairs are item-major: later items follow in order
-  while (i < b) {
-    const int64_t s = useg[u], e = useg[u + 1];
-    const int64_t r1 = min(e, b);
-    float* dst;
-    if (s >= a && e <= b) dst = S_u + (int64_t)u * D;          // complete inside this piece
-    else if (s < a) dst = part + (j * 2 + 0) * D;               // began in an earlier piece
-    else dst = part + (j * 2 + 1) * D;                          // continues into later pieces
-    for (int k0 = 0; k0 < ns; k0 += KB) {
-      f32x4 acc[KB];
+  const int u0 = item_of_wave(useg, nu, (int32_t)a, lane);   // pairs are item-major: later items follow in order
+  int32_t tr = 0, ue = n;
+  float wr = 0.0f;
+  if (lane < kPiece) {
+    if (a + lane < b) tr = csc_rows[a + lane];
+    ue = useg[min(u0 + lane + 1, nu)];                       // end of item u0 + lane (useg[nu] = n)
+  }
+  if (lane < kPiece && a + lane < b) wr = w[tr];
+  const int32_t us0 = useg[u0];
+  const int ns = (int)((D + 255) / 256);                     // 256-wide d slabs; lane owns 4 d of each
+  for (int k0 = 0; k0 < ns; k0 += kPieceSlabs) {
+    f32x4 acc[kPieceSlabs];
 #pragma unroll
-      for (int kk = 0; kk < KB; ++kk) acc[kk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      for (int64_t q = i; q < r1; ++q) {        // pair order: the sum order is fixed
-        const int64_t t = csc_rows[q];
-        const float wt = w[t];
+    for (int kk = 0; kk < kPieceSlabs; ++kk) acc[kk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    int k = 0;                                               // current item: u0 + k, pairs [s_k, e_k)
+    int64_t s_k = us0, e_k = lane_i32(ue, 0);
+    for (int64_t q0 = a; q0 < b; q0 += kPieceBatch) {
+      uint2 raw[kPieceBatch][kPieceSlabs];
 #pragma unroll
-        for (int kk = 0; kk < KB; ++kk) {
+      for (int bq = 0; bq < kPieceBatch; ++bq) {
+        const int i = (int)(q0 - a) + bq;
+        const int64_t t = lane_i32(tr, min(i, kPiece - 1));
+#pragma unroll
+        for (int kk = 0; kk < kPieceSlabs; ++kk) {
           const int64_t d = 4 * lane + 256 * (k0 + kk);
-          if (d < D) acc[kk] += wt * load_e4(A, 0, t * D + d);
+          raw[bq][kk] = (q0 + bq < b && d < D) ? *(const uint2*)(A + t * D + d) : uint2{0u, 0u};
         }
       }
 #pragma unroll
-      for (int kk = 0; kk < KB; ++kk) {
-        const int64_t d = 4 * lane + 256 * (k0 + kk);
-        if (d < D) *(f32x4*)(dst + d) = acc[kk];
+      for (int bq = 0; bq < kPieceBatch; ++bq) {
+        const int64_t q = q0 + bq;
+        if (q >= b) break;
+        const float wt = lane_f32(wr, (int)(q - a));
+#pragma unroll
+        for (int kk = 0; kk < kPieceSlabs; ++kk) {
+          const uint2 r = raw[bq][kk];
+          const f32x4 x = {__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u), __uint_as_float(r.y << 16),
+                           __uint_as_float(r.y & 0xffff0000u)};
+          acc[kk] += wt * x;
+        }
+        if (q + 1 == e_k || q + 1 == b) {                    // the item's last pair in this piece
+          float* dst;
+          if (s_k >= a && e_k <= b) dst = S_u + (int64_t)(u0 + k) * D;   // complete inside this piece
+          else if (s_k < a) dst = part + (j * 2 + 0) * D;                // began in an earlier piece
+          else dst = part + (j * 2 + 1) * D;                             // continues into later pieces
+#pragma unroll
+          for (int kk = 0; kk < kPieceSlabs; ++kk) {
+            const int64_t d = 4 * lane + 256 * (k0 + kk);
+            if (d < D) *(f32x4*)(dst + d) = acc[kk];
+            acc[kk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          }
+          ++k;
+          s_k = e_k;
+          e_k = lane_i32(ue, min(k, kPiece - 1));
+        }
       }
     }
-    i = r1;
-    ++u;
   }
 }
 
@@ -275,7 +376,7 @@ __global__ __launch_bounds__(256) void k_item_fixup(int64_t D, const int32_t* __
   const int64_t a = j * kPiece;
   if (a >= n) return;
   const int64_t b = min(a + kPiece, (int64_t)n);
-  const int u = item_of(useg, nu, (int32_t)(b - 1));
+  const int u = item_of_wave(useg, nu, (int32_t)(b - 1), threadIdx.x & 63);
   const int64_t s = useg[u], e = useg[u + 1];
   if (!(e > b && s >= a)) return;
   const int64_t j1 = (e - 1) / kPiece;
