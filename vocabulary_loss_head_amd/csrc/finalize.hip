@@ -404,25 +404,40 @@ __global__ __launch_bounds__(256) void k_item_fixup(int64_t D, const int32_t* __
 // its column before it writes it.
 constexpr int kRedGroup = 64;
 
+// All of a thread's loads are issued before its sums (indices clamped into the group), so
+// that a level costs one round trip to memory; the sums skip the clamped copies and keep
+// the split order.
 __global__ __launch_bounds__(256) void k_reduce_splits(const float* pa, const float* pb, int64_t S, int64_t N, float* oa,
                                                        float* ob, int mode) {
   const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t g = blockIdx.y;
   if (n >= N) return;
-  const int64_t s0 = g * kRedGroup, s1 = min(S, s0 + kRedGroup);
+  const int64_t s0 = g * kRedGroup;
+  const int cnt = (int)(min(S, s0 + kRedGroup) - s0);
+  const float* ca = pa + s0 * N + n;
+  float va[kRedGroup];
+#pragma unroll
+  for (int i = 0; i < kRedGroup; ++i) va[i] = ca[(int64_t)min(i, cnt - 1) * N];
   if (mode == 0) {
     float acc = 0.0f;
-    for (int64_t s = s0; s < s1; ++s) acc += pa[s * N + n];
+#pragma unroll
+    for (int i = 0; i < kRedGroup; ++i)
+      if (i < cnt) acc += va[i];
     oa[g * N + n] = acc;
   } else {
+    const float* cb = pb + s0 * N + n;
+    float vb[kRedGroup];
+#pragma unroll
+    for (int i = 0; i < kRedGroup; ++i) vb[i] = cb[(int64_t)min(i, cnt - 1) * N];
     float m = -__builtin_inff();
-    for (int64_t s = s0; s < s1; ++s) m = __builtin_fmaxf(m, pa[s * N + n]);
+#pragma unroll
+    for (int i = 0; i < kRedGroup; ++i)
+      if (i < cnt) m = __builtin_fmaxf(m, va[i]);
     float sum = 0.0f;
     if (m != -__builtin_inff()) {
-      for (int64_t s = s0; s < s1; ++s) {
-        const float ms = pa[s * N + n];
-        if (ms != -__builtin_inff()) sum += pb[s * N + n] * __builtin_amdgcn_exp2f((ms - m) * kLog2e);
-      }
+#pragma unroll
+      for (int i = 0; i < kRedGroup; ++i)
+        if (i < cnt && va[i] != -__builtin_inff()) sum += vb[i] * __builtin_amdgcn_exp2f((va[i] - m) * kLog2e);
     }
     oa[g * N + n] = m;
     ob[g * N + n] = sum;
