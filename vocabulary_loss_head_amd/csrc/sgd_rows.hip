@@ -82,17 +82,30 @@ __global__ __launch_bounds__(256) void k_weighted_t(const uint16_t* __restrict__
   AwT[i] = v;
 }
 
-// Workgroup g sweeps slice g % ns (ns = D / 128) over the blocks g / ns, g / ns + R, ...
-// (R = gridDim.x / ns); every wave of it runs the same blocks, so the barriers match.
+// Workgroup (block row r, slice s) sweeps columns 128 s .. 128 s + 127 (s < ns = D / 128)
+// over the blocks r, r + R, ... (R = gridDim.x / ns); every wave of it runs the same blocks,
+// so the barriers match. The ns slices of a block row read the same gradient-tile blocks:
+// consecutive workgroups go to the eight XCDs in turn, so when R is a multiple of 8 the
+// slices of row r are workgroups 8 i + r % 8 (one XCD, one L2) and each P block comes from
+// HBM once.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_sgd_rows(const SgdRowsParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[kLds];
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int D = p.D;
   const int ns = D / kSgdCols;
-  const int c0 = kSgdCols * (int)(blockIdx.x % ns);
   const int64_t rstep = gridDim.x / ns;
-  int64_t j = blockIdx.x / ns;
+  int64_t r, sl;
+  if (rstep % 8 == 0) {
+    const int64_t idx = blockIdx.x / 8;
+    r = blockIdx.x % 8 + 8 * (idx / ns);
+    sl = idx % ns;
+  } else {
+    r = blockIdx.x / ns;
+    sl = blockIdx.x % ns;
+  }
+  const int c0 = kSgdCols * (int)sl;
+  int64_t j = r;
   if (j >= p.nblk) return;
   const uint32_t l0 = lds_u32(lds);
 
@@ -108,7 +121,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   // c0 + 64 dh + 32 nt + l32 of split partial r
   const int th = wv & 1, dh = wv >> 1;
   const bool want_dA = p.dA_part != nullptr;
-  float* const part = want_dA ? p.dA_part + (int64_t)(blockIdx.x / ns) * p.T * D : nullptr;
+  float* const part = want_dA ? p.dA_part + r * p.T * D : nullptr;
   f32x16 dacc[2][2];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
