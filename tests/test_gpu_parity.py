@@ -103,9 +103,10 @@ def test_bce_closed_forms(B, T, D):
         np.testing.assert_allclose(out["loss"].cpu().numpy()[valid], w.V * math.log(2.0), rtol=1e-5)
 
 
-# 6,000 IDs: the radix passes form their own block offsets; 150,000 IDs (147 sort blocks of
-# 1,024): the histograms are scanned by a kernel of their own
-@pytest.mark.parametrize("T,V,L", [(300, 5000, 20), (3000, 200_000, 50)])
+# up to 4,096 IDs and 8,192 rows: one workgroup sorts them in LDS; 6,000 IDs: the radix
+# passes form their own block offsets; 150,000 IDs (147 sort blocks of 1,024): the
+# histograms are scanned by a kernel of their own
+@pytest.mark.parametrize("T,V,L", [(1, 50, 40), (200, 3000, 15), (300, 5000, 20), (3000, 200_000, 50)])
 def test_canonical_targets_bit_exact(B, T, V, L):
     _say(f"canonical targets T={T} V={V} L={L}")
     w = Workload("canon", "bce", T, 64, V, "bf16", None, None, "uniform_any", L=L, pad_id=0, mask_frac=0.3, seed=9)

@@ -381,9 +381,185 @@ static bool radix_sort(const TargetsWs& w, int32_t* kA, int32_t* vA, int32_t* kB
   return inB;
 }
 
+// ---- small problems: the whole pipeline in one workgroup ---------------------------------
+// Up to kSmallPairs IDs and kSmallRows rows, the same steps run in LDS in one launch instead
+// of about twenty: the (item, row) pairs are sorted as 64-bit keys by a bitonic network
+// (equal keys are repeats of one pair, so the order matches the stable radix sorts), then
+// the unique pairs as (row, item) keys. Every output equals the multi-kernel pipeline's.
+constexpr int kSmallPairs = 4096;
+constexpr int kSmallRows = 8192;
+constexpr int kSmallThreads = 1024;
+
+// exclusive scan of s[0 .. n) in place, s[n] = total (n <= 8 * kSmallThreads); returns the total
+__device__ int small_scan(int* s, int n, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  constexpr int PER = 8;
+  int v[PER];
+  int sum = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = tid * PER + k;
+    v[k] = i < n ? s[i] : 0;
+    sum += v[k];
+  }
+  int x = sum;                                  // inclusive scan over the wave's threads
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wv] = x;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int k = 0; k < kSmallThreads / 64; ++k) {
+      const int c = wsum[k];
+      wsum[k] = run;
+      run += c;
+    }
+    wsum[kSmallThreads / 64] = run;
+  }
+  __syncthreads();
+  int base = wsum[wv] + x - sum;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = tid * PER + k;
+    if (i < n) s[i] = base;
+    base += v[k];
+  }
+  const int total = wsum[kSmallThreads / 64];
+  if (tid == 0) s[n] = total;
+  __syncthreads();
+  return total;
+}
+
+// ascending bitonic sort of a[0 .. N), N a power of two (entries past the data hold ~0)
+__device__ void small_sort(unsigned long long* a, int N) {
+  for (int k = 2; k <= N; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < N; i += kSmallThreads) {
+        const int l = i ^ j;
+        if (l > i) {
+          const unsigned long long x = a[i], y = a[l];
+          if ((x > y) == ((i & k) == 0)) {
+            a[i] = y;
+            a[l] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+}
+
+__device__ __forceinline__ int small_pow2(int n) {
+  int N = 2;
+  while (N < n) N <<= 1;
+  return N;
+}
+
+__global__ __launch_bounds__(kSmallThreads) void k_targets_small(int64_t T, int64_t V, int64_t nnz,
+                                                                 const int32_t* __restrict__ row_ptr,
+                                                                 const int32_t* __restrict__ ids,
+                                                                 const uint8_t* __restrict__ mask, int32_t pad,
+                                                                 const TargetsWs w) {
+  __shared__ int s_off[kSmallRows + 1];                 // entries per row, then row offsets
+  __shared__ int s_flag[kSmallPairs + 1];               // run starts, then their positions
+  __shared__ unsigned long long s_key[kSmallPairs];     // (item, row) keys, then (row, item)
+  __shared__ unsigned long long s_u[kSmallPairs];       // the unique (item, row) keys
+  __shared__ int s_wsum[kSmallThreads / 64 + 1];
+  const int tid = threadIdx.x;
+  const int nT = (int)T;
+  unsigned long long bad = 0;
+  // 1. valid entries per row (malformed rows: one data error, no entries), their offsets,
+  //    and the pairs in row order
+  for (int t = tid; t < nT; t += kSmallThreads) {
+    const int64_t b = row_ptr[t], e = row_ptr[t + 1];
+    int c = 0;
+    if (b < 0 || e > nnz || e < b) {
+      ++bad;
+    } else if (mask == nullptr || mask[t] != 0) {
+      for (int64_t i = b; i < e; ++i) {
+        const int32_t v = ids[i];
+        if (pad >= 0 && v == pad) continue;
+        if (v < 0 || (int64_t)v >= V) { ++bad; continue; }
+        ++c;
+      }
+    }
+    s_off[t] = c;
+  }
+  __syncthreads();
+  const int n0 = small_scan(s_off, nT, s_wsum);
+  const int n0c = (int64_t)n0 > nnz ? (int)nnz : n0;   // overlapping rows: the excess is an error
+  if (tid == 0 && n0c < n0) bad += (unsigned long long)(n0 - n0c);
+  for (int t = tid; t < nT; t += kSmallThreads) {
+    if (s_off[t + 1] == s_off[t]) continue;
+    const int64_t b = row_ptr[t], e = row_ptr[t + 1];
+    int64_t o = s_off[t];
+    for (int64_t i = b; i < e; ++i) {
+      const int32_t v = ids[i];
+      if (pad >= 0 && v == pad) continue;
+      if (v < 0 || (int64_t)v >= V) continue;
+      if (o >= nnz) break;
+      s_key[o] = ((unsigned long long)(uint32_t)v << 32) | (uint32_t)t;
+      ++o;
+    }
+  }
+  // 2. item-major order; the first of each run of equal keys is a unique pair
+  const int N0 = small_pow2(n0c);
+  for (int i = n0c + tid; i < N0; i += kSmallThreads) s_key[i] = ~0ull;
+  __syncthreads();
+  if (n0c > 1) small_sort(s_key, N0);
+  for (int i = tid; i < n0c; i += kSmallThreads) s_flag[i] = (i == 0 || s_key[i] != s_key[i - 1]) ? 1 : 0;
+  __syncthreads();
+  const int n = small_scan(s_flag, n0c, s_wsum);
+  for (int i = tid; i < n0c; i += kSmallThreads) {
+    if (i == 0 || s_key[i] != s_key[i - 1]) {
+      const int q = s_flag[i];
+      const unsigned long long k = s_key[i];
+      s_u[q] = k;
+      w.csc_items[q] = (int32_t)(k >> 32);
+      w.csc_rows[q] = (int32_t)(k & 0xffffffffull);
+    }
+  }
+  __syncthreads();
+  // 3. unique items and their segment starts
+  for (int j = tid; j < n; j += kSmallThreads) s_flag[j] = (j == 0 || (s_u[j] >> 32) != (s_u[j - 1] >> 32)) ? 1 : 0;
+  __syncthreads();
+  const int nu = small_scan(s_flag, n, s_wsum);
+  for (int j = tid; j < n; j += kSmallThreads) {
+    if (j == 0 || (s_u[j] >> 32) != (s_u[j - 1] >> 32)) {
+      w.uitems[s_flag[j]] = (int32_t)(s_u[j] >> 32);
+      w.useg[s_flag[j]] = j;
+    }
+  }
+  if (tid == 0) w.useg[nu] = n;
+  // 4. canonical CSR: the unique pairs by row, items ascending within a row
+  const int N1 = small_pow2(n);
+  for (int j = tid; j < N1; j += kSmallThreads)
+    s_key[j] = j < n ? ((s_u[j] & 0xffffffffull) << 32) | (s_u[j] >> 32) : ~0ull;
+  __syncthreads();
+  if (n > 1) small_sort(s_key, N1);
+  for (int j = tid; j < n; j += kSmallThreads) w.cids[j] = (int32_t)(s_key[j] & 0xffffffffull);
+  for (int j = tid; j <= n; j += kSmallThreads) {
+    const int r_prev = j == 0 ? -1 : (int)(s_key[j - 1] >> 32);
+    const int r_cur = j == n ? nT : (int)(s_key[j] >> 32);
+    for (int r = r_prev + 1; r <= r_cur; ++r) w.crow[r] = j;
+  }
+  if (tid == 0) {
+    w.counts[0] = n0c;
+    w.counts[1] = n;
+    w.counts[2] = nu;
+  }
+  if (bad) atomicAdd(w.err, bad);
+}
+
 hipError_t launch_targets(const TargetsWs& w, int64_t T, int64_t V, int64_t nnz,
                           const int32_t* row_ptr, const int32_t* ids, const uint8_t* mask, int32_t pad_id,
                           const int64_t* ce_target, int64_t ignore_index, hipStream_t st) {
+  if (ce_target == nullptr && nnz <= kSmallPairs && T <= kSmallRows) {
+    k_targets_small<<<1, kSmallThreads, 0, st>>>(T, V, nnz, row_ptr, ids, mask, pad_id, w);
+    return hipGetLastError();
+  }
   const int64_t cap = ce_target ? T : nnz;     // capacity of every pair array
   // 1. valid entries per row, their offsets, compacted (item, row) pairs in row order
   if (ce_target) {
