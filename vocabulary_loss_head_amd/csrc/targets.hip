@@ -451,6 +451,37 @@ __device__ void small_sort(unsigned long long* a, int N) {
     }
 }
 
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+  const int lo = __shfl_xor((int)(uint32_t)v, m, 64), hi = __shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// the same network for N <= kSmallThreads with one key per thread: exchanges between
+// lanes of one wave go through shuffles, wider ones through LDS, so only the steps with
+// partners 64 or more apart take barriers (10 of the 55 at N = 1024)
+__device__ void small_sort_lanes(unsigned long long* a, int N) {
+  const int i = threadIdx.x;
+  unsigned long long x = i < N ? a[i] : ~0ull;
+  for (int k = 2; k <= N; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      unsigned long long y;
+      if (j >= 64) {
+        if (i < N) a[i] = x;
+        __syncthreads();
+        y = i < N ? a[i ^ j] : ~0ull;
+        __syncthreads();
+      } else {
+        y = shfl_xor_u64(x, j);
+      }
+      // the lower index of a pair keeps the minimum in an ascending block, the maximum in
+      // a descending one; the upper index the other
+      const bool keep_min = ((i & j) == 0) == ((i & k) == 0);
+      x = keep_min ? (x < y ? x : y) : (x < y ? y : x);
+    }
+  if (i < N) a[i] = x;
+  __syncthreads();
+}
+
 __device__ __forceinline__ int small_pow2(int n) {
   int N = 2;
   while (N < n) N <<= 1;
@@ -466,10 +497,13 @@ __global__ __launch_bounds__(kSmallThreads) void k_targets_small(int64_t T, int6
   __shared__ int s_flag[kSmallPairs + 1];               // run starts, then their positions
   __shared__ unsigned long long s_key[kSmallPairs];     // (item, row) keys, then (row, item)
   __shared__ unsigned long long s_u[kSmallPairs];       // the unique (item, row) keys
+  __shared__ int32_t s_ids[kSmallPairs];                // the IDs, read once
   __shared__ int s_wsum[kSmallThreads / 64 + 1];
   const int tid = threadIdx.x;
   const int nT = (int)T;
   unsigned long long bad = 0;
+  for (int i = tid; i < (int)nnz; i += kSmallThreads) s_ids[i] = ids[i];
+  __syncthreads();
   // 1. valid entries per row (malformed rows: one data error, no entries), their offsets,
   //    and the pairs in row order
   for (int t = tid; t < nT; t += kSmallThreads) {
@@ -479,7 +513,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_targets_small(int64_t T, int6
       ++bad;
     } else if (mask == nullptr || mask[t] != 0) {
       for (int64_t i = b; i < e; ++i) {
-        const int32_t v = ids[i];
+        const int32_t v = s_ids[i];
         if (pad >= 0 && v == pad) continue;
         if (v < 0 || (int64_t)v >= V) { ++bad; continue; }
         ++c;
@@ -496,7 +530,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_targets_small(int64_t T, int6
     const int64_t b = row_ptr[t], e = row_ptr[t + 1];
     int64_t o = s_off[t];
     for (int64_t i = b; i < e; ++i) {
-      const int32_t v = ids[i];
+      const int32_t v = s_ids[i];
       if (pad >= 0 && v == pad) continue;
       if (v < 0 || (int64_t)v >= V) continue;
       if (o >= nnz) break;
@@ -508,7 +542,10 @@ __global__ __launch_bounds__(kSmallThreads) void k_targets_small(int64_t T, int6
   const int N0 = small_pow2(n0c);
   for (int i = n0c + tid; i < N0; i += kSmallThreads) s_key[i] = ~0ull;
   __syncthreads();
-  if (n0c > 1) small_sort(s_key, N0);
+  if (n0c > 1) {
+    if (N0 <= kSmallThreads) small_sort_lanes(s_key, N0);
+    else small_sort(s_key, N0);
+  }
   for (int i = tid; i < n0c; i += kSmallThreads) s_flag[i] = (i == 0 || s_key[i] != s_key[i - 1]) ? 1 : 0;
   __syncthreads();
   const int n = small_scan(s_flag, n0c, s_wsum);
@@ -538,7 +575,10 @@ __global__ __launch_bounds__(kSmallThreads) void k_targets_small(int64_t T, int6
   for (int j = tid; j < N1; j += kSmallThreads)
     s_key[j] = j < n ? ((s_u[j] & 0xffffffffull) << 32) | (s_u[j] >> 32) : ~0ull;
   __syncthreads();
-  if (n > 1) small_sort(s_key, N1);
+  if (n > 1) {
+    if (N1 <= kSmallThreads) small_sort_lanes(s_key, N1);
+    else small_sort(s_key, N1);
+  }
   for (int j = tid; j < n; j += kSmallThreads) w.cids[j] = (int32_t)(s_key[j] & 0xffffffffull);
   for (int j = tid; j <= n; j += kSmallThreads) {
     const int r_prev = j == 0 ? -1 : (int)(s_key[j - 1] >> 32);
