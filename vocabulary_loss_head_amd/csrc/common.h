@@ -57,6 +57,12 @@ __device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
 }
+// The same copy with the non-temporal hint, for data read once in a pass (the E stream of
+// the small-row heads): it is kept from displacing data the next kernel reads again.
+__device__ __forceinline__ void lds_dma16_nt(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :: "v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
+}
 __device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                :: "v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(512, 1) void k_logits_rows(const LogitsRowsParams p
       const int kb = wv + 8 * x;
       if (kb >= NC) break;
       const uint32_t src = crow[x] >= 0 ? (uint32_t)(min(crow[x], rmax) * D + ccol[x]) : 0u;
-      lds_dma16(base, src, l0 + (uint32_t)(q * EB + kb * 1024));
+      lds_dma16_nt(base, src, l0 + (uint32_t)(q * EB + kb * 1024));
     }
   };
   // wait until block k's copies are in: n later blocks' copies (ncp each) may stay in flight

@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       // LDS piece lane & 7 of row 8 wv + (lane >> 3) holds the row's piece (lane & 7) ^ (lane >> 3)
       int64_t v = vb + 8 * wv + (lane >> 3);
       v = v < p.V ? v : p.V - 1;
-      lds_dma16(p.E + vb * D, (uint32_t)((v - vb) * D + c0 + 16 * ((lane & 7) ^ (lane >> 3))),
+      lds_dma16_nt(p.E + vb * D, (uint32_t)((v - vb) * D + c0 + 16 * ((lane & 7) ^ (lane >> 3))),
                 l0 + (uint32_t)(kOffE + q * kEImg + wv * 1024));
     }
     {
@@ -253,7 +253,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         rr = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, rr, true);
         o[k4] = (uint32_t)rr;
       }
-      *(uint4*)(p.E + v * D + c0 + 16 * pc) = uint4{o[0], o[1], o[2], o[3]};
+      // each E piece is written once per pass: stored with the non-temporal hint, as it is read
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, (u32x4*)(p.E + v * D + c0 + 16 * pc));
     }
     __syncthreads();                             // buffer q and the stage are free again
     q ^= 1;
