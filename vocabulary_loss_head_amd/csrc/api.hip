@@ -243,7 +243,8 @@ ChunkPlan make_chunk_plan(int64_t T, int64_t D, int64_t V, int64_t cap, bool q8 
   if (sk < 1) sk = 1;
   c.kps = round_up(ceil_div(vc, sk), 32);
   c.sk = ceil_div(vc, c.kps);
-  c.sk_rows = e_fp8 && cl::sgd_rows_supported(c.Tp, D) ? cl::sgd_rows_dA_splits(ceil_div(std::min(vc, V), 32), D) : 0;
+  // (the nearest-even shape has the most block rows, so its count bounds both roundings)
+  c.sk_rows = e_fp8 && cl::sgd_rows_supported(c.Tp, D) ? cl::sgd_rows_dA_splits(ceil_div(std::min(vc, V), 32), D, 0) : 0;
   c.flag_bn = cl::gemm_tile_n_of(cl::GEMM_EPI_CE_P, vc, T > 0 ? T : 1, D);
   c.flag_ld = ceil_div(T > 0 ? T : 1, c.flag_bn);
   return c;
@@ -525,6 +526,7 @@ struct ChunkJob {
   const void* A_dE;      // the dE product's activations operand (NULL: A)
   const uint16_t* AwT;   // non-NULL: the SGD product runs as whole-row updates (sgd_rows.hip)
   bool rows_dA;          // with AwT: that product also forms the dA partials (no separate dA product)
+  int64_t dA_splits;     // rows_dA: its partial count
   bool rows_logits;      // the BCE logits product streams 32-item blocks (logits_rows.hip)
   int k3_epi;            // -1: none, GEMM_EPI_DE or GEMM_EPI_SGD
   const int32_t* uitems; const int32_t* counts; const float* S_u; const int32_t* imap;
@@ -598,8 +600,9 @@ cutloss_status run_chunks(const ChunkJob& j, hipStream_t st) {
       cl::SgdRowsParams s{};
       s.V = pl.V; s.v0 = v0; s.nblk = ceil_div(vlen, 32); s.D = (int)pl.D;
       s.P = j.P; s.AwT = j.AwT; s.S_u = j.S_u; s.imap = j.imap; s.E = (uint8_t*)j.E; s.lr = j.lr;
+      s.sr = j.sr; s.sr_seed = j.sr_seed;
       if (j.rows_dA) {
-        s.T = pl.T; s.dA_part = j.part_dA; s.dA_splits = pl.sk_rows; s.dA_first = c == 0;
+        s.T = pl.T; s.dA_part = j.part_dA; s.dA_splits = j.dA_splits; s.dA_first = c == 0;
       }
       CL_HIP(cl::launch_sgd_rows(s, st), "chunk SGD rows");
     } else if (j.k3_epi >= 0) {
@@ -629,11 +632,11 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
   const int e_fp8 = p->e_dtype == CUTLOSS_FP8_E4M3;
   const Ws2 w = carve_chunked(ws, pl, grad, dA != nullptr, dE_mode != 0, counts != nullptr, true, !e_fp8);
   CL_TRY(check_ws(ws, ws_bytes, w.bytes));
-  // FP8 SGD with nearest-even rounding over at most 128 rows: whole-row updates, which also
-  // form the dA partials from the E they read before updating it
-  const bool sgd_rows = dE_mode == 2 && e_fp8 && sr == 0 && w.AwT != nullptr;
+  // FP8 SGD over at most 128 rows (either rounding): whole-row updates, which also form the
+  // dA partials from the E they read before updating it
+  const bool sgd_rows = dE_mode == 2 && e_fp8 && w.AwT != nullptr;
   const bool rows_dA = sgd_rows && dA != nullptr && pl.sk_rows > 0;
-  const int64_t n_dA = rows_dA ? pl.sk_rows : pl.sk;
+  const int64_t n_dA = rows_dA ? cl::sgd_rows_dA_splits(ceil_div(std::min(pl.Vc, pl.V), 32), pl.D, sr) : pl.sk;
   {
     Phase ph(CUTLOSS_PHASE_TARGETS, st);
     CL_HIP(cl::launch_zero_u64(w.err, 4, st), "zero counters");
@@ -674,6 +677,7 @@ cutloss_status bce_run_chunked(const cutloss_bce_problem* p, const float* dloss,
   j.A_dE = dE_mode != 0 ? w.Aw : nullptr;
   j.AwT = sgd_rows ? w.AwT : nullptr;
   j.rows_dA = rows_dA;
+  j.dA_splits = n_dA;
   j.k1_epi = grad ? cl::GEMM_EPI_BCE_P : (counts ? cl::GEMM_EPI_BCE_METRICS : cl::GEMM_EPI_BCE_LOSS);
   // FP8 E over at most 128 rows (BCE loss, with P or with the metrics' counts): the
   // streaming logits product

@@ -77,7 +77,7 @@ int gemm_tile_n_of(int epi, int64_t M, int64_t N, int64_t D);   // 128 or 256 fo
 
 // ----------------------------------------------------------------------------------
 // FP8 SGD product for heads of at most 128 rows (sgd_rows.hip): E <- E4M3(E - lr (P^T A_w
-// - S)) with nearest-even rounding, whole E rows of 32 items per workgroup.
+// - S)) with nearest-even or stochastic rounding, whole E rows of 32 items per workgroup.
 // ----------------------------------------------------------------------------------
 struct SgdRowsParams {
   int64_t V;             // items; rows at or past V are neither read for real nor written
@@ -90,6 +90,7 @@ struct SgdRowsParams {
   const int32_t* imap;   // [V] item -> unique-item index, -1 for none
   uint8_t* E;            // [V][D] E4M3FN, updated in place
   float lr;
+  int sr; uint64_t sr_seed;   // stochastic rounding keyed by (sr_seed, v, d) when sr != 0, else nearest-even
   // dA (optional): dA_part[r][t][d] (r < dA_splits, t < T) += sum over the items that block
   // row r of the chunk covers of P[t][v] E[v][d], E read before its update; dA_first: the
   // chunk starts the sums (its partials are stored, not added to). NULL: no dA.
@@ -100,7 +101,7 @@ struct SgdRowsParams {
 };
 bool sgd_rows_supported(int64_t Tp, int64_t D);   // Tp: rows of the gradient tile (128)
 // the dA partials of a head whose first chunk has nblk 32-item blocks: one per block row
-int64_t sgd_rows_dA_splits(int64_t nblk, int64_t D);
+int64_t sgd_rows_dA_splits(int64_t nblk, int64_t D, int sr);
 
 // ----------------------------------------------------------------------------------
 // BCE logits product for FP8 E and heads of at most 128 rows (logits_rows.hip): loss

@@ -26,6 +26,7 @@
 //    over from one chunk to the next (loaded at the start, stored at the end), so that the
 //    separate dA product and its second pass over E and P are not needed.
 #include "launch.h"
+#include "sr.h"
 
 #include <algorithm>
 
@@ -88,7 +89,9 @@ __global__ __launch_bounds__(256) void k_weighted_t(const uint16_t* __restrict__
 // consecutive workgroups go to the eight XCDs in turn, so when R is a multiple of 8 the
 // slices of row r are workgroups 8 i + r % 8 (one XCD, one L2) and each P block comes from
 // HBM once.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_sgd_rows(const SgdRowsParams p) {
+// SR: stochastic rounding (the uniforms' Philox work needs registers: two waves per SIMD)
+template <bool SR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SR ? 2 : 3))) void k_sgd_rows(const SgdRowsParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[kLds];
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -239,16 +242,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       const uint4 e = *(const uint4*)(lds + kOffE + q * kEImg + it * kSgdCols + 16 * (pc ^ (it & 7)));
       const uint32_t w4[4] = {e.x, e.y, e.z, e.w};
       uint32_t o[4];
+      uint32_t hw[8];                            // SR: the uniforms of columns c0 + 16 pc .. + 15
+      if constexpr (SR) sr_uniforms16(p.sr_seed, v, c0 + 16 * pc, hw);
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) {
-        // two E4M3 values per conversion; the clamp to +-448 keeps the hardware conversion
-        // from turning |x| > 464 into NaN (saturating nearest-even)
+        // two E4M3 values per conversion; nearest-even: the clamp to +-448 keeps the hardware
+        // conversion from turning |x| > 464 into NaN (saturating); stochastic: the rounded
+        // values lie on the grid, so the conversion is exact
         const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w4[k4], false);
         const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w4[k4], true);
-        const float e0 = __builtin_amdgcn_fmed3f(__builtin_fmaf(-p.lr, g[4 * k4], lo[0]), -kFp8Max, kFp8Max);
-        const float e1 = __builtin_amdgcn_fmed3f(__builtin_fmaf(-p.lr, g[4 * k4 + 1], lo[1]), -kFp8Max, kFp8Max);
-        const float e2 = __builtin_amdgcn_fmed3f(__builtin_fmaf(-p.lr, g[4 * k4 + 2], hi[0]), -kFp8Max, kFp8Max);
-        const float e3 = __builtin_amdgcn_fmed3f(__builtin_fmaf(-p.lr, g[4 * k4 + 3], hi[1]), -kFp8Max, kFp8Max);
+        const float y0 = __builtin_fmaf(-p.lr, g[4 * k4], lo[0]), y1 = __builtin_fmaf(-p.lr, g[4 * k4 + 1], lo[1]);
+        const float y2 = __builtin_fmaf(-p.lr, g[4 * k4 + 2], hi[0]), y3 = __builtin_fmaf(-p.lr, g[4 * k4 + 3], hi[1]);
+        float e0, e1, e2, e3;
+        if constexpr (SR) {
+          e0 = sr_fp8(y0, sr_h16(hw, 4 * k4));
+          e1 = sr_fp8(y1, sr_h16(hw, 4 * k4 + 1));
+          e2 = sr_fp8(y2, sr_h16(hw, 4 * k4 + 2));
+          e3 = sr_fp8(y3, sr_h16(hw, 4 * k4 + 3));
+        } else {
+          e0 = __builtin_amdgcn_fmed3f(y0, -kFp8Max, kFp8Max);
+          e1 = __builtin_amdgcn_fmed3f(y1, -kFp8Max, kFp8Max);
+          e2 = __builtin_amdgcn_fmed3f(y2, -kFp8Max, kFp8Max);
+          e3 = __builtin_amdgcn_fmed3f(y3, -kFp8Max, kFp8Max);
+        }
         int rr = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
         rr = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, rr, true);
         o[k4] = (uint32_t)rr;
@@ -277,8 +293,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 
 bool sgd_rows_supported(int64_t Tp, int64_t D) { return Tp == kSgdRows && D % 128 == 0 && D >= 128 && D <= 1024; }
 
-int64_t sgd_rows_dA_splits(int64_t nblk, int64_t D) {
-  return std::max<int64_t>(1, std::min<int64_t>(nblk, 768 / std::max<int64_t>(1, D / kSgdCols)));
+// block rows of workgroups: three workgroups per CU (two with stochastic rounding), a
+// multiple of 8 where there are that many, so that a row's slices share an XCD
+static int64_t sgd_rows_max(int64_t ns, int sr) {
+  const int64_t r = (sr ? 512 : 768) / ns;
+  return r >= 8 ? r / 8 * 8 : r;
+}
+
+int64_t sgd_rows_dA_splits(int64_t nblk, int64_t D, int sr) {
+  return std::max<int64_t>(1, std::min<int64_t>(nblk, sgd_rows_max(std::max<int64_t>(1, D / kSgdCols), sr)));
 }
 
 hipError_t launch_weighted_transpose(const void* A, const float* w, int64_t T, int64_t D, uint16_t* AwT,
@@ -295,16 +318,18 @@ hipError_t launch_sgd_rows(const SgdRowsParams& p, hipStream_t st) {
     return hipErrorInvalidValue;
   // every block starts inside the vocabulary (the copies address rows relative to it)
   if (p.v0 + (p.nblk - 1) * kSgdItems >= p.V) return hipErrorInvalidValue;
-  // about three workgroups per CU (51 KB of LDS each), every slice with the same block rows
+  // about three workgroups per CU (51 KB of LDS each; two with stochastic rounding), every
+  // slice with the same block rows
   const int64_t ns = p.D / kSgdCols;
-  int64_t rows = std::max<int64_t>(1, std::min<int64_t>(p.nblk, 768 / ns));
+  int64_t rows = std::max<int64_t>(1, std::min<int64_t>(p.nblk, sgd_rows_max(ns, p.sr)));
   if (p.dA_part != nullptr) {
     // one dA partial per block row: the first chunk writes every one of them
-    if (p.T < 1 || p.T > kSgdRows || p.dA_splits < 1 || p.dA_splits > 768 / ns) return hipErrorInvalidValue;
+    if (p.T < 1 || p.T > kSgdRows || p.dA_splits < 1 || p.dA_splits > sgd_rows_max(ns, p.sr)) return hipErrorInvalidValue;
     if (p.dA_first && p.nblk < p.dA_splits) return hipErrorInvalidValue;
     rows = std::min<int64_t>(p.nblk, p.dA_splits);
   }
-  k_sgd_rows<<<(unsigned)(ns * rows), 256, 0, st>>>(p);
+  if (p.sr) k_sgd_rows<true><<<(unsigned)(ns * rows), 256, 0, st>>>(p);
+  else k_sgd_rows<false><<<(unsigned)(ns * rows), 256, 0, st>>>(p);
   return hipGetLastError();
 }
 
