@@ -17,7 +17,7 @@ from oracle.stochastic import decode, sr_round, uniform16
 from workloads import make, workload
 from workloads.gen import Workload
 
-from gpu_util import canonical, check_loss, decode_inputs, upload
+from gpu_util import bf16_to_f64, canonical, check_grad, check_loss, decode_inputs, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -32,13 +32,14 @@ def _say(msg):
     print(f"[case] {msg}", flush=True)
 
 
-def _run_sr(B, g, w, seed, lr, want_loss=False):
+def _run_sr(B, g, w, seed, lr, want_loss=False, want_dA=False):
     prob = B.bce_problem(g["A"], g["E"], g["row_ptr"], g["ids"], g["mask"], w.pad_id)
     ws = B.workspace(B.cutloss_bce_workspace_size(prob, B.OP_BWD_SGD_EX), g["A"].device)
     loss = torch.empty(w.T, dtype=torch.float32, device=g["A"].device) if want_loss else None
-    B.cutloss_bce_bwd_sgd_ex(prob, None, lr, None, loss, ws, stochastic=True, seed=seed)
+    dA = torch.empty(w.T, w.D, dtype=torch.bfloat16, device=g["A"].device) if want_dA else None
+    B.cutloss_bce_bwd_sgd_ex(prob, None, lr, dA, loss, ws, stochastic=True, seed=seed)
     torch.cuda.synchronize()
-    return loss
+    return (loss, dA) if want_dA else loss
 
 
 def _codes(t: torch.Tensor, fmt):
@@ -76,9 +77,11 @@ def test_sr_sgd_small(B, fmt, D, monkeypatch):
     crow, cids, _ = canonical(inp, w.V, -1)
     g = upload(inp)
     seed = 0x0123456789ABCDEF + D
-    loss = _run_sr(B, g, w, seed, w.lr, want_loss=True)
-    _, dE_ref = H.bce_grads(A64, E64, crow, cids, inp["mask"])
+    # dA is formed from E before the update (for FP8 E at most 128 rows: inside the SGD pass)
+    loss, dA = _run_sr(B, g, w, seed, w.lr, want_loss=True, want_dA=True)
+    dA_ref, dE_ref = H.bce_grads(A64, E64, crow, cids, inp["mask"])
     check_loss(loss.cpu().numpy(), H.bce_loss(A64, E64, crow, cids, inp["mask"]), what="sr sgd loss")
+    check_grad(bf16_to_f64(dA), dA_ref, "sr sgd dA")
     _check_sr(_codes(g["E"], fmt), inp["E"], np.arange(w.V), dE_ref, w.lr, seed, fmt)
 
 
