@@ -134,6 +134,97 @@ def test_canonical_targets_bit_exact(B, T, V, L):
     assert B.cutloss_read_data_errors(ws) == n_bad and n_bad > 0
 
 
+def _targets_model(row_ptr, ids, mask, V, pad, nnz):
+    """The canonicalization's documented handling of malformed input, row by row: a row with
+    b < 0, e > nnz or e < b is one data error and has no positives; IDs outside [0, V) are
+    errors; valid entries are laid out in row order and cut at nnz (overlapping rows of a
+    non-monotone row_ptr), the excess counted as errors; repeats count once."""
+    T = len(row_ptr) - 1
+    cnt, bad = [], 0
+    for t in range(T):
+        b, e = int(row_ptr[t]), int(row_ptr[t + 1])
+        if b < 0 or e > nnz or e < b:
+            bad += 1
+            cnt.append(0)
+            continue
+        c = 0
+        if mask[t]:
+            for i in range(b, e):
+                v = int(ids[i])
+                if pad >= 0 and v == pad:
+                    continue
+                if v < 0 or v >= V:
+                    bad += 1
+                    continue
+                c += 1
+        cnt.append(c)
+    off = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int64)
+    pairs = [None] * nnz
+    for t in range(T):
+        if cnt[t] == 0:
+            continue
+        o = int(off[t])
+        for i in range(int(row_ptr[t]), int(row_ptr[t + 1])):
+            v = int(ids[i])
+            if (pad >= 0 and v == pad) or v < 0 or v >= V:
+                continue
+            if o >= nnz:
+                break
+            pairs[o] = (v, t)
+            o += 1
+    total = int(off[-1])
+    n0 = min(total, nnz)
+    bad += total - n0
+    uniq = sorted(set(pairs[:n0]))                        # (item, row)
+    by_row = sorted((r, v) for v, r in uniq)
+    crow = np.zeros(T + 1, dtype=np.int64)
+    for r, _ in by_row:
+        crow[r + 1] += 1
+    crow = np.cumsum(crow)
+    cids = np.array([v for _, v in by_row], dtype=np.int64)
+    items = np.array([v for v, _ in uniq], dtype=np.int64)
+    rows = np.array([r for _, r in uniq], dtype=np.int64)
+    return crow, cids, items, rows, bad
+
+
+# malformed rows (e < b, e > nnz) and overlapping rows whose entries exceed nnz: the
+# single-workgroup path (500 IDs) and the radix pipeline (6,000 IDs) give the model's result
+@pytest.mark.parametrize("T,L", [(50, 10), (600, 10)])
+def test_canonical_targets_malformed_rows(B, T, L):
+    _say(f"canonical targets, malformed rows T={T} L={L}")
+    rng = np.random.default_rng(31 + T)
+    V = 4000
+    lens = rng.integers(0, 2 * L, size=T)
+    lens[0] = 2 * L
+    lens[-1] = 0
+    row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    nnz = int(row_ptr[-1])
+    ids = rng.integers(-2, V + 3, size=nnz).astype(np.int32)
+    k = T // 5
+    row_ptr[k] = row_ptr[k + 1] + 20                      # row k - 1 overlaps, row k has e < b
+    row_ptr[T] = nnz + 5                                  # the last row ends past nnz
+    mask = np.ones(T, dtype=np.uint8)                     # every row counts, so the overlap exceeds nnz
+    dev = torch.device("cuda:0")
+    A = torch.zeros(T, 64, dtype=torch.bfloat16, device=dev)
+    E = torch.zeros(V, 64, dtype=torch.bfloat16, device=dev)
+    g_rp = torch.from_numpy(row_ptr).to(dev)
+    g_ids = torch.from_numpy(ids).to(dev)
+    g_mask = torch.from_numpy(mask).to(dev)
+    prob = B.bce_problem(A, E, g_rp, g_ids, g_mask, 0)
+    ws = B.workspace(B.cutloss_bce_workspace_size(prob, B.OP_BWD), dev)
+    crow = torch.empty(T + 1, dtype=torch.int32, device=dev)
+    cids, items, rows = (torch.empty(nnz, dtype=torch.int32, device=dev) for _ in range(3))
+    nu = B.cutloss_bce_canonical_targets(prob, crow, cids, items, rows, ws)
+    ref_crow, ref_cids, ref_items, ref_rows, ref_bad = _targets_model(row_ptr, ids, mask, V, 0, nnz)
+    assert ref_bad >= 10                                  # two malformed rows and the entries cut at nnz
+    assert nu == len(ref_cids)
+    assert np.array_equal(crow.cpu().numpy(), ref_crow)
+    assert np.array_equal(cids.cpu().numpy()[:nu], ref_cids)
+    assert np.array_equal(items.cpu().numpy()[:nu], ref_items)
+    assert np.array_equal(rows.cpu().numpy()[:nu], ref_rows)
+    assert B.cutloss_read_data_errors(ws) == ref_bad
+
+
 def test_determinism(B):
     _say("determinism")
     w = Workload("det", "bce", 200, 256, 9000, "bf16", None, None, "zipf", L=8, pad_id=0, mask_frac=0.1, seed=11)
