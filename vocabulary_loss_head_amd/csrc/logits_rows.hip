@@ -10,10 +10,11 @@
 //  * a workgroup has eight waves: wave w holds rows 32 (w % 4) .. + 32 of A over one half of D
 //    in registers as the MFMA's B operand (D/8 VGPRs: 96 at D = 768), one workgroup per CU;
 //  * persistent workgroups walk the chunk's 32-item blocks. A block's E rows (32 x D bytes)
-//    are copied into LDS with global_load_lds two blocks ahead, into three buffers, at a
-//    row stride of D + 16 bytes, so that the fragment reads of the 32 items spread over the
-//    banks and every read is a per-lane base plus an immediate;
-//  * a wave widens each 8-byte fragment of its half (four instructions for 8 values) and
+//    are copied into LDS with global_load_lds up to four blocks ahead, into as many buffers
+//    as fit, at a row stride of D + 16 bytes (an odd number of 16-byte bank slots), so that
+//    the 16-byte fragment reads of 16 items at once meet distinct banks and every read is a
+//    per-lane base plus an immediate;
+//  * a wave widens each 8-byte half of a fragment (four instructions for 8 values) and
 //    issues D/32 MFMAs per block; the two halves of a row quarter then exchange partial
 //    logits through LDS, so that each finishes 16 of the 32 items;
 //  * each lane sums its row's softplus terms in registers across blocks (the log taken once
@@ -84,11 +85,14 @@ __global__ __launch_bounds__(512, 1) void k_logits_rows(const LogitsRowsParams p
       if constexpr (CNT) p.part_b[(p.part_base + sl) * p.T + r] = 0.0f;
     }
 
-  // the held B operand: row t of A, columns DH dh + 16 ks + 8 h .. + 8 (zero past T)
+  // the held B operand: row t of A; k step ks takes columns DH dh + 32 (ks / 2) + 16 h +
+  // 8 (ks % 2) .. + 8 (zero past T), so that one 16-byte fragment read of E serves a pair of
+  // k steps (the same k order on both operands)
   bf16x8 ast[KH];
 #pragma unroll
   for (int ks = 0; ks < KH; ++ks)
-    ast[ks] = t_ok ? *(const bf16x8*)(p.A + (int64_t)t * D + DH * dh + 16 * ks + 8 * h) : bf16x8{};
+    ast[ks] = t_ok ? *(const bf16x8*)(p.A + (int64_t)t * D + DH * dh + 32 * (ks >> 1) + 16 * h + 8 * (ks & 1))
+                   : bf16x8{};
 
   // copies of block bb into buffer q, copy kb = wv + 8 x: image byte o holds item o / ER,
   // byte o % ER of its row (the pad bytes and the bytes past the image fetch the block's
@@ -153,16 +157,22 @@ __global__ __launch_bounds__(512, 1) void k_logits_rows(const LogitsRowsParams p
     wait_for(min(LA, left));
     __syncthreads();
   };
-  // the wave's half of block b's logits: A operand item l32, columns DH dh + 16 ks + 8 h .. + 8
+  // the wave's half of block b's logits, item l32 as the A operand
   auto product = [&]() {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const uint32_t eb = l0 + (uint32_t)(q * EB + l32 * ER + DH * dh + 8 * h);
-    u32x2 raw[KH];                               // every fragment read is issued up front
+    // lane (item l32, half h) reads 16 bytes, columns DH dh + 32 s + 16 h .. + 16, for k steps
+    // 2 s and 2 s + 1: 16 lanes a cycle, 16 rows whose stride (D + 16 bytes, an odd number of
+    // 16-byte slots) puts them in distinct banks
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const uint32_t eb = l0 + (uint32_t)(q * EB + l32 * ER + DH * dh + 16 * h);
+    u32x4 raw[KH / 2];                           // every fragment read is issued up front
 #pragma unroll
-    for (int ks = 0; ks < KH; ++ks) raw[ks] = *(const CL_LDS u32x2*)(uintptr_t)(eb + (uint32_t)(16 * ks));
+    for (int s2 = 0; s2 < KH / 2; ++s2) raw[s2] = *(const CL_LDS u32x4*)(uintptr_t)(eb + (uint32_t)(32 * s2));
     f32x16 acc = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KH; ++ks) acc = mfma32(fp8x8_to_bf16x8(uint2{raw[ks][0], raw[ks][1]}), ast[ks], acc);
+    for (int ks = 0; ks < KH; ++ks) {
+      const u32x4& r = raw[ks >> 1];
+      acc = mfma32(fp8x8_to_bf16x8((ks & 1) ? uint2{r[2], r[3]} : uint2{r[0], r[1]}), ast[ks], acc);
+    }
     return acc;
   };
   // result register i holds item 8 (i >> 2) + 4 h + (i & 3): half dh keeps items
