@@ -37,8 +37,12 @@ namespace {
 constexpr int kSgdItems = 32;                      // items per block
 constexpr int kSgdRows = 128;                      // rows (k) of a gradient-tile block
 constexpr int kSgdCols = 128;                      // columns of a workgroup's slice (4 waves x 32)
-constexpr int kPRow = 2 * kSgdItems + 16;          // LDS stride of a block row (bytes)
-constexpr int kPImg = 12 * 1024;                   // LDS image of a block: 10 KB used, 3 copies a wave
+// LDS image of a gradient-tile block: rows of 64 bytes, unpadded, the 16-byte piece c of row
+// r stored at piece c ^ ((r / 4) mod 4). The transposed reads of the SGD product take 4
+// consecutive rows per half-wave (256 bytes, every bank once); the dA product's 16-byte reads
+// take 16 consecutive rows, which the XOR spreads over the 16 slots.
+constexpr int kPRow = 2 * kSgdItems;
+constexpr int kPImg = kSgdRows * kPRow;            // 8 KB, two copies a wave
 // the items' slices of E: 32 rows of 128 bytes, the 16-byte piece c of row v stored at piece
 // c ^ (v & 7) of the row, so that the transposed reads (8 rows, one piece) meet 8 bank groups
 constexpr int kEImg = kSgdItems * kSgdCols;
@@ -48,7 +52,7 @@ constexpr int kOffE = 2 * kPImg;
 constexpr int kOffMap = kOffE + 2 * kEImg;
 constexpr int kOffStage = kOffMap + 2 * kMapImg;
 constexpr int kLds = kOffStage + kSgdItems * kStageRow;
-constexpr int kCopies = 5;                         // copy instructions a wave issues per block
+constexpr int kCopies = 4;                         // copy instructions a wave issues per block
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p) { return (uint32_t)(uintptr_t)p; }
 
@@ -139,19 +143,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SR ? 2 : 3)
         }
       }
     }
-  // copies of block jb into buffer q, kCopies per wave: image byte o of the P block holds
-  // row o / kPRow, byte o % kPRow (pad bytes fetch byte 0); wave wv copies the 128-byte
-  // slices of items 8 wv .. 8 wv + 7 and (in its own slot) the 32 items' indices. Rows
-  // past V fetch row V - 1 and are not written back.
+  // copies of block jb into buffer q, kCopies per wave: image piece c' of row r holds the
+  // block's piece c' ^ ((r / 4) mod 4) of that row; wave wv copies the 128-byte slices of
+  // items 8 wv .. 8 wv + 7 and (in its own slot) the 32 items' indices. Rows past V fetch
+  // row V - 1 and are not written back.
   auto issue = [&](int64_t jb, int q) {
     const uint16_t* blk = p.P + jb * (kSgdRows * kSgdItems);
 #pragma unroll
-    for (int x = 0; x < 3; ++x) {
+    for (int x = 0; x < kPImg / 4096; ++x) {
       const int kb = wv + 4 * x;
       const int o = kb * 1024 + 16 * lane;
-      const int r = o / kPRow, c = o - r * kPRow;
-      const uint32_t src = (r < kSgdRows && c < 2 * kSgdItems) ? (uint32_t)(r * 2 * kSgdItems + c) : 0u;
-      lds_dma16(blk, src, l0 + (uint32_t)(q * kPImg + kb * 1024));
+      const int r = o / kPRow, c = (o % kPRow) / 16;
+      lds_dma16(blk, (uint32_t)(r * kPRow + 16 * (c ^ ((r >> 2) & 3))), l0 + (uint32_t)(q * kPImg + kb * 1024));
     }
     const int64_t vb = p.v0 + jb * kSgdItems;
     {
@@ -173,13 +176,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SR ? 2 : 3)
   issue(j, 0);
   const int s = lane & 15;
   // transposed reads of a block: lane (item l32) receives rows 8 h + m and 8 h + 4 + m
-  // (m = 0..3) of k step ks, from the 16-lane group's row and item offsets
-  const uint32_t ta0 = (uint32_t)((8 * h + (s >> 2)) * kPRow + 2 * (4 * (s & 3) + 16 * ((lane >> 4) & 1)));
+  // (m = 0..3) of k step ks, from the 16-lane group's row and item offsets: byte
+  // 8 (s & 3) + 32 g of the row (g = (lane >> 4) & 1), i.e. piece (s & 3) / 2 + 2 g, which
+  // those rows store at that piece ^ 2h and ^ (2h + 1)
+  const int tpc = ((s & 3) >> 1) + 2 * ((lane >> 4) & 1);
+  const uint32_t ta0 = (uint32_t)((8 * h + (s >> 2)) * kPRow + 16 * (tpc ^ (2 * h)) + 8 * (s & 1));
+  const uint32_t tb0 = (uint32_t)((8 * h + 4 + (s >> 2)) * kPRow + 16 * (tpc ^ (2 * h + 1)) + 8 * (s & 1));
   const int it = tid >> 3, pc = tid & 7;         // the update's item and 16-column piece
   // dA operands: the block's rows 64 th + 32 mt + l32 at items 16 ks + 8 h (16 bytes), and
   // the E slice read transposed: in 16-lane group gq, lane s addresses item row
   // 16 ks + 8 h + (s >> 1), bytes 8 (s & 1) of piece 4 dh + 2 nt + (gq & 1) (swizzled)
-  const uint32_t pa0 = (uint32_t)((64 * th + l32) * kPRow + 2 * 8 * h);
+  const uint32_t pa0 = (uint32_t)((64 * th + l32) * kPRow);
+  const int pfl = (l32 >> 2) & 3;                // the rows' piece XOR
+  const uint32_t pk0 = (uint32_t)(16 * (h ^ pfl)), pk1 = (uint32_t)(16 * ((2 + h) ^ pfl));
   const uint32_t eb0 = (uint32_t)((8 * h + (s >> 1)) * kSgdCols + 8 * (s & 1));
   const int epc = 4 * dh + ((lane >> 4) & 1);
   int q = 0;
@@ -189,12 +198,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SR ? 2 : 3)
     if (more) wait_vm<kCopies>(); else wait_vm<0>();
     __syncthreads();                             // block j's copies are visible
 
-    const uint32_t ta = l0 + (uint32_t)(q * kPImg) + ta0;
+    const uint32_t ta = l0 + (uint32_t)(q * kPImg) + ta0, tb = l0 + (uint32_t)(q * kPImg) + tb0;
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < kSgdRows / 16; ++ks) {
-      const bf16x8 a = cat_bf16(read_tr16(ta + (uint32_t)(16 * ks * kPRow)),
-                                read_tr16(ta + (uint32_t)((16 * ks + 4) * kPRow)));
+      const bf16x8 a = cat_bf16(read_tr16(ta + (uint32_t)(16 * ks * kPRow)), read_tr16(tb + (uint32_t)(16 * ks * kPRow)));
       acc = mfma32(a, bst[ks], acc);
     }
     if (want_dA) {
@@ -205,7 +213,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SR ? 2 : 3)
         bf16x8 pa[2], eb8[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
-          pa[mt] = *(const CL_LDS bf16x8*)(uintptr_t)(pb + (uint32_t)(32 * mt * kPRow + 32 * ks));
+          pa[mt] = *(const CL_LDS bf16x8*)(uintptr_t)(pb + (uint32_t)(32 * mt * kPRow) + (ks ? pk1 : pk0));
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
           eb8[nt] = fp8x8_to_bf16x8(read_tr8(eb + (uint32_t)(16 * ks * kSgdCols + 16 * ((epc + 2 * nt) ^ (s >> 1)))));
