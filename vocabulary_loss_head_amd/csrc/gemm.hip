@@ -971,27 +971,30 @@ hipError_t gemm_bn(const GemmParams& p, dim3 grid, hipStream_t st) {
 // workgroup, read as 128-byte row pieces of E and written as 128-byte row pieces of Et.
 __global__ __launch_bounds__(256) void k_transpose_chunk(const uint16_t* __restrict__ E, int64_t vlen, int64_t D,
                                                          uint16_t* __restrict__ Et, int64_t ld) {
-  constexpr int S = 72;                        // LDS row stride (halfwords), keeps 16 B alignment
-  __shared__ uint16_t t[64 * S];               // t[d][v]
+  // t[v][d] in 128-byte rows, the 16-byte chunk k of row v stored at chunk k ^ ((v / 8) mod 8):
+  // written 16 bytes a lane (two rows x 8 chunks per 16 lanes: distinct slots) and read a
+  // halfword a lane down a column (8 rows 8 apart per wave: 8 different chunks)
+  __shared__ uint4 t[64 * 8];
   const int tid = threadIdx.x;
   const int64_t v0 = (int64_t)blockIdx.x * 64, d0 = (int64_t)blockIdx.y * 64;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int r = tid / 8 + 32 * h, c = (tid % 8) * 8;
+    const int r = tid / 8 + 32 * h, k = tid % 8;
     uint4 x = {0u, 0u, 0u, 0u};
-    if (v0 + r < vlen) x = *(const uint4*)(E + (v0 + r) * D + d0 + c);
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      t[(c + 2 * j) * S + r] = (uint16_t)(w[j] & 0xffffu);
-      t[(c + 2 * j + 1) * S + r] = (uint16_t)(w[j] >> 16);
-    }
+    if (v0 + r < vlen) x = *(const uint4*)(E + (v0 + r) * D + d0 + 8 * k);
+    t[r * 8 + (k ^ ((r >> 3) & 7))] = x;
   }
   __syncthreads();
+  const uint16_t* const th = (const uint16_t*)t;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int d = tid / 8 + 32 * h, c = (tid % 8) * 8;
-    *(uint4*)(Et + (d0 + d) * ld + v0 + c) = *(const uint4*)(t + d * S + c);
+    const int d = tid / 8 + 32 * h, k = tid % 8;   // rows 8 k .. 8 k + 7 (their v / 8 is k)
+    const int col = 8 * ((d >> 3) ^ k) + (d & 7);
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = (uint32_t)th[(8 * k + 2 * i) * 64 + col] | ((uint32_t)th[(8 * k + 2 * i + 1) * 64 + col] << 16);
+    *(uint4*)(Et + (d0 + d) * ld + v0 + 8 * k) = uint4{o[0], o[1], o[2], o[3]};
   }
 }
 
