@@ -283,7 +283,8 @@ cutloss_status cutloss_bce_positive_logits(const cutloss_bce_problem* p, float* 
  *   2 row finalization (loss, lse, dA), 3 row weights + sparse item sums,
  *   4 cols sweep (dE or the fused SGD step); the chunked path records its three
  *   products per chunk as 5 logits + epilogue, 6 dA product, 7 dE product (or the
- *   fused SGD step).
+ *   fused SGD step; for FP8 E over at most 128 rows that step also forms dA, and phase 6
+ *   records no launch).
  * cutloss_profile_read synchronizes on the recorded events, writes the summed
  * milliseconds and the number of recorded launches per phase (arrays of n entries),
  * and clears the records. Enabling costs one event record per phase boundary.
