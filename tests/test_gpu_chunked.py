@@ -96,8 +96,11 @@ def _sgd_case(B, T, D, V, seed):
     dev = g["A"].device
     prob = B.bce_problem(g["A"], g["E"], g["row_ptr"], g["ids"], g["mask"], -1)
     # one workspace for the unfused backward and the SGD step: large enough for both
-    ws = B.workspace(max(B.cutloss_bce_workspace_size(prob, B.OP_BWD), B.cutloss_bce_workspace_size(prob, B.OP_BWD_SGD)),
-                     dev)
+    ws = B.workspace(max(B.cutloss_bce_workspace_size(prob, B.OP_FWD), B.cutloss_bce_workspace_size(prob, B.OP_BWD),
+                         B.cutloss_bce_workspace_size(prob, B.OP_BWD_SGD)), dev)
+    # the forward alone (for T <= 128 and D <= 768 the streaming logits product's loss-only mode)
+    lossf = torch.empty(w.T, dtype=torch.float32, device=dev)
+    B.cutloss_bce_fwd(prob, lossf, ws)
     dE = torch.empty(w.V, w.D, dtype=torch.bfloat16, device=dev)
     dA = torch.empty(w.T, w.D, dtype=torch.bfloat16, device=dev)
     B.cutloss_bce_bwd(prob, None, dA, dE, None, ws)
@@ -110,7 +113,9 @@ def _sgd_case(B, T, D, V, seed):
     check_grad(bf16_to_f64(dA), dA_ref, "dA (fp8 E)")
     # the fused call reads E before updating it: its dA and loss are those of the old E
     check_grad(bf16_to_f64(dA2), dA_ref, "dA (fused SGD call)")
-    check_loss(loss.cpu().numpy(), H.bce_loss(A64, E64, crow, cids, inp["mask"]), what="sgd fused loss")
+    loss_ref = H.bce_loss(A64, E64, crow, cids, inp["mask"])
+    check_loss(lossf.cpu().numpy(), loss_ref, what="forward loss")
+    check_loss(loss.cpu().numpy(), loss_ref, what="sgd fused loss")
     from test_gpu_parity import _check_sgd
     _check_sgd(g["E"].cpu().numpy(), inp["E"], dE_ref, w.lr)
 
@@ -125,10 +130,13 @@ def test_sgd_fp8_chunked_ragged(B):
     _sgd_case(B, 130, 192, 1537, 32)
 
 
-@pytest.mark.parametrize("T,D,V", [(1, 128, 33), (128, 1024, 700), (97, 896, 1000)])
+@pytest.mark.parametrize("T,D,V", [(1, 128, 33), (128, 1024, 700), (97, 896, 1000), (64, 256, 1000),
+                                   (128, 384, 517), (100, 512, 2049), (7, 640, 300)])
 def test_sgd_fp8_whole_rows(B, T, D, V):
     """The nearest-even FP8 SGD of heads of at most 128 rows updates whole E rows: one row,
-    a 32-item block that ends a row past the vocabulary, eight and seven 128-column slices."""
+    a 32-item block that ends a row past the vocabulary, eight and seven 128-column slices,
+    and two to five slices; at D <= 768 the logits come from the streaming logits product
+    (each of its head widths: loss-only forward, loss and gradient tile for the backward)."""
     _say(f"fp8 SGD whole rows T={T} D={D} V={V}")
     _sgd_case(B, T, D, V, 40 + T)
 
