@@ -67,7 +67,8 @@ def _check_counts(got, inp, crow, cids, rows, A64, E64):
 
 
 @pytest.mark.parametrize("T,D,V,e", [(70, 64, 3001, "bf16"), (129, 128, 1001, "bf16"), (200, 256, 4097, "bf16"),
-                                     (90, 384, 2100, "bf16"), (64, 256, 1500, "fp8"), (40, 1088, 900, "bf16")])
+                                     (90, 384, 2100, "bf16"), (64, 256, 1500, "fp8"), (40, 1088, 900, "bf16"),
+                                     (100, 640, 1700, "fp8"), (128, 768, 3000, "fp8")])
 def test_metrics_small(B, T, D, V, e, monkeypatch):
     monkeypatch.setenv("CUTLOSS_MAX_CHUNK_ITEMS", "512")
     _say(f"metrics T={T} D={D} V={V} E {e}")

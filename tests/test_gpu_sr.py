@@ -66,7 +66,8 @@ def _check_sr(E_new, E_old, items, dE_ref, lr, seed, fmt):
     assert frac < (1e-2 if fmt == "fp8" else 0.15)
 
 
-@pytest.mark.parametrize("fmt,D", [("fp8", 128), ("fp8", 768), ("bf16", 256), ("bf16", 320)])
+@pytest.mark.parametrize("fmt,D", [("fp8", 128), ("fp8", 384), ("fp8", 768), ("fp8", 1024), ("bf16", 256),
+                                   ("bf16", 320)])
 def test_sr_sgd_small(B, fmt, D, monkeypatch):
     monkeypatch.setenv("CUTLOSS_MAX_CHUNK_ITEMS", "512")
     _say(f"sr sgd {fmt} T=40 D={D} V=2000")
