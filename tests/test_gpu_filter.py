@@ -74,7 +74,7 @@ def _case(T, D, V, scale, seed):
     return make(w)
 
 
-@pytest.mark.parametrize("D", [128, 256, 384])
+@pytest.mark.parametrize("D", [64, 128, 256, 384])
 def test_filter_off_is_exact(B, D, monkeypatch):
     monkeypatch.setenv("CUTLOSS_MAX_CHUNK_ITEMS", "512")
     _say(f"filter eps=0, D={D}")
@@ -84,7 +84,7 @@ def test_filter_off_is_exact(B, D, monkeypatch):
     assert np.array_equal(a0, a1) and np.array_equal(e0, e1)
 
 
-@pytest.mark.parametrize("D", [128, 256, 384])
+@pytest.mark.parametrize("D", [64, 128, 256, 384])
 def test_filter_within_dropped_bound(B, D, monkeypatch):
     monkeypatch.setenv("CUTLOSS_MAX_CHUNK_ITEMS", "512")
     eps = 2.0 ** -12
