@@ -299,7 +299,7 @@ def _check_sgd(E_new, E_old, dE_ref, lr, fmt="fp8", max_frac=1e-2):
     assert frac < max_frac
 
 
-@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_sgd_bf16_fused_sweeps(B, D):
     """bf16 E at D in {64, 128, 256}: the cols sweep applies E <- bf16(E - lr dE) in place
     in its epilogue (dE never stored); the rows sweep of the same call reads E first."""
